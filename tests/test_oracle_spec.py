@@ -1,0 +1,79 @@
+"""Pins for speculative rounds and the low-precision read copy in the oracle.
+
+* commit(k) equals replaying the first k drafts: the replay driver's verify
+  outputs and its effective state after each commit equal those of plain
+  decode with per-draft snapshots (the definition stepped token by token).
+* Rejected drafts never touch the checkpoint: a commit that does not fold
+  leaves the checkpoint bits unchanged.
+* Read-copy isolation: the checkpoint bits after every flush are identical
+  with and without the NVFP4 read copy, while the outputs do differ (so the
+  copy is really what the non-flush steps read).
+"""
+import numpy as np
+
+import workloads as W
+from oracle import decode
+
+
+def _spec_case(batch=3, K=4, rounds=24):
+    w = W.TINY_M2.with_(batch=batch, max_draft=K, seed=11)
+    p = W.m2_params(w)
+    H0 = np.random.default_rng(12).standard_normal((batch, w.nheads, w.headdim, w.dstate)) * 0.3
+    return w, p, H0
+
+
+def test_commit_equals_replaying_accepted_drafts():
+    w, p, H0 = _spec_case()
+    K = w.max_draft
+    conv = decode.M2Conventional(H0, p["A"], p["D"])
+    rep = decode.M2Replay(H0, p["A"], p["D"], max_draft=K)
+    folds = 0
+    for rnd in range(24):
+        drafts = [W.m2_step(w, rnd * K + d, range(w.batch)) for d in range(K)]
+        acc = W.accepted_counts(w.seed, rnd, w.batch, K)
+        before = rep.ckpt.copy()
+        y_rep = rep.spec_append(drafts)
+        n0 = list(rep.ring.n_ckpt)
+        rep.spec_commit(acc)
+        y_conv = conv.spec_round(drafts, acc)
+        assert np.linalg.norm(y_rep - y_conv) <= 1e-12 * np.linalg.norm(y_conv)
+        np.testing.assert_allclose(rep.effective_state(), conv.H, rtol=1e-11, atol=1e-12)
+        for b in range(w.batch):
+            if rep.ring.n_ckpt[b] == n0[b]:
+                assert np.array_equal(rep.ckpt[b], before[b])
+            else:
+                folds += 1
+    assert folds > 0
+    assert rep.ring.err == [0] * w.batch
+
+
+def test_plain_steps_continue_after_spec():
+    w, p, H0 = _spec_case(batch=2)
+    K = w.max_draft
+    conv = decode.M2Conventional(H0, p["A"], p["D"])
+    rep = decode.M2Replay(H0, p["A"], p["D"], max_draft=K)
+    for rnd in range(5):
+        drafts = [W.m2_step(w, rnd * K + d, range(w.batch)) for d in range(K)]
+        acc = W.accepted_counts(w.seed, rnd, w.batch, K)
+        rep.spec_append(drafts)
+        rep.spec_commit(acc)
+        conv.spec_round(drafts, acc)
+    for t in range(100, 140):
+        tk = W.m2_step(w, t, range(w.batch))
+        y1, y2 = conv.step(tk), rep.step(tk)
+        assert np.linalg.norm(y2 - y1) <= 1e-12 * np.linalg.norm(y1)
+
+
+def test_read_copy_isolation():
+    w = W.TINY_M2.with_(seed=13)
+    p = W.m2_params(w)
+    H0 = np.random.default_rng(14).standard_normal((w.batch, w.nheads, w.headdim, w.dstate)).astype(np.float32)
+    plain = decode.M2Replay(H0, p["A"], p["D"], ckpt_fmt="f32")
+    rc = decode.M2Replay(H0, p["A"], p["D"], ckpt_fmt="f32", read_copy="nvfp4")
+    differ = 0.0
+    for t in range(48):
+        tk = W.m2_step(w, t, range(w.batch))
+        y1, y2 = plain.step(tk), rc.step(tk)
+        differ = max(differ, np.abs(y1 - y2).max())
+        assert np.array_equal(plain.ckpt, rc.ckpt)
+    assert differ > 1e-4
