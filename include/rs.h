@@ -1,0 +1,256 @@
+/*
+ * rs.h - C ABI of the ReplaySSM SSM-layer decode step on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (ReplaySSM news coverage, sitech.ge page, section
+ * "How ReplaySSM works"): each sequence's SSM-layer state is kept as a
+ * high-precision checkpoint plus a buffer (ring) of the most recent input
+ * records. A non-flush step appends the current input and computes the output
+ * from checkpoint + buffer without writing any state. When the 16-entry buffer
+ * fills, a flush step folds the buffered inputs into the checkpoint, writes it
+ * once and clears the buffer. Outputs equal those of conventional decoding up
+ * to floating-point rounding. Speculative decoding appends draft inputs and
+ * commits the accepted prefix by moving a pointer, with no state snapshots
+ * (same page, "Reducing state traffic and simplifying rollback"). An optional
+ * low-precision copy of the checkpoint serves reads while the recurrence keeps
+ * its own precision (same page, "Bounding quantization error").
+ *
+ * Layer types (news.hamidun.com ReplaySSM page, "Why hybrid models became the
+ * norm"): Mamba-2 and Gated DeltaNet.
+ *
+ *   Mamba-2, per sequence b and head h (group g = h / (nheads / ngroups)):
+ *     a = exp(dt * A[h]);  H = a*H + dt * x B^T;  y = H C + D[h] * x
+ *   Gated DeltaNet, per sequence b and value head h (qk head = h / (n_v / n_qk)):
+ *     alpha = exp(g);  S = alpha * S (I - beta k k^T) + beta v k^T;  o = S q
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ---------------------------------------------------------------------------
+ * Ownership. The caller allocates and owns every device buffer, sized from
+ *   the rs_layer that rs_init fills. The library allocates nothing, keeps no
+ *   global state and never synchronises; there is nothing to destroy.
+ * Pointers. Device pointers (hipMalloc'd or equivalent), 16-byte aligned.
+ *   rs_layer, rs_buffers, rs_inputs and rs_params structs themselves are host
+ *   memory, read during the call only.
+ * Streams. `stream` is a hipStream_t (NULL = the default stream). Every kernel
+ *   is enqueued on it and the call returns without waiting. Calls that touch
+ *   the same buffers must be ordered on one stream by the caller. Calls that
+ *   overlap on the same buffers race.
+ * Errors. Problems visible on the host return a negative rs_status and launch
+ *   nothing. Contract violations that depend on device-resident buffer state
+ *   (see rs_meta.err) set sticky bits in that sequence's meta record and leave
+ *   the sequence's checkpoint, buffer and counters unchanged; its outputs for
+ *   that call are not written.
+ * Initial state. The caller zero-fills `meta` (and `ring`, optionally),
+ *   writes the initial checkpoint in the layout below, and, if a read copy is
+ *   configured, calls rs_requant_read_copy once before the first step.
+ *
+ * ---------------------------------------------------------------------------
+ * Device layouts (all row-major, innermost index last)
+ * ---------------------------------------------------------------------------
+ * Mamba-2 (P = headdim, N = dstate, G = ngroups, R = ring = 16):
+ *   checkpoint  RS_F32: float [batch][nheads][N][P]; element H[b][h][p][n] is
+ *               at ((b*nheads + h)*N + n)*P + p (the state stored transposed,
+ *               headdim innermost).
+ *               RS_F16: binary16 in the same order.
+ *               RS_FP8E4M3: uint8 E4M3FN codes in the same order, then
+ *               float scale[batch][nheads] at byte offset ck_scale_off.
+ *               RS_NVFP4: an NVFP4 block (below) per matrix.
+ *   ring        in_dtype arrays at the byte offsets in rs_layer:
+ *               x [batch][nheads][R][P], B [batch][G][R][N], C [batch][G][R][N],
+ *               dt [batch][nheads][R]. Buffer entry i of sequence b (0-based,
+ *               i < len + nd) is in slot (n_ckpt + i) mod R.
+ *   inputs      x [batch][nheads][P], B and C [batch][G][N], dt [batch][nheads]
+ *               (in_dtype); drafts stack K tokens in front: [K][batch][...].
+ *   params      A, D: float [nheads].
+ *   output      y: float [batch][nheads][P]; for drafts [K][batch][nheads][P].
+ * Gated DeltaNet (dk = head_k_dim, dv = head_v_dim, Hv = n_v_heads, Hk = n_qk_heads):
+ *   checkpoint  RS_F32: float [batch][Hv][dk][dv]; element S[b][h][v][k] is at
+ *               ((b*Hv + h)*dk + k)*dv + v.
+ *   ring        q and k [batch][Hk][R][dk] (in_dtype), v [batch][Hv][R][dv]
+ *               (in_dtype), g and beta float [batch][Hv][R].
+ *   inputs      q, k [batch][Hk][dk], v [batch][Hv][dv] (in_dtype);
+ *               g (= log alpha) and beta: float [batch][Hv].
+ *   output      o: float [batch][Hv][dv].
+ * NVFP4 block (read copy, or the uniform NVFP4 checkpoint), for the stored
+ *   matrices M[b][h] of rows x cols (rows = N or dk, cols = P or dv):
+ *     codes   uint8 [batch][heads][rows][cols/2]: two E2M1 codes per byte,
+ *             even column in the low nibble; code = sign<<3 | magnitude index
+ *             into {0, .5, 1, 1.5, 2, 3, 4, 6};
+ *     scales  uint8 [batch][heads][rows][cols/16] E4M3FN block scales, at
+ *             byte offset nv_scale_off;
+ *     tscale  float [batch][heads] tensor scales, at byte offset nv_tscale_off.
+ *   Value = e2m1(code) * (e4m3(scale) * tscale). Quantization, in float32:
+ *   tscale = amax/2688 (1 if 0); scale = E4M3(block_amax / (6*tscale)),
+ *   round-to-nearest-even, saturating; code = E2M1(x / (e4m3(scale)*tscale)),
+ *   round-to-nearest-even, saturating (all zero if that divisor is 0).
+ * Snapshots (conventional mode with max_draft > 0): float
+ *   [max_draft][batch][heads][rows][cols], the state after each draft.
+ * meta: rs_meta[batch], followed by library work space (meta_bytes in all).
+ */
+#ifndef RS_H
+#define RS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t rs_status;
+
+/* status codes */
+#define RS_OK 0
+#define RS_E_ARG (-1)        /* null pointer, bad size, inconsistent shape */
+#define RS_E_DTYPE (-2)      /* unsupported dtype or dtype combination */
+#define RS_E_ALIGN (-3)      /* device pointer not 16-byte aligned */
+#define RS_E_MODE (-4)       /* call not valid for the layer's mode or config */
+#define RS_E_LAUNCH (-5)     /* a kernel launch failed (hipGetLastError) */
+#define RS_E_UNSUPPORTED (-6)/* shape outside the compiled kernel set */
+
+/* layer kinds */
+#define RS_MAMBA2 1
+#define RS_GDN 2
+
+/* modes */
+#define RS_REPLAY 0          /* checkpoint + ring (ReplaySSM) */
+#define RS_CONVENTIONAL 1    /* live state read and written every step (baseline) */
+
+/* dtypes */
+#define RS_NONE 0
+#define RS_F32 1
+#define RS_BF16 2
+#define RS_F16 3
+#define RS_FP8E4M3 4
+#define RS_NVFP4 5
+
+/* sticky device-side error bits in rs_meta.err */
+#define RS_ERR_FULL 1        /* non-flush step on a full buffer (len == ring-1) */
+#define RS_ERR_OVERFLOW 2    /* append would exceed the ring, or K out of range */
+#define RS_ERR_COMMIT 4      /* commit count outside [0, nd] */
+#define RS_ERR_PENDING 8     /* plain step while drafts are pending */
+
+typedef struct rs_config {
+  int32_t kind;          /* RS_MAMBA2 | RS_GDN */
+  int32_t mode;          /* RS_REPLAY | RS_CONVENTIONAL */
+  int32_t batch;         /* sequences, >= 1 */
+  int32_t nheads, headdim, dstate, ngroups;              /* Mamba-2 */
+  int32_t n_qk_heads, n_v_heads, head_k_dim, head_v_dim; /* Gated DeltaNet */
+  int32_t ring;          /* buffer entries; must be 16 */
+  int32_t max_draft;     /* 0 = no speculative decoding; else 1..ring/2 */
+  int32_t in_dtype;      /* RS_F32 | RS_BF16 (GDN g and beta are always float) */
+  int32_t ckpt_dtype;    /* RS_F32 | RS_F16 | RS_FP8E4M3 | RS_NVFP4 (uniform comparator) */
+  int32_t read_copy;     /* RS_NONE | RS_NVFP4 */
+  int32_t fuse_requant;  /* 1: flush and commit-fold rewrite the read copy in their epilogue */
+} rs_config;
+
+/* Per-sequence buffer counters (32 bytes). */
+typedef struct rs_meta {
+  int64_t n_ckpt;        /* tokens folded into the checkpoint */
+  int32_t len;           /* committed buffer entries */
+  int32_t nd;            /* pending draft entries */
+  int32_t err;           /* sticky RS_ERR_* bits */
+  uint32_t arrive;       /* library-internal; zero between calls */
+  int32_t reserved[2];
+} rs_meta;
+
+/* Filled by rs_init. Plain data; the caller keeps it. */
+typedef struct rs_layer {
+  rs_config cfg;
+  int32_t heads;         /* state matrices per sequence: nheads | n_v_heads */
+  int32_t in_heads;      /* B/C groups | qk heads */
+  int32_t rows, cols;    /* stored matrix: rows = dstate | dk, cols = headdim | dv */
+  uint64_t ckpt_bytes, ring_bytes, read_copy_bytes, meta_bytes, snap_bytes;
+  /* ring arrays, byte offsets into the ring buffer */
+  uint64_t ring_x_off, ring_B_off, ring_C_off, ring_dt_off;               /* Mamba-2 */
+  uint64_t ring_q_off, ring_k_off, ring_v_off, ring_g_off, ring_beta_off; /* GDN */
+  /* checkpoint extras, byte offsets into the checkpoint buffer */
+  uint64_t ck_scale_off;                     /* RS_FP8E4M3 per-matrix scales */
+  uint64_t ck_nv_scale_off, ck_nv_tscale_off;/* RS_NVFP4 checkpoint */
+  /* read copy, byte offsets into the read-copy buffer */
+  uint64_t nv_scale_off, nv_tscale_off;
+  uint64_t meta_work_off;                    /* library work space inside meta */
+  uint32_t magic;                            /* set by rs_init */
+  uint32_t reserved;
+} rs_layer;
+
+typedef struct rs_buffers {
+  void* ckpt;            /* checkpoint (or live state in conventional mode) */
+  void* ring;            /* replay mode */
+  void* read_copy;       /* when read_copy != RS_NONE */
+  void* meta;            /* replay mode: meta_bytes, zero-filled before first use */
+  void* snap;            /* conventional mode with max_draft > 0 */
+} rs_buffers;
+
+typedef struct rs_inputs {
+  const void *x, *B, *C, *dt;          /* Mamba-2 */
+  const void *q, *k, *v, *g, *beta;    /* Gated DeltaNet */
+} rs_inputs;
+
+typedef struct rs_params {
+  const float *A, *D;    /* Mamba-2 per-head; unused for GDN */
+} rs_params;
+
+/* Validate cfg and fill *out with sizes and offsets. Host only: no device
+ * call, no allocation. Returns RS_E_ARG / RS_E_DTYPE / RS_E_MODE /
+ * RS_E_UNSUPPORTED for an invalid or uncompiled configuration. */
+rs_status rs_init(const rs_config* cfg, rs_layer* out);
+
+/* Conventional decode step (sitech.ge ReplaySSM page, "How ReplaySSM works":
+ * conventional decoding reads and writes the full state at every step).
+ * Conventional-mode layers only; y receives the step output. */
+rs_status rs_step_conventional(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in,
+                               const rs_params* prm, float* y, void* stream);
+
+/* Non-flush step (same page and section): appends the current input to
+ * buffer slot (n_ckpt + len) mod 16, writes y from checkpoint (or its read
+ * copy) plus buffer, writes no state; len += 1. Replay mode. Device errors:
+ * RS_ERR_FULL if len == 15, RS_ERR_PENDING if drafts are pending. */
+rs_status rs_step_nonflush(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in,
+                           const rs_params* prm, float* y, void* stream);
+
+/* Flush step (same page and section): folds the len stored entries and the
+ * current input into the checkpoint, writes it once (and the read copy when
+ * fuse_requant), writes y; n_ckpt += len + 1, len = 0. Valid at any fill.
+ * Replay mode. Device error: RS_ERR_PENDING. */
+rs_status rs_step_flush(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in,
+                        const rs_params* prm, float* y, void* stream);
+
+/* Speculative append (same page, "Reducing state traffic and simplifying
+ * rollback": draft inputs enter the buffer until verification; verification
+ * reads outputs only, as a small matrix product, without forming
+ * intermediate states). `drafts` holds K stacked tokens; y receives the K
+ * verify outputs [K][batch][...]. Replay mode: writes the drafts to the
+ * slots after the committed entries, nd = K, no state write (device error
+ * RS_ERR_OVERFLOW when nd != 0 or len + K > 16). Conventional mode: the
+ * snapshot baseline; steps the live state through the drafts and writes the
+ * state after each draft to snap[d]. Mamba-2 only; 1 <= K <= max_draft. */
+rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inputs* drafts,
+                         int32_t K, const rs_params* prm, float* y, void* stream);
+
+/* Speculative commit (same section): accepted is a device int32[batch].
+ * Replay mode: len += accepted[b], nd = 0; rejected drafts are dropped by
+ * the pointer move alone. If then len > 16 - max_draft, the len committed
+ * entries are folded into the checkpoint (one write), n_ckpt += len, len = 0.
+ * Device error RS_ERR_COMMIT when accepted[b] is outside [0, nd].
+ * Conventional mode: live state = snap[accepted[b] - 1] where accepted[b] >= 1
+ * (values outside [0, max_draft] leave the sequence unchanged). Mamba-2 only. */
+rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted,
+                         const rs_params* prm, void* stream);
+
+/* Rewrite the whole NVFP4 read copy from the stored checkpoint (same page,
+ * "Bounding quantization error"). Needs read_copy == RS_NVFP4. Bit-identical
+ * to what a flush with fuse_requant writes for the same checkpoint. */
+rs_status rs_requant_read_copy(const rs_layer* L, const rs_buffers* buf, void* stream);
+
+/* Static string for a status code. */
+const char* rs_status_string(rs_status s);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int32_t rs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_H */

@@ -1,0 +1,261 @@
+// Device-side helpers shared by the ReplaySSM decode kernels (gfx950).
+//
+// - element conversion of the input dtypes (fp32, bf16 bit patterns);
+// - codecs of the stored-state formats (fp32, fp16, E4M3 with a per-matrix
+//   scale, NVFP4 with E4M3 block scales and an fp32 tensor scale); the NVFP4
+//   and E4M3 rules are those of the OCP microscaling / 8-bit float formats,
+//   the formats the sitech.ge ReplaySSM page ("Bounding quantization error")
+//   names for its low-precision reads;
+// - the thread -> tile mapping used by every state-streaming kernel: a stored
+//   state matrix is rows x cols (cols innermost), a 256-thread workgroup
+//   covers it in passes, each thread owns E consecutive columns of one row per
+//   pass, so reductions over rows stay in registers and only the final partial
+//   sums cross lanes;
+// - the per-sequence arrival counter that lets the last workgroup of a
+//   sequence advance that sequence's buffer counters.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "rs.h"
+
+namespace rs {
+
+constexpr int kThreads = 256;
+constexpr int kRing = 16;
+
+enum Fmt { FMT_F32 = 0, FMT_F16 = 1, FMT_FP8 = 2, FMT_NVFP4 = 3 };
+
+// ----------------------------------------------------------------------------
+// input element types
+// ----------------------------------------------------------------------------
+struct bf16 {
+  uint16_t u;
+};
+
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16 v) { return __uint_as_float(static_cast<uint32_t>(v.u) << 16); }
+
+// ----------------------------------------------------------------------------
+// E4M3FN and E2M1 codecs (round to nearest, ties to even, saturating)
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float e4m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
+  float mag = (e == 0) ? static_cast<float>(m) * 0.001953125f  // m * 2^-9
+                       : __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
+  return (code & 0x80u) ? -mag : mag;
+}
+
+// Non-negative finite float -> E4M3FN code 0..126.
+__device__ __forceinline__ uint32_t e4m3_encode_mag(float x) {
+  if (!(x < 448.0f)) return 0x7Eu;                       // saturate (also 448 itself)
+  if (x < 0.015625f) {                                   // below 2^-6: subnormal grid 2^-9
+    return static_cast<uint32_t>(rintf(x * 512.0f));     // 8 -> code 8 = 2^-6, still right
+  }
+  const uint32_t bits = __float_as_uint(x);
+  int e = static_cast<int>((bits >> 23) & 255u) - 127;   // 2^e <= x < 2^(e+1), e in [-6, 8]
+  const float mant = __uint_as_float((bits & 0x7FFFFFu) | 0x3F800000u);  // [1, 2)
+  uint32_t m = static_cast<uint32_t>(rintf((mant - 1.0f) * 8.0f));
+  if (m == 8u) { m = 0u; ++e; }
+  return (static_cast<uint32_t>(e + 7) << 3) | m;
+}
+
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  // magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
+  const uint32_t i = code & 7u;
+  // i < 4: 0.5 i;  i >= 4: 2^(1 + (i-4)/2) * (1.5 if i odd else 1)
+  float mag = (i < 4u) ? 0.5f * static_cast<float>(i)
+                       : static_cast<float>(1u << (((i - 4u) >> 1) + 1u)) * ((i & 1u) ? 1.5f : 1.0f);
+  return (code & 8u) ? -mag : mag;
+}
+
+// float -> E2M1 code (sign in bit 3), nearest-even, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_encode(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 31) << 3;
+  const float m = fabsf(q);
+  uint32_t c;
+  if (m <= 0.25f) c = 0;
+  else if (m < 0.75f) c = 1;
+  else if (m <= 1.25f) c = 2;
+  else if (m < 1.75f) c = 3;
+  else if (m <= 2.5f) c = 4;
+  else if (m < 3.5f) c = 5;
+  else if (m <= 5.0f) c = 6;
+  else c = 7;
+  return sign | c;
+}
+
+// ----------------------------------------------------------------------------
+// streaming (nontemporal) vector loads and stores
+// ----------------------------------------------------------------------------
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t vu4 __attribute__((ext_vector_type(4)));
+typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 nt_load(const float4* p) {
+  const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 nt_load(const uint4* p) {
+  const vu4 v = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 nt_load(const uint2* p) {
+  const vu2 v = __builtin_nontemporal_load(reinterpret_cast<const vu2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t nt_load(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ void nt_store(float4 v, float4* p) {
+  vf4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<vf4*>(p));
+}
+__device__ __forceinline__ void nt_store(uint4 v, uint4* p) {
+  vu4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<vu4*>(p));
+}
+__device__ __forceinline__ void nt_store(uint2 v, uint2* p) {
+  vu2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<vu2*>(p));
+}
+__device__ __forceinline__ void nt_store(uint32_t v, uint32_t* p) { __builtin_nontemporal_store(v, p); }
+
+// ----------------------------------------------------------------------------
+// stored-state access
+// ----------------------------------------------------------------------------
+// One layer's state buffer in a given format. `data` points at matrix 0;
+// matrix t (t = b*heads + h) starts at t*rows*cols elements.
+struct StateBuf {
+  void* data;          // f32 / f16 values, E4M3 codes, or packed E2M1 codes
+  uint8_t* nv_scale;   // NVFP4 block scales [t][rows][cols/16]
+  float* tscale;       // FP8 per-matrix scale or NVFP4 tensor scale [t]
+};
+
+// Thread -> (row, column chunk) mapping of a rows x cols matrix: each thread
+// owns E consecutive columns of one row per pass.
+template <int E_, int NR, int NC>
+struct TileMap {
+  static constexpr int E = E_;                         // consecutive columns per thread
+  static constexpr int TPR = NC / E;                   // threads per row
+  static constexpr int RPP = kThreads / TPR;           // rows per pass
+  static constexpr int PASSES = (NR + RPP - 1) / RPP;
+  static_assert(NC % E == 0, "cols must be a multiple of the chunk");
+  static_assert(TPR >= 1 && TPR <= 64 && (64 % TPR) == 0, "a row must fit in one wavefront");
+};
+
+// Raw (undecoded) chunk of E elements of format FMT. fp32 takes E = 4 or 8;
+// the other formats take E = 8 (an NVFP4 block of 16 spans two threads).
+template <int FMT, int E>
+struct Raw;
+template <>
+struct Raw<FMT_F32, 4> { float4 v; };
+template <>
+struct Raw<FMT_F32, 8> { float4 v, w; };
+template <>
+struct Raw<FMT_F16, 8> { uint4 v; };
+template <>
+struct Raw<FMT_FP8, 8> { uint2 v; };
+template <>
+struct Raw<FMT_NVFP4, 8> { uint32_t v; uint32_t s; };
+
+template <int FMT, int E, int NC>
+__device__ __forceinline__ Raw<FMT, E> load_chunk(const StateBuf& sb, size_t mat, int NR, int row, int c) {
+  Raw<FMT, E> r;
+  const size_t elem = (mat * NR + row) * NC + static_cast<size_t>(c) * E;
+  if constexpr (FMT == FMT_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(sb.data) + elem);
+    r.v = nt_load(p);
+    if constexpr (E == 8) r.w = nt_load(p + 1);
+  } else if constexpr (FMT == FMT_F16) {
+    r.v = nt_load(reinterpret_cast<const uint4*>(static_cast<const __half*>(sb.data) + elem));
+  } else if constexpr (FMT == FMT_FP8) {
+    r.v = nt_load(reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(sb.data) + elem));
+  } else {
+    r.v = nt_load(reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(sb.data) + elem / 2));
+    r.s = sb.nv_scale[elem / 16];
+  }
+  return r;
+}
+
+// Per-matrix scalar needed to decode (FP8 scale, NVFP4 tensor scale).
+template <int FMT>
+__device__ __forceinline__ float mat_scale(const StateBuf& sb, size_t mat) {
+  if constexpr (FMT == FMT_FP8 || FMT == FMT_NVFP4) return sb.tscale[mat];
+  return 1.0f;
+}
+
+template <int FMT, int E>
+__device__ __forceinline__ void decode_chunk(const Raw<FMT, E>& r, float ms, float* v) {
+  if constexpr (FMT == FMT_F32) {
+    v[0] = r.v.x; v[1] = r.v.y; v[2] = r.v.z; v[3] = r.v.w;
+    if constexpr (E == 8) { v[4] = r.w.x; v[5] = r.w.y; v[6] = r.w.z; v[7] = r.w.w; }
+  } else if constexpr (FMT == FMT_F16) {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] & 0xFFFFu)));
+      v[2 * i + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
+    }
+  } else if constexpr (FMT == FMT_FP8) {
+    const uint32_t w[2] = {r.v.x, r.v.y};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e4m3_value((w[i >> 2] >> ((i & 3) * 8)) & 0xFFu) * ms;
+  } else {
+    const float sd = e4m3_value(r.s) * ms;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e2m1_value((r.v >> (4 * i)) & 15u) * sd;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// wavefront helpers
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum_stride(float v, int from) {
+  // sum over lanes that agree on (lane mod from); from is a power of two < 64
+  for (int off = from; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float group_sum16(float v) {
+  // sum over aligned groups of 16 lanes
+  v += __shfl_xor(v, 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Workgroups are handed to the eight XCDs round-robin; give each XCD a
+// contiguous range of tiles so the heads of one sequence (which share that
+// sequence's B/C or k/q records) meet in the same L2.
+__device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
+  if ((nblocks & 7) != 0) return bid;
+  const int per = nblocks >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+// Arrival at the end of a per-sequence step: the last of `expected`
+// workgroups of the sequence applies `update` to its meta record and resets
+// the counter. Every workgroup of the sequence read the record before
+// arriving, so nobody reads it after it changes within this launch.
+template <typename F>
+__device__ __forceinline__ void arrive_and_update(rs_meta* m, int expected, F update) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t old = atomicAdd(&m->arrive, 1u);
+    if (old == static_cast<uint32_t>(expected - 1)) {
+      update(m);
+      atomicExch(&m->arrive, 0u);
+    }
+  }
+}
+
+}  // namespace rs

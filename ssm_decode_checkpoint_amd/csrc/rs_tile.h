@@ -1,0 +1,241 @@
+// Workgroup-level state-tile routines shared by the Mamba-2 and Gated DeltaNet
+// kernels: load a stored matrix into registers, reduce it against vectors,
+// round it to a checkpoint format, and store it (with the per-matrix and
+// per-block scales that format needs).
+#pragma once
+
+#include "rs_device.h"
+
+namespace rs {
+
+// A stored rows x cols matrix held by one 256-thread workgroup:
+// v[k][i] = M[row(k)][col0() + i] with c = tid % TPR, row(k) = tid / TPR + k*RPP.
+// Rows past the matrix hold zeros.
+template <int E, int NR, int NC>
+struct RegTile {
+  using TM = TileMap<E, NR, NC>;
+  static constexpr int P = TM::PASSES;
+  float v[P][E];
+
+  __device__ __forceinline__ static int col0() { return static_cast<int>(threadIdx.x % TM::TPR) * E; }
+  __device__ __forceinline__ static int row(int k) { return static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP; }
+};
+
+template <int FMT, int E, int NR, int NC>
+struct RawTile {
+  using TM = TileMap<E, NR, NC>;
+  Raw<FMT, E> r[TM::PASSES];
+  float ms;
+
+  __device__ __forceinline__ void issue(const StateBuf& sb, size_t mat) {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
+      if (row < NR) r[k] = load_chunk<FMT, E, NC>(sb, mat, NR, row, static_cast<int>(threadIdx.x % TM::TPR));
+    }
+    ms = mat_scale<FMT>(sb, mat);
+  }
+  __device__ __forceinline__ void decode(RegTile<E, NR, NC>& dst, float mult = 1.0f) const {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
+      float t[E];
+      if (row < NR) {
+        decode_chunk<FMT, E>(r[k], ms, t);
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) t[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < E; ++i) dst.v[k][i] = t[i] * mult;
+    }
+  }
+};
+
+// out[q][col] = sum_rows M[row][col] * w[q*ws + row] for Q weight vectors in
+// LDS. `red` is LDS scratch of 4*Q*NC floats; `out` is LDS of Q*NC floats.
+// Contains workgroup barriers; all threads must call.
+template <int Q, int E, int NR, int NC>
+__device__ __forceinline__ void tile_matvec(const RegTile<E, NR, NC>& M, const float* w, int ws, float* red,
+                                            float* out) {
+  using TM = TileMap<E, NR, NC>;
+  float acc[Q][E];
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[q][i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < TM::PASSES; ++k) {
+    const int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
+    if (row < NR) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
+        const float wr = w[q * ws + row];
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[q][i] += M.v[k][i] * wr;
+      }
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int q = 0; q < Q; ++q)
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[q][i] = wave_sum_stride(acc[q][i], TM::TPR);
+  if (lane < TM::TPR) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q)
+#pragma unroll
+      for (int i = 0; i < E; ++i) red[(wave * Q + q) * NC + lane * E + i] = acc[q][i];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < Q * NC; idx += kThreads) {
+    out[idx] = (red[idx] + red[Q * NC + idx]) + (red[2 * Q * NC + idx] + red[3 * Q * NC + idx]);
+  }
+  __syncthreads();
+}
+
+// Workgroup max of |M|; every thread gets it. Contains barriers.
+template <int E, int NR, int NC>
+__device__ __forceinline__ float tile_absmax(const RegTile<E, NR, NC>& M, float* scratch4) {
+  float m = 0.0f;
+#pragma unroll
+  for (int k = 0; k < RegTile<E, NR, NC>::P; ++k)
+#pragma unroll
+    for (int i = 0; i < E; ++i) m = fmaxf(m, fabsf(M.v[k][i]));
+  m = wave_max(m);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch4[threadIdx.x >> 6] = m;
+  __syncthreads();
+  return fmaxf(fmaxf(scratch4[0], scratch4[1]), fmaxf(scratch4[2], scratch4[3]));
+}
+
+// FP8 (E4M3, one scale per matrix) code of x given the matrix scale.
+__device__ __forceinline__ uint32_t fp8_code(float x, float sc) {
+  return e4m3_encode_mag(fabsf(x) / sc) | ((__float_as_uint(x) >> 31) << 7);
+}
+
+__device__ __forceinline__ float fp8_scale_of(float amax) {
+  const float sc = amax / 448.0f;
+  return sc == 0.0f ? 1.0f : sc;
+}
+
+__device__ __forceinline__ float nvfp4_tscale_of(float amax) {
+  const float ts = amax / 2688.0f;
+  return ts == 0.0f ? 1.0f : ts;
+}
+
+// NVFP4 block scale code and its decoded scale for a block whose |max| is bm.
+__device__ __forceinline__ uint32_t nvfp4_block_code(float bm, float ts) { return e4m3_encode_mag(bm / (6.0f * ts)); }
+
+__device__ __forceinline__ uint32_t nvfp4_code(float x, float sd) { return (sd == 0.0f) ? 0u : e2m1_encode(x / sd); }
+
+// Replace M by the value it reads back as after being stored in FMT (scales
+// computed from M itself, as tile_store does). All threads must call.
+template <int FMT, int E, int NR, int NC>
+__device__ __forceinline__ void tile_round_trip(RegTile<E, NR, NC>& M, float* scratch4) {
+  if constexpr (FMT == FMT_F16) {
+#pragma unroll
+    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k)
+#pragma unroll
+      for (int i = 0; i < E; ++i) M.v[k][i] = __half2float(__float2half_rn(M.v[k][i]));
+  } else if constexpr (FMT == FMT_FP8) {
+    const float sc = fp8_scale_of(tile_absmax(M, scratch4));
+#pragma unroll
+    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k)
+#pragma unroll
+      for (int i = 0; i < E; ++i) M.v[k][i] = e4m3_value(fp8_code(M.v[k][i], sc)) * sc;
+  } else if constexpr (FMT == FMT_NVFP4) {
+    static_assert(E == 8, "NVFP4 blocks span two threads of eight columns");
+    const float ts = nvfp4_tscale_of(tile_absmax(M, scratch4));
+#pragma unroll
+    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
+      float bm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) bm = fmaxf(bm, fabsf(M.v[k][i]));
+      bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+      const float sd = e4m3_value(nvfp4_block_code(bm, ts)) * ts;
+#pragma unroll
+      for (int i = 0; i < E; ++i) M.v[k][i] = e2m1_value(nvfp4_code(M.v[k][i], sd)) * sd;
+    }
+  }
+}
+
+// Store M into sb in format FMT. FP8 and NVFP4 compute their scales from M.
+// All threads must call.
+template <int FMT, int E, int NR, int NC>
+__device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const RegTile<E, NR, NC>& M,
+                                           float* scratch4) {
+  using TM = TileMap<E, NR, NC>;
+  const int c = static_cast<int>(threadIdx.x % TM::TPR);
+  if constexpr (FMT == FMT_F32) {
+    float* base = static_cast<float*>(sb.data) + mat * NR * NC;
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = RegTile<E, NR, NC>::row(k);
+      if (row < NR) {
+        float4* dst = reinterpret_cast<float4*>(base + row * NC + c * E);
+        nt_store(make_float4(M.v[k][0], M.v[k][1], M.v[k][2], M.v[k][3]), dst);
+        if constexpr (E == 8)
+          nt_store(make_float4(M.v[k][4], M.v[k][5], M.v[k][6], M.v[k][7]), dst + 1);
+      }
+    }
+  } else if constexpr (FMT == FMT_F16) {
+    static_assert(E == 8, "fp16 state chunks are eight elements");
+    __half* base = static_cast<__half*>(sb.data) + mat * NR * NC;
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = RegTile<E, NR, NC>::row(k);
+      if (row < NR) {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = __half_as_ushort(__float2half_rn(M.v[k][2 * i]));
+          const uint32_t hi = __half_as_ushort(__float2half_rn(M.v[k][2 * i + 1]));
+          w[i] = lo | (hi << 16);
+        }
+        nt_store(make_uint4(w[0], w[1], w[2], w[3]),
+                                    reinterpret_cast<uint4*>(base + row * NC + c * E));
+      }
+    }
+  } else if constexpr (FMT == FMT_FP8) {
+    static_assert(E == 8, "fp8 state chunks are eight elements");
+    const float sc = fp8_scale_of(tile_absmax(M, scratch4));
+    uint8_t* base = static_cast<uint8_t*>(sb.data) + mat * NR * NC;
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = RegTile<E, NR, NC>::row(k);
+      if (row < NR) {
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i >> 2] |= fp8_code(M.v[k][i], sc) << ((i & 3) * 8);
+        nt_store(make_uint2(w[0], w[1]), reinterpret_cast<uint2*>(base + row * NC + c * E));
+      }
+    }
+    if (threadIdx.x == 0) sb.tscale[mat] = sc;
+  } else {
+    static_assert(E == 8, "NVFP4 blocks span two threads of eight columns");
+    const float ts = nvfp4_tscale_of(tile_absmax(M, scratch4));
+    uint8_t* base = static_cast<uint8_t*>(sb.data) + mat * NR * NC / 2;
+    uint8_t* sbase = sb.nv_scale + mat * NR * NC / 16;
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = RegTile<E, NR, NC>::row(k);
+      float bm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(M.v[k][i]));
+      bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+      const uint32_t s = nvfp4_block_code(bm, ts);
+      const float sd = e4m3_value(s) * ts;
+      uint32_t w = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w |= nvfp4_code(M.v[k][i], sd) << (4 * i);
+      if (row < NR) {
+        nt_store(w, reinterpret_cast<uint32_t*>(base + (row * NC + c * 8) / 2));
+        if ((c & 1) == 0) sbase[(row * NC + c * 8) / 16] = static_cast<uint8_t>(s);
+      }
+    }
+    if (threadIdx.x == 0) sb.tscale[mat] = ts;
+  }
+}
+
+}  // namespace rs

@@ -1,0 +1,131 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point
+include/rs.h declares, sizes buffers as the header documents, and rejects
+invalid configurations and arguments before launching anything. No device
+call is made here."""
+import ctypes as C
+import re
+import os
+
+import pytest
+
+import ssm_decode_checkpoint_amd as rs
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rs.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    return sorted(set(re.findall(r"^\s*(?:rs_status|const char\*|int32_t)\s+(rs_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) >= {"rs_init", "rs_step_conventional", "rs_step_nonflush", "rs_step_flush",
+                          "rs_spec_append", "rs_spec_commit", "rs_requant_read_copy"}
+    lib = rs.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert rs.rs_version() >= 100
+    assert rs.status_string(rs.RS_E_ALIGN).startswith("pointer")
+
+
+def test_struct_sizes_match_header():
+    assert C.sizeof(rs.RsConfig) == 17 * 4
+    assert C.sizeof(rs.RsBuffers) == 5 * 8
+    assert C.sizeof(rs.RsInputs) == 9 * 8
+
+
+def _m2(**kw):
+    base = dict(batch=256, nheads=128, headdim=64, dstate=128, ngroups=8)
+    base.update(kw)
+    b = base.pop("batch")
+    return rs.make_config(rs.RS_MAMBA2, b, **base)
+
+
+def test_mamba2_layout_sizes():
+    st, L = rs.rs_init(_m2())
+    assert st == rs.RS_OK
+    assert L.ckpt_bytes == 256 * 128 * 64 * 128 * 4          # 4 MiB per sequence, fp32
+    assert (L.heads, L.in_heads, L.rows, L.cols) == (128, 8, 128, 64)
+    ring = 256 * 16 * (128 * 64 + 2 * 8 * 128 + 128) * 2    # x, B, C, dt bf16, 16 slots
+    assert ring <= L.ring_bytes < ring + 4 * 256
+    assert L.ring_x_off == 0 and L.ring_B_off >= 256 * 128 * 16 * 64 * 2
+    assert L.meta_bytes >= 256 * 32 and L.read_copy_bytes == 0 and L.snap_bytes == 0
+    st, L = rs.rs_init(_m2(read_copy=rs.RS_NVFP4))
+    mats = 256 * 128
+    assert L.read_copy_bytes >= mats * (8192 // 2 + 8192 // 16 + 4)
+    assert L.nv_scale_off >= mats * 4096 and L.nv_tscale_off >= L.nv_scale_off + mats * 512
+    st, L = rs.rs_init(_m2(mode=rs.RS_CONVENTIONAL, max_draft=4, batch=512))
+    assert L.snap_bytes == 4 * 512 * 128 * 64 * 128 * 4 and L.ring_bytes == 0
+    st, L = rs.rs_init(_m2(ckpt_dtype=rs.RS_FP8E4M3))
+    assert L.ckpt_bytes >= mats * 8192 + mats * 4 and L.ck_scale_off >= mats * 8192
+
+
+def test_gdn_layout_sizes():
+    cfg = rs.make_config(rs.RS_GDN, 256, n_qk_heads=16, n_v_heads=32, head_k_dim=128, head_v_dim=128)
+    st, L = rs.rs_init(cfg, raise_on_error=False)
+    assert st == rs.RS_OK or st == rs.RS_E_UNSUPPORTED
+    if st == rs.RS_OK:
+        assert L.ckpt_bytes == 256 * 32 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ring=8), rs.RS_E_ARG),
+    (dict(batch=0), rs.RS_E_ARG),
+    (dict(ngroups=3), rs.RS_E_ARG),
+    (dict(dstate=96), rs.RS_E_UNSUPPORTED),
+    (dict(in_dtype=rs.RS_F16), rs.RS_E_DTYPE),
+    (dict(ckpt_dtype=rs.RS_BF16), rs.RS_E_DTYPE),
+    (dict(read_copy=rs.RS_F16), rs.RS_E_DTYPE),
+    (dict(ckpt_dtype=rs.RS_NVFP4, read_copy=rs.RS_NVFP4), rs.RS_E_DTYPE),
+    (dict(mode=rs.RS_CONVENTIONAL, ckpt_dtype=rs.RS_F16), rs.RS_E_DTYPE),
+    (dict(mode=7), rs.RS_E_MODE),
+    (dict(max_draft=9), rs.RS_E_ARG),
+    (dict(fuse_requant=2), rs.RS_E_ARG),
+])
+def test_init_rejects(kw, code):
+    st, _ = rs.rs_init(_m2(**kw), raise_on_error=False)
+    assert st == code
+
+
+def test_calls_reject_before_launch():
+    _, L = rs.rs_init(_m2(batch=2, nheads=8, headdim=16, dstate=16, ngroups=1))
+    lib = rs.lib()
+    y = C.c_void_p(0x1000)
+    bufs = rs.RsBuffers(0x1000, 0x2000, None, 0x3000, None)
+    inp = rs.RsInputs(0x1000, 0x1000, 0x1000, 0x1000, None, None, None, None, None)
+    prm = rs.RsParams(0x1000, 0x1000)
+    # uninitialised layer
+    assert lib.rs_step_nonflush(C.byref(rs.RsLayer()), C.byref(bufs), C.byref(inp), C.byref(prm), y, None) == rs.RS_E_ARG
+    # null output / null input pointers
+    assert lib.rs_step_nonflush(C.byref(L), C.byref(bufs), C.byref(inp), C.byref(prm), None, None) == rs.RS_E_ARG
+    bad = rs.RsInputs(0x1000, None, 0x1000, 0x1000, None, None, None, None, None)
+    assert lib.rs_step_flush(C.byref(L), C.byref(bufs), C.byref(bad), C.byref(prm), y, None) == rs.RS_E_ARG
+    # misaligned pointers
+    mis = rs.RsInputs(0x1004, 0x1000, 0x1000, 0x1000, None, None, None, None, None)
+    assert lib.rs_step_nonflush(C.byref(L), C.byref(bufs), C.byref(mis), C.byref(prm), y, None) == rs.RS_E_ALIGN
+    assert lib.rs_step_nonflush(C.byref(L), C.byref(bufs), C.byref(inp), C.byref(prm), C.c_void_p(0x1008), None) == rs.RS_E_ALIGN
+    misb = rs.RsBuffers(0x1010, 0x2004, None, 0x3000, None)
+    assert lib.rs_step_nonflush(C.byref(L), C.byref(misb), C.byref(inp), C.byref(prm), y, None) == rs.RS_E_ALIGN
+    # mode mismatches
+    assert lib.rs_step_conventional(C.byref(L), C.byref(bufs), C.byref(inp), C.byref(prm), y, None) == rs.RS_E_MODE
+    assert lib.rs_spec_append(C.byref(L), C.byref(bufs), C.byref(inp), 2, C.byref(prm), y, None) == rs.RS_E_MODE
+    assert lib.rs_spec_commit(C.byref(L), C.byref(bufs), C.c_void_p(0x1000), C.byref(prm), None) == rs.RS_E_MODE
+    assert lib.rs_requant_read_copy(C.byref(L), C.byref(bufs), None) == rs.RS_E_MODE
+    # draft count out of range on a speculative layer
+    _, Ls = rs.rs_init(_m2(batch=2, nheads=8, headdim=16, dstate=16, ngroups=1, max_draft=4))
+    assert lib.rs_spec_append(C.byref(Ls), C.byref(bufs), C.byref(inp), 5, C.byref(prm), y, None) == rs.RS_E_ARG
+    assert lib.rs_spec_append(C.byref(Ls), C.byref(bufs), C.byref(inp), 0, C.byref(prm), y, None) == rs.RS_E_ARG
+    # conventional spec layer without snapshot buffer
+    _, Lc = rs.rs_init(_m2(batch=2, nheads=8, headdim=16, dstate=16, ngroups=1, max_draft=4,
+                           mode=rs.RS_CONVENTIONAL))
+    nosnap = rs.RsBuffers(0x1000, None, None, None, None)
+    assert lib.rs_spec_append(C.byref(Lc), C.byref(nosnap), C.byref(inp), 4, C.byref(prm), y, None) == rs.RS_E_ARG
+    assert lib.rs_step_nonflush(C.byref(Lc), C.byref(nosnap), C.byref(inp), C.byref(prm), y, None) == rs.RS_E_MODE
+    # replay layer without ring/meta
+    noring = rs.RsBuffers(0x1000, None, None, None, None)
+    assert lib.rs_step_nonflush(C.byref(L), C.byref(noring), C.byref(inp), C.byref(prm), y, None) == rs.RS_E_ARG
+    # read copy configured but missing
+    _, Lr = rs.rs_init(_m2(batch=2, nheads=8, headdim=16, dstate=16, ngroups=1, read_copy=rs.RS_NVFP4))
+    assert lib.rs_step_nonflush(C.byref(Lr), C.byref(bufs), C.byref(inp), C.byref(prm), y, None) == rs.RS_E_ARG
+    assert lib.rs_requant_read_copy(C.byref(Lr), C.byref(bufs), None) == rs.RS_E_ARG
