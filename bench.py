@@ -34,7 +34,7 @@ RING = 16
 HBM_PEAK_GBS = 8000.0
 METRIC = "SSM-layer decode tokens/s at batch 256 + achieved HBM GB/s (% of peak) vs conventional"
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["ssm_decode_checkpoint_amd/csrc/rs_mamba2.hip", "ssm_decode_checkpoint_amd/csrc/rs_tile.h",
+KERNEL_SOURCES = ["ssm_decode_checkpoint_amd/csrc/rs_mamba2_kernels.h", "ssm_decode_checkpoint_amd/csrc/rs_tile.h",
                   "ssm_decode_checkpoint_amd/csrc/rs_device.h"]
 
 
@@ -242,7 +242,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed windows")
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
-    ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences in the CPU oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -252,7 +252,7 @@ def main():
         sys.exit(2)
     out = run_gpu(args)
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(W.M2_NEMOTRON, args.cpu_seqs)
+        out["cpu_baseline"] = cpu_baseline(W.M2_NEMOTRON, args.cpu_seqs, windows=2)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -243,13 +243,15 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
 
 // Arrival at the end of a per-sequence step: the last of `expected`
 // workgroups of the sequence applies `update` to its meta record and resets
-// the counter. Every workgroup of the sequence read the record before
-// arriving, so nobody reads it after it changes within this launch.
+// the counter. Every workgroup of the sequence consumed its read of the
+// record before arriving, so nobody reads it after it changes within this
+// launch; the next launch sees the update through the kernel boundary. No
+// device-wide fence is needed (on gfx950 one would write back and invalidate
+// the XCD's whole L2 from every workgroup).
 template <typename F>
 __device__ __forceinline__ void arrive_and_update(rs_meta* m, int expected, F update) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
     const uint32_t old = atomicAdd(&m->arrive, 1u);
     if (old == static_cast<uint32_t>(expected - 1)) {
       update(m);

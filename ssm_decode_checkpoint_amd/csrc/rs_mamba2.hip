@@ -1,697 +1,27 @@
-// Mamba-2 decode kernels for gfx950: conventional read-modify-write step,
-// ReplaySSM non-flush and flush steps, speculative append / commit (ReplaySSM
-// and the snapshot baseline), and the NVFP4 read-copy quantizer.
-//
-// Per sequence b and head h (group g = h / heads_per_group), the layer is
-//   a = exp(dt*A);  H = a*H + dt*x B^T;  y = H C + D*x
-// and with checkpoint H0 and buffer entries 1..j (entry j the current token)
-//   y_j = l_j (H0 C_j) + sum_i w_{j,i} dt_i (B_i.C_j) x_i + D x_j
-//   fold: H = l_m H0 + sum_i (w_{m,i} dt_i x_i) B_i^T
-// with l_j = prod_{l<=j} a_l and w_{j,i} = prod_{i<l<=j} a_l (sitech.ge
-// ReplaySSM page, "How ReplaySSM works": outputs from checkpoint + buffer on
-// non-flush steps, one checkpoint write per window on the flush step).
-//
-// Work decomposition: one 256-thread workgroup per (sequence, head) state
-// matrix, stored transposed as [dstate][headdim] so that y = H C is a sum over
-// rows that each thread accumulates in registers. The buffer records the
-// workgroup needs (<= 16 x, B, dt and the current C) are staged in LDS while
-// the state loads are in flight. Decay weights are direct products of the
-// per-entry factors exp(dt*A).
-#include "rs_device.h"
-#include "rs_tile.h"
+// Mamba-2 shape dispatch: each compiled (dstate, headdim) pair has its kernels
+// instantiated in its own translation unit (rs_m2_<rows>x<cols>.hip).
 #include "rs_internal.h"
 
 namespace rs {
 
-// ----------------------------------------------------------------------------
-// staging of buffer records into LDS
-// ----------------------------------------------------------------------------
 template <int NR, int NC>
-struct M2Smem {
-  float B[kRing][NR];
-  float X[kRing][NC];
-  float Cw[8][NR];        // C vectors the outputs are read with (current token, or drafts)
-  float dt[kRing];
-  float a[kRing];         // exp(dt*A)
-  float w[8][kRing];      // per-output weights  w_{j,i} dt_i (B_i . C_j)
-  float L[8];             // l_j per output
-  float red[4 * 8 * NC];  // reduction scratch
-  float out[8 * NC];      // matvec results
-  float xt[kRing][NC];    // fold coefficients w_{m,i} dt_i x_i
-  float s4[4];
-};
+void m2_launch_shape(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st);
 
-// Where buffer entry e of the current window comes from: the ring (e < nring)
-// or a token array (entries nring.. come from `tok` stacked with stride tstride).
-template <typename TIN>
-struct EntrySrc {
-  const TIN* ring;      // this sequence/head (or group) ring base: [kRing][len]
-  const TIN* tok;       // first new token's record
-  size_t tstride;       // elements between consecutive new tokens
-  long long nck;        // n_ckpt
-  int nring;            // entries held in the ring
-  int width;            // record length
-  __device__ __forceinline__ const TIN* at(int e) const {
-    return e < nring ? ring + static_cast<size_t>((nck + e) & (kRing - 1)) * width
-                     : tok + static_cast<size_t>(e - nring) * tstride;
-  }
-};
-
-template <typename TIN>
-__device__ __forceinline__ void stage_rows(float* dst, int stride, const EntrySrc<TIN>& src, int n) {
-  for (int idx = threadIdx.x; idx < n * src.width; idx += kThreads) {
-    const int e = idx / src.width, r = idx - e * src.width;
-    dst[e * stride + r] = to_f(src.at(e)[r]);
-  }
-}
-
-// a[e] = exp(dt_e * A) for e < n.
-__device__ __forceinline__ void stage_decays(float* a, const float* dt, float A, int n) {
-  if (static_cast<int>(threadIdx.x) < n) a[threadIdx.x] = expf(dt[threadIdx.x] * A);
-}
-
-// For outputs q = 0..nq-1 reading entries 0..J_q-1 (J_q = j0 + q):
-//   L[q] = prod_{l<J_q} a_l;  w[q][e] = prod_{e<l<J_q} a_l * dt_e * (B_e . C_q)
-// Dots use groups of 16 lanes (one per (q, e) pair per round).
-template <int NR, int NC>
-__device__ __forceinline__ void output_weights(M2Smem<NR, NC>& s, int j0, int nq) {
-  const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
-  for (int pair = grp; pair < nq * kRing; pair += kThreads / 16) {
-    const int q = pair / kRing, e = pair - q * kRing;
-    const int J = j0 + q;
-    float part = 0.0f;
-    if (e < J)
-      for (int n = ln; n < NR; n += 16) part += s.B[e][n] * s.Cw[q][n];
-    part = group_sum16(part);
-    if (ln == 0 && e < J) {
-      float w = 1.0f;
-      for (int l = e + 1; l < J; ++l) w *= s.a[l];
-      s.w[q][e] = w * s.dt[e] * part;
-    }
-  }
-  if (static_cast<int>(threadIdx.x) < nq) {
-    const int J = j0 + threadIdx.x;
-    float L = 1.0f;
-    for (int l = 0; l < J; ++l) L *= s.a[l];
-    s.L[threadIdx.x] = L;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// conventional step (baseline): read + write the full state
-// ----------------------------------------------------------------------------
-template <typename TIN, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_conv_kernel(M2Args a) {
-  constexpr int E = 4;
-  __shared__ M2Smem<NR, NC> s;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  RawTile<FMT_F32, E, NR, NC> raw;
-  raw.issue(a.ck, tile);
-  const TIN* inB = static_cast<const TIN*>(a.B) + (static_cast<size_t>(b) * a.ngroups + g) * NR;
-  const TIN* inC = static_cast<const TIN*>(a.C) + (static_cast<size_t>(b) * a.ngroups + g) * NR;
-  const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
-  for (int i = threadIdx.x; i < NR; i += kThreads) {
-    s.B[0][i] = to_f(inB[i]);
-    s.Cw[0][i] = to_f(inC[i]);
-  }
-  for (int i = threadIdx.x; i < NC; i += kThreads) s.X[0][i] = to_f(inX[i]);
-  __syncthreads();
-  const float dt = to_f(static_cast<const TIN*>(a.dt)[tile]);
-  const float decay = expf(dt * a.A[h]);
-  RegTile<E, NR, NC> H;
-  raw.decode(H);
-  const int c0 = RegTile<E, NR, NC>::col0();
-  float dtx[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) dtx[i] = dt * s.X[0][c0 + i];
-#pragma unroll
-  for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
-    const int row = RegTile<E, NR, NC>::row(k);
-    if (row < NR) {
-      const float br = s.B[0][row];
-#pragma unroll
-      for (int i = 0; i < E; ++i) H.v[k][i] = decay * H.v[k][i] + dtx[i] * br;
-    }
-  }
-  tile_store<FMT_F32>(a.ck, tile, H, s.s4);
-  tile_matvec<1>(H, &s.Cw[0][0], NR, s.red, s.out);
-  for (int p = threadIdx.x; p < NC; p += kThreads)
-    a.y[static_cast<size_t>(tile) * NC + p] = s.out[p] + a.D[h] * s.X[0][p];
-}
-
-// ----------------------------------------------------------------------------
-// non-flush step: y from checkpoint (or read copy) + buffer; append; no state write
-// ----------------------------------------------------------------------------
-template <typename TIN, int RDF, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
-  constexpr int E = (RDF == FMT_F32) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  rs_meta* mp = a.meta + b;
-  const int len = mp->len, nd = mp->nd;
-  const long long nck = mp->n_ckpt;
-  const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
-  if (errbit == 0) {
-    const int j = len + 1;
-    RawTile<RDF, E, NR, NC> raw;
-    raw.issue(a.rd, tile);
-    const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
-    const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
-    const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
-    const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
-    const TIN* inDt = static_cast<const TIN*>(a.dt) + tile;
-    TIN* rB = static_cast<TIN*>(a.rB) + bg * kRing * NR;
-    TIN* rC = static_cast<TIN*>(a.rC) + bg * kRing * NR;
-    TIN* rX = static_cast<TIN*>(a.rx) + static_cast<size_t>(tile) * kRing * NC;
-    TIN* rDt = static_cast<TIN*>(a.rdt) + static_cast<size_t>(tile) * kRing;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, inB, 0, nck, len, NR}, j);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, inX, 0, nck, len, NC}, j);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, inDt, 0, nck, len, 1}, j);
-    for (int i = threadIdx.x; i < NR; i += kThreads) s.Cw[0][i] = to_f(inC[i]);
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], j);
-    __syncthreads();
-    output_weights(s, j, 1);
-    RegTile<E, NR, NC> H;
-    raw.decode(H);
-    tile_matvec<1>(H, &s.Cw[0][0], NR, s.red, s.out);  // barriers inside also publish s.w / s.L
-    const float Dh = a.D[h];
-    for (int p = threadIdx.x; p < NC; p += kThreads) {
-      float yv = s.L[0] * s.out[p];
-      for (int e = 0; e < j; ++e) yv += s.w[0][e] * s.X[e][p];
-      a.y[static_cast<size_t>(tile) * NC + p] = yv + Dh * s.X[j - 1][p];
-    }
-    // append the current record (bit copies)
-    const int slot = static_cast<int>((nck + len) & (kRing - 1));
-    for (int p = threadIdx.x; p < NC; p += kThreads) rX[slot * NC + p] = inX[p];
-    if (threadIdx.x == 0) rDt[slot] = inDt[0];
-    if (h % a.hpg == 0) {
-      for (int n = threadIdx.x; n < NR; n += kThreads) {
-        rB[slot * NR + n] = inB[n];
-        rC[slot * NR + n] = inC[n];
-      }
-    }
-  }
-  arrive_and_update(mp, a.nheads, [&](rs_meta* m) {
-    if (errbit) m->err |= errbit;
-    else m->len = len + 1;
-  });
-}
-
-// ----------------------------------------------------------------------------
-// fold body shared by the flush step and the commit fold
-// H <- l_m H + sum_e B_e xt_e^T with xt_e = w_{m,e} dt_e x_e (entries staged)
-// ----------------------------------------------------------------------------
-template <int E, int NR, int NC>
-__device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, M2Smem<NR, NC>& s, int m) {
-  // coefficients
-  if (static_cast<int>(threadIdx.x) < m) {
-    const int e = threadIdx.x;
-    float w = 1.0f;
-    for (int l = e + 1; l < m; ++l) w *= s.a[l];
-    s.w[0][e] = w * s.dt[e];
-  }
-  if (threadIdx.x == 0) {
-    float L = 1.0f;
-    for (int l = 0; l < m; ++l) L *= s.a[l];
-    s.L[0] = L;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < m * NC; idx += kThreads) {
-    const int e = idx / NC, p = idx - e * NC;
-    s.xt[e][p] = s.w[0][e] * s.X[e][p];
-  }
-  __syncthreads();
-  const float L = s.L[0];
-  const int c0 = RegTile<E, NR, NC>::col0();
-#pragma unroll
-  for (int k = 0; k < RegTile<E, NR, NC>::P; ++k)
-#pragma unroll
-    for (int i = 0; i < E; ++i) H.v[k][i] *= L;
-  for (int e = 0; e < m; ++e) {
-    float xt[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) xt[i] = s.xt[e][c0 + i];
-#pragma unroll
-    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
-      const int row = RegTile<E, NR, NC>::row(k);
-      if (row < NR) {
-        const float br = s.B[e][row];
-#pragma unroll
-        for (int i = 0; i < E; ++i) H.v[k][i] += br * xt[i];
-      }
-    }
-  }
-}
-
-// Store the folded tile in the checkpoint format, and the NVFP4 read copy of
-// the stored values when asked.
-template <int CKF, bool RC, int E, int NR, int NC>
-__device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTile<E, NR, NC>& H, float* s4) {
-  tile_store<CKF>(a.ck, tile, H, s4);
-  if constexpr (RC) {
-    if (a.fuse_rc) {
-      tile_round_trip<CKF>(H, s4);
-      tile_store<FMT_NVFP4>(a.rc, tile, H, s4);
-    }
-  }
-}
-
-// ----------------------------------------------------------------------------
-// flush step: fold len stored entries + the current token, write once, y
-// ----------------------------------------------------------------------------
-template <typename TIN, int CKF, bool RC, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
-  constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  rs_meta* mp = a.meta + b;
-  const int len = mp->len, nd = mp->nd;
-  const long long nck = mp->n_ckpt;
-  const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
-  const int m = len + 1;
-  if (errbit == 0) {
-    RawTile<CKF, E, NR, NC> raw;
-    raw.issue(a.ck, tile);
-    const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
-    const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
-    const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
-    const TIN* rB = static_cast<const TIN*>(a.rB) + bg * kRing * NR;
-    const TIN* rX = static_cast<const TIN*>(a.rx) + static_cast<size_t>(tile) * kRing * NC;
-    const TIN* rDt = static_cast<const TIN*>(a.rdt) + static_cast<size_t>(tile) * kRing;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, static_cast<const TIN*>(a.B) + bg * NR, 0, nck, len, NR}, m);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, inX, 0, nck, len, NC}, m);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, static_cast<const TIN*>(a.dt) + tile, 0, nck, len, 1}, m);
-    for (int i = threadIdx.x; i < NR; i += kThreads) s.Cw[0][i] = to_f(inC[i]);
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], m);
-    __syncthreads();
-    RegTile<E, NR, NC> H;
-    raw.decode(H);
-    fold_tile(H, s, m);
-    tile_matvec<1>(H, &s.Cw[0][0], NR, s.red, s.out);
-    const float Dh = a.D[h];
-    for (int p = threadIdx.x; p < NC; p += kThreads)
-      a.y[static_cast<size_t>(tile) * NC + p] = s.out[p] + Dh * s.X[m - 1][p];
-    store_folded<CKF, RC>(a, tile, H, s.s4);
-  }
-  arrive_and_update(mp, a.nheads, [&](rs_meta* mm) {
-    if (errbit) {
-      mm->err |= errbit;
-    } else {
-      mm->n_ckpt = nck + m;
-      mm->len = 0;
-    }
-  });
-}
-
-// ----------------------------------------------------------------------------
-// speculative append (ReplaySSM): K verify outputs from checkpoint + buffer +
-// drafts, drafts written to the ring, no state write
-// ----------------------------------------------------------------------------
-template <typename TIN, int RDF, int NR, int NC, int KQ>
-__global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
-  constexpr int E = (RDF == FMT_F32) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  const int K = a.K;
-  rs_meta* mp = a.meta + b;
-  const int len = mp->len, nd = mp->nd;
-  const long long nck = mp->n_ckpt;
-  const int errbit = (nd != 0 || len + K > kRing) ? RS_ERR_OVERFLOW : 0;
-  if (errbit == 0) {
-    RawTile<RDF, E, NR, NC> raw;
-    raw.issue(a.rd, tile);
-    const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
-    const size_t gstride = static_cast<size_t>(a.batch) * a.ngroups * NR;   // between drafts (B, C)
-    const size_t xstride = static_cast<size_t>(a.batch) * a.nheads * NC;    // between drafts (x)
-    const size_t dstride = static_cast<size_t>(a.batch) * a.nheads;         // between drafts (dt)
-    const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
-    const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
-    const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
-    const TIN* inDt = static_cast<const TIN*>(a.dt) + tile;
-    TIN* rB = static_cast<TIN*>(a.rB) + bg * kRing * NR;
-    TIN* rC = static_cast<TIN*>(a.rC) + bg * kRing * NR;
-    TIN* rX = static_cast<TIN*>(a.rx) + static_cast<size_t>(tile) * kRing * NC;
-    TIN* rDt = static_cast<TIN*>(a.rdt) + static_cast<size_t>(tile) * kRing;
-    const int n = len + K;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, inB, gstride, nck, len, NR}, n);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, inX, xstride, nck, len, NC}, n);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, inDt, dstride, nck, len, 1}, n);
-    stage_rows(&s.Cw[0][0], NR, EntrySrc<TIN>{inC, inC, gstride, 0, 0, NR}, K);
-    for (int idx = K * NR + threadIdx.x; idx < KQ * NR; idx += kThreads) (&s.Cw[0][0])[idx] = 0.0f;
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], n);
-    __syncthreads();
-    output_weights(s, len + 1, K);
-    RegTile<E, NR, NC> H;
-    raw.decode(H);
-    tile_matvec<KQ>(H, &s.Cw[0][0], NR, s.red, s.out);
-    const float Dh = a.D[h];
-    for (int idx = threadIdx.x; idx < K * NC; idx += kThreads) {
-      const int d = idx / NC, p = idx - d * NC;
-      const int J = len + d + 1;
-      float yv = s.L[d] * s.out[d * NC + p];
-      for (int e = 0; e < J; ++e) yv += s.w[d][e] * s.X[e][p];
-      a.y[d * xstride + static_cast<size_t>(tile) * NC + p] = yv + Dh * s.X[J - 1][p];
-    }
-    // drafts into the ring (bit copies)
-    for (int idx = threadIdx.x; idx < K * NC; idx += kThreads) {
-      const int d = idx / NC, p = idx - d * NC;
-      const int slot = static_cast<int>((nck + len + d) & (kRing - 1));
-      rX[slot * NC + p] = inX[d * xstride + p];
-    }
-    if (static_cast<int>(threadIdx.x) < K) {
-      const int d = threadIdx.x;
-      rDt[(nck + len + d) & (kRing - 1)] = inDt[d * dstride];
-    }
-    if (h % a.hpg == 0) {
-      for (int idx = threadIdx.x; idx < K * NR; idx += kThreads) {
-        const int d = idx / NR, r = idx - d * NR;
-        const int slot = static_cast<int>((nck + len + d) & (kRing - 1));
-        rB[slot * NR + r] = inB[d * gstride + r];
-        rC[slot * NR + r] = inC[d * gstride + r];
-      }
-    }
-  }
-  arrive_and_update(mp, a.nheads, [&](rs_meta* m) {
-    if (errbit) m->err |= errbit;
-    else m->nd = K;
-  });
-}
-
-// ----------------------------------------------------------------------------
-// speculative commit (ReplaySSM), part 1: counters, and the list of sequences
-// whose committed entries must be folded now. One workgroup; the list is in
-// ascending sequence order.
-// ----------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void m2_commit_meta_kernel(M2Args a) {
-  __shared__ int wsum[16];
-  __shared__ int base;
-  if (threadIdx.x == 0) base = 0;
-  __syncthreads();
-  for (int b0 = 0; b0 < a.batch; b0 += 1024) {
-    const int b = b0 + threadIdx.x;
-    int fold = 0, m = 0;
-    long long nck = 0;
-    if (b < a.batch) {
-      rs_meta* mp = a.meta + b;
-      const int k = a.accepted[b];
-      const int nd = mp->nd;
-      if (k < 0 || k > nd) {
-        mp->err |= RS_ERR_COMMIT;
-      } else {
-        const int len = mp->len + k;
-        mp->nd = 0;
-        nck = mp->n_ckpt;
-        if (len > kRing - a.kmax) {
-          fold = 1;
-          m = len;
-          mp->n_ckpt = nck + len;
-          mp->len = 0;
-        } else {
-          mp->len = len;
-        }
-      }
-    }
-    // ordered compaction: inclusive scan of `fold` over the 1024 threads
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = fold;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int before = base;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    if (fold) {
-      FoldItem it;
-      it.b = b;
-      it.m = m;
-      it.nck = nck;
-      a.work[before + incl - 1] = it;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += wsum[w];
-      base += tot;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *a.work_count = base;
-}
-
-// part 2: fold the listed sequences' committed entries, one head per work
-// item, over a fixed grid (every workgroup leaves when the list is done)
-template <typename TIN, int CKF, bool RC, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
-  constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
-  const int total = *a.work_count * a.nheads;
-  for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const FoldItem it = a.work[item / a.nheads];
-    const int h = item - (item / a.nheads) * a.nheads;
-    const int b = it.b, g = h / a.hpg, m = it.m;
-    const size_t tile = static_cast<size_t>(b) * a.nheads + h;
-    RawTile<CKF, E, NR, NC> raw;
-    raw.issue(a.ck, tile);
-    const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
-    const TIN* rB = static_cast<const TIN*>(a.rB) + bg * kRing * NR;
-    const TIN* rX = static_cast<const TIN*>(a.rx) + tile * kRing * NC;
-    const TIN* rDt = static_cast<const TIN*>(a.rdt) + tile * kRing;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, rB, 0, it.nck, m, NR}, m);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, rX, 0, it.nck, m, NC}, m);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, rDt, 0, it.nck, m, 1}, m);
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], m);
-    __syncthreads();
-    RegTile<E, NR, NC> H;
-    raw.decode(H);
-    fold_tile(H, s, m);
-    store_folded<CKF, RC>(a, tile, H, s.s4);
-    __syncthreads();
-  }
-}
-
-// ----------------------------------------------------------------------------
-// snapshot baseline: step the live state through K drafts, write each state
-// to snap[d], K outputs; the live state is not written here
-// ----------------------------------------------------------------------------
-template <typename TIN, int NR, int NC, int KMAX>
-__global__ __launch_bounds__(kThreads) void m2_conv_spec_kernel(M2Args a) {
-  constexpr int E = 4;
-  __shared__ M2Smem<NR, NC> s;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  const int K = a.K;
-  RawTile<FMT_F32, E, NR, NC> raw;
-  raw.issue(a.ck, tile);
-  const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
-  const size_t gstride = static_cast<size_t>(a.batch) * a.ngroups * NR;
-  const size_t xstride = static_cast<size_t>(a.batch) * a.nheads * NC;
-  const size_t dstride = static_cast<size_t>(a.batch) * a.nheads;
-  const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
-  const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
-  const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
-  const TIN* inDt = static_cast<const TIN*>(a.dt) + tile;
-  stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{inB, inB, gstride, 0, 0, NR}, K);
-  stage_rows(&s.Cw[0][0], NR, EntrySrc<TIN>{inC, inC, gstride, 0, 0, NR}, K);
-  stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{inX, inX, xstride, 0, 0, NC}, K);
-  stage_rows(&s.dt[0], 1, EntrySrc<TIN>{inDt, inDt, dstride, 0, 0, 1}, K);
-  __syncthreads();
-  stage_decays(s.a, s.dt, a.A[h], K);
-  __syncthreads();
-  RegTile<E, NR, NC> H;
-  raw.decode(H);
-  const int c0 = RegTile<E, NR, NC>::col0();
-  const float Dh = a.D[h];
-  const size_t snap_stride = static_cast<size_t>(a.batch) * a.nheads;   // matrices per snapshot
-  for (int d = 0; d < K; ++d) {
-    const float decay = s.a[d];
-    float dtx[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) dtx[i] = s.dt[d] * s.X[d][c0 + i];
-#pragma unroll
-    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
-      const int row = RegTile<E, NR, NC>::row(k);
-      if (row < NR) {
-        const float br = s.B[d][row];
-#pragma unroll
-        for (int i = 0; i < E; ++i) H.v[k][i] = decay * H.v[k][i] + dtx[i] * br;
-      }
-    }
-    StateBuf sn{a.snap, nullptr, nullptr};
-    tile_store<FMT_F32>(sn, d * snap_stride + tile, H, s.s4);
-    tile_matvec<1>(H, &s.Cw[d][0], NR, s.red, s.out);
-    for (int p = threadIdx.x; p < NC; p += kThreads)
-      a.y[d * xstride + static_cast<size_t>(tile) * NC + p] = s.out[p] + Dh * s.X[d][p];
-  }
-}
-
-// snapshot baseline commit: live <- snap[k-1] for 1 <= k <= max_draft
-template <int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_restore_kernel(M2Args a) {
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / a.nheads;
-  const int k = a.accepted[b];
-  if (k < 1 || k > a.kmax) return;
-  const size_t snap_stride = static_cast<size_t>(a.batch) * a.nheads;
-  const float4* src = reinterpret_cast<const float4*>(a.snap + ((k - 1) * snap_stride + tile) * NR * NC);
-  float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.ck.data) + static_cast<size_t>(tile) * NR * NC);
-  for (int i = threadIdx.x; i < NR * NC / 4; i += kThreads) nt_store(nt_load(src + i), dst + i);
-}
-
-// ----------------------------------------------------------------------------
-// standalone read-copy quantizer: NVFP4 copy of the stored checkpoint
-// ----------------------------------------------------------------------------
-template <int CKF, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void requant_kernel(StateBuf ck, StateBuf rc) {
-  __shared__ float s4[4];
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  RawTile<CKF, 8, NR, NC> raw;
-  raw.issue(ck, tile);
-  RegTile<8, NR, NC> H;
-  raw.decode(H);
-  tile_store<FMT_NVFP4>(rc, tile, H, s4);
-}
-
-// ----------------------------------------------------------------------------
-// host launchers
-// ----------------------------------------------------------------------------
-namespace {
-
-template <int NR, int NC>
-struct M2Shape {
-  template <typename TIN>
-  static void conv(const M2Args& a, int grid, hipStream_t st) {
-    m2_conv_kernel<TIN, NR, NC><<<grid, kThreads, 0, st>>>(a);
-  }
-  template <typename TIN>
-  static void nonflush(const M2Args& a, int rdf, int grid, hipStream_t st) {
-    switch (rdf) {
-      case FMT_F32: m2_nonflush_kernel<TIN, FMT_F32, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_F16: m2_nonflush_kernel<TIN, FMT_F16, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_FP8: m2_nonflush_kernel<TIN, FMT_FP8, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      default: m2_nonflush_kernel<TIN, FMT_NVFP4, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-    }
-  }
-  template <typename TIN, bool RC>
-  static void flush_rc(const M2Args& a, int ckf, int grid, hipStream_t st) {
-    switch (ckf) {
-      case FMT_F32: m2_flush_kernel<TIN, FMT_F32, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_F16: m2_flush_kernel<TIN, FMT_F16, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_FP8: m2_flush_kernel<TIN, FMT_FP8, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      default: m2_flush_kernel<TIN, FMT_NVFP4, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-    }
-  }
-  template <typename TIN>
-  static void flush(const M2Args& a, int ckf, bool rc, int grid, hipStream_t st) {
-    if (rc) flush_rc<TIN, true>(a, ckf, grid, st);
-    else flush_rc<TIN, false>(a, ckf, grid, st);
-  }
-  template <typename TIN, int KQ>
-  static void spec_append_k(const M2Args& a, int rdf, int grid, hipStream_t st) {
-    switch (rdf) {
-      case FMT_F32: m2_spec_append_kernel<TIN, FMT_F32, NR, NC, KQ><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_F16: m2_spec_append_kernel<TIN, FMT_F16, NR, NC, KQ><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_FP8: m2_spec_append_kernel<TIN, FMT_FP8, NR, NC, KQ><<<grid, kThreads, 0, st>>>(a); break;
-      default: m2_spec_append_kernel<TIN, FMT_NVFP4, NR, NC, KQ><<<grid, kThreads, 0, st>>>(a); break;
-    }
-  }
-  template <typename TIN>
-  static void spec_append(const M2Args& a, int rdf, int grid, hipStream_t st) {
-    if (a.K <= 1) spec_append_k<TIN, 1>(a, rdf, grid, st);
-    else if (a.K <= 2) spec_append_k<TIN, 2>(a, rdf, grid, st);
-    else if (a.K <= 4) spec_append_k<TIN, 4>(a, rdf, grid, st);
-    else spec_append_k<TIN, 8>(a, rdf, grid, st);
-  }
-  template <typename TIN, bool RC>
-  static void commit_fold_rc(const M2Args& a, int ckf, int grid, hipStream_t st) {
-    switch (ckf) {
-      case FMT_F32: m2_commit_fold_kernel<TIN, FMT_F32, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_F16: m2_commit_fold_kernel<TIN, FMT_F16, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_FP8: m2_commit_fold_kernel<TIN, FMT_FP8, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-      default: m2_commit_fold_kernel<TIN, FMT_NVFP4, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
-    }
-  }
-  template <typename TIN>
-  static void commit_fold(const M2Args& a, int ckf, bool rc, int grid, hipStream_t st) {
-    if (rc) commit_fold_rc<TIN, true>(a, ckf, grid, st);
-    else commit_fold_rc<TIN, false>(a, ckf, grid, st);
-  }
-  template <typename TIN>
-  static void conv_spec(const M2Args& a, int grid, hipStream_t st) {
-    m2_conv_spec_kernel<TIN, NR, NC, kMaxDraft><<<grid, kThreads, 0, st>>>(a);
-  }
-  static void restore(const M2Args& a, int grid, hipStream_t st) {
-    m2_restore_kernel<NR, NC><<<grid, kThreads, 0, st>>>(a);
-  }
-  static void requant(const StateBuf& ck, const StateBuf& rc, int ckf, int grid, hipStream_t st) {
-    switch (ckf) {
-      case FMT_F32: requant_kernel<FMT_F32, NR, NC><<<grid, kThreads, 0, st>>>(ck, rc); break;
-      case FMT_F16: requant_kernel<FMT_F16, NR, NC><<<grid, kThreads, 0, st>>>(ck, rc); break;
-      case FMT_FP8: requant_kernel<FMT_FP8, NR, NC><<<grid, kThreads, 0, st>>>(ck, rc); break;
-      default: requant_kernel<FMT_NVFP4, NR, NC><<<grid, kThreads, 0, st>>>(ck, rc); break;
-    }
-  }
-};
-
-// Calls f.template operator()<NR, NC>() for a compiled (dstate, headdim) pair.
-template <typename F>
-bool m2_with_shape(int dstate, int headdim, F&& f) {
-  if (dstate == 16 && headdim == 16) { f(M2Shape<16, 16>{}); return true; }
-  if (dstate == 64 && headdim == 64) { f(M2Shape<64, 64>{}); return true; }
-  if (dstate == 128 && headdim == 64) { f(M2Shape<128, 64>{}); return true; }
-  if (dstate == 128 && headdim == 128) { f(M2Shape<128, 128>{}); return true; }
-  return false;
-}
-
-}  // namespace
+extern template void m2_launch_shape<16, 16>(M2Op, const M2Args&, const M2Launch&, hipStream_t);
+extern template void m2_launch_shape<64, 64>(M2Op, const M2Args&, const M2Launch&, hipStream_t);
+extern template void m2_launch_shape<128, 64>(M2Op, const M2Args&, const M2Launch&, hipStream_t);
+extern template void m2_launch_shape<128, 128>(M2Op, const M2Args&, const M2Launch&, hipStream_t);
 
 bool m2_shape_supported(int dstate, int headdim) {
-  return m2_with_shape(dstate, headdim, [](auto) {});
+  return (dstate == 16 && headdim == 16) || (dstate == 64 && headdim == 64) || (dstate == 128 && headdim == 64) ||
+         (dstate == 128 && headdim == 128);
 }
 
 void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st) {
-  const bool bf = l.in_bf16;
-  m2_with_shape(l.rows, l.cols, [&](auto S) {
-    using Sh = decltype(S);
-    switch (op) {
-      case M2Op::Conv:
-        if (bf) Sh::template conv<bf16>(a, l.grid, st); else Sh::template conv<float>(a, l.grid, st);
-        break;
-      case M2Op::NonFlush:
-        if (bf) Sh::template nonflush<bf16>(a, l.rdf, l.grid, st); else Sh::template nonflush<float>(a, l.rdf, l.grid, st);
-        break;
-      case M2Op::Flush:
-        if (bf) Sh::template flush<bf16>(a, l.ckf, l.rc, l.grid, st); else Sh::template flush<float>(a, l.ckf, l.rc, l.grid, st);
-        break;
-      case M2Op::SpecAppend:
-        if (bf) Sh::template spec_append<bf16>(a, l.rdf, l.grid, st); else Sh::template spec_append<float>(a, l.rdf, l.grid, st);
-        break;
-      case M2Op::CommitMeta:
-        m2_commit_meta_kernel<<<1, 1024, 0, st>>>(a);
-        break;
-      case M2Op::CommitFold:
-        if (bf) Sh::template commit_fold<bf16>(a, l.ckf, l.rc, l.grid, st); else Sh::template commit_fold<float>(a, l.ckf, l.rc, l.grid, st);
-        break;
-      case M2Op::ConvSpec:
-        if (bf) Sh::template conv_spec<bf16>(a, l.grid, st); else Sh::template conv_spec<float>(a, l.grid, st);
-        break;
-      case M2Op::Restore:
-        Sh::restore(a, l.grid, st);
-        break;
-      case M2Op::Requant:
-        Sh::requant(a.ck, a.rc, l.ckf, l.grid, st);
-        break;
-    }
-  });
+  if (l.rows == 16 && l.cols == 16) m2_launch_shape<16, 16>(op, a, l, st);
+  else if (l.rows == 64 && l.cols == 64) m2_launch_shape<64, 64>(op, a, l, st);
+  else if (l.rows == 128 && l.cols == 64) m2_launch_shape<128, 64>(op, a, l, st);
+  else if (l.rows == 128 && l.cols == 128) m2_launch_shape<128, 128>(op, a, l, st);
 }
 
 }  // namespace rs
