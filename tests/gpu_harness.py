@@ -77,9 +77,12 @@ def load_state_f32(layer, bufs, logical: np.ndarray):
     rs.ckpt_f32_view(layer, bufs).copy_(torch.from_numpy(st).to(DEV))
 
 
-def read_state_f32(layer, bufs) -> np.ndarray:
-    """fp32 checkpoint back in logical layout [b, heads, P|dv, N|dk]."""
-    return np.swapaxes(rs.ckpt_f32_view(layer, bufs).cpu().numpy(), -1, -2)
+def read_state_f32(layer, bufs, seqs=None) -> np.ndarray:
+    """fp32 checkpoint (optionally only some sequences) in logical layout [b, heads, P|dv, N|dk]."""
+    v = rs.ckpt_f32_view(layer, bufs)
+    if seqs is not None:
+        v = v[torch.as_tensor(seqs, device=v.device)]
+    return np.swapaxes(v.cpu().numpy(), -1, -2)
 
 
 def read_meta(layer, bufs):

@@ -228,7 +228,7 @@ def test_nemotron_batch256_sampled():
     assert worst_r <= 1e-5 and worst_c <= 1e-5     # fp32 arithmetic on exact bf16 inputs
     nck, ln, nd, err, arrive = read_meta(layer, bufs)
     assert (nck == 32).all() and (ln == 0).all() and not err.any() and not arrive.any()
-    st = read_state_f32(layer, bufs)[seqs]
+    st = read_state_f32(layer, bufs, seqs)
     assert rel_l2(st, ref.H) <= 1e-5
 
 
