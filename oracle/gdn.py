@@ -60,7 +60,7 @@ def step(S, q, k, v, g, beta):
     alpha = np.exp(g)
     eye = np.eye(dk)
     P = eye[None, None] - beta[:, :, None, None] * kk[:, :, :, None] * kk[:, :, None, :]
-    Sn = alpha[:, :, None, None] * np.einsum("bhvk,bhkj->bhvj", S, P) \
+    Sn = alpha[:, :, None, None] * np.matmul(S, P) \
         + beta[:, :, None, None] * v[:, :, :, None] * kk[:, :, None, :]
     o = np.einsum("bhvk,bhk->bhv", Sn, qq)
     return Sn, o

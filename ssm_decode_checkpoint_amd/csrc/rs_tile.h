@@ -238,4 +238,31 @@ __device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const
   }
 }
 
+// H <- L*H + sum_{e<m} row[e][r] * col[e][c]: a rank-m update of the held
+// matrix from LDS vectors (row: m x NR, stride rs; col: m x NC, stride cs),
+// accumulated in entry order. No barriers.
+template <int E, int NR, int NC>
+__device__ __forceinline__ void tile_rank_update(RegTile<E, NR, NC>& H, float L, const float* row, int rs,
+                                                 const float* col, int cs, int m) {
+  const int c0 = RegTile<E, NR, NC>::col0();
+#pragma unroll
+  for (int k = 0; k < RegTile<E, NR, NC>::P; ++k)
+#pragma unroll
+    for (int i = 0; i < E; ++i) H.v[k][i] *= L;
+  for (int e = 0; e < m; ++e) {
+    float xc[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) xc[i] = col[e * cs + c0 + i];
+#pragma unroll
+    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
+      const int r = RegTile<E, NR, NC>::row(k);
+      if (r < NR) {
+        const float br = row[e * rs + r];
+#pragma unroll
+        for (int i = 0; i < E; ++i) H.v[k][i] += br * xc[i];
+      }
+    }
+  }
+}
+
 }  // namespace rs
