@@ -1,18 +1,25 @@
 """Benchmark: ReplaySSM SSM-layer decode on one MI355X vs the same-GPU conventional kernel.
 
-Default workload: the Nemotron-style Mamba-2 layer at serving batch 256
-(128 heads, headdim 64, dstate 128, 8 groups, bf16 inputs, fp32 checkpoint,
-4 MiB of state per sequence), seeded synthetic inputs resident in HBM.
+Default workload (the one the headline metric is quoted on): the
+Nemotron-style Mamba-2 layer at serving batch 256 (128 heads, headdim 64,
+dstate 128, 8 groups, bf16 inputs, fp32 checkpoint, 4 MiB of state per
+sequence), seeded synthetic inputs resident in HBM.
 
 One "step" is one full buffer window: 15 non-flush steps (append + output
 from checkpoint and buffer) and one flush step (fold, one checkpoint write),
 i.e. 16 decode tokens for all 256 sequences; `value` is decode tokens/s over
 the K timed windows. The conventional read-modify-write kernel is timed on
-the same windows for comparison.
+the same windows for comparison. The JSON line carries the roofline of the
+dominant kernel (the non-flush step) measured with HIP events on the launch
+stream, and the fp64 CPU oracle timed on a bounded sample of the workload.
 
-Prints one JSON line with the roofline of the dominant kernel (the non-flush
-step) measured with HIP events on the launch stream, and the fp64 CPU oracle
-timed on a bounded sample of the same workload.
+Other workloads (each one more JSON line, only when asked with --workload):
+  gdn      Qwen3.5-style Gated DeltaNet layer, batch 256 (UT-form non-flush)
+  spec     speculative decode on 120B-class Mamba-2 shapes, batch 512, 4 drafts
+           per round: ReplaySSM append + commit vs snapshot / restore
+  lowprec  Nemotron shapes at batch 64: fp32 / fp16 / fp8 checkpoints with and
+           without the NVFP4 read copy, and the uniform NVFP4 checkpoint;
+           optionally (--lowprec-error-steps) y error vs fp64 over length
 """
 from __future__ import annotations
 
@@ -50,17 +57,40 @@ def kernel_source_hash() -> str:
 # algorithmic bytes per sequence (what the method must move; cache effects not counted)
 # ---------------------------------------------------------------------------
 
-def m2_bytes(w: W.Mamba2Workload):
+def m2_bytes(w: W.Mamba2Workload, ckpt_bytes_per_elem: float = 4.0, read_bytes_per_elem: float = None):
+    """Per-sequence bytes of each Mamba-2 step. The checkpoint element costs
+    ckpt_bytes_per_elem when written or folded from, and read_bytes_per_elem
+    when a non-flush step reads it through a read copy (the flush then also
+    writes the copy)."""
     s_in = 2 if w.in_dtype == "bf16" else 4
     H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
-    S = H * P * N * 4
+    rd = ckpt_bytes_per_elem if read_bytes_per_elem is None else read_bytes_per_elem
+    S = H * P * N * ckpt_bytes_per_elem
+    S_read = H * P * N * rd
     E_in = (H * P + 2 * G * N + H) * s_in      # x, B, C, dt of the current token
     E_old = (H * P + G * N + H) * s_in         # x, B, dt of a held entry (C is not re-read)
     Y = H * P * 4
-    nonflush = {j: S + (j - 1) * E_old + 2 * E_in + Y for j in range(1, RING)}
-    flush = 2 * S + (RING - 1) * E_old + E_in + Y
-    conv = 2 * S + E_in + Y
+    rc_write = 0.0 if read_bytes_per_elem is None else H * P * N * rd
+    nonflush = {j: S_read + (j - 1) * E_old + 2 * E_in + Y for j in range(1, RING)}
+    flush = 2 * S + (RING - 1) * E_old + E_in + Y + rc_write
+    conv = 2 * H * P * N * 4 + E_in + Y
     return {"state": S, "E_in": E_in, "E_old": E_old, "Y": Y, "nonflush": nonflush, "flush": flush, "conv": conv}
+
+
+def gdn_bytes(w: W.GDNWorkload):
+    """Per-sequence bytes of each Gated DeltaNet step. A held entry is re-read
+    as its k, its decay g and its solved row u (fp32); each non-flush step
+    appends the record (q, k, v, g, beta) and the new entry's u."""
+    s_in = 2 if w.in_dtype == "bf16" else 4
+    S = w.n_v * w.dv * w.dk * 4
+    E_in = 2 * w.n_qk * w.dk * s_in + w.n_v * w.dv * s_in + 2 * w.n_v * 4   # q, k, v, g, beta
+    Urow = w.n_v * w.dv * 4
+    E_old = w.n_qk * w.dk * s_in + Urow + w.n_v * 4                          # k, u, g of a held entry
+    O = w.n_v * w.dv * 4
+    nonflush = {j: S + (j - 1) * E_old + 2 * E_in + Urow + O for j in range(1, RING)}
+    flush = 2 * S + (RING - 1) * E_old + E_in + O
+    conv = 2 * S + E_in + O
+    return {"state": S, "E_in": E_in, "E_old": E_old, "O": O, "nonflush": nonflush, "flush": flush, "conv": conv}
 
 
 # ---------------------------------------------------------------------------
@@ -89,15 +119,15 @@ def cpu_baseline(w: W.Mamba2Workload, nseq: int, windows: int = 1):
     ntok = nseq * RING * windows
     return {"value": ntok / wall, "unit": "tokens/s", "cores": max(1, int(round(cpu / wall))), "kind": "oracle",
             "sample": f"fp64 ReplaySSM oracle (checkpoint + buffer, plain numpy) on {nseq} of {w.batch} sequences "
-                      f"x {RING * windows} decode steps ({windows} window) of the {w.name} workload; "
+                      f"x {RING * windows} decode steps ({windows} windows) of the {w.name} workload; "
                       f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
 
 
 # ---------------------------------------------------------------------------
-# GPU run
+# GPU helpers
 # ---------------------------------------------------------------------------
 
-def traffic_from_profile(name: str, launch_bytes_alg: float):
+def traffic_from_profile(name: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they
     were taken on the current kernel sources."""
     path = os.path.join(PROFILES, "counters_" + name + ".json")
@@ -110,131 +140,351 @@ def traffic_from_profile(name: str, launch_bytes_alg: float):
     return c.get("hbm_bytes_per_launch")
 
 
-def run_gpu(args):
-    import torch
-    import ssm_decode_checkpoint_amd as rs
-    from ssm_decode_checkpoint_amd import RS_CONVENTIONAL, RS_REPLAY
+class Timer:
+    """HIP-event timing of a sequence of launches on torch's current stream
+    (the stream every library call here is enqueued on)."""
 
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def run(self, fn, K, warm, nmarks, reset=None):
+        torch = self.torch
+        for _ in range(warm):
+            fn(None)
+        if reset is not None:
+            reset()
+        torch.cuda.synchronize()
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nmarks)] for _ in range(K)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(self.stream)
+        for k in range(K):
+            fn(evs[k])
+        t1.record(self.stream)
+        torch.cuda.synchronize()
+        total = t0.elapsed_time(t1)
+        per = np.array([[evs[k][i][0].elapsed_time(evs[k][i][1]) for i in range(nmarks)] for k in range(K)])
+        return total, per
+
+
+def _marked(ev, i, stream, call):
+    if ev is not None:
+        ev[i][0].record(stream)
+    call()
+    if ev is not None:
+        ev[i][1].record(stream)
+
+
+def _bf16_dev(torch, arr, dev):
+    return torch.from_numpy(W.bf16_bits(arr).view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+
+def _m2_layer(rs, w, B, mode, dev, ckpt=None, read_copy=None, fuse=1, max_draft=0):
+    cfg = rs.make_config(rs.RS_MAMBA2, B, mode=mode, nheads=w.nheads, headdim=w.headdim, dstate=w.dstate,
+                         ngroups=w.ngroups, in_dtype=rs.RS_BF16 if w.in_dtype == "bf16" else rs.RS_F32,
+                         ckpt_dtype=rs.RS_F32 if ckpt is None else ckpt,
+                         read_copy=rs.RS_NONE if read_copy is None else read_copy, fuse_requant=fuse,
+                         max_draft=max_draft)
+    _, layer = rs.rs_init(cfg)
+    return layer, rs.alloc_buffers(layer, dev)
+
+
+def _m2_load_init(torch, rs, w, layer, bufs, dev):
+    ck = rs.ckpt_f32_view(layer, bufs)
+    for b in range(layer.cfg.batch):
+        ck[b].copy_(torch.from_numpy(np.ascontiguousarray(W.m2_init_state(w, b).transpose(0, 2, 1))).to(dev))
+
+
+def _m2_pool(torch, w, B, dev, t0=0, n=RING):
+    pool = []
+    for t in range(t0, t0 + n):
+        tk = W.m2_step(w, t, range(B))
+        pool.append({k: (_bf16_dev(torch, v, dev) if w.in_dtype == "bf16" else torch.from_numpy(v).to(dev))
+                     for k, v in tk.items()})
+    return pool
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def bench_mamba2(args, torch, rs):
     w = W.M2_NEMOTRON
     dev = "cuda"
-    torch.cuda.set_device(0)
     B = w.batch
     p = W.m2_params(w)
     A = torch.from_numpy(p["A"]).to(dev)
     D = torch.from_numpy(p["D"]).to(dev)
-
-    def mk(mode):
-        cfg = rs.make_config(rs.RS_MAMBA2, B, mode=mode, nheads=w.nheads, headdim=w.headdim, dstate=w.dstate,
-                             ngroups=w.ngroups, in_dtype=rs.RS_BF16, ckpt_dtype=rs.RS_F32)
-        _, layer = rs.rs_init(cfg)
-        return layer, rs.alloc_buffers(layer, dev)
-
-    rl, rb = mk(RS_REPLAY)
-    cl, cb = mk(RS_CONVENTIONAL)
-    # initial checkpoint N(0, 0.1^2) from the seeded generator, stored [b][h][N][P]
-    ck = rs.ckpt_f32_view(rl, rb)
-    for b in range(B):
-        ck[b].copy_(torch.from_numpy(np.ascontiguousarray(W.m2_init_state(w, b).transpose(0, 2, 1))))
-    rs.ckpt_f32_view(cl, cb).copy_(ck)
-    # one window of seeded step inputs, resident in HBM, reused every window
-    pool = []
-    for t in range(RING):
-        tk = W.m2_step(w, t, range(B))
-        pool.append({k: torch.from_numpy(W.bf16_bits(v).view(np.int16).copy()).view(torch.bfloat16).to(dev)
-                     for k, v in tk.items()})
+    rl, rb = _m2_layer(rs, w, B, rs.RS_REPLAY, dev)
+    cl, cb = _m2_layer(rs, w, B, rs.RS_CONVENTIONAL, dev)
+    _m2_load_init(torch, rs, w, rl, rb, dev)
+    rs.ckpt_f32_view(cl, cb).copy_(rs.ckpt_f32_view(rl, rb))
+    pool = _m2_pool(torch, w, B, dev)
     y = torch.empty(B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
+    tm = Timer(torch)
 
-    def replay_window(ev=None):
+    def replay_window(ev):
         for t in range(RING):
-            if ev is not None:
-                ev[t][0].record(stream)
-            if t == RING - 1:
-                rs.rs_step_flush(rl, rb, pool[t], A, D, y)
-            else:
-                rs.rs_step_nonflush(rl, rb, pool[t], A, D, y)
-            if ev is not None:
-                ev[t][1].record(stream)
+            fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
+            _marked(ev, t, tm.stream, lambda: fn(rl, rb, pool[t], A, D, y))
 
-    def conv_window(ev=None):
+    def conv_window(ev):
         for t in range(RING):
-            if ev is not None:
-                ev[t][0].record(stream)
-            rs.rs_step_conventional(cl, cb, pool[t], A, D, y)
-            if ev is not None:
-                ev[t][1].record(stream)
-
-    def timed(fn, K, warm):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(RING)] for _ in range(K)]
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for k in range(K):
-            fn(evs[k])
-        t1.record(stream)
-        torch.cuda.synchronize()
-        total = t0.elapsed_time(t1)
-        per = np.array([[evs[k][t][0].elapsed_time(evs[k][t][1]) for t in range(RING)] for k in range(K)])
-        return total, per
+            _marked(ev, t, tm.stream, lambda: rs.rs_step_conventional(cl, cb, pool[t], A, D, y))
 
     K, warm = args.steps, args.warmup
-    wall0 = time.perf_counter()
-    total_r, per_r = timed(replay_window, K, warm)
-    total_c, per_c = timed(conv_window, K, warm)
-    wall = time.perf_counter() - wall0
-
+    total_r, per_r = tm.run(replay_window, K, warm, RING)
+    total_c, per_c = tm.run(conv_window, K, warm, RING)
     byt = m2_bytes(w)
     ntok = B * RING * K
     value = ntok / (total_r * 1e-3)
     conv_value = ntok / (total_c * 1e-3)
-    # dominant kernel: the non-flush step (15 of 16 launches per window)
     nf_ms = per_r[:, : RING - 1]
-    nf_bytes = sum(byt["nonflush"][j] for j in range(1, RING)) * B      # one window of non-flush launches
+    nf_bytes = sum(byt["nonflush"][j] for j in range(1, RING)) * B
     nf_avg_ms = float(nf_ms.mean())
-    nf_avg_bytes = nf_bytes / (RING - 1)
     nf_gbs = nf_bytes / (nf_ms.sum(axis=1).mean() * 1e-3) / 1e9
     fl_ms = float(per_r[:, RING - 1].mean())
-    fl_gbs = byt["flush"] * B / (fl_ms * 1e-3) / 1e9
     cv_ms = float(per_c.mean())
-    cv_gbs = byt["conv"] * B / (cv_ms * 1e-3) / 1e9
     win_bytes = nf_bytes + byt["flush"] * B
     win_ms = total_r / K
-    traffic = traffic_from_profile("m2_nonflush_b256", nf_avg_bytes)
-    out = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": warm,
-        "ms_per_step": win_ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
+    return {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm,
+        "ms_per_step": win_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
                    "ngroups": w.ngroups, "inputs": "bf16", "checkpoint": "f32", "ring": RING,
                    "step": "one 16-token window: 15 non-flush + 1 flush", "parallelism": "none"},
         "roofline": {"bound": "hbm", "achieved": nf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": nf_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": nf_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile("m2_nonflush_b256"),
                      "kernel": "m2_nonflush_kernel", "avg_launch_ms": nf_avg_ms,
-                     "alg_bytes_per_launch": nf_avg_bytes},
+                     "alg_bytes_per_launch": nf_bytes / (RING - 1)},
         "replay": {"tokens_per_s": value, "window_ms": win_ms, "window_alg_bytes": win_bytes,
                    "window_gbs": win_bytes / (win_ms * 1e-3) / 1e9,
                    "nonflush_avg_ms": nf_avg_ms, "nonflush_gbs": nf_gbs,
-                   "flush_ms": fl_ms, "flush_gbs": fl_gbs},
-        "conventional": {"tokens_per_s": conv_value, "step_ms": cv_ms, "gbs": cv_gbs,
+                   "nonflush_by_fill_ms": [float(x) for x in nf_ms.mean(axis=0)],
+                   "flush_ms": fl_ms, "flush_gbs": byt["flush"] * B / (fl_ms * 1e-3) / 1e9},
+        "conventional": {"tokens_per_s": conv_value, "step_ms": cv_ms,
+                         "gbs": byt["conv"] * B / (cv_ms * 1e-3) / 1e9,
                          "window_ms": total_c / K, "window_alg_bytes": byt["conv"] * B * RING},
         "speedup_vs_conventional": value / conv_value,
         "bytes_ratio_conventional_over_replay": byt["conv"] * B * RING / win_bytes,
-        "gpu_wall_s": wall,
     }
+
+
+def bench_gdn(args, torch, rs):
+    w = W.GDN_QWEN
+    dev = "cuda"
+    B = w.batch
+    gp = W.gdn_params(w)
+
+    def mk(mode):
+        cfg = rs.make_config(rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk, n_v_heads=w.n_v, head_k_dim=w.dk,
+                             head_v_dim=w.dv, in_dtype=rs.RS_BF16)
+        _, layer = rs.rs_init(cfg)
+        return layer, rs.alloc_buffers(layer, dev)
+
+    rl, rb = mk(rs.RS_REPLAY)
+    cl, cb = mk(rs.RS_CONVENTIONAL)
+    ck = rs.ckpt_f32_view(rl, rb)
+    for b in range(B):
+        ck[b].copy_(torch.from_numpy(np.ascontiguousarray(W.gdn_init_state(w, b).transpose(0, 2, 1))).to(dev))
+    rs.ckpt_f32_view(cl, cb).copy_(ck)
+    pool = []
+    for t in range(RING):
+        tk = W.gdn_step(w, t, range(B), gp)
+        d = {k: _bf16_dev(torch, tk[k], dev) for k in ("q", "k", "v")}
+        d["g"] = torch.from_numpy(tk["g"]).to(dev)
+        d["beta"] = torch.from_numpy(tk["beta"]).to(dev)
+        pool.append(d)
+    o = torch.empty(B, w.n_v, w.dv, dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+
+    def replay_window(ev):
+        for t in range(RING):
+            fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
+            _marked(ev, t, tm.stream, lambda: fn(rl, rb, pool[t], None, None, o))
+
+    def conv_window(ev):
+        for t in range(RING):
+            _marked(ev, t, tm.stream, lambda: rs.rs_step_conventional(cl, cb, pool[t], None, None, o))
+
+    K, warm = args.steps, args.warmup
+    total_r, per_r = tm.run(replay_window, K, warm, RING)
+    total_c, per_c = tm.run(conv_window, K, warm, RING)
+    byt = gdn_bytes(w)
+    ntok = B * RING * K
+    nf_ms = per_r[:, : RING - 1]
+    nf_bytes = sum(byt["nonflush"][j] for j in range(1, RING)) * B
+    nf_gbs = nf_bytes / (nf_ms.sum(axis=1).mean() * 1e-3) / 1e9
+    fl_ms = float(per_r[:, RING - 1].mean())
+    cv_ms = float(per_c.mean())
+    win_bytes = nf_bytes + byt["flush"] * B
+    value = ntok / (total_r * 1e-3)
+    conv_value = ntok / (total_c * 1e-3)
+    return {
+        "metric": "GDN-layer decode tokens/s at batch 256 + achieved HBM GB/s vs conventional",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm, "ms_per_step": total_r / K,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_qk": w.n_qk, "n_v": w.n_v, "dk": w.dk, "dv": w.dv,
+                   "inputs": "bf16", "checkpoint": "f32", "step": "one 16-token window: 15 non-flush + 1 flush"},
+        "roofline": {"bound": "hbm", "achieved": nf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nf_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "gdn_nonflush_kernel",
+                     "avg_launch_ms": float(nf_ms.mean()), "alg_bytes_per_launch": nf_bytes / (RING - 1)},
+        "replay": {"tokens_per_s": value, "window_ms": total_r / K, "window_alg_bytes": win_bytes,
+                   "window_gbs": win_bytes / (total_r / K * 1e-3) / 1e9, "nonflush_avg_ms": float(nf_ms.mean()),
+                   "nonflush_by_fill_ms": [float(x) for x in nf_ms.mean(axis=0)],
+                   "flush_ms": fl_ms, "flush_gbs": byt["flush"] * B / (fl_ms * 1e-3) / 1e9},
+        "conventional": {"tokens_per_s": conv_value, "step_ms": cv_ms,
+                         "gbs": byt["conv"] * B / (cv_ms * 1e-3) / 1e9},
+        "speedup_vs_conventional": value / conv_value,
+        "bytes_ratio_conventional_over_replay": byt["conv"] * B * RING / win_bytes,
+    }
+
+
+def bench_spec(args, torch, rs):
+    w = W.M2_SPEC
+    dev = "cuda"
+    B, K = w.batch, w.max_draft
+    p = W.m2_params(w)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    rl, rb = _m2_layer(rs, w, B, rs.RS_REPLAY, dev, max_draft=K)
+    cl, cb = _m2_layer(rs, w, B, rs.RS_CONVENTIONAL, dev, max_draft=K)
+    _m2_load_init(torch, rs, w, rl, rb, dev)
+    rs.ckpt_f32_view(cl, cb).copy_(rs.ckpt_f32_view(rl, rb))
+    rounds = args.spec_rounds
+    # a pool of 8 rounds of draft inputs (reused cyclically) and the seeded acceptance of every round
+    npool = min(rounds, 8)
+    drafts = []
+    for r in range(npool):
+        toks = [W.m2_step(w, r * K + d, range(B)) for d in range(K)]
+        drafts.append({k: _bf16_dev(torch, np.stack([t[k] for t in toks]), dev) for k in ("x", "B", "C", "dt")})
+    accs_np = [W.accepted_counts(w.seed, r, B, K) for r in range(rounds)]
+    accs = [torch.from_numpy(a).to(dev) for a in accs_np]
+    committed = int(sum(a.sum() for a in accs_np))
+    y = torch.empty(K, B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+    st = tm.stream
+
+    def replay_all(ev):
+        for r in range(rounds):
+            _marked(ev, 2 * r, st, lambda: rs.rs_spec_append(rl, rb, drafts[r % npool], K, A, D, y))
+            _marked(ev, 2 * r + 1, st, lambda: rs.rs_spec_commit(rl, rb, accs[r], A, D))
+
+    def snap_all(ev):
+        for r in range(rounds):
+            _marked(ev, 2 * r, st, lambda: rs.rs_spec_append(cl, cb, drafts[r % npool], K, A, D, y))
+            _marked(ev, 2 * r + 1, st, lambda: rs.rs_spec_commit(cl, cb, accs[r], A, D))
+
+    # one timed "step" = all rounds; the buffer counters restart from empty for the timed pass
+    total_r, per_r = tm.run(replay_all, 1, 1, 2 * rounds, reset=lambda: rb.meta.zero_())
+    total_c, per_c = tm.run(snap_all, 1, 1, 2 * rounds)
+    S = w.nheads * w.headdim * w.dstate * 4
+    return {
+        "metric": "speculative decode committed tokens/s at batch 512, 4 drafts (ReplaySSM vs snapshot/restore)",
+        "value": committed / (total_r * 1e-3), "unit": "committed tokens/s", "n_gpus": 1, "steps": 1,
+        "warmup": 1, "ms_per_step": total_r, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "drafts": K, "rounds": rounds, "accepted": "U{0..4} per round",
+                   "mean_accepted": committed / (rounds * B), "step": f"{rounds} rounds of append + commit"},
+        "replay": {"append_ms": float(per_r[0, 0::2].mean()), "commit_ms": float(per_r[0, 1::2].mean()),
+                   "round_ms": total_r / rounds,
+                   "append_ckpt_read_gbs": S * B / (per_r[0, 0::2].mean() * 1e-3) / 1e9},
+        "snapshot_baseline": {"committed_tokens_per_s": committed / (total_c * 1e-3),
+                              "append_ms": float(per_c[0, 0::2].mean()), "restore_ms": float(per_c[0, 1::2].mean()),
+                              "round_ms": total_c / rounds},
+        "speedup_vs_snapshot": total_c / total_r,
+    }
+
+
+LOWPREC_VARIANTS = [("f32", None), ("f32", "nvfp4"), ("f16", "nvfp4"), ("fp8", "nvfp4"), ("f16", None),
+                    ("fp8", None), ("nvfp4", None)]
+
+
+def bench_lowprec(args, torch, rs):
+    w = W.M2_LOWPREC
+    dev = "cuda"
+    B = w.batch
+    p = W.m2_params(w)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    code = {"f32": rs.RS_F32, "f16": rs.RS_F16, "fp8": rs.RS_FP8E4M3, "nvfp4": rs.RS_NVFP4}
+    ebytes = {"f32": 4.0, "f16": 2.0, "fp8": 1.0 + 4.0 / 8192, "nvfp4": 0.5 + 1.0 / 16 + 4.0 / 8192}
+    pool = _m2_pool(torch, w, B, dev)
+    y = torch.empty(B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+    out = {"metric": "low-precision-read decode tokens/s, Mamba-2 batch 64 (per checkpoint / read-copy format)",
+           "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": w.name, "batch": B, "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
+                      "note": "state 256 MiB at batch 64 fits the 256 MB last-level cache; GB/s are effective"},
+           "variants": {}}
+    for fmt, rc in LOWPREC_VARIANTS:
+        layer, bufs = _m2_layer(rs, w, B, rs.RS_REPLAY, dev, ckpt=code[fmt],
+                                read_copy=rs.RS_NVFP4 if rc else None, fuse=1)
+
+        def window(ev):
+            for t in range(RING):
+                fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
+                _marked(ev, t, tm.stream, lambda: fn(layer, bufs, pool[t], A, D, y))
+
+        total, per = tm.run(window, args.steps, args.warmup, RING)
+        byt = m2_bytes(w, ebytes[fmt], ebytes["nvfp4"] if rc else None)
+        win_bytes = sum(byt["nonflush"].values()) * B + byt["flush"] * B
+        name = fmt + ("+nvfp4_reads" if rc else "")
+        out["variants"][name] = {"tokens_per_s": B * RING * args.steps / (total * 1e-3),
+                                 "window_ms": total / args.steps, "window_alg_bytes": win_bytes,
+                                 "window_gbs": win_bytes / (total / args.steps * 1e-3) / 1e9,
+                                 "nonflush_avg_ms": float(per[:, :RING - 1].mean()),
+                                 "flush_ms": float(per[:, RING - 1].mean())}
+        del layer, bufs
+        torch.cuda.empty_cache()
+    out["value"] = out["variants"]["f32+nvfp4_reads"]["tokens_per_s"]
+    out["ms_per_step"] = out["variants"]["f32+nvfp4_reads"]["window_ms"]
+    if args.lowprec_error_steps:
+        out["error_over_length"] = lowprec_error(args, torch, rs)
     return out
+
+
+def lowprec_error(args, torch, rs):
+    """Relative L2 error of y vs the fp64 recurrence over length, per format, on a
+    few sequences of the low-precision workload (inputs drawn step by step)."""
+    from oracle import decode
+    w = W.M2_LOWPREC
+    nb = args.lowprec_error_seqs
+    dev = "cuda"
+    p = W.m2_params(w)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    code = {"f32": rs.RS_F32, "f16": rs.RS_F16, "fp8": rs.RS_FP8E4M3, "nvfp4": rs.RS_NVFP4}
+    layers = {}
+    for fmt, rc in LOWPREC_VARIANTS:
+        layers[fmt + ("+nvfp4_reads" if rc else "")] = _m2_layer(rs, w, nb, rs.RS_REPLAY, dev, ckpt=code[fmt],
+                                                                 read_copy=rs.RS_NVFP4 if rc else None, fuse=1)
+    exact = decode.M2Conventional(W.m2_init_states(w, range(nb)), p["A"], p["D"])
+    y = torch.empty(nb, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    steps = args.lowprec_error_steps
+    every = max(1, steps // 16)
+    curve = {k: [] for k in layers}
+    acc = {k: [0.0, 0.0] for k in layers}
+    for t in range(steps):
+        tk = W.m2_step(w, t, range(nb))
+        dtk = {k: _bf16_dev(torch, v, dev) for k, v in tk.items()}
+        ye = exact.step(tk)
+        for name, (layer, bufs) in layers.items():
+            fn = rs.rs_step_flush if t % RING == RING - 1 else rs.rs_step_nonflush
+            fn(layer, bufs, dtk, A, D, y)
+            yg = y.cpu().numpy().astype(np.float64)
+            acc[name][0] += float(np.sum((yg - ye) ** 2))
+            acc[name][1] += float(np.sum(ye ** 2))
+        if (t + 1) % every == 0:
+            for name in layers:
+                curve[name].append([t + 1, (acc[name][0] / acc[name][1]) ** 0.5])
+                acc[name] = [0.0, 0.0]
+            print(f"lowprec error: step {t + 1} of {steps}", file=sys.stderr, flush=True)
+    return {"sequences": nb, "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
 
 
 def main():
@@ -244,18 +494,27 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "lowprec"],
+                    help="workloads to run (default: mamba2 only); repeat for several")
+    ap.add_argument("--spec-rounds", type=int, default=64)
+    ap.add_argument("--lowprec-error-steps", type=int, default=0)
+    ap.add_argument("--lowprec-error-seqs", type=int, default=2)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step needs no "
               f"collective, so N GPUs would each run this single-GPU workload on their own batch shard.",
               file=sys.stderr)
         sys.exit(2)
-    out = run_gpu(args)
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(W.M2_NEMOTRON, args.cpu_seqs, windows=2)
-    else:
-        out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    import torch
+    import ssm_decode_checkpoint_amd as rs
+    torch.cuda.set_device(0)
+    for wl in (args.workload or ["mamba2"]):
+        fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec}[wl]
+        out = fn(args, torch, rs)
+        if wl == "mamba2":
+            out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(W.M2_NEMOTRON, args.cpu_seqs, windows=2)
+        print(json.dumps(out), flush=True)
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -67,7 +67,11 @@
  *   checkpoint  RS_F32: float [batch][Hv][dk][dv]; element S[b][h][v][k] is at
  *               ((b*Hv + h)*dk + k)*dv + v.
  *   ring        q and k [batch][Hk][R][dk] (in_dtype), v [batch][Hv][R][dv]
- *               (in_dtype), g and beta float [batch][Hv][R].
+ *               (in_dtype), g and beta float [batch][Hv][R]; and, beside each
+ *               held entry i, u float [batch][Hv][R][dv]: its row of the
+ *               triangular system u_i = beta_i (v_i - alpha_i S_{i-1} k_i),
+ *               which depends only on the checkpoint and entries <= i, so the
+ *               library writes it once, on the step that appends entry i.
  *   inputs      q, k [batch][Hk][dk], v [batch][Hv][dv] (in_dtype);
  *               g (= log alpha) and beta: float [batch][Hv].
  *   output      o: float [batch][Hv][dv].
@@ -164,6 +168,7 @@ typedef struct rs_layer {
   /* ring arrays, byte offsets into the ring buffer */
   uint64_t ring_x_off, ring_B_off, ring_C_off, ring_dt_off;               /* Mamba-2 */
   uint64_t ring_q_off, ring_k_off, ring_v_off, ring_g_off, ring_beta_off; /* GDN */
+  uint64_t ring_u_off;   /* GDN: solution row u of each held entry (library-maintained) */
   /* checkpoint extras, byte offsets into the checkpoint buffer */
   uint64_t ck_scale_off;                     /* RS_FP8E4M3 per-matrix scales */
   uint64_t ck_nv_scale_off, ck_nv_tscale_off;/* RS_NVFP4 checkpoint */

@@ -42,7 +42,7 @@ class RsLayer(C.Structure):
                 ("cols", C.c_int32)] + [(n, C.c_uint64) for n in (
                     "ckpt_bytes", "ring_bytes", "read_copy_bytes", "meta_bytes", "snap_bytes",
                     "ring_x_off", "ring_B_off", "ring_C_off", "ring_dt_off",
-                    "ring_q_off", "ring_k_off", "ring_v_off", "ring_g_off", "ring_beta_off",
+                    "ring_q_off", "ring_k_off", "ring_v_off", "ring_g_off", "ring_beta_off", "ring_u_off",
                     "ck_scale_off", "ck_nv_scale_off", "ck_nv_tscale_off", "nv_scale_off", "nv_tscale_off",
                     "meta_work_off")] + [("magic", C.c_uint32), ("reserved", C.c_uint32)]
 

@@ -160,6 +160,7 @@ GDNArgs gdn_args(const rs_layer* L, const rs_buffers* buf) {
     a.rv = r + L->ring_v_off;
     a.rg = r + L->ring_g_off;
     a.rbeta = r + L->ring_beta_off;
+    a.ru = r + L->ring_u_off;
     a.meta = static_cast<rs_meta*>(buf->meta);
   }
   return a;
@@ -260,6 +261,7 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
       L.ring_v_off = off; off = align_up(off + B * c.n_v_heads * kRing * c.head_v_dim * sin);
       L.ring_g_off = off; off = align_up(off + B * c.n_v_heads * kRing * 4);
       L.ring_beta_off = off; off = align_up(off + B * c.n_v_heads * kRing * 4);
+      L.ring_u_off = off; off = align_up(off + B * c.n_v_heads * kRing * c.head_v_dim * 4);
     }
     L.ring_bytes = off;
     L.meta_work_off = align_up(B * sizeof(rs_meta));

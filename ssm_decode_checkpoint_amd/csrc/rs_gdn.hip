@@ -12,11 +12,16 @@
 // (sitech.ge ReplaySSM page, "How ReplaySSM works": output from checkpoint +
 // buffer without a state write; one checkpoint write when the buffer fills.)
 //
+// The u_t are the rows of the unit lower-triangular system (I + L) U =
+// diag(beta)(V - diag(gamma) K S0^T) solved by forward substitution. Row t
+// depends only on S0 and entries <= t, so it is solved once, on the step that
+// appends entry t, and kept beside that entry in the ring; every step then
+// needs just S0 k_j and S0 q_j from its single read of S0, plus length-dv
+// vector work over the held rows.
+//
 // One 256-thread workgroup per (sequence, value head) state, stored as
 // [dk][dv] (value index innermost) so that S0 k and S0 q are sums over rows
-// held in registers. The j+1 matrix-vector products S0 [k_1 .. k_j, q_j]
-// share the single read of S0; the triangular solve (size <= 16) and the
-// output combination run on LDS vectors of length dv.
+// held in registers.
 #include "rs_device.h"
 #include "rs_tile.h"
 #include "rs_internal.h"
@@ -27,32 +32,19 @@ namespace {
 
 template <int NK, int NV>
 struct GSmem {
-  float W[kRing + 4][NK];    // k_1 .. k_m, then q, then zero rows up to the matvec chunk
-  float V[kRing][NV];        // v_i; reused for the fold columns r_{m,i} u_i
-  float U[kRing][NV];        // u_i
-  float out[kRing + 4][NV];  // S0 W_r
+  float K[kRing][NK];    // k of entries 0..m-1
+  float W[4][NK];        // matvec weights: k_cur, q, 0, 0
+  float U[kRing][NV];    // u of entries 0..m-1 (the current one computed here)
+  float vc[NV];          // v of the current token
+  float out[4][NV];      // S0 k_cur, S0 q
   float red[4 * 4 * NV];
-  float KK[kRing][kRing];    // beta_i r_{i,l} (k_i . k_l), l < i
-  float coef[kRing];         // r_{j,i} (k_i . q_j)
-  float al[kRing], be[kRing], gam[kRing];
+  float kk[kRing];       // beta_cur r_{cur,i} (k_cur . k_i), i < cur
+  float kq[kRing];       // r_{cur,i} (k_i . q), i <= cur
+  float rr[kRing];       // r_{cur,i}
+  float al[kRing];
+  float gam, bet;
   float s4[4];
 };
-
-template <typename TIN>
-__device__ __forceinline__ const TIN* ring_row(const TIN* base, long long nck, int e, int width) {
-  return base + static_cast<size_t>((nck + e) & (kRing - 1)) * width;
-}
-
-// Load n records (entries 0..n-1: ring for e < nring, `cur` for e == nring) into LDS rows.
-template <typename TIN>
-__device__ __forceinline__ void stage(float* dst, int stride, const TIN* ring, const TIN* cur, long long nck,
-                                      int nring, int n, int width) {
-  for (int idx = threadIdx.x; idx < n * width; idx += kThreads) {
-    const int e = idx / width, r = idx - e * width;
-    const TIN* src = e < nring ? ring_row(ring, nck, e, width) : cur;
-    dst[e * stride + r] = to_f(src[r]);
-  }
-}
 
 struct GPtrs {
   size_t tile;
@@ -68,96 +60,87 @@ __device__ __forceinline__ GPtrs gdn_tile(const GDNArgs& a) {
   return p;
 }
 
-// Stage entries 0..m-1 (k into W rows, v into V rows, alpha, beta), with the
-// current token as entry m-1 when cur is true, and the read vector q into W[m].
+__device__ __forceinline__ int slot_of(long long nck, int e) { return static_cast<int>((nck + e) & (kRing - 1)); }
+
+// Stage the window's entries 0..m-1 (entry m-1 is the current token, the
+// others come from the ring): k rows, u rows of the held entries, the decays,
+// and the current v, beta, and the matvec weights [k_cur, q, 0, 0].
 template <typename TIN, int NK, int NV>
 __device__ __forceinline__ void gdn_stage(GSmem<NK, NV>& s, const GDNArgs& a, const GPtrs& p, long long nck,
-                                          int nring, int m, bool with_q) {
+                                          int m) {
+  const int held = m - 1;
   const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
   const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
-  const TIN* rv = static_cast<const TIN*>(a.rv) + p.tile * kRing * NV;
+  const float* ru = static_cast<const float*>(a.ru) + p.tile * kRing * NV;
   const float* rg = static_cast<const float*>(a.rg) + p.tile * kRing;
-  const float* rbt = static_cast<const float*>(a.rbeta) + p.tile * kRing;
   const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
+  const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
   const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
-  stage(&s.W[0][0], NK, rk, ik, nck, nring, m, NK);
-  stage(&s.V[0][0], NV, rv, iv, nck, nring, m, NV);
-  if (with_q) {
-    const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
-    for (int i = threadIdx.x; i < NK; i += kThreads) s.W[m][i] = to_f(iq[i]);
+  for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) {
+    const int e = idx / NK, n = idx - e * NK;
+    s.K[e][n] = to_f(e < held ? rk[slot_of(nck, e) * NK + n] : ik[n]);
   }
-  // zero the rows after the staged ones that a 4-wide matvec chunk may read
-  // (up to the end of the chunk holding the last row, and the 4 rows from q)
-  const int used = m + (with_q ? 1 : 0);
-  int end = (used + 3) & ~3;
-  if (with_q && end < m + 4) end = m + 4;
-  for (int idx = used * NK + threadIdx.x; idx < end * NK; idx += kThreads) (&s.W[0][0])[idx] = 0.0f;
+  for (int idx = threadIdx.x; idx < held * NV; idx += kThreads) {
+    const int e = idx / NV, v = idx - e * NV;
+    s.U[e][v] = ru[slot_of(nck, e) * NV + v];
+  }
+  for (int n = threadIdx.x; n < NK; n += kThreads) {
+    s.W[0][n] = to_f(ik[n]);
+    s.W[1][n] = to_f(iq[n]);
+    s.W[2][n] = 0.0f;
+    s.W[3][n] = 0.0f;
+  }
+  for (int v = threadIdx.x; v < NV; v += kThreads) s.vc[v] = to_f(iv[v]);
   if (static_cast<int>(threadIdx.x) < m) {
     const int e = threadIdx.x;
-    const bool ring = e < nring;
-    const float g = ring ? rg[(nck + e) & (kRing - 1)] : a.g[p.tile];
-    const float bt = ring ? rbt[(nck + e) & (kRing - 1)] : a.beta[p.tile];
-    s.al[e] = expf(g);
-    s.be[e] = bt;
+    s.al[e] = expf(e < held ? rg[slot_of(nck, e)] : a.g[p.tile]);
   }
+  if (threadIdx.x == 0) s.bet = a.beta[p.tile];
 }
 
-// S0 W_r for rows r < rows (in chunks of four weight vectors); results in s.out.
+// Dots and decays for the current entry cur = m-1 (after staging is visible):
+//   kk[i] = beta_cur r_{cur,i} (k_cur . k_i) for i < cur
+//   kq[i] = r_{cur,i} (k_i . q) for i <= cur;  rr[i] = r_{cur,i};  gam = gamma_cur
 template <int NK, int NV>
-__device__ __forceinline__ void gdn_products(const RegTile<4, NK, NV>& S, GSmem<NK, NV>& s, int rows) {
-  for (int q0 = 0; q0 < rows; q0 += 4) tile_matvec<4>(S, &s.W[q0][0], NK, s.red, &s.out[q0][0]);
-}
-
-// r_{t,i} = prod_{i<l<=t} alpha_l (0-based entries)
-__device__ __forceinline__ float decay_between(const float* al, int i, int t) {
-  float r = 1.0f;
-  for (int l = i + 1; l <= t; ++l) r *= al[l];
-  return r;
-}
-
-// Gram terms, gammas, then u_0..u_{m-1} by forward substitution (u in s.U).
-// If with_q, also coef[i] = r_{m-1,i} (k_i . q) for the output.
-template <int NK, int NV>
-__device__ __forceinline__ void gdn_solve(GSmem<NK, NV>& s, int m, bool with_q) {
+__device__ __forceinline__ void gdn_dots(GSmem<NK, NV>& s, int m) {
+  const int cur = m - 1;
   const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
-  // pairs (i, l) with l < i < m, plus (i, q) for i < m when with_q
-  const int npair = m * (m - 1) / 2;
-  const int ntot = npair + (with_q ? m : 0);
-  for (int pr = grp; pr < ntot; pr += kThreads / 16) {
-    int i, l;
-    if (pr < npair) {
-      i = 1;
-      int rem = pr;
-      while (rem >= i) { rem -= i; ++i; }
-      l = rem;
-    } else {
-      i = pr - npair;
-      l = m;  // the q row
-    }
+  for (int pr = grp; pr < 2 * m - 1; pr += kThreads / 16) {
+    const bool isq = pr >= cur;
+    const int i = isq ? pr - cur : pr;
+    const float* other = isq ? &s.W[1][0] : &s.K[cur][0];
     float part = 0.0f;
-    for (int n = ln; n < NK; n += 16) part += s.W[i][n] * s.W[l][n];
+    for (int n = ln; n < NK; n += 16) part += s.K[i][n] * other[n];
     part = group_sum16(part);
     if (ln == 0) {
-      if (l < m) s.KK[i][l] = s.be[i] * decay_between(s.al, l, i) * part;
-      else s.coef[i] = decay_between(s.al, i, m - 1) * part;
+      float r = 1.0f;
+      for (int l = i + 1; l <= cur; ++l) r *= s.al[l];
+      if (isq) {
+        s.kq[i] = r * part;
+        s.rr[i] = r;
+      } else {
+        s.kk[i] = s.bet * r * part;
+      }
     }
   }
   if (threadIdx.x == 0) {
     float gm = 1.0f;
-    for (int e = 0; e < m; ++e) {
-      gm *= s.al[e];
-      s.gam[e] = gm;
-    }
+    for (int e = 0; e <= cur; ++e) gm *= s.al[e];
+    s.gam = gm;
   }
-  __syncthreads();
-  for (int v = threadIdx.x; v < NV; v += kThreads) {
-    for (int i = 0; i < m; ++i) {
-      float u = s.be[i] * (s.V[i][v] - s.gam[i] * s.out[i][v]);
-      for (int l = 0; l < i; ++l) u -= s.KK[i][l] * s.U[l][v];
-      s.U[i][v] = u;
-    }
-  }
-  __syncthreads();
+}
+
+// u_cur[v] = beta (v_cur - gamma S0 k_cur) - sum_{i<cur} kk[i] u_i, stored in U[cur];
+// returns o[v] = gamma S0 q + sum_{i<=cur} kq[i] u_i for the thread's column v.
+template <int NK, int NV>
+__device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NV>& s, int m, int v) {
+  const int cur = m - 1;
+  float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]);
+  for (int i = 0; i < cur; ++i) u -= s.kk[i] * s.U[i][v];
+  s.U[cur][v] = u;
+  float o = s.gam * s.out[1][v];
+  for (int i = 0; i <= cur; ++i) o += s.kq[i] * s.U[i][v];
+  return o;
 }
 
 }  // namespace
@@ -181,57 +164,56 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
     s.W[2][i] = 0.0f;
     s.W[3][i] = 0.0f;
   }
-  for (int i = threadIdx.x; i < NV; i += kThreads) s.V[0][i] = to_f(iv[i]);
+  for (int i = threadIdx.x; i < NV; i += kThreads) s.vc[i] = to_f(iv[i]);
   __syncthreads();
   // k . q (one 16-lane group)
   if (threadIdx.x < 16) {
     float part = 0.0f;
     for (int n = threadIdx.x; n < NK; n += 16) part += s.W[0][n] * s.W[1][n];
     part = group_sum16(part);
-    if (threadIdx.x == 0) s.coef[0] = part;
+    if (threadIdx.x == 0) s.kq[0] = part;
   }
   const float alpha = expf(a.g[p.tile]);
   const float beta = a.beta[p.tile];
   RegTile<4, NK, NV> S;
   raw.decode(S);
-  tile_matvec<4>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // out[0] = S k, out[1] = S q
-  for (int v = threadIdx.x; v < NV; v += kThreads) s.U[0][v] = beta * (s.V[0][v] - alpha * s.out[0][v]);
+  tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // out[0] = S k, out[1] = S q
+  for (int v = threadIdx.x; v < NV; v += kThreads) s.U[0][v] = beta * (s.vc[v] - alpha * s.out[0][v]);
   __syncthreads();
   tile_rank_update(S, alpha, &s.W[0][0], NK, &s.U[0][0], NV, 1);
   tile_store<FMT_F32>(a.ck, p.tile, S, s.s4);
-  const float kq = s.coef[0];
+  const float kq = s.kq[0];
   for (int v = threadIdx.x; v < NV; v += kThreads) a.o[p.tile * NV + v] = alpha * s.out[1][v] + kq * s.U[0][v];
 }
 
 // ----------------------------------------------------------------------------
-// non-flush step: o from checkpoint + buffer (UT form), append, no state write
+// non-flush step: o from checkpoint + buffer, append (with its u row), no state write
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV> s;
   const GPtrs p = gdn_tile(a);
+  RawTile<FMT_F32, 4, NK, NV> raw;   // start streaming before the counters arrive
+  raw.issue(a.ck, p.tile);
   rs_meta* mp = a.meta + p.b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
   if (errbit == 0) {
     const int j = len + 1;
-    RawTile<FMT_F32, 4, NK, NV> raw;
-    raw.issue(a.ck, p.tile);
-    gdn_stage<TIN>(s, a, p, nck, len, j, true);
+    gdn_stage<TIN>(s, a, p, nck, j);
     __syncthreads();
+    gdn_dots(s, j);
     RegTile<4, NK, NV> S;
     raw.decode(S);
-    gdn_products(S, s, j + 1);                 // barriers inside publish the staged rows too
-    gdn_solve(s, j, true);
-    const float gj = s.gam[j - 1];
+    tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // barriers inside publish the dots
+    const int slot = slot_of(nck, len);
+    float* ru = static_cast<float*>(a.ru) + p.tile * kRing * NV;
     for (int v = threadIdx.x; v < NV; v += kThreads) {
-      float o = gj * s.out[j][v];
-      for (int i = 0; i < j; ++i) o += s.coef[i] * s.U[i][v];
-      a.o[p.tile * NV + v] = o;
+      a.o[p.tile * NV + v] = gdn_row_and_output(s, j, v);
+      ru[slot * NV + v] = s.U[j - 1][v];
     }
     // append the current record (bit copies)
-    const int slot = static_cast<int>((nck + len) & (kRing - 1));
     const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
     TIN* rv = static_cast<TIN*>(a.rv) + p.tile * kRing * NV;
     const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
@@ -258,36 +240,33 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// flush step: fold the len stored entries and the current token, write once, o
+// flush step: fold the len held entries and the current token, write once, o
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV> s;
   const GPtrs p = gdn_tile(a);
+  RawTile<FMT_F32, 4, NK, NV> raw;
+  raw.issue(a.ck, p.tile);
   rs_meta* mp = a.meta + p.b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
   if (errbit == 0) {
-    RawTile<FMT_F32, 4, NK, NV> raw;
-    raw.issue(a.ck, p.tile);
-    gdn_stage<TIN>(s, a, p, nck, len, m, true);
+    gdn_stage<TIN>(s, a, p, nck, m);
     __syncthreads();
+    gdn_dots(s, m);
     RegTile<4, NK, NV> S;
     raw.decode(S);
-    gdn_products(S, s, m);
-    gdn_solve(s, m, false);
-    // fold columns r_{m,i} u_i into V (v is no longer needed)
-    for (int idx = threadIdx.x; idx < m * NV; idx += kThreads) {
-      const int i = idx / NV, v = idx - i * NV;
-      s.V[i][v] = decay_between(s.al, i, m - 1) * s.U[i][v];
+    tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);
+    for (int v = threadIdx.x; v < NV; v += kThreads) {
+      a.o[p.tile * NV + v] = gdn_row_and_output(s, m, v);
+      // fold columns r_{cur,i} u_i (same thread, same column v)
+      for (int i = 0; i < m; ++i) s.U[i][v] *= s.rr[i];
     }
     __syncthreads();
-    tile_rank_update(S, s.gam[m - 1], &s.W[0][0], NK, &s.V[0][0], NV, m);
-    // o = S_m q from the folded state (q sits in W[m]; W[m+1..] are zero)
-    tile_matvec<4>(S, &s.W[m][0], NK, s.red, &s.out[0][0]);
-    for (int v = threadIdx.x; v < NV; v += kThreads) a.o[p.tile * NV + v] = s.out[0][v];
+    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NV, m);
     tile_store<FMT_F32>(a.ck, p.tile, S, s.s4);
   }
   arrive_and_update(mp, a.nv, [&](rs_meta* mm) {

@@ -53,7 +53,7 @@ void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st);
 struct GDNArgs {
   int batch, nv, nqk, vpk;   // vpk = value heads per qk head
   StateBuf ck;
-  void *rq, *rk, *rv, *rg, *rbeta;
+  void *rq, *rk, *rv, *rg, *rbeta, *ru;
   rs_meta* meta;
   const void *q, *k, *v;
   const float *g, *beta;

@@ -28,18 +28,20 @@ namespace rs {
 // ----------------------------------------------------------------------------
 // staging of buffer records into LDS
 // ----------------------------------------------------------------------------
-template <int NR, int NC>
+// LDS of one Mamba-2 workgroup: NE buffer entries, Q outputs, and (XT) the
+// fold coefficients. Sized per kernel so residency is not limited by LDS.
+template <int NR, int NC, int NE, int Q, bool XT>
 struct M2Smem {
-  float B[kRing][NR];
-  float X[kRing][NC];
-  float Cw[8][NR];        // C vectors the outputs are read with (current token, or drafts)
-  float dt[kRing];
-  float a[kRing];         // exp(dt*A)
-  float w[8][kRing];      // per-output weights  w_{j,i} dt_i (B_i . C_j)
-  float L[8];             // l_j per output
-  float red[4 * 8 * NC];  // reduction scratch
-  float out[8 * NC];      // matvec results
-  float xt[kRing][NC];    // fold coefficients w_{m,i} dt_i x_i
+  float B[NE][NR];
+  float X[NE][NC];
+  float Cw[Q][NR];        // C vectors the outputs are read with (current token, or drafts)
+  float dt[NE];
+  float a[NE];            // exp(dt*A)
+  float w[Q][NE];         // per-output weights  w_{j,i} dt_i (B_i . C_j)
+  float L[Q];             // l_j per output
+  float red[4 * Q * NC];  // reduction scratch
+  float out[Q * NC];      // matvec results
+  float xt[XT ? NE : 1][NC];  // fold coefficients w_{m,i} dt_i x_i
   float s4[4];
 };
 
@@ -104,11 +106,13 @@ __device__ __forceinline__ void stage_decays(float* a, const float* dt, float A,
 // For outputs q = 0..nq-1 reading entries 0..J_q-1 (J_q = j0 + q):
 //   L[q] = prod_{l<J_q} a_l;  w[q][e] = prod_{e<l<J_q} a_l * dt_e * (B_e . C_q)
 // Dots use groups of 16 lanes (one per (q, e) pair per round).
-template <int NR, int NC>
-__device__ __forceinline__ void output_weights(M2Smem<NR, NC>& s, int j0, int nq) {
+template <typename SM>
+__device__ __forceinline__ void output_weights(SM& s, int j0, int nq) {
   const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
-  for (int pair = grp; pair < nq * kRing; pair += kThreads / 16) {
-    const int q = pair / kRing, e = pair - q * kRing;
+  constexpr int NE = sizeof(s.dt) / sizeof(float);
+  constexpr int NR = sizeof(s.B[0]) / sizeof(float);
+  for (int pair = grp; pair < nq * NE; pair += kThreads / 16) {
+    const int q = pair / NE, e = pair - q * NE;
     const int J = j0 + q;
     float part = 0.0f;
     if (e < J)
@@ -134,7 +138,7 @@ __device__ __forceinline__ void output_weights(M2Smem<NR, NC>& s, int j0, int nq
 template <typename TIN, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_conv_kernel(M2Args a) {
   constexpr int E = 4;
-  __shared__ M2Smem<NR, NC> s;
+  __shared__ M2Smem<NR, NC, 1, 1, false> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   RawTile<FMT_F32, E, NR, NC> raw;
@@ -177,17 +181,18 @@ __global__ __launch_bounds__(kThreads) void m2_conv_kernel(M2Args a) {
 template <typename TIN, int RDF, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   constexpr int E = (RDF == FMT_F32) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
+  __shared__ M2Smem<NR, NC, kRing, 1, false> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
+  // the tile address does not depend on the buffer counters: start streaming first
+  RawTile<RDF, E, NR, NC> raw;
+  raw.issue(a.rd, tile);
   rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
   if (errbit == 0) {
     const int j = len + 1;
-    RawTile<RDF, E, NR, NC> raw;
-    raw.issue(a.rd, tile);
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
     const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
     const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
 // fold body shared by the flush step and the commit fold
 // H <- l_m H + sum_e B_e xt_e^T with xt_e = w_{m,e} dt_e x_e (entries staged)
 // ----------------------------------------------------------------------------
-template <int E, int NR, int NC>
-__device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, M2Smem<NR, NC>& s, int m) {
+template <int E, int NR, int NC, typename SM>
+__device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, SM& s, int m) {
   // coefficients
   if (static_cast<int>(threadIdx.x) < m) {
     const int e = threadIdx.x;
@@ -296,17 +301,17 @@ __device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTi
 template <typename TIN, int CKF, bool RC, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
   constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
+  __shared__ M2Smem<NR, NC, kRing, 1, true> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
+  RawTile<CKF, E, NR, NC> raw;
+  raw.issue(a.ck, tile);
   rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
   if (errbit == 0) {
-    RawTile<CKF, E, NR, NC> raw;
-    raw.issue(a.ck, tile);
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
     const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
     const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
@@ -346,17 +351,17 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
 template <typename TIN, int RDF, int NR, int NC, int KQ>
 __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
   constexpr int E = (RDF == FMT_F32) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
+  __shared__ M2Smem<NR, NC, kRing, KQ, false> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const int K = a.K;
+  RawTile<RDF, E, NR, NC> raw;
+  raw.issue(a.rd, tile);
   rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = (nd != 0 || len + K > kRing) ? RS_ERR_OVERFLOW : 0;
   if (errbit == 0) {
-    RawTile<RDF, E, NR, NC> raw;
-    raw.issue(a.rd, tile);
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
     const size_t gstride = static_cast<size_t>(a.batch) * a.ngroups * NR;   // between drafts (B, C)
     const size_t xstride = static_cast<size_t>(a.batch) * a.nheads * NC;    // between drafts (x)
@@ -483,7 +488,7 @@ static __global__ __launch_bounds__(1024) void m2_commit_meta_kernel(M2Args a) {
 template <typename TIN, int CKF, bool RC, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
   constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
-  __shared__ M2Smem<NR, NC> s;
+  __shared__ M2Smem<NR, NC, kRing, 1, true> s;
   const int total = *a.work_count * a.nheads;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const FoldItem it = a.work[item / a.nheads];
@@ -517,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
 template <typename TIN, int NR, int NC, int KMAX>
 __global__ __launch_bounds__(kThreads) void m2_conv_spec_kernel(M2Args a) {
   constexpr int E = 4;
-  __shared__ M2Smem<NR, NC> s;
+  __shared__ M2Smem<NR, NC, KMAX, KMAX, false> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const int K = a.K;
