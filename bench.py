@@ -487,6 +487,20 @@ def lowprec_error(args, torch, rs):
     return {"sequences": nb, "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
 
 
+def bench_copy(args, torch, rs):
+    """A plain 1 GiB device copy (torch's copy kernel): the known-size reference
+    that HBM traffic counters are scaled by."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    tm = Timer(torch)
+    total, per = tm.run(lambda ev: _marked(ev, 0, tm.stream, lambda: dst.copy_(src)), args.steps, args.warmup, 1)
+    ms = float(per.mean())
+    return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,7 +508,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "lowprec"],
+    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "lowprec", "copy"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
@@ -509,7 +523,8 @@ def main():
     import ssm_decode_checkpoint_amd as rs
     torch.cuda.set_device(0)
     for wl in (args.workload or ["mamba2"]):
-        fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec}[wl]
+        fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
+              "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
         if wl == "mamba2":
             out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(W.M2_NEMOTRON, args.cpu_seqs, windows=2)
