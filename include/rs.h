@@ -154,7 +154,7 @@ typedef struct rs_meta {
   int32_t len;           /* committed buffer entries */
   int32_t nd;            /* pending draft entries */
   int32_t err;           /* sticky RS_ERR_* bits */
-  uint32_t arrive;       /* library-internal; zero between calls */
+  uint32_t arrive;       /* reserved, zero */
   int32_t reserved[2];
 } rs_meta;
 

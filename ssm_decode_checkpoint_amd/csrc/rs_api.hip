@@ -309,10 +309,12 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const MetaOp mop = flush ? MetaOp::Flush : MetaOp::NonFlush;
   if (L->cfg.kind == RS_GDN) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(flush ? GDNOp::Flush : GDNOp::NonFlush, a, gdn_launch_cfg(L), st);
+    meta_advance(a.meta, L->cfg.batch, mop, 0, st);
     return launched();
   }
   M2Args a;
@@ -321,6 +323,7 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (rs_status s = m2_inputs(in, prm, &a)) return s;
   a.y = y;
   m2_launch(flush ? M2Op::Flush : M2Op::NonFlush, a, l, st);
+  meta_advance(a.meta, L->cfg.batch, mop, 0, st);
   return launched();
 }
 
@@ -354,6 +357,7 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
     m2_launch(M2Op::ConvSpec, a, l, st);
   } else {
     m2_launch(M2Op::SpecAppend, a, l, st);
+    meta_advance(a.meta, L->cfg.batch, MetaOp::Append, K, st);
   }
   return launched();
 }

@@ -11,8 +11,6 @@
 //   covers it in passes, each thread owns E consecutive columns of one row per
 //   pass, so reductions over rows stay in registers and only the final partial
 //   sums cross lanes;
-// - the per-sequence arrival counter that lets the last workgroup of a
-//   sequence advance that sequence's buffer counters.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -239,25 +237,6 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
   if ((nblocks & 7) != 0) return bid;
   const int per = nblocks >> 3;
   return (bid & 7) * per + (bid >> 3);
-}
-
-// Arrival at the end of a per-sequence step: the last of `expected`
-// workgroups of the sequence applies `update` to its meta record and resets
-// the counter. Every workgroup of the sequence consumed its read of the
-// record before arriving, so nobody reads it after it changes within this
-// launch; the next launch sees the update through the kernel boundary. No
-// device-wide fence is needed (on gfx950 one would write back and invalidate
-// the XCD's whole L2 from every workgroup).
-template <typename F>
-__device__ __forceinline__ void arrive_and_update(rs_meta* m, int expected, F update) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomicAdd(&m->arrive, 1u);
-    if (old == static_cast<uint32_t>(expected - 1)) {
-      update(m);
-      atomicExch(&m->arrive, 0u);
-    }
-  }
 }
 
 }  // namespace rs

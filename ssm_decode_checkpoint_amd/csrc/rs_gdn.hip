@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   const GPtrs p = gdn_tile(a);
   RawTile<FMT_F32, 4, NK, NV> raw;   // start streaming before the counters arrive
   raw.issue(a.ck, p.tile);
-  rs_meta* mp = a.meta + p.b;
+  const rs_meta* mp = a.meta + p.b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
@@ -233,10 +233,6 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
       }
     }
   }
-  arrive_and_update(mp, a.nv, [&](rs_meta* m) {
-    if (errbit) m->err |= errbit;
-    else m->len = len + 1;
-  });
 }
 
 // ----------------------------------------------------------------------------
@@ -248,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
   const GPtrs p = gdn_tile(a);
   RawTile<FMT_F32, 4, NK, NV> raw;
   raw.issue(a.ck, p.tile);
-  rs_meta* mp = a.meta + p.b;
+  const rs_meta* mp = a.meta + p.b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
@@ -269,14 +265,6 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
     tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NV, m);
     tile_store<FMT_F32>(a.ck, p.tile, S, s.s4);
   }
-  arrive_and_update(mp, a.nv, [&](rs_meta* mm) {
-    if (errbit) {
-      mm->err |= errbit;
-    } else {
-      mm->n_ckpt = nck + m;
-      mm->len = 0;
-    }
-  });
 }
 
 // ----------------------------------------------------------------------------

@@ -46,6 +46,10 @@ struct M2Launch {
   int grid;
 };
 
+// Counter advance that follows a step kernel (the step kernels only read the counters).
+enum class MetaOp { NonFlush = 0, Flush = 1, Append = 2 };
+void meta_advance(rs_meta* meta, int batch, MetaOp op, int K, hipStream_t st);
+
 bool m2_shape_supported(int dstate, int headdim);
 void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st);
 

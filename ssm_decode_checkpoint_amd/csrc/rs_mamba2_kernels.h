@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   // the tile address does not depend on the buffer counters: start streaming first
   RawTile<RDF, E, NR, NC> raw;
   raw.issue(a.rd, tile);
-  rs_meta* mp = a.meta + b;
+  const rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
@@ -230,10 +230,6 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
       }
     }
   }
-  arrive_and_update(mp, a.nheads, [&](rs_meta* m) {
-    if (errbit) m->err |= errbit;
-    else m->len = len + 1;
-  });
 }
 
 // ----------------------------------------------------------------------------
@@ -306,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   RawTile<CKF, E, NR, NC> raw;
   raw.issue(a.ck, tile);
-  rs_meta* mp = a.meta + b;
+  const rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
@@ -334,14 +330,6 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
       a.y[static_cast<size_t>(tile) * NC + p] = s.out[p] + Dh * s.X[m - 1][p];
     store_folded<CKF, RC>(a, tile, H, s.s4);
   }
-  arrive_and_update(mp, a.nheads, [&](rs_meta* mm) {
-    if (errbit) {
-      mm->err |= errbit;
-    } else {
-      mm->n_ckpt = nck + m;
-      mm->len = 0;
-    }
-  });
 }
 
 // ----------------------------------------------------------------------------
@@ -357,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
   const int K = a.K;
   RawTile<RDF, E, NR, NC> raw;
   raw.issue(a.rd, tile);
-  rs_meta* mp = a.meta + b;
+  const rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = (nd != 0 || len + K > kRing) ? RS_ERR_OVERFLOW : 0;
@@ -414,10 +402,6 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
       }
     }
   }
-  arrive_and_update(mp, a.nheads, [&](rs_meta* m) {
-    if (errbit) m->err |= errbit;
-    else m->nd = K;
-  });
 }
 
 // ----------------------------------------------------------------------------
