@@ -76,14 +76,8 @@ __device__ __forceinline__ void gdn_stage(GSmem<NK, NV>& s, const GDNArgs& a, co
   const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
   const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
   const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
-  for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) {
-    const int e = idx / NK, n = idx - e * NK;
-    s.K[e][n] = to_f(e < held ? rk[slot_of(nck, e) * NK + n] : ik[n]);
-  }
-  for (int idx = threadIdx.x; idx < held * NV; idx += kThreads) {
-    const int e = idx / NV, v = idx - e * NV;
-    s.U[e][v] = ru[slot_of(nck, e) * NV + v];
-  }
+  stage_rows(&s.K[0][0], NK, EntrySrc<TIN>{rk, ik, 0, nck, held, NK}, m);
+  stage_rows(&s.U[0][0], NV, EntrySrc<float>{ru, ru, 0, nck, held, NV}, held);
   for (int n = threadIdx.x; n < NK; n += kThreads) {
     s.W[0][n] = to_f(ik[n]);
     s.W[1][n] = to_f(iq[n]);

@@ -94,6 +94,46 @@ __device__ __forceinline__ void tile_matvec(const RegTile<E, NR, NC>& M, const f
   __syncthreads();
 }
 
+// out[t][col] = sum_rows M_t[row][col] * w[row] for T held matrices and one
+// LDS weight vector; `red` is 4*T*NC floats of LDS, `out` T*NC. Barriers inside.
+template <int T, int E, int NR, int NC>
+__device__ __forceinline__ void tiles_matvec(const RegTile<E, NR, NC> (&M)[T], const float* w, float* red,
+                                             float* out) {
+  using TM = TileMap<E, NR, NC>;
+  float acc[T][E];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[t][i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < TM::PASSES; ++k) {
+    const int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
+    if (row < NR) {
+      const float wr = w[row];
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < E; ++i) acc[t][i] += M[t].v[k][i] * wr;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int i = 0; i < E; ++i) acc[t][i] = wave_sum_stride(acc[t][i], TM::TPR);
+  if (lane < TM::TPR) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int i = 0; i < E; ++i) red[(wave * T + t) * NC + lane * E + i] = acc[t][i];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * NC; idx += kThreads) {
+    out[idx] = (red[idx] + red[T * NC + idx]) + (red[2 * T * NC + idx] + red[3 * T * NC + idx]);
+  }
+  __syncthreads();
+}
+
 // Workgroup max of |M|; every thread gets it. Contains barriers.
 template <int E, int NR, int NC>
 __device__ __forceinline__ float tile_absmax(const RegTile<E, NR, NC>& M, float* scratch4) {
@@ -261,6 +301,59 @@ __device__ __forceinline__ void tile_rank_update(RegTile<E, NR, NC>& H, float L,
 #pragma unroll
         for (int i = 0; i < E; ++i) H.v[k][i] += br * xc[i];
       }
+    }
+  }
+}
+
+// Where buffer entry e of the current window comes from: the ring (e < nring)
+// or a token array (entries nring.. come from `tok` stacked with stride tstride).
+template <typename TIN>
+struct EntrySrc {
+  const TIN* ring;      // this sequence/head (or group) ring base: [kRing][len]
+  const TIN* tok;       // first new token's record
+  size_t tstride;       // elements between consecutive new tokens
+  long long nck;        // n_ckpt
+  int nring;            // entries held in the ring
+  int width;            // record length
+  __device__ __forceinline__ const TIN* at(int e) const {
+    return e < nring ? ring + static_cast<size_t>((nck + e) & (kRing - 1)) * width
+                     : tok + static_cast<size_t>(e - nring) * tstride;
+  }
+};
+
+// 16-byte chunk of input elements -> floats
+__device__ __forceinline__ void unpack16(const uint4& u, const float*, float* d) {
+  d[0] = __uint_as_float(u.x); d[1] = __uint_as_float(u.y); d[2] = __uint_as_float(u.z); d[3] = __uint_as_float(u.w);
+}
+__device__ __forceinline__ void unpack16(const uint4& u, const bf16*, float* d) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    d[2 * i] = __uint_as_float(w[i] << 16);
+    d[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// Copy n records of src.width elements into LDS rows (stride floats apart),
+// 16 bytes per load when the record length allows it.
+template <typename TIN>
+__device__ __forceinline__ void stage_rows(float* dst, int stride, const EntrySrc<TIN>& src, int n) {
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  if (src.width % V == 0) {
+    const int per = src.width / V;
+    for (int idx = threadIdx.x; idx < n * per; idx += kThreads) {
+      const int e = idx / per, c = idx - e * per;
+      const uint4 u = *reinterpret_cast<const uint4*>(src.at(e) + c * V);
+      float t[V];
+      unpack16(u, static_cast<const TIN*>(nullptr), t);
+      float* d = dst + e * stride + c * V;
+#pragma unroll
+      for (int i = 0; i < V; ++i) d[i] = t[i];
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < n * src.width; idx += kThreads) {
+      const int e = idx / src.width, r = idx - e * src.width;
+      dst[e * stride + r] = to_f(src.at(e)[r]);
     }
   }
 }
