@@ -36,6 +36,14 @@ struct bf16 {
 __device__ __forceinline__ float to_f(float v) { return v; }
 __device__ __forceinline__ float to_f(bf16 v) { return __uint_as_float(static_cast<uint32_t>(v.u) << 16); }
 
+// Inverse of to_f for values that came from T (exact: no rounding happens).
+template <typename T>
+__device__ __forceinline__ T from_f(float v);
+template <>
+__device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ bf16 from_f<bf16>(float v) { return bf16{static_cast<uint16_t>(__float_as_uint(v) >> 16)}; }
+
 // ----------------------------------------------------------------------------
 // E4M3FN and E2M1 codecs (round to nearest, ties to even, saturating)
 // ----------------------------------------------------------------------------

@@ -125,108 +125,146 @@ __global__ __launch_bounds__(kThreads) void m2_conv_kernel(M2Args a) {
 // ----------------------------------------------------------------------------
 // non-flush step: y from checkpoint (or read copy) + buffer; append; no state write
 // ----------------------------------------------------------------------------
-// A workgroup serves HPW consecutive heads of one group: their states stream
-// in together (HPW x 32 KiB in flight), and the group's B records, the
-// current C and the dots B_i . C_j are staged and computed once for all of them.
-template <int NR, int NC, int HPW>
+// Vector loads return in issue order. The buffer records this workgroup needs
+// (<= 16 B and x rows, dt, the current C) are therefore loaded into registers
+// first, the 32 KiB state tile right after them, and only then are the records
+// moved to LDS: the state-independent work (decays, dots B_i . C_j, weights,
+// the buffer part of y) runs while the tile streams in, and the tail after
+// its arrival is one reduction and the y store.
+template <int NR, int NC>
 struct M2NfSmem {
   float B[kRing][NR];
-  float X[HPW][kRing][NC];
+  float X[kRing][NC];
   float C[NR];
-  float dt[HPW][kRing];
-  float a[HPW][kRing];
-  float dot[kRing];          // B_i . C_j
-  float w[HPW][kRing];       // w_{j,i} dt_i (B_i . C_j)
-  float L[HPW];
-  float red[4 * HPW * NC];
-  float out[HPW * NC];
+  float dt[kRing];
+  float a[kRing];
+  float w[kRing];            // w_{j,i} dt_i (B_i . C_j)
+  float L;
+  float red[4 * NC];
+  float out[NC];
 };
 
-template <typename TIN, int RDF, int NR, int NC, int HPW>
+// Up to CH 16-byte chunks per thread of a record region, loaded into registers.
+template <typename TIN, int CH>
+struct RegChunks {
+  uint4 c[CH];
+  // region of n records of `width` elements: record e comes from src(e)
+  template <typename SRC>
+  __device__ __forceinline__ void load(const SRC& src, int n, int width) {
+    constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+    const int per = width / V;
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      q = q < n * per ? q : 0;   // unconditional load from a valid record (n >= 1)
+      const int e = q / per, k = q - e * per;
+      c[r] = *reinterpret_cast<const uint4*>(src.at(e) + k * V);
+    }
+  }
+  __device__ __forceinline__ void to_lds(float* dst, int stride, int n, int width) const {
+    constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+    const int per = width / V;
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      const int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      if (q < n * per) {
+        const int e = q / per, k = q - e * per;
+        float t[V];
+        unpack16(c[r], static_cast<const TIN*>(nullptr), t);
+#pragma unroll
+        for (int i = 0; i < V; ++i) dst[e * stride + k * V + i] = t[i];
+      }
+    }
+  }
+};
+
+template <typename TIN, int RDF, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   constexpr int E = (RDF == FMT_F32) ? 4 : 8;
-  __shared__ M2NfSmem<NR, NC, HPW> s;
-  const int unit = xcd_tile(blockIdx.x, gridDim.x);   // one unit = HPW heads of one sequence
-  const int per_seq = a.nheads / HPW;
-  const int b = unit / per_seq, h0 = (unit - b * per_seq) * HPW, g = h0 / a.hpg;
-  const size_t tile0 = static_cast<size_t>(b) * a.nheads + h0;
-  // the tile addresses do not depend on the buffer counters: start streaming first
-  RawTile<RDF, E, NR, NC> raw[HPW];
-#pragma unroll
-  for (int hh = 0; hh < HPW; ++hh) raw[hh].issue(a.rd, tile0 + hh);
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
+  constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
+  constexpr int CX = (kRing * NC / V + kThreads - 1) / kThreads;
+  constexpr int CC = (NR / V + kThreads - 1) / kThreads;
+  __shared__ M2NfSmem<NR, NC> s;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
+  const float Ah = a.A[h], Dh = a.D[h];
   const rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
-  if (errbit == 0) {
-    const int j = len + 1;
-    const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
-    const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
-    const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
-    const TIN* inX = static_cast<const TIN*>(a.x) + tile0 * NC;
-    const TIN* inDt = static_cast<const TIN*>(a.dt) + tile0;
-    TIN* rB = static_cast<TIN*>(a.rB) + bg * kRing * NR;
-    TIN* rC = static_cast<TIN*>(a.rC) + bg * kRing * NR;
-    TIN* rX = static_cast<TIN*>(a.rx) + tile0 * kRing * NC;
-    TIN* rDt = static_cast<TIN*>(a.rdt) + tile0 * kRing;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, inB, 0, nck, len, NR}, j);
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) {
-      stage_rows(&s.X[hh][0][0], NC, EntrySrc<TIN>{rX + hh * kRing * NC, inX + hh * NC, 0, nck, len, NC}, j);
-      stage_rows(&s.dt[hh][0], 1, EntrySrc<TIN>{rDt + hh * kRing, inDt + hh, 0, nck, len, 1}, j);
-    }
-    stage_rows(&s.C[0], NR, EntrySrc<TIN>{inC, inC, 0, 0, 0, NR}, 1);
-    __syncthreads();
-    // decays per head, and the dots B_i . C_j (groups of 16 lanes)
-    for (int idx = threadIdx.x; idx < HPW * j; idx += kThreads) {
-      const int hh = idx / j, e = idx - hh * j;
-      s.a[hh][e] = expf(s.dt[hh][e] * a.A[h0 + hh]);
-    }
-    {
-      const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
-      for (int e = grp; e < j; e += kThreads / 16) {
-        float part = 0.0f;
-        for (int n = ln; n < NR; n += 16) part += s.B[e][n] * s.C[n];
-        part = group_sum16(part);
-        if (ln == 0) s.dot[e] = part;
+  if (errbit != 0) return;
+  const int j = len + 1;
+  const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
+  const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
+  const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
+  const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
+  const TIN* inDt = static_cast<const TIN*>(a.dt) + tile;
+  TIN* rB = static_cast<TIN*>(a.rB) + bg * kRing * NR;
+  TIN* rC = static_cast<TIN*>(a.rC) + bg * kRing * NR;
+  TIN* rX = static_cast<TIN*>(a.rx) + static_cast<size_t>(tile) * kRing * NC;
+  TIN* rDt = static_cast<TIN*>(a.rdt) + static_cast<size_t>(tile) * kRing;
+  // 1. buffer records into registers
+  RegChunks<TIN, CB> cb;
+  RegChunks<TIN, CX> cx;
+  RegChunks<TIN, CC> cc;
+  cb.load(EntrySrc<TIN>{rB, inB, 0, nck, len, NR}, j, NR);
+  cx.load(EntrySrc<TIN>{rX, inX, 0, nck, len, NC}, j, NC);
+  cc.load(EntrySrc<TIN>{inC, inC, 0, 0, 0, NR}, 1, NR);
+  const int de = static_cast<int>(threadIdx.x) < j ? static_cast<int>(threadIdx.x) : j - 1;
+  const float dtv = to_f(*(de < len ? rDt + ((nck + de) & (kRing - 1)) : inDt));
+  // 2. the state tile
+  RawTile<RDF, E, NR, NC> raw;
+  raw.issue(a.rd, tile);
+  // 3. records to LDS, then the state-independent work
+  cb.to_lds(&s.B[0][0], NR, j, NR);
+  cx.to_lds(&s.X[0][0], NC, j, NC);
+  cc.to_lds(s.C, NR, 1, NR);
+  if (static_cast<int>(threadIdx.x) < j) {
+    s.dt[threadIdx.x] = dtv;
+    s.a[threadIdx.x] = expf(dtv * Ah);
+  }
+  __syncthreads();
+  {
+    const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+    for (int e = grp; e < j; e += kThreads / 16) {
+      float part = 0.0f;
+      for (int n = ln; n < NR; n += 16) part += s.B[e][n] * s.C[n];
+      part = group_sum16(part);
+      if (ln == 0) {
+        float w = 1.0f;
+        for (int l = e + 1; l < j; ++l) w *= s.a[l];
+        s.w[e] = w * s.dt[e] * part;
       }
     }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < HPW * j; idx += kThreads) {
-      const int hh = idx / j, e = idx - hh * j;
-      float w = 1.0f;
-      for (int l = e + 1; l < j; ++l) w *= s.a[hh][l];
-      s.w[hh][e] = w * s.dt[hh][e] * s.dot[e];
-    }
-    if (static_cast<int>(threadIdx.x) < HPW) {
-      const int hh = threadIdx.x;
+    if (threadIdx.x == 0) {
       float L = 1.0f;
-      for (int l = 0; l < j; ++l) L *= s.a[hh][l];
-      s.L[hh] = L;
+      for (int l = 0; l < j; ++l) L *= s.a[l];
+      s.L = L;
     }
-    RegTile<E, NR, NC> H[HPW];
-#pragma unroll
-    for (int hh = 0; hh < HPW; ++hh) raw[hh].decode(H[hh]);
-    tiles_matvec<HPW>(H, s.C, s.red, s.out);   // barriers inside also publish s.w / s.L
-    for (int idx = threadIdx.x; idx < HPW * NC; idx += kThreads) {
-      const int hh = idx / NC, p = idx - hh * NC;
-      float yv = s.L[hh] * s.out[hh * NC + p];
-      for (int e = 0; e < j; ++e) yv += s.w[hh][e] * s.X[hh][e][p];
-      a.y[(tile0 + hh) * NC + p] = yv + a.D[h0 + hh] * s.X[hh][j - 1][p];
-    }
-    // append the current record (bit copies)
-    const int slot = static_cast<int>((nck + len) & (kRing - 1));
-    for (int idx = threadIdx.x; idx < HPW * NC; idx += kThreads) {
-      const int hh = idx / NC, p = idx - hh * NC;
-      rX[(hh * kRing + slot) * NC + p] = inX[hh * NC + p];
-    }
-    if (static_cast<int>(threadIdx.x) < HPW) rDt[threadIdx.x * kRing + slot] = inDt[threadIdx.x];
-    if (h0 % a.hpg == 0) {
-      for (int n = threadIdx.x; n < NR; n += kThreads) {
-        rB[slot * NR + n] = inB[n];
-        rC[slot * NR + n] = inC[n];
-      }
-    }
+  }
+  __syncthreads();
+  float buf = 0.0f;   // buffer part of y for column p = threadIdx.x
+  if (static_cast<int>(threadIdx.x) < NC) {
+    const int p = threadIdx.x;
+    buf = Dh * s.X[j - 1][p];
+    for (int e = 0; e < j; ++e) buf += s.w[e] * s.X[e][p];
+  }
+  // 4. the reduction over the state, y
+  RegTile<E, NR, NC> H;
+  raw.decode(H);
+  tile_matvec<1>(H, s.C, NR, s.red, s.out);
+  if (static_cast<int>(threadIdx.x) < NC) s.out[threadIdx.x] = s.L * s.out[threadIdx.x] + buf;
+  __syncthreads();
+  store_rows_nt(a.y + static_cast<size_t>(tile) * NC, s.out, NC);
+  // 5. append the current record from its staged copy (exact: the values came from TIN)
+  const int slot = static_cast<int>((nck + len) & (kRing - 1));
+  store_row_as(rX + slot * NC, &s.X[j - 1][0], NC);
+  if (threadIdx.x == 0) rDt[slot] = from_f<TIN>(s.dt[j - 1]);
+  if (h % a.hpg == 0) {
+    store_row_as(rB + slot * NR, &s.B[j - 1][0], NR);
+    store_row_as(rC + slot * NR, s.C, NR);
   }
 }
 
@@ -589,21 +627,14 @@ struct M2Shape {
   static void conv(const M2Args& a, int grid, hipStream_t st) {
     m2_conv_kernel<TIN, NR, NC><<<grid, kThreads, 0, st>>>(a);
   }
-  template <typename TIN, int HPW>
-  static void nonflush_h(const M2Args& a, int rdf, int grid, hipStream_t st) {
-    switch (rdf) {
-      case FMT_F32: m2_nonflush_kernel<TIN, FMT_F32, NR, NC, HPW><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_F16: m2_nonflush_kernel<TIN, FMT_F16, NR, NC, HPW><<<grid, kThreads, 0, st>>>(a); break;
-      case FMT_FP8: m2_nonflush_kernel<TIN, FMT_FP8, NR, NC, HPW><<<grid, kThreads, 0, st>>>(a); break;
-      default: m2_nonflush_kernel<TIN, FMT_NVFP4, NR, NC, HPW><<<grid, kThreads, 0, st>>>(a); break;
-    }
-  }
-  // One head per workgroup: measured faster than two (batch-256 Nemotron shapes,
-  // 0.180 vs 0.197 ms), since the per-workgroup tail, not the bytes in flight,
-  // bounds the stream.
   template <typename TIN>
   static void nonflush(const M2Args& a, int rdf, int grid, hipStream_t st) {
-    nonflush_h<TIN, 1>(a, rdf, grid, st);
+    switch (rdf) {
+      case FMT_F32: m2_nonflush_kernel<TIN, FMT_F32, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+      case FMT_F16: m2_nonflush_kernel<TIN, FMT_F16, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+      case FMT_FP8: m2_nonflush_kernel<TIN, FMT_FP8, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+      default: m2_nonflush_kernel<TIN, FMT_NVFP4, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+    }
   }
   template <typename TIN, bool RC>
   static void flush_rc(const M2Args& a, int ckf, int grid, hipStream_t st) {

@@ -27,11 +27,16 @@ struct RawTile {
   Raw<FMT, E> r[TM::PASSES];
   float ms;
 
+  // Every thread issues all its loads unconditionally (rows past a matrix
+  // smaller than one pass are clamped to its last row and ignored when
+  // decoding): loads under a branch would be merged through a wait, which
+  // serialises the stream.
   __device__ __forceinline__ void issue(const StateBuf& sb, size_t mat) {
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
-      const int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
-      if (row < NR) r[k] = load_chunk<FMT, E, NC>(sb, mat, NR, row, static_cast<int>(threadIdx.x % TM::TPR));
+      int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
+      if constexpr (NR % TM::RPP != 0 || TM::RPP > NR) row = row < NR ? row : NR - 1;
+      r[k] = load_chunk<FMT, E, NC>(sb, mat, NR, row, static_cast<int>(threadIdx.x % TM::TPR));
     }
     ms = mat_scale<FMT>(sb, mat);
   }
@@ -40,14 +45,10 @@ struct RawTile {
     for (int k = 0; k < TM::PASSES; ++k) {
       const int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
       float t[E];
-      if (row < NR) {
-        decode_chunk<FMT, E>(r[k], ms, t);
-      } else {
+      decode_chunk<FMT, E>(r[k], ms, t);
+      const bool in = (NR % TM::RPP == 0 && TM::RPP <= NR) || row < NR;
 #pragma unroll
-        for (int i = 0; i < E; ++i) t[i] = 0.0f;
-      }
-#pragma unroll
-      for (int i = 0; i < E; ++i) dst.v[k][i] = t[i] * mult;
+      for (int i = 0; i < E; ++i) dst.v[k][i] = in ? t[i] * mult : 0.0f;
     }
   }
 };
@@ -303,6 +304,47 @@ __device__ __forceinline__ void tile_rank_update(RegTile<E, NR, NC>& H, float L,
       }
     }
   }
+}
+
+// Copy `n` input elements (a record row) between global buffers, 16 bytes per
+// lane where the length allows; used for ring appends (bit copies).
+template <typename T>
+__device__ __forceinline__ void copy_row(T* dst, const T* src, int n) {
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  if (n % V == 0) {
+    for (int i = threadIdx.x; i < n / V; i += kThreads)
+      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+  } else {
+    for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
+  }
+}
+
+// Write n LDS floats that came from T back to a global T row (exact), 16 bytes
+// per lane where the length allows (n % (16/sizeof(T)) == 0, dst 16-byte aligned).
+template <typename T>
+__device__ __forceinline__ void store_row_as(T* dst, const float* src, int n) {
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  if (n % V != 0) {
+    for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = from_f<T>(src[i]);
+  } else if constexpr (sizeof(T) == 4) {
+    for (int i = threadIdx.x; i < n / 4; i += kThreads)
+      reinterpret_cast<float4*>(dst)[i] = make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]);
+  } else {
+    for (int i = threadIdx.x; i < n / 8; i += kThreads) {
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = (__float_as_uint(src[8 * i + 2 * k]) >> 16) | (__float_as_uint(src[8 * i + 2 * k + 1]) & 0xFFFF0000u);
+      reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// Stream n floats from LDS to global with 16-byte non-temporal stores
+// (n % 4 == 0, dst 16-byte aligned).
+__device__ __forceinline__ void store_rows_nt(float* dst, const float* src, int n) {
+  for (int i = threadIdx.x; i < n / 4; i += kThreads)
+    nt_store(make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]), reinterpret_cast<float4*>(dst) + i);
 }
 
 // Where buffer entry e of the current window comes from: the ring (e < nring)
