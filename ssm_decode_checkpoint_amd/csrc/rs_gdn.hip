@@ -64,33 +64,57 @@ __device__ __forceinline__ int slot_of(long long nck, int e) { return static_cas
 
 // Stage the window's entries 0..m-1 (entry m-1 is the current token, the
 // others come from the ring): k rows, u rows of the held entries, the decays,
-// and the current v, beta, and the matvec weights [k_cur, q, 0, 0].
+// and the current v, beta, and the matvec weights [k_cur, q, 0, 0]. Loads go
+// to registers first (load), so the caller can issue the state tile after
+// them and still have the records while the tile streams in (vector loads
+// return in order); store moves them to LDS.
 template <typename TIN, int NK, int NV>
-__device__ __forceinline__ void gdn_stage(GSmem<NK, NV>& s, const GDNArgs& a, const GPtrs& p, long long nck,
-                                          int m) {
-  const int held = m - 1;
-  const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
-  const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
-  const float* ru = static_cast<const float*>(a.ru) + p.tile * kRing * NV;
-  const float* rg = static_cast<const float*>(a.rg) + p.tile * kRing;
-  const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
-  const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
-  const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
-  stage_rows(&s.K[0][0], NK, EntrySrc<TIN>{rk, ik, 0, nck, held, NK}, m);
-  stage_rows(&s.U[0][0], NV, EntrySrc<float>{ru, ru, 0, nck, held, NV}, held);
-  for (int n = threadIdx.x; n < NK; n += kThreads) {
-    s.W[0][n] = to_f(ik[n]);
-    s.W[1][n] = to_f(iq[n]);
-    s.W[2][n] = 0.0f;
-    s.W[3][n] = 0.0f;
+struct GStage {
+  static constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  static constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
+  static constexpr int CU = (kRing * NV / 4 + kThreads - 1) / kThreads;
+  static constexpr int CQ = (NK / VK + kThreads - 1) / kThreads;
+  static constexpr int CV = (NV / VK + kThreads - 1) / kThreads;
+  RegChunks<TIN, CK> k;
+  RegChunks<float, CU> u;
+  RegChunks<TIN, CQ> q, kc;
+  RegChunks<TIN, CV> v;
+  float g, beta;
+
+  __device__ __forceinline__ void load(const GDNArgs& a, const GPtrs& p, long long nck, int m) {
+    const int held = m - 1;
+    const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
+    const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
+    const float* ru = static_cast<const float*>(a.ru) + p.tile * kRing * NV;
+    const float* rg = static_cast<const float*>(a.rg) + p.tile * kRing;
+    const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
+    const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
+    const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
+    k.load(EntrySrc<TIN>{rk, ik, 0, nck, held, NK}, m, NK);
+    // with no held entry every lane reads the ring's first row and stores nothing
+    u.load(EntrySrc<float>{ru, ru, 0, nck, held, NV}, held, NV);
+    q.load(EntrySrc<TIN>{iq, iq, 0, 0, 0, NK}, 1, NK);
+    kc.load(EntrySrc<TIN>{ik, ik, 0, 0, 0, NK}, 1, NK);
+    v.load(EntrySrc<TIN>{iv, iv, 0, 0, 0, NV}, 1, NV);
+    const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+    g = *(e < held ? rg + slot_of(nck, e) : a.g + p.tile);
+    beta = a.beta[p.tile];
   }
-  for (int v = threadIdx.x; v < NV; v += kThreads) s.vc[v] = to_f(iv[v]);
-  if (static_cast<int>(threadIdx.x) < m) {
-    const int e = threadIdx.x;
-    s.al[e] = expf(e < held ? rg[slot_of(nck, e)] : a.g[p.tile]);
+  __device__ __forceinline__ void store(GSmem<NK, NV>& s, int m) const {
+    const int held = m - 1;
+    k.to_lds(&s.K[0][0], NK, m, NK);
+    u.to_lds(&s.U[0][0], NV, held, NV);
+    kc.to_lds(&s.W[0][0], NK, 1, NK);
+    q.to_lds(&s.W[1][0], NK, 1, NK);
+    v.to_lds(s.vc, NV, 1, NV);
+    for (int n = threadIdx.x; n < NK; n += kThreads) {
+      s.W[2][n] = 0.0f;
+      s.W[3][n] = 0.0f;
+    }
+    if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(g);
+    if (threadIdx.x == 0) s.bet = beta;
   }
-  if (threadIdx.x == 0) s.bet = a.beta[p.tile];
-}
+};
 
 // Dots and decays for the current entry cur = m-1 (after staging is visible):
 //   kk[i] = beta_cur r_{cur,i} (k_cur . k_i) for i < cur
@@ -187,15 +211,17 @@ template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV> s;
   const GPtrs p = gdn_tile(a);
-  RawTile<FMT_F32, 4, NK, NV> raw;   // start streaming before the counters arrive
-  raw.issue(a.ck, p.tile);
   const rs_meta* mp = a.meta + p.b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
   if (errbit == 0) {
     const int j = len + 1;
-    gdn_stage<TIN>(s, a, p, nck, j);
+    GStage<TIN, NK, NV> stg;
+    stg.load(a, p, nck, j);            // records first, then the state tile
+    RawTile<FMT_F32, 4, NK, NV> raw;
+    raw.issue(a.ck, p.tile);
+    stg.store(s, j);
     __syncthreads();
     gdn_dots(s, j);
     RegTile<4, NK, NV> S;
@@ -236,15 +262,17 @@ template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV> s;
   const GPtrs p = gdn_tile(a);
-  RawTile<FMT_F32, 4, NK, NV> raw;
-  raw.issue(a.ck, p.tile);
   const rs_meta* mp = a.meta + p.b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
   if (errbit == 0) {
-    gdn_stage<TIN>(s, a, p, nck, m);
+    GStage<TIN, NK, NV> stg;
+    stg.load(a, p, nck, m);            // records first, then the state tile
+    RawTile<FMT_F32, 4, NK, NV> raw;
+    raw.issue(a.ck, p.tile);
+    stg.store(s, m);
     __syncthreads();
     gdn_dots(s, m);
     RegTile<4, NK, NV> S;

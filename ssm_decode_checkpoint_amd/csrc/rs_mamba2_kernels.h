@@ -144,40 +144,6 @@ struct M2NfSmem {
   float out[NC];
 };
 
-// Up to CH 16-byte chunks per thread of a record region, loaded into registers.
-template <typename TIN, int CH>
-struct RegChunks {
-  uint4 c[CH];
-  // region of n records of `width` elements: record e comes from src(e)
-  template <typename SRC>
-  __device__ __forceinline__ void load(const SRC& src, int n, int width) {
-    constexpr int V = 16 / static_cast<int>(sizeof(TIN));
-    const int per = width / V;
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      int q = static_cast<int>(threadIdx.x) + r * kThreads;
-      q = q < n * per ? q : 0;   // unconditional load from a valid record (n >= 1)
-      const int e = q / per, k = q - e * per;
-      c[r] = *reinterpret_cast<const uint4*>(src.at(e) + k * V);
-    }
-  }
-  __device__ __forceinline__ void to_lds(float* dst, int stride, int n, int width) const {
-    constexpr int V = 16 / static_cast<int>(sizeof(TIN));
-    const int per = width / V;
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int q = static_cast<int>(threadIdx.x) + r * kThreads;
-      if (q < n * per) {
-        const int e = q / per, k = q - e * per;
-        float t[V];
-        unpack16(c[r], static_cast<const TIN*>(nullptr), t);
-#pragma unroll
-        for (int i = 0; i < V; ++i) dst[e * stride + k * V + i] = t[i];
-      }
-    }
-  }
-};
-
 template <typename TIN, int RDF, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   constexpr int E = (RDF == FMT_F32) ? 4 : 8;
@@ -333,11 +299,15 @@ __device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTi
 template <typename TIN, int CKF, bool RC, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
   constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
+  constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
+  constexpr int CX = (kRing * NC / V + kThreads - 1) / kThreads;
+  constexpr int CC = (NR / V + kThreads - 1) / kThreads;
   __shared__ M2Smem<NR, NC, kRing, 1, true> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  RawTile<CKF, E, NR, NC> raw;
-  raw.issue(a.ck, tile);
+  const float Ah = a.A[h];
   const rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
@@ -345,17 +315,31 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
   const int m = len + 1;
   if (errbit == 0) {
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
+    const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
     const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
     const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
+    const TIN* inDt = static_cast<const TIN*>(a.dt) + tile;
     const TIN* rB = static_cast<const TIN*>(a.rB) + bg * kRing * NR;
     const TIN* rX = static_cast<const TIN*>(a.rx) + static_cast<size_t>(tile) * kRing * NC;
     const TIN* rDt = static_cast<const TIN*>(a.rdt) + static_cast<size_t>(tile) * kRing;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, static_cast<const TIN*>(a.B) + bg * NR, 0, nck, len, NR}, m);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, inX, 0, nck, len, NC}, m);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, static_cast<const TIN*>(a.dt) + tile, 0, nck, len, 1}, m);
-    for (int i = threadIdx.x; i < NR; i += kThreads) s.Cw[0][i] = to_f(inC[i]);
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], m);
+    // records into registers, then the state tile, then records to LDS
+    RegChunks<TIN, CB> cb;
+    RegChunks<TIN, CX> cx;
+    RegChunks<TIN, CC> cc;
+    cb.load(EntrySrc<TIN>{rB, inB, 0, nck, len, NR}, m, NR);
+    cx.load(EntrySrc<TIN>{rX, inX, 0, nck, len, NC}, m, NC);
+    cc.load(EntrySrc<TIN>{inC, inC, 0, 0, 0, NR}, 1, NR);
+    const int de = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+    const float dtv = to_f(*EntrySrc<TIN>{rDt, inDt, 0, nck, len, 1}.at(de));
+    RawTile<CKF, E, NR, NC> raw;
+    raw.issue(a.ck, tile);
+    cb.to_lds(&s.B[0][0], NR, m, NR);
+    cx.to_lds(&s.X[0][0], NC, m, NC);
+    cc.to_lds(&s.Cw[0][0], NR, 1, NR);
+    if (static_cast<int>(threadIdx.x) < m) {
+      s.dt[threadIdx.x] = dtv;
+      s.a[threadIdx.x] = expf(dtv * Ah);
+    }
     __syncthreads();
     RegTile<E, NR, NC> H;
     raw.decode(H);
@@ -375,12 +359,16 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
 template <typename TIN, int RDF, int NR, int NC, int KQ>
 __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
   constexpr int E = (RDF == FMT_F32) ? 4 : 8;
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
+  constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
+  constexpr int CX = (kRing * NC / V + kThreads - 1) / kThreads;
+  constexpr int CC = (KQ * NR / V + kThreads - 1) / kThreads;
   __shared__ M2Smem<NR, NC, kRing, KQ, false> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const int K = a.K;
-  RawTile<RDF, E, NR, NC> raw;
-  raw.issue(a.rd, tile);
+  const float Ah = a.A[h];
   const rs_meta* mp = a.meta + b;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
@@ -399,13 +387,25 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
     TIN* rX = static_cast<TIN*>(a.rx) + static_cast<size_t>(tile) * kRing * NC;
     TIN* rDt = static_cast<TIN*>(a.rdt) + static_cast<size_t>(tile) * kRing;
     const int n = len + K;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, inB, gstride, nck, len, NR}, n);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, inX, xstride, nck, len, NC}, n);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, inDt, dstride, nck, len, 1}, n);
-    stage_rows(&s.Cw[0][0], NR, EntrySrc<TIN>{inC, inC, gstride, 0, 0, NR}, K);
+    // records into registers, then the state tile, then records to LDS
+    RegChunks<TIN, CB> cb;
+    RegChunks<TIN, CX> cx;
+    RegChunks<TIN, CC> cc;
+    cb.load(EntrySrc<TIN>{rB, inB, gstride, nck, len, NR}, n, NR);
+    cx.load(EntrySrc<TIN>{rX, inX, xstride, nck, len, NC}, n, NC);
+    cc.load(EntrySrc<TIN>{inC, inC, gstride, 0, 0, NR}, K, NR);
+    const int de = static_cast<int>(threadIdx.x) < n ? static_cast<int>(threadIdx.x) : n - 1;
+    const float dtv = to_f(*EntrySrc<TIN>{rDt, inDt, dstride, nck, len, 1}.at(de));
+    RawTile<RDF, E, NR, NC> raw;
+    raw.issue(a.rd, tile);
+    cb.to_lds(&s.B[0][0], NR, n, NR);
+    cx.to_lds(&s.X[0][0], NC, n, NC);
+    cc.to_lds(&s.Cw[0][0], NR, K, NR);
     for (int idx = K * NR + threadIdx.x; idx < KQ * NR; idx += kThreads) (&s.Cw[0][0])[idx] = 0.0f;
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], n);
+    if (static_cast<int>(threadIdx.x) < n) {
+      s.dt[threadIdx.x] = dtv;
+      s.a[threadIdx.x] = expf(dtv * Ah);
+    }
     __syncthreads();
     output_weights(s, len + 1, K);
     RegTile<E, NR, NC> H;
@@ -508,6 +508,10 @@ static __global__ __launch_bounds__(1024) void m2_commit_meta_kernel(M2Args a) {
 template <typename TIN, int CKF, bool RC, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
   constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
+  constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
+  constexpr int CX = (kRing * NC / V + kThreads - 1) / kThreads;
   __shared__ M2Smem<NR, NC, kRing, 1, true> s;
   const int total = *a.work_count * a.nheads;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -515,17 +519,25 @@ __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
     const int h = item - (item / a.nheads) * a.nheads;
     const int b = it.b, g = h / a.hpg, m = it.m;
     const size_t tile = static_cast<size_t>(b) * a.nheads + h;
-    RawTile<CKF, E, NR, NC> raw;
-    raw.issue(a.ck, tile);
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
     const TIN* rB = static_cast<const TIN*>(a.rB) + bg * kRing * NR;
     const TIN* rX = static_cast<const TIN*>(a.rx) + tile * kRing * NC;
     const TIN* rDt = static_cast<const TIN*>(a.rdt) + tile * kRing;
-    stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{rB, rB, 0, it.nck, m, NR}, m);
-    stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{rX, rX, 0, it.nck, m, NC}, m);
-    stage_rows(&s.dt[0], 1, EntrySrc<TIN>{rDt, rDt, 0, it.nck, m, 1}, m);
-    __syncthreads();
-    stage_decays(s.a, s.dt, a.A[h], m);
+    // records into registers, then the state tile, then records to LDS
+    RegChunks<TIN, CB> cb;
+    RegChunks<TIN, CX> cx;
+    cb.load(EntrySrc<TIN>{rB, rB, 0, it.nck, m, NR}, m, NR);
+    cx.load(EntrySrc<TIN>{rX, rX, 0, it.nck, m, NC}, m, NC);
+    const int de = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+    const float dtv = to_f(*EntrySrc<TIN>{rDt, rDt, 0, it.nck, m, 1}.at(de));
+    RawTile<CKF, E, NR, NC> raw;
+    raw.issue(a.ck, tile);
+    cb.to_lds(&s.B[0][0], NR, m, NR);
+    cx.to_lds(&s.X[0][0], NC, m, NC);
+    if (static_cast<int>(threadIdx.x) < m) {
+      s.dt[threadIdx.x] = dtv;
+      s.a[threadIdx.x] = expf(dtv * a.A[h]);
+    }
     __syncthreads();
     RegTile<E, NR, NC> H;
     raw.decode(H);

@@ -400,4 +400,38 @@ __device__ __forceinline__ void stage_rows(float* dst, int stride, const EntrySr
   }
 }
 
+// Up to CH 16-byte chunks per thread of a record region, loaded into registers.
+template <typename TIN, int CH>
+struct RegChunks {
+  uint4 c[CH];
+  // region of n records of `width` elements: record e comes from src(e)
+  template <typename SRC>
+  __device__ __forceinline__ void load(const SRC& src, int n, int width) {
+    constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+    const int per = width / V;
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      q = q < n * per ? q : 0;   // unconditional load from a valid record (n >= 1)
+      const int e = q / per, k = q - e * per;
+      c[r] = *reinterpret_cast<const uint4*>(src.at(e) + k * V);
+    }
+  }
+  __device__ __forceinline__ void to_lds(float* dst, int stride, int n, int width) const {
+    constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+    const int per = width / V;
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      const int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      if (q < n * per) {
+        const int e = q / per, k = q - e * per;
+        float t[V];
+        unpack16(c[r], static_cast<const TIN*>(nullptr), t);
+#pragma unroll
+        for (int i = 0; i < V; ++i) dst[e * stride + k * V + i] = t[i];
+      }
+    }
+  }
+};
+
 }  // namespace rs
