@@ -149,22 +149,31 @@ class Timer:
         self.stream = torch.cuda.current_stream()
 
     def run(self, fn, K, warm, nmarks, reset=None):
+        """Total time of K steps with nothing but the launches in the timed
+        region, then a second pass of K steps with events around each marked
+        call for the per-call breakdown (those events add their own gaps, so
+        the total never comes from that pass). `reset` runs before each pass."""
         torch = self.torch
         for _ in range(warm):
             fn(None)
         if reset is not None:
             reset()
-        torch.cuda.synchronize()
-        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nmarks)] for _ in range(K)]
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(self.stream)
         for k in range(K):
-            fn(evs[k])
+            fn(None)
         t1.record(self.stream)
         torch.cuda.synchronize()
         total = t0.elapsed_time(t1)
+        if reset is not None:
+            reset()
+        evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nmarks)] for _ in range(K)]
+        torch.cuda.synchronize()
+        for k in range(K):
+            fn(evs[k])
+        torch.cuda.synchronize()
         per = np.array([[evs[k][i][0].elapsed_time(evs[k][i][1]) for i in range(nmarks)] for k in range(K)])
         return total, per
 

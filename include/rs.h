@@ -154,7 +154,7 @@ typedef struct rs_meta {
   int32_t len;           /* committed buffer entries */
   int32_t nd;            /* pending draft entries */
   int32_t err;           /* sticky RS_ERR_* bits */
-  uint32_t arrive;       /* reserved, zero */
+  uint32_t arrive;       /* workgroups counted in during a step launch; zero between calls */
   int32_t reserved[2];
 } rs_meta;
 

@@ -20,13 +20,17 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librs.so")
-SOURCES = ["rs_api.hip", "rs_meta.hip", "rs_mamba2.hip", "rs_m2_16x16.hip", "rs_m2_64x64.hip", "rs_m2_128x64.hip",
+SOURCES = ["rs_api.hip", "rs_mamba2.hip", "rs_m2_16x16.hip", "rs_m2_64x64.hip", "rs_m2_128x64.hip",
            "rs_m2_128x128.hip", "rs_gdn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+# -packed-fp32-ops: no packed fp32 instructions. The atomic optimizer is off
+# because it rewrites a one-lane atomic into a wave scan that waits for every
+# load in flight, which stalls the counter arrival behind the state stream.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -16,6 +16,16 @@ constexpr uint64_t kAlign = 256;
 
 uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// Library work space inside the meta buffer, after rs_meta[batch]: the commit
+// fold list (FoldItem[batch]) and its count, then the first-level arrival
+// counters (arrive_groups of up to two workgroups per head, per sequence).
+uint64_t arrive_off(const rs_layer& L) {
+  return L.meta_work_off + align_up(static_cast<uint64_t>(L.cfg.batch) * sizeof(FoldItem)) + kAlign;
+}
+uint64_t arrive_bytes(const rs_layer& L) {
+  return static_cast<uint64_t>(L.cfg.batch) * arrive_groups(2 * L.heads) * kArriveStride * sizeof(uint32_t);
+}
+
 int in_size(int32_t dt) { return dt == RS_F32 ? 4 : 2; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -107,6 +117,7 @@ rs_status m2_args(const rs_layer* L, const rs_buffers* buf, M2Args* a, M2Launch*
     a->rC = r + L->ring_C_off;
     a->rdt = r + L->ring_dt_off;
     a->meta = static_cast<rs_meta*>(buf->meta);
+    a->arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(buf->meta) + arrive_off(*L));
     char* w = static_cast<char*>(buf->meta) + L->meta_work_off;
     a->work = reinterpret_cast<FoldItem*>(w);
     a->work_count = reinterpret_cast<int*>(w + align_up(static_cast<uint64_t>(c.batch) * sizeof(FoldItem)));
@@ -162,6 +173,7 @@ GDNArgs gdn_args(const rs_layer* L, const rs_buffers* buf) {
     a.rbeta = r + L->ring_beta_off;
     a.ru = r + L->ring_u_off;
     a.meta = static_cast<rs_meta*>(buf->meta);
+    a.arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(buf->meta) + arrive_off(*L));
   }
   return a;
 }
@@ -265,7 +277,7 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
     }
     L.ring_bytes = off;
     L.meta_work_off = align_up(B * sizeof(rs_meta));
-    L.meta_bytes = L.meta_work_off + align_up(B * sizeof(FoldItem)) + kAlign;
+    L.meta_bytes = arrive_off(L) + arrive_bytes(L);
     if (c.read_copy == RS_NVFP4) {
       const StateLayout r = state_layout(RS_NVFP4, mats, rc);
       L.read_copy_bytes = r.bytes;
@@ -309,12 +321,10 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const MetaOp mop = flush ? MetaOp::Flush : MetaOp::NonFlush;
   if (L->cfg.kind == RS_GDN) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(flush ? GDNOp::Flush : GDNOp::NonFlush, a, gdn_launch_cfg(L), st);
-    meta_advance(a.meta, L->cfg.batch, mop, 0, st);
     return launched();
   }
   M2Args a;
@@ -323,7 +333,6 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (rs_status s = m2_inputs(in, prm, &a)) return s;
   a.y = y;
   m2_launch(flush ? M2Op::Flush : M2Op::NonFlush, a, l, st);
-  meta_advance(a.meta, L->cfg.batch, mop, 0, st);
   return launched();
 }
 
@@ -357,7 +366,6 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
     m2_launch(M2Op::ConvSpec, a, l, st);
   } else {
     m2_launch(M2Op::SpecAppend, a, l, st);
-    meta_advance(a.meta, L->cfg.batch, MetaOp::Append, K, st);
   }
   return launched();
 }

@@ -19,9 +19,11 @@
 // needs just S0 k_j and S0 q_j from its single read of S0, plus length-dv
 // vector work over the held rows.
 //
-// One 256-thread workgroup per (sequence, value head) state, stored as
-// [dk][dv] (value index innermost) so that S0 k and S0 q are sums over rows
-// held in registers.
+// States are stored as [dk][dv] (value index innermost) so that S0 k and S0 q
+// are sums over rows held in registers. One 256-thread workgroup per column
+// slice of a (sequence, value head) state in the ReplaySSM steps: dv = 128 is
+// split into two slices of 64 columns (32 KiB of fp32 each), smaller states
+// are one slice; the conventional step takes the whole state.
 #include "rs_device.h"
 #include "rs_tile.h"
 #include "rs_internal.h"
@@ -30,14 +32,21 @@ namespace rs {
 
 namespace {
 
-template <int NK, int NV>
+// Value columns split across NS workgroups: with k, q, g, beta fixed, column v
+// of the stored state (row v of S) evolves and is read out on its own, so a
+// workgroup owns the columns c0..c0+NVS-1 of one state and repeats the few
+// length-dk dots of the other slices.
+template <int NV>
+constexpr int gdn_slices() { return NV >= 128 ? 2 : 1; }
+
+template <int NK, int NVS>
 struct GSmem {
   float K[kRing][NK];    // k of entries 0..m-1
   float W[4][NK];        // matvec weights: k_cur, q, 0, 0
-  float U[kRing][NV];    // u of entries 0..m-1 (the current one computed here)
-  float vc[NV];          // v of the current token
-  float out[4][NV];      // S0 k_cur, S0 q
-  float red[4 * 4 * NV];
+  float U[kRing][NVS];   // u of entries 0..m-1 (the current one computed here), own columns
+  float vc[NVS];         // v of the current token, own columns
+  float out[4][NVS];     // S0 k_cur, S0 q
+  float red[4 * 4 * NVS];
   float kk[kRing];       // beta_cur r_{cur,i} (k_cur . k_i), i < cur
   float kq[kRing];       // r_{cur,i} (k_i . q), i <= cur
   float rr[kRing];       // r_{cur,i}
@@ -47,34 +56,80 @@ struct GSmem {
 };
 
 struct GPtrs {
-  size_t tile;
+  size_t st;       // state index b * n_v + h
   int b, h, kh;
+  int half, c0;    // column slice and its first column
 };
 
+template <int NV, int NS>
 __device__ __forceinline__ GPtrs gdn_tile(const GDNArgs& a) {
   GPtrs p;
-  p.tile = static_cast<size_t>(xcd_tile(blockIdx.x, gridDim.x));
-  p.b = static_cast<int>(p.tile / a.nv);
-  p.h = static_cast<int>(p.tile - static_cast<size_t>(p.b) * a.nv);
+  const size_t t = static_cast<size_t>(xcd_tile(blockIdx.x, gridDim.x));
+  p.st = t / NS;
+  p.half = static_cast<int>(t - p.st * NS);
+  p.c0 = p.half * (NV / NS);
+  p.b = static_cast<int>(p.st / a.nv);
+  p.h = static_cast<int>(p.st - static_cast<size_t>(p.b) * a.nv);
   p.kh = p.h / a.vpk;
   return p;
 }
 
 __device__ __forceinline__ int slot_of(long long nck, int e) { return static_cast<int>((nck + e) & (kRing - 1)); }
 
+// fp32 columns c0..c0+NVS-1 of state `st` ([NK][NV], value index innermost)
+// as a RegTile<4, NK, NVS>: each thread owns 4 consecutive columns of one row
+// per pass. Loads are issued unconditionally (rows past NK are clamped and
+// dropped when decoding).
+template <int NK, int NV, int NVS>
+struct GSlice {
+  using TM = TileMap<4, NK, NVS>;
+  float4 r[TM::PASSES];
+  __device__ __forceinline__ static size_t off(size_t st, int c0, int row) {
+    return (st * NK + row) * NV + c0 + RegTile<4, NK, NVS>::col0();
+  }
+  __device__ __forceinline__ void issue(const float* base, size_t st, int c0) {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      int row = RegTile<4, NK, NVS>::row(k);
+      if constexpr (NK % TM::RPP != 0 || TM::RPP > NK) row = row < NK ? row : NK - 1;
+      r[k] = nt_load(reinterpret_cast<const float4*>(base + off(st, c0, row)));
+    }
+  }
+  __device__ __forceinline__ void decode(RegTile<4, NK, NVS>& d) const {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const bool in = (NK % TM::RPP == 0 && TM::RPP <= NK) || RegTile<4, NK, NVS>::row(k) < NK;
+      d.v[k][0] = in ? r[k].x : 0.0f;
+      d.v[k][1] = in ? r[k].y : 0.0f;
+      d.v[k][2] = in ? r[k].z : 0.0f;
+      d.v[k][3] = in ? r[k].w : 0.0f;
+    }
+  }
+  __device__ __forceinline__ static void store(float* base, size_t st, int c0, const RegTile<4, NK, NVS>& S) {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = RegTile<4, NK, NVS>::row(k);
+      if (row < NK)
+        nt_store(make_float4(S.v[k][0], S.v[k][1], S.v[k][2], S.v[k][3]),
+                 reinterpret_cast<float4*>(base + off(st, c0, row)));
+    }
+  }
+};
+
 // Stage the window's entries 0..m-1 (entry m-1 is the current token, the
-// others come from the ring): k rows, u rows of the held entries, the decays,
-// and the current v, beta, and the matvec weights [k_cur, q, 0, 0]. Loads go
-// to registers first (load), so the caller can issue the state tile after
-// them and still have the records while the tile streams in (vector loads
-// return in order); store moves them to LDS.
-template <typename TIN, int NK, int NV>
+// others come from the ring): k rows, the own columns of the held entries' u
+// rows, the decays, and the current v (own columns), beta, and the matvec
+// weights [k_cur, q, 0, 0]. Loads go to registers first (load), so the caller
+// can issue the state tile after them and still have the records while the
+// tile streams in (vector loads return in order); store moves them to LDS.
+template <typename TIN, int NK, int NV, int NVS>
 struct GStage {
   static constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NK % VK == 0 && NVS % VK == 0 && NVS % 4 == 0, "records are whole 16-byte chunks");
   static constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
-  static constexpr int CU = (kRing * NV / 4 + kThreads - 1) / kThreads;
+  static constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
   static constexpr int CQ = (NK / VK + kThreads - 1) / kThreads;
-  static constexpr int CV = (NV / VK + kThreads - 1) / kThreads;
+  static constexpr int CV = (NVS / VK + kThreads - 1) / kThreads;
   RegChunks<TIN, CK> k;
   RegChunks<float, CU> u;
   RegChunks<TIN, CQ> q, kc;
@@ -85,28 +140,29 @@ struct GStage {
     const int held = m - 1;
     const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
     const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
-    const float* ru = static_cast<const float*>(a.ru) + p.tile * kRing * NV;
-    const float* rg = static_cast<const float*>(a.rg) + p.tile * kRing;
+    const float* ru = static_cast<const float*>(a.ru) + p.st * kRing * NV + p.c0;
+    const float* rg = static_cast<const float*>(a.rg) + p.st * kRing;
     const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
     const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
-    const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
+    const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
     k.load(EntrySrc<TIN>{rk, ik, 0, nck, held, NK}, m, NK);
-    // with no held entry every lane reads the ring's first row and stores nothing
-    u.load(EntrySrc<float>{ru, ru, 0, nck, held, NV}, held, NV);
+    // u rows are NV apart, NVS of them are ours; with no held entry every lane
+    // reads the ring's first row and stores nothing
+    u.load(EntrySrc<float>{ru, ru, 0, nck, held, NV}, held, NVS);
     q.load(EntrySrc<TIN>{iq, iq, 0, 0, 0, NK}, 1, NK);
     kc.load(EntrySrc<TIN>{ik, ik, 0, 0, 0, NK}, 1, NK);
-    v.load(EntrySrc<TIN>{iv, iv, 0, 0, 0, NV}, 1, NV);
+    v.load(EntrySrc<TIN>{iv, iv, 0, 0, 0, NVS}, 1, NVS);
     const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
-    g = *(e < held ? rg + slot_of(nck, e) : a.g + p.tile);
-    beta = a.beta[p.tile];
+    g = *(e < held ? rg + slot_of(nck, e) : a.g + p.st);
+    beta = a.beta[p.st];
   }
-  __device__ __forceinline__ void store(GSmem<NK, NV>& s, int m) const {
+  __device__ __forceinline__ void store(GSmem<NK, NVS>& s, int m) const {
     const int held = m - 1;
     k.to_lds(&s.K[0][0], NK, m, NK);
-    u.to_lds(&s.U[0][0], NV, held, NV);
+    u.to_lds(&s.U[0][0], NVS, held, NVS);
     kc.to_lds(&s.W[0][0], NK, 1, NK);
     q.to_lds(&s.W[1][0], NK, 1, NK);
-    v.to_lds(s.vc, NV, 1, NV);
+    v.to_lds(s.vc, NVS, 1, NVS);
     for (int n = threadIdx.x; n < NK; n += kThreads) {
       s.W[2][n] = 0.0f;
       s.W[3][n] = 0.0f;
@@ -119,8 +175,8 @@ struct GStage {
 // Dots and decays for the current entry cur = m-1 (after staging is visible):
 //   kk[i] = beta_cur r_{cur,i} (k_cur . k_i) for i < cur
 //   kq[i] = r_{cur,i} (k_i . q) for i <= cur;  rr[i] = r_{cur,i};  gam = gamma_cur
-template <int NK, int NV>
-__device__ __forceinline__ void gdn_dots(GSmem<NK, NV>& s, int m) {
+template <int NK, int NVS>
+__device__ __forceinline__ void gdn_dots(GSmem<NK, NVS>& s, int m) {
   const int cur = m - 1;
   const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
   for (int pr = grp; pr < 2 * m - 1; pr += kThreads / 16) {
@@ -150,8 +206,8 @@ __device__ __forceinline__ void gdn_dots(GSmem<NK, NV>& s, int m) {
 
 // u_cur[v] = beta (v_cur - gamma S0 k_cur) - sum_{i<cur} kk[i] u_i, stored in U[cur];
 // returns o[v] = gamma S0 q + sum_{i<=cur} kq[i] u_i for the thread's column v.
-template <int NK, int NV>
-__device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NV>& s, int m, int v) {
+template <int NK, int NVS>
+__device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NVS>& s, int m, int v) {
   const int cur = m - 1;
   float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]);
   for (int i = 0; i < cur; ++i) u -= s.kk[i] * s.U[i][v];
@@ -168,21 +224,23 @@ __device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NV>& s, int m, int
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
-  __shared__ GSmem<NK, NV> s;
-  const GPtrs p = gdn_tile(a);
-  RawTile<FMT_F32, 4, NK, NV> raw;
-  raw.issue(a.ck, p.tile);
+  constexpr int NVS = NV;   // whole state per workgroup (measured faster for read + write)
+  __shared__ GSmem<NK, NVS> s;
+  const GPtrs p = gdn_tile<NV, 1>(a);
+  float* ck = static_cast<float*>(a.ck.data);
+  GSlice<NK, NV, NVS> raw;
+  raw.issue(ck, p.st, p.c0);
   const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
   const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
   const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
-  const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
+  const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
   for (int i = threadIdx.x; i < NK; i += kThreads) {
     s.W[0][i] = to_f(ik[i]);
     s.W[1][i] = to_f(iq[i]);
     s.W[2][i] = 0.0f;
     s.W[3][i] = 0.0f;
   }
-  for (int i = threadIdx.x; i < NV; i += kThreads) s.vc[i] = to_f(iv[i]);
+  for (int i = threadIdx.x; i < NVS; i += kThreads) s.vc[i] = to_f(iv[i]);
   __syncthreads();
   // k . q (one 16-lane group)
   if (threadIdx.x < 16) {
@@ -191,17 +249,18 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
     part = group_sum16(part);
     if (threadIdx.x == 0) s.kq[0] = part;
   }
-  const float alpha = expf(a.g[p.tile]);
-  const float beta = a.beta[p.tile];
-  RegTile<4, NK, NV> S;
+  const float alpha = expf(a.g[p.st]);
+  const float beta = a.beta[p.st];
+  RegTile<4, NK, NVS> S;
   raw.decode(S);
   tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // out[0] = S k, out[1] = S q
-  for (int v = threadIdx.x; v < NV; v += kThreads) s.U[0][v] = beta * (s.vc[v] - alpha * s.out[0][v]);
+  for (int v = threadIdx.x; v < NVS; v += kThreads) s.U[0][v] = beta * (s.vc[v] - alpha * s.out[0][v]);
   __syncthreads();
-  tile_rank_update(S, alpha, &s.W[0][0], NK, &s.U[0][0], NV, 1);
-  tile_store<FMT_F32>(a.ck, p.tile, S, s.s4);
+  tile_rank_update(S, alpha, &s.W[0][0], NK, &s.U[0][0], NVS, 1);
+  GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
   const float kq = s.kq[0];
-  for (int v = threadIdx.x; v < NV; v += kThreads) a.o[p.tile * NV + v] = alpha * s.out[1][v] + kq * s.U[0][v];
+  for (int v = threadIdx.x; v < NVS; v += kThreads)
+    a.o[p.st * NV + p.c0 + v] = alpha * s.out[1][v] + kq * s.U[0][v];
 }
 
 // ----------------------------------------------------------------------------
@@ -209,50 +268,60 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
-  __shared__ GSmem<NK, NV> s;
-  const GPtrs p = gdn_tile(a);
-  const rs_meta* mp = a.meta + p.b;
+  constexpr int NVS = NV / gdn_slices<NV>();
+  __shared__ GSmem<NK, NVS> s;
+  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+  rs_meta* mp = a.meta + p.b;
+  const int wg = p.h * gdn_slices<NV>() + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * gdn_slices<NV>()) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
-  if (errbit == 0) {
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, wg, nck, len, nd);
+  } else {
     const int j = len + 1;
-    GStage<TIN, NK, NV> stg;
+    GStage<TIN, NK, NV, NVS> stg;
     stg.load(a, p, nck, j);            // records first, then the state tile
-    RawTile<FMT_F32, 4, NK, NV> raw;
-    raw.issue(a.ck, p.tile);
+    GSlice<NK, NV, NVS> raw;
+    raw.issue(static_cast<const float*>(a.ck.data), p.st, p.c0);
+    arr.arrive(actr, wg, nck, len, nd);
     stg.store(s, j);
     __syncthreads();
     gdn_dots(s, j);
-    RegTile<4, NK, NV> S;
+    RegTile<4, NK, NVS> S;
     raw.decode(S);
     tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // barriers inside publish the dots
     const int slot = slot_of(nck, len);
-    float* ru = static_cast<float*>(a.ru) + p.tile * kRing * NV;
-    for (int v = threadIdx.x; v < NV; v += kThreads) {
-      a.o[p.tile * NV + v] = gdn_row_and_output(s, j, v);
-      ru[slot * NV + v] = s.U[j - 1][v];
+    float* ru = static_cast<float*>(a.ru) + (p.st * kRing + slot) * NV + p.c0;
+    for (int v = threadIdx.x; v < NVS; v += kThreads) {
+      a.o[p.st * NV + p.c0 + v] = gdn_row_and_output(s, j, v);
+      ru[v] = s.U[j - 1][v];
     }
-    // append the current record (bit copies)
-    const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
-    TIN* rv = static_cast<TIN*>(a.rv) + p.tile * kRing * NV;
-    const TIN* iv = static_cast<const TIN*>(a.v) + p.tile * NV;
-    for (int v = threadIdx.x; v < NV; v += kThreads) rv[slot * NV + v] = iv[v];
-    if (threadIdx.x == 0) {
-      static_cast<float*>(a.rg)[p.tile * kRing + slot] = a.g[p.tile];
-      static_cast<float*>(a.rbeta)[p.tile * kRing + slot] = a.beta[p.tile];
-    }
-    if (p.h % a.vpk == 0) {
-      TIN* rk = static_cast<TIN*>(a.rk) + bk * kRing * NK;
-      TIN* rq = static_cast<TIN*>(a.rq) + bk * kRing * NK;
-      const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
-      const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
-      for (int n = threadIdx.x; n < NK; n += kThreads) {
-        rk[slot * NK + n] = ik[n];
-        rq[slot * NK + n] = iq[n];
+    // append the current record (bit copies); each slice its own v columns
+    TIN* rv = static_cast<TIN*>(a.rv) + (p.st * kRing + slot) * NV + p.c0;
+    const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
+    for (int v = threadIdx.x; v < NVS; v += kThreads) rv[v] = iv[v];
+    if (p.half == 0) {
+      if (threadIdx.x == 0) {
+        static_cast<float*>(a.rg)[p.st * kRing + slot] = a.g[p.st];
+        static_cast<float*>(a.rbeta)[p.st * kRing + slot] = a.beta[p.st];
+      }
+      if (p.h % a.vpk == 0) {
+        const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
+        TIN* rk = static_cast<TIN*>(a.rk) + bk * kRing * NK;
+        TIN* rq = static_cast<TIN*>(a.rq) + bk * kRing * NK;
+        const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
+        const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
+        for (int n = threadIdx.x; n < NK; n += kThreads) {
+          rk[slot * NK + n] = ik[n];
+          rq[slot * NK + n] = iq[n];
+        }
       }
     }
   }
+  arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::NonFlush, 0, nck, len, nd);
 }
 
 // ----------------------------------------------------------------------------
@@ -260,33 +329,42 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
-  __shared__ GSmem<NK, NV> s;
-  const GPtrs p = gdn_tile(a);
-  const rs_meta* mp = a.meta + p.b;
+  constexpr int NVS = NV / gdn_slices<NV>();
+  __shared__ GSmem<NK, NVS> s;
+  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+  rs_meta* mp = a.meta + p.b;
+  const int wg = p.h * gdn_slices<NV>() + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * gdn_slices<NV>()) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
-  if (errbit == 0) {
-    GStage<TIN, NK, NV> stg;
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, wg, nck, len, nd);
+  } else {
+    float* ck = static_cast<float*>(a.ck.data);
+    GStage<TIN, NK, NV, NVS> stg;
     stg.load(a, p, nck, m);            // records first, then the state tile
-    RawTile<FMT_F32, 4, NK, NV> raw;
-    raw.issue(a.ck, p.tile);
+    GSlice<NK, NV, NVS> raw;
+    raw.issue(ck, p.st, p.c0);
+    arr.arrive(actr, wg, nck, len, nd);
     stg.store(s, m);
     __syncthreads();
     gdn_dots(s, m);
-    RegTile<4, NK, NV> S;
+    RegTile<4, NK, NVS> S;
     raw.decode(S);
     tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);
-    for (int v = threadIdx.x; v < NV; v += kThreads) {
-      a.o[p.tile * NV + v] = gdn_row_and_output(s, m, v);
+    for (int v = threadIdx.x; v < NVS; v += kThreads) {
+      a.o[p.st * NV + p.c0 + v] = gdn_row_and_output(s, m, v);
       // fold columns r_{cur,i} u_i (same thread, same column v)
       for (int i = 0; i < m; ++i) s.U[i][v] *= s.rr[i];
     }
     __syncthreads();
-    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NV, m);
-    tile_store<FMT_F32>(a.ck, p.tile, S, s.s4);
+    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
   }
+  arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
 }
 
 // ----------------------------------------------------------------------------
@@ -295,8 +373,9 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
 namespace {
 
 template <int NK, int NV>
-void gdn_launch_shape(GDNOp op, const GDNArgs& a, const GDNLaunch& l, hipStream_t st) {
+void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   const bool bf = l.in_bf16;
+  if (op != GDNOp::Conv) l.grid *= gdn_slices<NV>();   // one workgroup per column slice of each state
   switch (op) {
     case GDNOp::Conv:
       if (bf) gdn_conv_kernel<bf16, NK, NV><<<l.grid, kThreads, 0, st>>>(a);

@@ -156,11 +156,17 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const float Ah = a.A[h], Dh = a.D[h];
-  const rs_meta* mp = a.meta + b;
+  rs_meta* mp = a.meta + b;
+  uint32_t* actr = a.arrive + static_cast<size_t>(b) * arrive_groups(a.nheads) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
-  if (errbit != 0) return;
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, h, nck, len, nd);
+    arr.finish(mp, actr, h, a.nheads, MetaOp::NonFlush, 0, nck, len, nd);
+    return;
+  }
   const int j = len + 1;
   const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
   const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
@@ -180,9 +186,10 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   cc.load(EntrySrc<TIN>{inC, inC, 0, 0, 0, NR}, 1, NR);
   const int de = static_cast<int>(threadIdx.x) < j ? static_cast<int>(threadIdx.x) : j - 1;
   const float dtv = to_f(*(de < len ? rDt + ((nck + de) & (kRing - 1)) : inDt));
-  // 2. the state tile
+  // 2. the state tile, then the arrival count
   RawTile<RDF, E, NR, NC> raw;
   raw.issue(a.rd, tile);
+  arr.arrive(actr, h, nck, len, nd);
   // 3. records to LDS, then the state-independent work
   cb.to_lds(&s.B[0][0], NR, j, NR);
   cx.to_lds(&s.X[0][0], NC, j, NC);
@@ -232,6 +239,7 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
     store_row_as(rB + slot * NR, &s.B[j - 1][0], NR);
     store_row_as(rC + slot * NR, s.C, NR);
   }
+  arr.finish(mp, actr, h, a.nheads, MetaOp::NonFlush, 0, nck, len, nd);
 }
 
 // ----------------------------------------------------------------------------
@@ -308,12 +316,16 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const float Ah = a.A[h];
-  const rs_meta* mp = a.meta + b;
+  rs_meta* mp = a.meta + b;
+  uint32_t* actr = a.arrive + static_cast<size_t>(b) * arrive_groups(a.nheads) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
-  if (errbit == 0) {
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, h, nck, len, nd);
+  } else {
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
     const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
     const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
@@ -333,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
     const float dtv = to_f(*EntrySrc<TIN>{rDt, inDt, 0, nck, len, 1}.at(de));
     RawTile<CKF, E, NR, NC> raw;
     raw.issue(a.ck, tile);
+    arr.arrive(actr, h, nck, len, nd);
     cb.to_lds(&s.B[0][0], NR, m, NR);
     cx.to_lds(&s.X[0][0], NC, m, NC);
     cc.to_lds(&s.Cw[0][0], NR, 1, NR);
@@ -350,6 +363,7 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
       a.y[static_cast<size_t>(tile) * NC + p] = s.out[p] + Dh * s.X[m - 1][p];
     store_folded<CKF, RC>(a, tile, H, s.s4);
   }
+  arr.finish(mp, actr, h, a.nheads, MetaOp::Flush, 0, nck, len, nd);
 }
 
 // ----------------------------------------------------------------------------
@@ -369,11 +383,15 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const int K = a.K;
   const float Ah = a.A[h];
-  const rs_meta* mp = a.meta + b;
+  rs_meta* mp = a.meta + b;
+  uint32_t* actr = a.arrive + static_cast<size_t>(b) * arrive_groups(a.nheads) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = (nd != 0 || len + K > kRing) ? RS_ERR_OVERFLOW : 0;
-  if (errbit == 0) {
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, h, nck, len, nd);
+  } else {
     const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
     const size_t gstride = static_cast<size_t>(a.batch) * a.ngroups * NR;   // between drafts (B, C)
     const size_t xstride = static_cast<size_t>(a.batch) * a.nheads * NC;    // between drafts (x)
@@ -398,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
     const float dtv = to_f(*EntrySrc<TIN>{rDt, inDt, dstride, nck, len, 1}.at(de));
     RawTile<RDF, E, NR, NC> raw;
     raw.issue(a.rd, tile);
+    arr.arrive(actr, h, nck, len, nd);
     cb.to_lds(&s.B[0][0], NR, n, NR);
     cx.to_lds(&s.X[0][0], NC, n, NC);
     cc.to_lds(&s.Cw[0][0], NR, K, NR);
@@ -438,6 +457,7 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
       }
     }
   }
+  arr.finish(mp, actr, h, a.nheads, MetaOp::Append, K, nck, len, nd);
 }
 
 // ----------------------------------------------------------------------------

@@ -154,3 +154,35 @@ def test_qwen_batch256_sampled():
     nck, ln, nd, err, arrive = read_meta(rl, rb)
     assert (nck == 32).all() and (ln == 0).all() and not err.any() and not arrive.any()
     assert rel_l2(read_state_f32(rl, rb, seqs), ref.S) <= 1e-5
+
+
+def test_error_bits_leave_state_unchanged_then_flush():
+    """dk = dv = 128 (two column slices per state). A non-flush step on a full
+    buffer is refused for every sequence: sticky RS_ERR_FULL, outputs not
+    written, checkpoint and ring untouched, counters as they were. The flush
+    that follows folds the 16 accepted tokens as if the refused one never came."""
+    w = W.TINY_GDN.with_(batch=3, n_qk=2, n_v=4, dk=128, dv=128, init_std=0.3, seed=97)
+    gp = W.gdn_params(w)
+    S0 = W.gdn_init_states(w, range(w.batch))
+    layer, bufs = gdn_layer(w)
+    load_state_f32(layer, bufs, S0)
+    ref = decode.GDNConventional(S0)
+    for t in range(15):
+        tok = W.gdn_step(w, t, range(w.batch), gp)
+        o = y_buf(w.batch, w.n_v, w.dv)
+        rs.rs_step_nonflush(layer, bufs, gdn_tok_dev(tok, w.in_dtype), None, None, o)
+        assert rel_l2(o.cpu().numpy(), ref.step(tok)) <= 1e-5
+    ck, ring = bufs.ckpt.clone(), bufs.ring.clone()
+    o = y_buf(w.batch, w.n_v, w.dv)
+    rs.rs_step_nonflush(layer, bufs, gdn_tok_dev(W.gdn_step(w, 99, range(w.batch), gp), w.in_dtype), None, None, o)
+    nck, ln, nd, err, arrive = read_meta(layer, bufs)
+    assert (err == rs.RS_ERR_FULL).all() and (ln == 15).all() and (nck == 0).all() and not arrive.any()
+    assert torch.isnan(o).all()
+    assert torch.equal(ck, bufs.ckpt) and torch.equal(ring, bufs.ring)
+    tok = W.gdn_step(w, 15, range(w.batch), gp)
+    o = y_buf(w.batch, w.n_v, w.dv)
+    rs.rs_step_flush(layer, bufs, gdn_tok_dev(tok, w.in_dtype), None, None, o)
+    assert rel_l2(o.cpu().numpy(), ref.step(tok)) <= 1e-5
+    nck, ln, nd, err, arrive = read_meta(layer, bufs)
+    assert (err == rs.RS_ERR_FULL).all() and (ln == 0).all() and (nck == 16).all() and not arrive.any()
+    assert rel_l2(read_state_f32(layer, bufs), ref.S) <= 1e-5
