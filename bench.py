@@ -42,7 +42,8 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "SSM-layer decode tokens/s at batch 256 + achieved HBM GB/s (% of peak) vs conventional"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["ssm_decode_checkpoint_amd/csrc/rs_mamba2_kernels.h", "ssm_decode_checkpoint_amd/csrc/rs_tile.h",
-                  "ssm_decode_checkpoint_amd/csrc/rs_device.h"]
+                  "ssm_decode_checkpoint_amd/csrc/rs_device.h", "ssm_decode_checkpoint_amd/csrc/rs_internal.h",
+                  "ssm_decode_checkpoint_amd/build.py"]
 
 
 def kernel_source_hash() -> str:
@@ -282,6 +283,70 @@ def bench_mamba2(args, torch, rs):
     }
 
 
+SWEEP_BATCHES = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
+
+
+def bench_sweep(args, torch, rs):
+    """Conventional vs ReplaySSM decode over batch sizes on the Nemotron-style
+    Mamba-2 layer shapes (128 heads, 64 x 128 fp32 state, bf16 inputs). Each
+    batch times whole 16-token windows of both paths; the inputs are the first
+    B sequences of one resident 16-step pool. Below about 64 sequences the
+    checkpoint (4 MiB per sequence) fits the 256 MB last-level cache, so GB/s
+    there are effective rather than HBM rates."""
+    w = W.M2_NEMOTRON
+    dev = "cuda"
+    p = W.m2_params(w)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    bmax = max(SWEEP_BATCHES)
+    pool = _m2_pool(torch, w, bmax, dev)
+    byt = m2_bytes(w)
+    tm = Timer(torch)
+    rows = []
+    for B in SWEEP_BATCHES:
+        sub = [{k: v[:B] for k, v in tk.items()} for tk in pool]
+        rl, rb = _m2_layer(rs, w, B, rs.RS_REPLAY, dev)
+        cl, cb = _m2_layer(rs, w, B, rs.RS_CONVENTIONAL, dev)
+        y = torch.empty(B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+
+        def replay_window(ev):
+            for t in range(RING):
+                fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
+                _marked(ev, t, tm.stream, lambda: fn(rl, rb, sub[t], A, D, y))
+
+        def conv_window(ev):
+            for t in range(RING):
+                _marked(ev, t, tm.stream, lambda: rs.rs_step_conventional(cl, cb, sub[t], A, D, y))
+
+        total_r, per_r = tm.run(replay_window, args.steps, args.warmup, RING)
+        total_c, _ = tm.run(conv_window, args.steps, args.warmup, RING)
+        ntok = B * RING * args.steps
+        win_bytes = (sum(byt["nonflush"].values()) + byt["flush"]) * B
+        rows.append({"batch": B,
+                     "replay_tokens_per_s": ntok / (total_r * 1e-3),
+                     "conventional_tokens_per_s": ntok / (total_c * 1e-3),
+                     "speedup": total_c / total_r,
+                     "replay_window_ms": total_r / args.steps,
+                     "conventional_window_ms": total_c / args.steps,
+                     "replay_nonflush_ms": float(per_r[:, :RING - 1].mean()),
+                     "replay_flush_ms": float(per_r[:, RING - 1].mean()),
+                     "replay_window_gbs": win_bytes / (total_r / args.steps * 1e-3) / 1e9,
+                     "conventional_gbs": byt["conv"] * B * RING / (total_c / args.steps * 1e-3) / 1e9})
+        print(f"sweep: batch {B} done", file=sys.stderr, flush=True)
+        del rl, rb, cl, cb, y
+        torch.cuda.empty_cache()
+    best = max(rows, key=lambda r: r["replay_tokens_per_s"])
+    return {"metric": "SSM-layer decode tokens/s over batch size, ReplaySSM vs conventional (Mamba-2)",
+            "value": best["replay_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": best["replay_window_ms"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "mamba2_nemotron_batch_sweep", "batches": list(SWEEP_BATCHES),
+                       "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                       "inputs": "bf16", "checkpoint": "f32",
+                       "step": "one 16-token window per path: 15 non-flush + 1 flush vs 16 conventional"},
+            "rows": rows}
+
+
 def bench_gdn(args, torch, rs):
     w = W.GDN_QWEN
     dev = "cuda"
@@ -459,9 +524,16 @@ def bench_lowprec(args, torch, rs):
 
 def lowprec_error(args, torch, rs):
     """Relative L2 error of y vs the fp64 recurrence over length, per format, on a
-    few sequences of the low-precision workload (inputs drawn step by step)."""
+    few sequences of the low-precision workload (inputs drawn step by step).
+    The GPU runs every head; the fp64 reference and the error cover every 8th
+    head (heads are independent; head 8k keeps its B/C group k div 2 under the
+    contiguous head-to-group map, so the sampled heads form a layer of their own)."""
     from oracle import decode
     w = W.M2_LOWPREC
+    if args.lowprec_slow_decay:
+        # stress run outside the C5 configuration: |A| in (0.002, 0.02) keeps ~99% of the
+        # checkpoint across a 16-token window, so an error stored in it is carried over
+        w = w.with_(name="mamba2_lowprec_b64_slow_decay", a_range=(0.002, 0.02))
     nb = args.lowprec_error_seqs
     dev = "cuda"
     p = W.m2_params(w)
@@ -472,7 +544,9 @@ def lowprec_error(args, torch, rs):
     for fmt, rc in LOWPREC_VARIANTS:
         layers[fmt + ("+nvfp4_reads" if rc else "")] = _m2_layer(rs, w, nb, rs.RS_REPLAY, dev, ckpt=code[fmt],
                                                                  read_copy=rs.RS_NVFP4 if rc else None, fuse=1)
-    exact = decode.M2Conventional(W.m2_init_states(w, range(nb)), p["A"], p["D"])
+    hs = np.arange(0, w.nheads, 8)
+    assert w.nheads % 8 == 0 and (w.nheads // w.ngroups) % 8 == 0
+    exact = decode.M2Conventional(W.m2_init_states(w, range(nb))[:, hs], p["A"][hs], p["D"][hs])
     y = torch.empty(nb, w.nheads, w.headdim, dtype=torch.float32, device=dev)
     steps = args.lowprec_error_steps
     every = max(1, steps // 16)
@@ -481,11 +555,11 @@ def lowprec_error(args, torch, rs):
     for t in range(steps):
         tk = W.m2_step(w, t, range(nb))
         dtk = {k: _bf16_dev(torch, v, dev) for k, v in tk.items()}
-        ye = exact.step(tk)
+        ye = exact.step({**tk, "x": tk["x"][:, hs], "dt": tk["dt"][:, hs]})
         for name, (layer, bufs) in layers.items():
             fn = rs.rs_step_flush if t % RING == RING - 1 else rs.rs_step_nonflush
             fn(layer, bufs, dtk, A, D, y)
-            yg = y.cpu().numpy().astype(np.float64)
+            yg = y[:, hs].cpu().numpy().astype(np.float64)
             acc[name][0] += float(np.sum((yg - ye) ** 2))
             acc[name][1] += float(np.sum(ye ** 2))
         if (t + 1) % every == 0:
@@ -493,7 +567,8 @@ def lowprec_error(args, torch, rs):
                 curve[name].append([t + 1, (acc[name][0] / acc[name][1]) ** 0.5])
                 acc[name] = [0.0, 0.0]
             print(f"lowprec error: step {t + 1} of {steps}", file=sys.stderr, flush=True)
-    return {"sequences": nb, "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
+    return {"workload": w.name, "a_range": list(w.a_range), "sequences": nb, "heads": [int(h) for h in hs],
+            "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
 
 
 def bench_copy(args, torch, rs):
@@ -517,11 +592,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "lowprec", "copy"],
+    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "lowprec", "copy", "sweep"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
     ap.add_argument("--lowprec-error-seqs", type=int, default=2)
+    ap.add_argument("--lowprec-slow-decay", action="store_true",
+                    help="error run with slowly decaying heads (outside the C5 configuration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode step needs no "
@@ -533,6 +610,7 @@ def main():
     torch.cuda.set_device(0)
     for wl in (args.workload or ["mamba2"]):
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
+              "sweep": bench_sweep,
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
         if wl == "mamba2":

@@ -129,3 +129,11 @@ def test_spec_low_precision(ckpt, rc, fmt, gate):
                       oracle_rc="nvfp4" if rc == rs.RS_NVFP4 else None)
     print(f"spec {fmt}{' + nvfp4 reads' if rc else ''}: vs same-format oracle {ws:.2e}, vs exact {we:.2e}")
     assert ws <= gate
+
+
+def test_mamba2_batch1_full_heads():
+    """One sequence of the 128-head Nemotron-style layer (the small end of the
+    batch sweep): 128 workgroups share one sequence's counters."""
+    w = W.M2_NEMOTRON.with_(batch=1, init_std=0.1, seed=120)
+    worst = _replay_vs_conv(w, 32, 1e-5)
+    assert worst <= 1e-5, worst

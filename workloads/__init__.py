@@ -34,7 +34,7 @@ the 16-bit patterns that are uploaded to the device.
 from __future__ import annotations
 
 from dataclasses import dataclass, replace
-from typing import Dict, Iterable, Sequence
+from typing import Dict, Iterable, Sequence, Tuple
 
 import numpy as np
 
@@ -96,6 +96,7 @@ class Mamba2Workload:
     steps: int
     seed: int
     max_draft: int = 0
+    a_range: Tuple[float, float] = (1.0, 16.0)   # |A| is log-uniform on this range
 
     def with_(self, **kw) -> "Mamba2Workload":
         return replace(self, **kw)
@@ -153,7 +154,7 @@ def _as_in(x: np.ndarray, in_dtype: str) -> np.ndarray:
 def m2_params(w: Mamba2Workload) -> Dict[str, np.ndarray]:
     """Per-head fp32 A (< 0) and D."""
     g = rng_for(w.seed, KEY_PARAMS)
-    A = -np.exp(g.uniform(np.log(1.0), np.log(16.0), size=w.nheads))
+    A = -np.exp(g.uniform(np.log(w.a_range[0]), np.log(w.a_range[1]), size=w.nheads))
     D = g.standard_normal(w.nheads)
     return {"A": A.astype(np.float32), "D": D.astype(np.float32)}
 
