@@ -179,15 +179,57 @@ class GDNConventional:
         self.S, o = gdn.step(self.S, tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])
         return o
 
+    def spec_round(self, drafts: Sequence[dict], accepted: np.ndarray) -> np.ndarray:
+        """Verify K drafts from the live state (keeping a snapshot per draft), then make
+        the snapshot after draft k[b] live. Returns the K outputs [K, b, n_v, dv]."""
+        S = self.S
+        snaps, os_ = [], []
+        for d in drafts:
+            S, o = gdn.step(S, d["q"], d["k"], d["v"], d["g"], d["beta"])
+            snaps.append(S)
+            os_.append(o)
+        for b, k in enumerate(np.asarray(accepted)):
+            if k >= 1:
+                self.S[b] = snaps[k - 1][b]
+        return np.stack(os_)
+
 
 class GDNReplay:
     """ReplaySSM decode of a Gated DeltaNet layer in fp64 (fp64 checkpoint)."""
 
-    def __init__(self, S0, ring: int = R):
+    def __init__(self, S0, ring: int = R, max_draft: int = 0):
         self.batch = S0.shape[0]
         self.ckpt = np.asarray(S0, dtype=np.float64).copy()
-        self.ring = RingModel(self.batch, ring, 0)
+        self.ring = RingModel(self.batch, ring, max_draft)
         self.entries: List[Dict[int, dict]] = [dict() for _ in range(self.batch)]
+
+    def spec_append(self, drafts: Sequence[dict]) -> np.ndarray:
+        """Append K drafts after the committed entries and return their verify outputs
+        [K, b, n_v, dv], each from the checkpoint and the buffer up to that draft; no
+        state is formed."""
+        K = len(drafts)
+        out = []
+        for b in range(self.batch):
+            held = [self.entries[b][s] for s in self.ring.committed_slots(b)]
+            slots = self.ring.spec_append(b, K)
+            dr = [_slice(d, b) for d in drafts]
+            if slots is None:
+                out.append(np.full((K, 1) + dr[0]["v"].shape[1:], np.nan))
+                continue
+            for s, d in zip(slots, dr):
+                self.entries[b][s] = d
+            os_ = [gdn.replay_output(self.ckpt[b:b + 1], held + dr[:i + 1], dr[i]["q"]) for i in range(K)]
+            out.append(np.stack(os_))
+        return np.concatenate(out, axis=1)
+
+    def spec_commit(self, accepted) -> None:
+        """Commit the first accepted[b] drafts of each sequence (a pointer move); fold
+        the committed entries into the checkpoint when room for the next round runs short."""
+        for b, k in enumerate(np.asarray(accepted)):
+            folded = self.ring.spec_commit(b, int(k))
+            if folded:
+                ents = [self.entries[b][s] for s in folded]
+                self.ckpt[b:b + 1] = gdn.replay_fold(self.ckpt[b:b + 1], ents)
 
     def step(self, tok, force_flush: bool = False) -> np.ndarray:
         outs = []

@@ -1,4 +1,5 @@
-"""Pins for speculative rounds and the low-precision read copy in the oracle.
+"""Pins for speculative rounds (Mamba-2 and Gated DeltaNet) and the low-precision
+read copy in the oracle.
 
 * commit(k) equals replaying the first k drafts: the replay driver's verify
   outputs and its effective state after each commit equal those of plain
@@ -77,3 +78,56 @@ def test_read_copy_isolation():
         differ = max(differ, np.abs(y1 - y2).max())
         assert np.array_equal(plain.ckpt, rc.ckpt)
     assert differ > 1e-4
+
+
+def _gdn_spec_case(batch=3, kmax=4):
+    w = W.TINY_GDN.with_(batch=batch, seed=15, init_std=0.3)
+    gp = W.gdn_params(w)
+    S0 = W.gdn_init_states(w, range(batch))
+    return w, gp, S0, kmax
+
+
+def test_gdn_commit_equals_replaying_accepted_drafts():
+    """Gated DeltaNet: verify outputs from checkpoint + buffer equal stepping the
+    drafts with snapshots; after each commit the effective state equals the state
+    after the accepted drafts; rejected drafts leave the checkpoint bits alone."""
+    w, gp, S0, kmax = _gdn_spec_case()
+    conv = decode.GDNConventional(S0)
+    rep = decode.GDNReplay(S0, max_draft=kmax)
+    folds = 0
+    t = 0
+    for rnd in range(30):
+        K = (2, 3, 4)[rnd % 3]
+        drafts = [W.gdn_step(w, t + d, range(w.batch), gp) for d in range(K)]
+        t += K
+        acc = W.accepted_counts(w.seed, rnd, w.batch, K)
+        before = rep.ckpt.copy()
+        o_rep = rep.spec_append(drafts)
+        n0 = list(rep.ring.n_ckpt)
+        rep.spec_commit(acc)
+        o_conv = conv.spec_round(drafts, acc)
+        assert np.linalg.norm(o_rep - o_conv) <= 1e-12 * np.linalg.norm(o_conv)
+        np.testing.assert_allclose(rep.effective_state(), conv.S, rtol=1e-11, atol=1e-12)
+        for b in range(w.batch):
+            if rep.ring.n_ckpt[b] == n0[b]:
+                assert np.array_equal(rep.ckpt[b], before[b])
+            else:
+                folds += 1
+    assert folds > 0
+    assert rep.ring.err == [0] * w.batch
+
+
+def test_gdn_plain_steps_continue_after_spec():
+    w, gp, S0, kmax = _gdn_spec_case(batch=2)
+    conv = decode.GDNConventional(S0)
+    rep = decode.GDNReplay(S0, max_draft=kmax)
+    for rnd in range(6):
+        drafts = [W.gdn_step(w, rnd * kmax + d, range(w.batch), gp) for d in range(kmax)]
+        acc = W.accepted_counts(w.seed, rnd, w.batch, kmax)
+        rep.spec_append(drafts)
+        rep.spec_commit(acc)
+        conv.spec_round(drafts, acc)
+    for t in range(100, 140):
+        tk = W.gdn_step(w, t, range(w.batch), gp)
+        o1, o2 = conv.step(tk), rep.step(tk)
+        assert np.linalg.norm(o2 - o1) <= 1e-12 * np.linalg.norm(o1)
