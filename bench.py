@@ -473,6 +473,74 @@ def bench_spec(args, torch, rs):
     }
 
 
+def bench_gdn_spec(args, torch, rs):
+    """Speculative decoding on the Qwen-style GDN layer: batch 256, 4 drafts per
+    round, seeded acceptance U{0..4}; ReplaySSM (append with cached u rows, commit
+    by pointer move, folds when room runs short) vs the snapshot/restore baseline."""
+    w = W.GDN_SPEC
+    dev = "cuda"
+    B, K = w.batch, w.max_draft
+    gp = W.gdn_params(w)
+
+    def mk(mode):
+        cfg = rs.make_config(rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk, n_v_heads=w.n_v, head_k_dim=w.dk,
+                             head_v_dim=w.dv, in_dtype=rs.RS_BF16, max_draft=K)
+        _, layer = rs.rs_init(cfg)
+        return layer, rs.alloc_buffers(layer, dev)
+
+    rl, rb = mk(rs.RS_REPLAY)
+    cl, cb = mk(rs.RS_CONVENTIONAL)
+    ck = rs.ckpt_f32_view(rl, rb)
+    for b in range(B):
+        ck[b].copy_(torch.from_numpy(np.ascontiguousarray(W.gdn_init_state(w, b).transpose(0, 2, 1))).to(dev))
+    rs.ckpt_f32_view(cl, cb).copy_(ck)
+    rounds = args.spec_rounds
+    npool = min(rounds, 8)
+    drafts = []
+    for r in range(npool):
+        toks = [W.gdn_step(w, r * K + d, range(B), gp) for d in range(K)]
+        d = {k: _bf16_dev(torch, np.stack([t[k] for t in toks]), dev) for k in ("q", "k", "v")}
+        for k in ("g", "beta"):
+            d[k] = torch.from_numpy(np.stack([t[k] for t in toks]).astype(np.float32)).to(dev)
+        drafts.append(d)
+    accs_np = [W.accepted_counts(w.seed, r, B, K) for r in range(rounds)]
+    accs = [torch.from_numpy(a).to(dev) for a in accs_np]
+    committed = int(sum(a.sum() for a in accs_np))
+    o = torch.empty(K, B, w.n_v, w.dv, dtype=torch.float32, device=dev)
+    tm = Timer(torch)
+    st = tm.stream
+
+    def replay_all(ev):
+        for r in range(rounds):
+            _marked(ev, 2 * r, st, lambda: rs.rs_spec_append(rl, rb, drafts[r % npool], K, None, None, o))
+            _marked(ev, 2 * r + 1, st, lambda: rs.rs_spec_commit(rl, rb, accs[r], None, None))
+
+    def snap_all(ev):
+        for r in range(rounds):
+            _marked(ev, 2 * r, st, lambda: rs.rs_spec_append(cl, cb, drafts[r % npool], K, None, None, o))
+            _marked(ev, 2 * r + 1, st, lambda: rs.rs_spec_commit(cl, cb, accs[r], None, None))
+
+    total_r, per_r = tm.run(replay_all, 1, 1, 2 * rounds, reset=lambda: rb.meta.zero_())
+    total_c, per_c = tm.run(snap_all, 1, 1, 2 * rounds)
+    S = w.n_v * w.dv * w.dk * 4
+    return {
+        "metric": "GDN speculative decode committed tokens/s at batch 256, 4 drafts (ReplaySSM vs snapshot/restore)",
+        "value": committed / (total_r * 1e-3), "unit": "committed tokens/s", "n_gpus": 1, "steps": 1,
+        "warmup": 1, "ms_per_step": total_r, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_qk": w.n_qk, "n_v": w.n_v, "dk": w.dk, "dv": w.dv,
+                   "drafts": K, "rounds": rounds, "accepted": "U{0..4} per round",
+                   "mean_accepted": committed / (rounds * B), "step": f"{rounds} rounds of append + commit"},
+        "replay": {"append_ms": float(per_r[0, 0::2].mean()), "commit_ms": float(per_r[0, 1::2].mean()),
+                   "round_ms": total_r / rounds,
+                   "append_ckpt_read_gbs": S * B / (per_r[0, 0::2].mean() * 1e-3) / 1e9},
+        "snapshot_baseline": {"committed_tokens_per_s": committed / (total_c * 1e-3),
+                              "append_ms": float(per_c[0, 0::2].mean()), "restore_ms": float(per_c[0, 1::2].mean()),
+                              "round_ms": total_c / rounds},
+        "speedup_vs_snapshot": total_c / total_r,
+    }
+
+
 LOWPREC_VARIANTS = [("f32", None), ("f32", "nvfp4"), ("f16", "nvfp4"), ("fp8", "nvfp4"), ("f16", None),
                     ("fp8", None), ("nvfp4", None)]
 
@@ -592,7 +660,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "lowprec", "copy", "sweep"],
+    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "gdn_spec", "lowprec", "copy", "sweep"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
@@ -610,7 +678,7 @@ def main():
     torch.cuda.set_device(0)
     for wl in (args.workload or ["mamba2"]):
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
-              "sweep": bench_sweep,
+              "sweep": bench_sweep, "gdn_spec": bench_gdn_spec,
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
         if wl == "mamba2":

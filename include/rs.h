@@ -73,8 +73,9 @@
  *               which depends only on the checkpoint and entries <= i, so the
  *               library writes it once, on the step that appends entry i.
  *   inputs      q, k [batch][Hk][dk], v [batch][Hv][dv] (in_dtype);
- *               g (= log alpha) and beta: float [batch][Hv].
- *   output      o: float [batch][Hv][dv].
+ *               g (= log alpha) and beta: float [batch][Hv]; drafts stack K
+ *               tokens in front: [K][batch][...].
+ *   output      o: float [batch][Hv][dv]; for drafts [K][batch][Hv][dv].
  * NVFP4 block (read copy, or the uniform NVFP4 checkpoint), for the stored
  *   matrices M[b][h] of rows x cols (rows = N or dk, cols = P or dv):
  *     codes   uint8 [batch][heads][rows][cols/2]: two E2M1 codes per byte,
@@ -229,7 +230,10 @@ rs_status rs_step_flush(const rs_layer* L, const rs_buffers* buf, const rs_input
  * slots after the committed entries, nd = K, no state write (device error
  * RS_ERR_OVERFLOW when nd != 0 or len + K > 16). Conventional mode: the
  * snapshot baseline; steps the live state through the drafts and writes the
- * state after each draft to snap[d]. Mamba-2 only; 1 <= K <= max_draft. */
+ * state after each draft to snap[d]. Both layer kinds (for Gated DeltaNet
+ * prm may be NULL; each draft's solved row u is written beside it in the
+ * ring, and it stays valid for an accepted prefix because it depends only on
+ * the checkpoint and earlier entries); 1 <= K <= max_draft. */
 rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inputs* drafts,
                          int32_t K, const rs_params* prm, float* y, void* stream);
 
@@ -239,7 +243,8 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
  * entries are folded into the checkpoint (one write), n_ckpt += len, len = 0.
  * Device error RS_ERR_COMMIT when accepted[b] is outside [0, nd].
  * Conventional mode: live state = snap[accepted[b] - 1] where accepted[b] >= 1
- * (values outside [0, max_draft] leave the sequence unchanged). Mamba-2 only. */
+ * (values outside [0, max_draft] leave the sequence unchanged). Both layer
+ * kinds; prm (A, D) is required for Mamba-2 only. */
 rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted,
                          const rs_params* prm, void* stream);
 

@@ -240,7 +240,7 @@ def ckpt_f32_view(layer: RsLayer, bufs: Buffers):
 
 def ring_view(layer: RsLayer, bufs: Buffers, name: str):
     """One ring array as a typed tensor: Mamba-2 x [b,H,16,P], B/C [b,G,16,N], dt [b,H,16];
-    GDN q/k [b,Hk,16,dk], v [b,Hv,16,dv], g/beta [b,Hv,16]."""
+    GDN q/k [b,Hk,16,dk], v [b,Hv,16,dv], g/beta [b,Hv,16], u [b,Hv,16,dv] (fp32)."""
     import torch
     c = layer.cfg
     b = c.batch
@@ -252,9 +252,9 @@ def ring_view(layer: RsLayer, bufs: Buffers, name: str):
     else:
         shapes = {"q": (b, c.n_qk_heads, 16, c.head_k_dim), "k": (b, c.n_qk_heads, 16, c.head_k_dim),
                   "v": (b, c.n_v_heads, 16, c.head_v_dim), "g": (b, c.n_v_heads, 16),
-                  "beta": (b, c.n_v_heads, 16)}
+                  "beta": (b, c.n_v_heads, 16), "u": (b, c.n_v_heads, 16, c.head_v_dim)}
     shp = shapes[name]
-    dt, sz = (torch.float32, 4) if name in ("g", "beta") else (edt, esz)
+    dt, sz = (torch.float32, 4) if name in ("g", "beta", "u") else (edt, esz)
     off = getattr(layer, f"ring_{name}_off")
     n = 1
     for s in shp:

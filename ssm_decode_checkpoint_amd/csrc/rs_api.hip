@@ -163,6 +163,7 @@ GDNArgs gdn_args(const rs_layer* L, const rs_buffers* buf) {
   a.nv = c.n_v_heads;
   a.nqk = c.n_qk_heads;
   a.vpk = c.n_v_heads / c.n_qk_heads;
+  a.kmax = c.max_draft;
   a.ck = StateBuf{buf->ckpt, nullptr, nullptr};
   if (c.mode == RS_REPLAY) {
     char* r = static_cast<char*>(buf->ring);
@@ -174,7 +175,25 @@ GDNArgs gdn_args(const rs_layer* L, const rs_buffers* buf) {
     a.ru = r + L->ring_u_off;
     a.meta = static_cast<rs_meta*>(buf->meta);
     a.arrive = reinterpret_cast<uint32_t*>(static_cast<char*>(buf->meta) + arrive_off(*L));
+    char* w = static_cast<char*>(buf->meta) + L->meta_work_off;
+    a.work = reinterpret_cast<FoldItem*>(w);
+    a.work_count = reinterpret_cast<int*>(w + align_up(static_cast<uint64_t>(c.batch) * sizeof(FoldItem)));
+  } else {
+    a.snap = static_cast<float*>(buf->snap);
   }
+  return a;
+}
+
+CommitArgs commit_args(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted) {
+  const rs_config& c = L->cfg;
+  CommitArgs a;
+  a.batch = c.batch;
+  a.kmax = c.max_draft;
+  a.meta = static_cast<rs_meta*>(buf->meta);
+  a.accepted = accepted;
+  char* w = static_cast<char*>(buf->meta) + L->meta_work_off;
+  a.work = reinterpret_cast<FoldItem*>(w);
+  a.work_count = reinterpret_cast<int*>(w + align_up(static_cast<uint64_t>(c.batch) * sizeof(FoldItem)));
   return a;
 }
 
@@ -247,7 +266,6 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
     if (static_cast<uint64_t>(c.batch) * c.n_v_heads > (1u << 30)) return RS_E_ARG;
     if (!gdn_shape_supported(c.head_k_dim, c.head_v_dim)) return RS_E_UNSUPPORTED;
     if (c.ckpt_dtype != RS_F32 || c.read_copy != RS_NONE) return RS_E_DTYPE;
-    if (c.max_draft != 0) return RS_E_MODE;
     L.heads = c.n_v_heads;
     L.in_heads = c.n_qk_heads;
     L.rows = c.head_k_dim;
@@ -349,10 +367,24 @@ rs_status rs_step_flush(const rs_layer* L, const rs_buffers* buf, const rs_input
 rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inputs* drafts, int32_t K,
                          const rs_params* prm, float* y, void* stream) {
   if (rs_status s = check_layer(L)) return s;
-  if (L->cfg.kind != RS_MAMBA2 || L->cfg.max_draft == 0) return RS_E_MODE;
+  if (L->cfg.max_draft == 0) return RS_E_MODE;
   if (K < 1 || K > L->cfg.max_draft) return RS_E_ARG;
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
+  if (L->cfg.kind == RS_GDN) {
+    GDNArgs a;
+    if (rs_status s = gdn_common(L, buf, drafts, y, &a)) return s;
+    a.K = K;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (L->cfg.mode == RS_CONVENTIONAL) {
+      if (!buf->snap) return RS_E_ARG;
+      if (!aligned16(buf->snap)) return RS_E_ALIGN;
+      gdn_launch(GDNOp::ConvSpec, a, gdn_launch_cfg(L), st);
+    } else {
+      gdn_launch(GDNOp::SpecAppend, a, gdn_launch_cfg(L), st);
+    }
+    return launched();
+  }
   M2Args a;
   M2Launch l;
   if (rs_status s = m2_args(L, buf, &a, &l)) return s;
@@ -373,22 +405,42 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
 rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted, const rs_params* prm,
                          void* stream) {
   if (rs_status s = check_layer(L)) return s;
-  if (L->cfg.kind != RS_MAMBA2 || L->cfg.max_draft == 0) return RS_E_MODE;
-  if (!accepted || !prm || !prm->A || !prm->D) return RS_E_ARG;
+  if (L->cfg.max_draft == 0) return RS_E_MODE;
+  if (!accepted) return RS_E_ARG;
   if (!aligned16(accepted)) return RS_E_ALIGN;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (L->cfg.kind == RS_GDN) {
+    if (!buf || !buf->ckpt) return RS_E_ARG;
+    if (L->cfg.mode == RS_REPLAY && (!buf->ring || !buf->meta)) return RS_E_ARG;
+    if (!aligned16(buf->ckpt)) return RS_E_ALIGN;
+    if (L->cfg.mode == RS_REPLAY && (!aligned16(buf->ring) || !aligned16(buf->meta))) return RS_E_ALIGN;
+    GDNArgs a = gdn_args(L, buf);
+    a.accepted = accepted;
+    GDNLaunch l = gdn_launch_cfg(L);
+    if (L->cfg.mode == RS_CONVENTIONAL) {
+      if (!buf->snap) return RS_E_ARG;
+      if (!aligned16(buf->snap)) return RS_E_ALIGN;
+      gdn_launch(GDNOp::Restore, a, l, st);
+    } else {
+      commit_meta(commit_args(L, buf, accepted), st);
+      if (hipGetLastError() != hipSuccess) return RS_E_LAUNCH;
+      gdn_launch(GDNOp::CommitFold, a, l, st);
+    }
+    return launched();
+  }
+  if (!prm || !prm->A || !prm->D) return RS_E_ARG;
   M2Args a;
   M2Launch l;
   if (rs_status s = m2_args(L, buf, &a, &l)) return s;
   a.accepted = accepted;
   a.A = prm->A;
   a.D = prm->D;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   if (L->cfg.mode == RS_CONVENTIONAL) {
     if (!buf->snap) return RS_E_ARG;
     if (!aligned16(buf->snap)) return RS_E_ALIGN;
     m2_launch(M2Op::Restore, a, l, st);
   } else {
-    m2_launch(M2Op::CommitMeta, a, l, st);
+    commit_meta(commit_args(L, buf, accepted), st);
     if (hipGetLastError() != hipSuccess) return RS_E_LAUNCH;
     const int tiles = L->cfg.batch * L->cfg.nheads;
     l.grid = tiles < 2048 ? tiles : 2048;

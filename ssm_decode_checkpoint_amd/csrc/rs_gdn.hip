@@ -188,7 +188,8 @@ __device__ __forceinline__ void gdn_dots(GSmem<NK, NVS>& s, int m) {
     part = group_sum16(part);
     if (ln == 0) {
       float r = 1.0f;
-      for (int l = i + 1; l <= cur; ++l) r *= s.al[l];
+#pragma unroll
+      for (int l = 1; l < kRing; ++l) r *= (l > i && l <= cur) ? s.al[l] : 1.0f;
       if (isq) {
         s.kq[i] = r * part;
         s.rr[i] = r;
@@ -199,7 +200,8 @@ __device__ __forceinline__ void gdn_dots(GSmem<NK, NVS>& s, int m) {
   }
   if (threadIdx.x == 0) {
     float gm = 1.0f;
-    for (int e = 0; e <= cur; ++e) gm *= s.al[e];
+#pragma unroll
+    for (int e = 0; e < kRing; ++e) gm *= e <= cur ? s.al[e] : 1.0f;
     s.gam = gm;
   }
 }
@@ -210,10 +212,14 @@ template <int NK, int NVS>
 __device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NVS>& s, int m, int v) {
   const int cur = m - 1;
   float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]);
-  for (int i = 0; i < cur; ++i) u -= s.kk[i] * s.U[i][v];
+  // fixed-length loops with selects: every LDS load is unconditional and in
+  // bounds, so they issue together instead of one round trip per entry
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i) u -= i < cur ? s.kk[i] * s.U[i][v] : 0.0f;
   s.U[cur][v] = u;
   float o = s.gam * s.out[1][v];
-  for (int i = 0; i <= cur; ++i) o += s.kq[i] * s.U[i][v];
+#pragma unroll
+  for (int i = 0; i < kRing; ++i) o += i <= cur ? s.kq[i] * s.U[i][v] : 0.0f;
   return o;
 }
 
@@ -358,7 +364,9 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
     for (int v = threadIdx.x; v < NVS; v += kThreads) {
       a.o[p.st * NV + p.c0 + v] = gdn_row_and_output(s, m, v);
       // fold columns r_{cur,i} u_i (same thread, same column v)
-      for (int i = 0; i < m; ++i) s.U[i][v] *= s.rr[i];
+#pragma unroll
+      for (int i = 0; i < kRing; ++i)
+        if (i < m) s.U[i][v] *= s.rr[i];
     }
     __syncthreads();
     tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
@@ -368,14 +376,385 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// speculative append (ReplaySSM): K drafts at window entries len..len+K-1. Each
+// draft's u row is solved in order (it depends on S0 and the entries before
+// it), its output read from the checkpoint and the buffer, and the drafts are
+// written to the ring with their u rows; no state is written. Because a u row
+// depends only on S0 and earlier entries, the rows of an accepted prefix stay
+// valid after the commit (sitech.ge ReplaySSM page, "Reducing state traffic
+// and simplifying rollback": drafts are appended until verification, the
+// verification outputs need no intermediate state).
+// ----------------------------------------------------------------------------
+namespace {
+
+template <int NK, int NVS, int KQ>
+struct GSpecSmem {
+  // k of window entries 0..n-1 (held, then drafts) for the dots; once they are
+  // done, the same space is the matvec scratch (4 KQ NVS floats), and after the
+  // matvecs the held-entry sums HU, HO (KQ NVS floats each)
+  static constexpr int KROWS = (4 * KQ * NVS + NK - 1) / NK > kRing ? (4 * KQ * NVS + NK - 1) / NK : kRing;
+  float K[KROWS][NK];
+  float W[2 * KQ][NK];         // matvec weights k_d, q_d per draft (zero past K)
+  float U[kRing][NVS];         // u rows, own columns (held from the ring, drafts solved here)
+  float V[KQ][NVS];            // v of the drafts, own columns
+  float out[2 * KQ][NVS];      // S0 k_d, S0 q_d
+  float kk[KQ][kRing];         // beta_d r_{e,i} (k_e . k_i) for i < e = len + d
+  float kq[KQ][kRing];         // r_{e,i} (k_i . q_d) for i <= e
+  float rt[KQ][kRing];         // r_{e,i} for i <= e
+  float al[kRing];             // alpha of window entry e
+  float gam[KQ];               // gamma of draft d's entry
+  float bet[KQ];
+};
+
+}  // namespace
+
+template <typename TIN, int NK, int NV, int KQ>
+__global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
+  constexpr int NS = gdn_slices<NV>();
+  constexpr int NVS = NV / NS;
+  constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NK % VK == 0 && NVS % VK == 0, "records are whole 16-byte chunks");
+  constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
+  constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
+  constexpr int CD = (KQ * NK / VK + kThreads - 1) / kThreads;
+  constexpr int CV = (KQ * NVS / VK + kThreads - 1) / kThreads;
+  __shared__ GSpecSmem<NK, NVS, KQ> s;
+  const GPtrs p = gdn_tile<NV, NS>(a);
+  const int K = a.K;
+  rs_meta* mp = a.meta + p.b;
+  const int wg = p.h * NS + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * NS) * kArriveStride;
+  const int len = mp->len, nd = mp->nd;
+  const long long nck = mp->n_ckpt;
+  const int errbit = (nd != 0 || len + K > kRing) ? RS_ERR_OVERFLOW : 0;
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, wg, nck, len, nd);
+  } else {
+    const int n = len + K;
+    const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
+    const size_t kstride = static_cast<size_t>(a.batch) * a.nqk * NK;   // between drafts (q, k)
+    const size_t vstride = static_cast<size_t>(a.batch) * a.nv * NV;    // between drafts (v, o)
+    const size_t gstride = static_cast<size_t>(a.batch) * a.nv;         // between drafts (g, beta)
+    const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
+    const float* ru = static_cast<const float*>(a.ru) + p.st * kRing * NV + p.c0;
+    const float* rg = static_cast<const float*>(a.rg) + p.st * kRing;
+    const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
+    const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
+    const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
+    // records into registers, then the state slice, then records to LDS
+    RegChunks<TIN, CK> ck;
+    RegChunks<float, CU> cu;
+    RegChunks<TIN, CD> cq, cd;
+    RegChunks<TIN, CV> cv;
+    ck.load(EntrySrc<TIN>{rk, ik, kstride, nck, len, NK}, n, NK);
+    cu.load(EntrySrc<float>{ru, ru, 0, nck, len, NV}, len, NVS);
+    cq.load(EntrySrc<TIN>{iq, iq, kstride, 0, 0, NK}, K, NK);
+    cd.load(EntrySrc<TIN>{ik, ik, kstride, 0, 0, NK}, K, NK);
+    cv.load(EntrySrc<TIN>{iv, iv, vstride, 0, 0, NVS}, K, NVS);
+    const int e = static_cast<int>(threadIdx.x) < n ? static_cast<int>(threadIdx.x) : n - 1;
+    const float gv = *(e < len ? rg + slot_of(nck, e) : a.g + static_cast<size_t>(e - len) * gstride + p.st);
+    const int dd = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
+    const float bv = a.beta[static_cast<size_t>(dd) * gstride + p.st];
+    GSlice<NK, NV, NVS> raw;
+    raw.issue(static_cast<const float*>(a.ck.data), p.st, p.c0);
+    arr.arrive(actr, wg, nck, len, nd);
+    ck.to_lds(&s.K[0][0], NK, n, NK);
+    cu.to_lds(&s.U[0][0], NVS, len, NVS);
+    cd.to_lds(&s.W[0][0], 2 * NK, K, NK);
+    cq.to_lds(&s.W[1][0], 2 * NK, K, NK);
+    for (int idx = 2 * K * NK + threadIdx.x; idx < 2 * KQ * NK; idx += kThreads) (&s.W[0][0])[idx] = 0.0f;
+    cv.to_lds(&s.V[0][0], NVS, K, NVS);
+    if (static_cast<int>(threadIdx.x) < n) s.al[threadIdx.x] = expf(gv);
+    if (static_cast<int>(threadIdx.x) < K) s.bet[threadIdx.x] = bv;
+    __syncthreads();
+    // decays r_{e,i} (direct products), one (draft, entry) pair per thread, and gamma
+    for (int idx = threadIdx.x; idx < K * kRing; idx += kThreads) {
+      const int d = idx / kRing, i = idx - d * kRing, ee = len + d;
+      if (i <= ee) {
+        float r = 1.0f;
+        for (int l = i + 1; l <= ee; ++l) r *= s.al[l];
+        s.rt[d][i] = r;
+        if (i == 0) s.gam[d] = r * s.al[0];
+      }
+    }
+    __syncthreads();
+    // dots per draft d (entry e = len + d), 16-lane groups
+    {
+      const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+      for (int pr = grp; pr < K * 2 * kRing; pr += kThreads / 16) {
+        const int d = pr / (2 * kRing), rem = pr - d * 2 * kRing;
+        const bool isq = rem >= kRing;
+        const int i = isq ? rem - kRing : rem;
+        const int ee = len + d;
+        if (isq ? i > ee : i >= ee) continue;   // uniform over the group
+        const float* other = isq ? &s.W[2 * d + 1][0] : &s.K[ee][0];
+        float part = 0.0f;
+        for (int c = ln; c < NK; c += 16) part += s.K[i][c] * other[c];
+        part = group_sum16(part);
+        if (ln == 0) {
+          if (isq) s.kq[d][i] = s.rt[d][i] * part;
+          else s.kk[d][i] = s.bet[d] * s.rt[d][i] * part;
+        }
+      }
+    }
+    float* red = &s.K[0][0];
+    float* HU = red;                 // [KQ][NVS], after the matvecs
+    float* HO = red + KQ * NVS;      // [KQ][NVS]
+    __syncthreads();                 // dots done: the k rows become scratch
+    RegTile<4, NK, NVS> S;
+    raw.decode(S);
+    // S0 [k_d, q_d]: weight rows 0..KQ-1, then KQ..2KQ-1 if drafts reach them (fewer
+    // accumulator registers and half the scratch of one 2KQ-row pass)
+    tile_matvec<KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);   // barriers inside publish the dots
+    if (2 * K > KQ) tile_matvec<KQ>(S, &s.W[KQ][0], NK, red, &s.out[KQ][0]);
+    // the held entries' part of every draft's row and output, all (draft, column) pairs at once
+    for (int idx = threadIdx.x; idx < K * NVS; idx += kThreads) {
+      const int d = idx / NVS, v = idx - d * NVS;
+      float hu = 0.0f, ho = 0.0f;
+#pragma unroll 4
+      for (int i = 0; i < len; ++i) {
+        const float ui = s.U[i][v];
+        hu += s.kk[d][i] * ui;
+        ho += s.kq[d][i] * ui;
+      }
+      HU[d * NVS + v] = hu;
+      HO[d * NVS + v] = ho;
+    }
+    __syncthreads();
+    // the drafts in order: each row also depends on the drafts before it
+    float* ruw = static_cast<float*>(a.ru) + p.st * kRing * NV + p.c0;
+    for (int v = threadIdx.x; v < NVS; v += kThreads) {
+      for (int d = 0; d < K; ++d) {
+        const int ee = len + d;
+        float u = s.bet[d] * (s.V[d][v] - s.gam[d] * s.out[2 * d][v]) - HU[d * NVS + v];
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {   // earlier drafts: entries len .. ee-1
+          const int i = len + j < kRing ? len + j : kRing - 1;
+          u -= j < d ? s.kk[d][i] * s.U[i][v] : 0.0f;
+        }
+        s.U[ee][v] = u;
+        float o = s.gam[d] * s.out[2 * d + 1][v] + HO[d * NVS + v];
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {   // drafts up to this one: entries len .. ee
+          const int i = len + j < kRing ? len + j : kRing - 1;
+          o += j <= d ? s.kq[d][i] * s.U[i][v] : 0.0f;
+        }
+        a.o[d * vstride + p.st * NV + p.c0 + v] = o;
+        ruw[slot_of(nck, ee) * NV + v] = u;
+      }
+    }
+    // drafts into the ring (bit copies); each slice its own v columns
+    TIN* rv = static_cast<TIN*>(a.rv) + p.st * kRing * NV + p.c0;
+    for (int idx = threadIdx.x; idx < K * NVS; idx += kThreads) {
+      const int d = idx / NVS, v = idx - d * NVS;
+      rv[slot_of(nck, len + d) * NV + v] = iv[d * vstride + v];
+    }
+    if (p.half == 0) {
+      if (static_cast<int>(threadIdx.x) < K) {
+        const int d = threadIdx.x, sl = slot_of(nck, len + d);
+        static_cast<float*>(a.rg)[p.st * kRing + sl] = a.g[d * gstride + p.st];
+        static_cast<float*>(a.rbeta)[p.st * kRing + sl] = a.beta[d * gstride + p.st];
+      }
+      if (p.h % a.vpk == 0) {
+        TIN* rkw = static_cast<TIN*>(a.rk) + bk * kRing * NK;
+        TIN* rqw = static_cast<TIN*>(a.rq) + bk * kRing * NK;
+        for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) {
+          const int d = idx / NK, c = idx - d * NK, sl = slot_of(nck, len + d);
+          rkw[sl * NK + c] = ik[d * kstride + c];
+          rqw[sl * NK + c] = iq[d * kstride + c];
+        }
+      }
+    }
+  }
+  arr.finish(mp, actr, wg, a.nv * NS, MetaOp::Append, K, nck, len, nd);
+}
+
+// ----------------------------------------------------------------------------
+// speculative commit (ReplaySSM), fold part: for each sequence listed by
+// commit_meta, S <- gamma_m S0 + sum_i r_{m,i} u_i k_i^T over its m committed
+// entries (u rows from the ring), one column slice per work item, over a
+// fixed grid (every workgroup leaves when the list is done)
+// ----------------------------------------------------------------------------
+template <typename TIN, int NK, int NV>
+__global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
+  constexpr int NS = gdn_slices<NV>();
+  constexpr int NVS = NV / NS;
+  constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
+  constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
+  __shared__ GSmem<NK, NVS> s;
+  const int per = a.nv * NS;
+  const int total = *a.work_count * per;
+  float* ckp = static_cast<float*>(a.ck.data);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const FoldItem it = a.work[item / per];
+    const int r = item - (item / per) * per;
+    const int h = r / NS, half = r - h * NS, c0 = half * NVS, m = it.m;
+    const size_t st = static_cast<size_t>(it.b) * a.nv + h;
+    const size_t bk = static_cast<size_t>(it.b) * a.nqk + h / a.vpk;
+    const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
+    const float* ru = static_cast<const float*>(a.ru) + st * kRing * NV + c0;
+    const float* rg = static_cast<const float*>(a.rg) + st * kRing;
+    RegChunks<TIN, CK> ck;
+    RegChunks<float, CU> cu;
+    ck.load(EntrySrc<TIN>{rk, rk, 0, it.nck, m, NK}, m, NK);
+    cu.load(EntrySrc<float>{ru, ru, 0, it.nck, m, NV}, m, NVS);
+    const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+    const float gv = rg[slot_of(it.nck, e)];
+    GSlice<NK, NV, NVS> raw;
+    raw.issue(ckp, st, c0);
+    ck.to_lds(&s.K[0][0], NK, m, NK);
+    cu.to_lds(&s.U[0][0], NVS, m, NVS);
+    if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(gv);
+    __syncthreads();
+    if (static_cast<int>(threadIdx.x) < m) {
+      float w = 1.0f;
+#pragma unroll
+      for (int l = 1; l < kRing; ++l) w *= (l > static_cast<int>(threadIdx.x) && l < m) ? s.al[l] : 1.0f;
+      s.rr[threadIdx.x] = w;
+    }
+    if (threadIdx.x == 0) {
+      float gm = 1.0f;
+#pragma unroll
+      for (int l = 0; l < kRing; ++l) gm *= l < m ? s.al[l] : 1.0f;
+      s.gam = gm;
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < NVS; v += kThreads)
+#pragma unroll
+      for (int i = 0; i < kRing; ++i)
+        if (i < m) s.U[i][v] *= s.rr[i];
+    __syncthreads();
+    RegTile<4, NK, NVS> S;
+    raw.decode(S);
+    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    GSlice<NK, NV, NVS>::store(ckp, st, c0, S);
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------
+// snapshot baseline: step the live state through K drafts, write each state to
+// snap[d] and each output; the live state is not written here (the restore
+// below makes the snapshot after the last accepted draft live)
+// ----------------------------------------------------------------------------
+namespace {
+
+template <int NK, int NVS, int KQ>
+struct GConvSpecSmem {
+  float W[2 * KQ][NK];   // k_d, q_d
+  float V[KQ][NVS];      // v_d, own columns
+  float out[2][NVS];     // S k_d, S q_d
+  float red[4 * 2 * NVS];
+  float U[NVS];
+  float kq[KQ], al[KQ], bet[KQ];
+};
+
+}  // namespace
+
+// One workgroup per column slice, as in the replay kernels (the delta rule is
+// column-independent in the stored layout): the whole 128 x 128 state in one
+// workgroup needs 132 registers per lane here and runs at 3 waves per SIMD.
+template <typename TIN, int NK, int NV, int KQ>
+__global__ __launch_bounds__(kThreads) void gdn_conv_spec_kernel(GDNArgs a) {
+  constexpr int NS = gdn_slices<NV>();
+  constexpr int NVS = NV / NS;
+  constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  constexpr int CD = (KQ * NK / VK + kThreads - 1) / kThreads;
+  constexpr int CV = (KQ * NVS / VK + kThreads - 1) / kThreads;
+  __shared__ GConvSpecSmem<NK, NVS, KQ> s;
+  const GPtrs p = gdn_tile<NV, NS>(a);
+  const int K = a.K;
+  const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
+  const size_t kstride = static_cast<size_t>(a.batch) * a.nqk * NK;
+  const size_t vstride = static_cast<size_t>(a.batch) * a.nv * NV;
+  const size_t gstride = static_cast<size_t>(a.batch) * a.nv;
+  const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
+  const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
+  const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
+  RegChunks<TIN, CD> cq, cd;
+  RegChunks<TIN, CV> cv;
+  cq.load(EntrySrc<TIN>{iq, iq, kstride, 0, 0, NK}, K, NK);
+  cd.load(EntrySrc<TIN>{ik, ik, kstride, 0, 0, NK}, K, NK);
+  cv.load(EntrySrc<TIN>{iv, iv, vstride, 0, 0, NVS}, K, NVS);
+  const int dd = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
+  const float gv = a.g[dd * gstride + p.st], bv = a.beta[dd * gstride + p.st];
+  float* ck = static_cast<float*>(a.ck.data);
+  GSlice<NK, NV, NVS> raw;
+  raw.issue(ck, p.st, p.c0);
+  cd.to_lds(&s.W[0][0], 2 * NK, K, NK);
+  cq.to_lds(&s.W[1][0], 2 * NK, K, NK);
+  cv.to_lds(&s.V[0][0], NVS, K, NVS);
+  if (static_cast<int>(threadIdx.x) < K) {
+    s.al[threadIdx.x] = expf(gv);
+    s.bet[threadIdx.x] = bv;
+  }
+  __syncthreads();
+  {
+    const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+    for (int d = grp; d < K; d += kThreads / 16) {
+      float part = 0.0f;
+      for (int c = ln; c < NK; c += 16) part += s.W[2 * d][c] * s.W[2 * d + 1][c];
+      part = group_sum16(part);
+      if (ln == 0) s.kq[d] = part;
+    }
+  }
+  RegTile<4, NK, NVS> S;
+  raw.decode(S);
+  for (int d = 0; d < K; ++d) {
+    tile_matvec<2>(S, &s.W[2 * d][0], NK, s.red, &s.out[0][0]);   // S k_d, S q_d (barriers inside)
+    const float al = s.al[d], be = s.bet[d], kq = s.kq[d];
+    for (int v = threadIdx.x; v < NVS; v += kThreads) {
+      const float u = be * (s.V[d][v] - al * s.out[0][v]);
+      s.U[v] = u;
+      a.o[d * vstride + p.st * NV + p.c0 + v] = al * s.out[1][v] + kq * u;
+    }
+    __syncthreads();
+    tile_rank_update(S, al, &s.W[2 * d][0], NK, s.U, NVS, 1);
+    GSlice<NK, NV, NVS>::store(a.snap + d * vstride * NK, p.st, p.c0, S);
+    __syncthreads();
+  }
+}
+
+// snapshot baseline commit: the snapshot after draft k[b] becomes the live state
+template <int NK, int NV>
+__global__ __launch_bounds__(kThreads) void gdn_restore_kernel(GDNArgs a) {
+  const GPtrs p = gdn_tile<NV, 1>(a);
+  const int k = a.accepted[p.b];
+  if (k < 1 || k > a.kmax) return;
+  const size_t mat = static_cast<size_t>(NK) * NV;
+  const float4* src = reinterpret_cast<const float4*>(
+      a.snap + (static_cast<size_t>(k - 1) * a.batch * a.nv + p.st) * mat);
+  float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.ck.data) + p.st * mat);
+  for (size_t i = threadIdx.x; i < mat / 4; i += kThreads) nt_store(nt_load(src + i), dst + i);
+}
+
+// ----------------------------------------------------------------------------
 // host side
 // ----------------------------------------------------------------------------
 namespace {
 
+template <typename TIN, int NK, int NV>
+void gdn_spec_append(const GDNArgs& a, int grid, hipStream_t st) {
+  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2><<<grid, kThreads, 0, st>>>(a);
+  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4><<<grid, kThreads, 0, st>>>(a);
+  else gdn_spec_append_kernel<TIN, NK, NV, 8><<<grid, kThreads, 0, st>>>(a);
+}
+
+template <typename TIN, int NK, int NV>
+void gdn_conv_spec(const GDNArgs& a, int grid, hipStream_t st) {
+  if (a.K <= 2) gdn_conv_spec_kernel<TIN, NK, NV, 2><<<grid, kThreads, 0, st>>>(a);
+  else if (a.K <= 4) gdn_conv_spec_kernel<TIN, NK, NV, 4><<<grid, kThreads, 0, st>>>(a);
+  else gdn_conv_spec_kernel<TIN, NK, NV, 8><<<grid, kThreads, 0, st>>>(a);
+}
+
 template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   const bool bf = l.in_bf16;
-  if (op != GDNOp::Conv) l.grid *= gdn_slices<NV>();   // one workgroup per column slice of each state
+  // replay steps and appends: one workgroup per column slice of each state
+  if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::SpecAppend || op == GDNOp::ConvSpec)
+    l.grid *= gdn_slices<NV>();
   switch (op) {
     case GDNOp::Conv:
       if (bf) gdn_conv_kernel<bf16, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
@@ -388,6 +767,24 @@ void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
     case GDNOp::Flush:
       if (bf) gdn_flush_kernel<bf16, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
       else gdn_flush_kernel<float, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
+      break;
+    case GDNOp::SpecAppend:
+      if (bf) gdn_spec_append<bf16, NK, NV>(a, l.grid, st);
+      else gdn_spec_append<float, NK, NV>(a, l.grid, st);
+      break;
+    case GDNOp::CommitFold: {
+      const int items = l.grid * gdn_slices<NV>();   // upper bound of listed work items
+      const int grid = items < 2048 ? items : 2048;
+      if (bf) gdn_commit_fold_kernel<bf16, NK, NV><<<grid, kThreads, 0, st>>>(a);
+      else gdn_commit_fold_kernel<float, NK, NV><<<grid, kThreads, 0, st>>>(a);
+      break;
+    }
+    case GDNOp::ConvSpec:
+      if (bf) gdn_conv_spec<bf16, NK, NV>(a, l.grid, st);
+      else gdn_conv_spec<float, NK, NV>(a, l.grid, st);
+      break;
+    case GDNOp::Restore:
+      gdn_restore_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a);
       break;
   }
 }

@@ -37,7 +37,7 @@ struct M2Args {
   const int32_t* accepted;
 };
 
-enum class M2Op { Conv, NonFlush, Flush, SpecAppend, CommitMeta, CommitFold, ConvSpec, Restore, Requant };
+enum class M2Op { Conv, NonFlush, Flush, SpecAppend, CommitFold, ConvSpec, Restore, Requant };
 
 struct M2Launch {
   int rows, cols;   // dstate, headdim
@@ -124,19 +124,35 @@ struct Arrival {
 bool m2_shape_supported(int dstate, int headdim);
 void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st);
 
+// Speculative commit, counter part (both layer kinds): len += accepted[b], nd = 0,
+// and the ordered list of sequences whose committed entries must be folded now.
+struct CommitArgs {
+  int batch, kmax;
+  rs_meta* meta;
+  const int32_t* accepted;
+  FoldItem* work;
+  int* work_count;
+};
+void commit_meta(const CommitArgs& a, hipStream_t st);
+
 // Gated DeltaNet
 struct GDNArgs {
   int batch, nv, nqk, vpk;   // vpk = value heads per qk head
-  StateBuf ck;
+  int K, kmax;               // speculative: drafts in this call, configured maximum
+  StateBuf ck;               // checkpoint, or live state (conventional)
+  float* snap;               // snapshot baseline states [kmax][batch][nv][dk][dv]
   void *rq, *rk, *rv, *rg, *rbeta, *ru;
   rs_meta* meta;
   uint32_t* arrive;     // first-level arrival counters, arrive_groups(workgroups per sequence) each
-  const void *q, *k, *v;
+  FoldItem* work;
+  int* work_count;
+  const int32_t* accepted;
+  const void *q, *k, *v;     // one token, or K drafts stacked [K][batch][...]
   const float *g, *beta;
-  float* o;
+  float* o;                  // [batch][nv][dv], or [K][batch][nv][dv]
 };
 
-enum class GDNOp { Conv, NonFlush, Flush };
+enum class GDNOp { Conv, NonFlush, Flush, SpecAppend, CommitFold, ConvSpec, Restore };
 
 struct GDNLaunch {
   int dk, dv;

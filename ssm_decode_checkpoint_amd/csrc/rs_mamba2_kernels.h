@@ -461,68 +461,9 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
 }
 
 // ----------------------------------------------------------------------------
-// speculative commit (ReplaySSM), part 1: counters, and the list of sequences
-// whose committed entries must be folded now. One workgroup; the list is in
-// ascending sequence order.
+// speculative commit (ReplaySSM): the counter part and its fold list are built
+// by commit_meta (rs_commit.hip); here the listed sequences are folded.
 // ----------------------------------------------------------------------------
-static __global__ __launch_bounds__(1024) void m2_commit_meta_kernel(M2Args a) {
-  __shared__ int wsum[16];
-  __shared__ int base;
-  if (threadIdx.x == 0) base = 0;
-  __syncthreads();
-  for (int b0 = 0; b0 < a.batch; b0 += 1024) {
-    const int b = b0 + threadIdx.x;
-    int fold = 0, m = 0;
-    long long nck = 0;
-    if (b < a.batch) {
-      rs_meta* mp = a.meta + b;
-      const int k = a.accepted[b];
-      const int nd = mp->nd;
-      if (k < 0 || k > nd) {
-        mp->err |= RS_ERR_COMMIT;
-      } else {
-        const int len = mp->len + k;
-        mp->nd = 0;
-        nck = mp->n_ckpt;
-        if (len > kRing - a.kmax) {
-          fold = 1;
-          m = len;
-          mp->n_ckpt = nck + len;
-          mp->len = 0;
-        } else {
-          mp->len = len;
-        }
-      }
-    }
-    // ordered compaction: inclusive scan of `fold` over the 1024 threads
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = fold;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int before = base;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    if (fold) {
-      FoldItem it;
-      it.b = b;
-      it.m = m;
-      it.nck = nck;
-      a.work[before + incl - 1] = it;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int w = 0; w < 16; ++w) tot += wsum[w];
-      base += tot;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *a.work_count = base;
-}
-
 // part 2: fold the listed sequences' committed entries, one head per work
 // item, over a fixed grid (every workgroup leaves when the list is done)
 template <typename TIN, int CKF, bool RC, int NR, int NC>
@@ -747,9 +688,6 @@ void m2_launch_shape(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st
       break;
     case M2Op::SpecAppend:
       if (bf) Sh::template spec_append<bf16>(a, l.rdf, l.grid, st); else Sh::template spec_append<float>(a, l.rdf, l.grid, st);
-      break;
-    case M2Op::CommitMeta:
-      m2_commit_meta_kernel<<<1, 1024, 0, st>>>(a);
       break;
     case M2Op::CommitFold:
       if (bf) Sh::template commit_fold<bf16>(a, l.ckf, l.rc, l.grid, st); else Sh::template commit_fold<float>(a, l.ckf, l.rc, l.grid, st);

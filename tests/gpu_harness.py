@@ -45,6 +45,13 @@ def m2_drafts_dev(drafts: list, in_dtype: str) -> dict:
     return {k: dev_in(np.stack([d[k] for d in drafts]), in_dtype) for k in ("x", "B", "C", "dt")}
 
 
+def gdn_drafts_dev(drafts: list, in_dtype: str) -> dict:
+    d = {k: dev_in(np.stack([t[k] for t in drafts]), in_dtype) for k in ("q", "k", "v")}
+    d["g"] = dev_f32(np.stack([t["g"] for t in drafts]))
+    d["beta"] = dev_f32(np.stack([t["beta"] for t in drafts]))
+    return d
+
+
 def gdn_tok_dev(tok: dict, in_dtype: str) -> dict:
     d = {k: dev_in(tok[k], in_dtype) for k in ("q", "k", "v")}
     d["g"] = dev_f32(tok["g"])
@@ -63,9 +70,10 @@ def m2_layer(w: W.Mamba2Workload, mode=rs.RS_REPLAY, ckpt_dtype=rs.RS_F32, read_
     return layer, rs.alloc_buffers(layer, DEV)
 
 
-def gdn_layer(w: W.GDNWorkload, mode=rs.RS_REPLAY, batch=None):
+def gdn_layer(w: W.GDNWorkload, mode=rs.RS_REPLAY, batch=None, max_draft=None):
     cfg = rs.make_config(rs.RS_GDN, w.batch if batch is None else batch, mode=mode, n_qk_heads=w.n_qk,
                          n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv,
+                         max_draft=w.max_draft if max_draft is None else max_draft,
                          in_dtype=rs.RS_BF16 if w.in_dtype == "bf16" else rs.RS_F32)
     _, layer = rs.rs_init(cfg)
     return layer, rs.alloc_buffers(layer, DEV)

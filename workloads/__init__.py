@@ -114,6 +114,7 @@ class GDNWorkload:
     init_std: float
     steps: int
     seed: int
+    max_draft: int = 0
 
     def with_(self, **kw) -> "GDNWorkload":
         return replace(self, **kw)
@@ -133,6 +134,9 @@ GDN_QWEN = GDNWorkload("gdn_qwen_b256", batch=256, n_qk=16, n_v=32, dk=128, dv=1
 M2_SPEC = Mamba2Workload("mamba2_spec_b512", batch=512, nheads=128, headdim=64, dstate=128,
                          ngroups=8, in_dtype="bf16", init_std=0.1, steps=64, seed=4,
                          max_draft=4)
+# Speculative decode on the Qwen-style GDN shapes: batch 256, 4 drafts per round, 64 rounds.
+GDN_SPEC = GDNWorkload("gdn_qwen_spec_b256", batch=256, n_qk=16, n_v=32, dk=128, dv=128,
+                       in_dtype="bf16", init_std=0.1, steps=64, seed=7, max_draft=4)
 # Low-precision reads on the Nemotron-style shapes at batch 64 (zero initial state).
 M2_LOWPREC = Mamba2Workload("mamba2_lowprec_b64", batch=64, nheads=128, headdim=64,
                             dstate=128, ngroups=8, in_dtype="bf16", init_std=0.0,
