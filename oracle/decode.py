@@ -29,7 +29,7 @@ from typing import Dict, List, Sequence
 
 import numpy as np
 
-from . import gdn, mamba2, quant
+from . import gdn, kda, mamba2, quant
 from .ring import RingModel, R
 
 
@@ -172,11 +172,15 @@ class M2Replay:
 
 
 class GDNConventional:
-    def __init__(self, S0):
+    """Plain decode of a delta-rule layer: rule = gdn (Gated DeltaNet) or kda
+    (Kimi Delta Attention, per-key-channel decay)."""
+
+    def __init__(self, S0, rule=gdn):
         self.S = np.asarray(S0, dtype=np.float64).copy()
+        self.rule = rule
 
     def step(self, tok) -> np.ndarray:
-        self.S, o = gdn.step(self.S, tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])
+        self.S, o = self.rule.step(self.S, tok["q"], tok["k"], tok["v"], tok["g"], tok["beta"])
         return o
 
     def spec_round(self, drafts: Sequence[dict], accepted: np.ndarray) -> np.ndarray:
@@ -185,7 +189,7 @@ class GDNConventional:
         S = self.S
         snaps, os_ = [], []
         for d in drafts:
-            S, o = gdn.step(S, d["q"], d["k"], d["v"], d["g"], d["beta"])
+            S, o = self.rule.step(S, d["q"], d["k"], d["v"], d["g"], d["beta"])
             snaps.append(S)
             os_.append(o)
         for b, k in enumerate(np.asarray(accepted)):
@@ -195,9 +199,11 @@ class GDNConventional:
 
 
 class GDNReplay:
-    """ReplaySSM decode of a Gated DeltaNet layer in fp64 (fp64 checkpoint)."""
+    """ReplaySSM decode of a delta-rule layer in fp64 (fp64 checkpoint); rule = gdn
+    or kda as for GDNConventional."""
 
-    def __init__(self, S0, ring: int = R, max_draft: int = 0):
+    def __init__(self, S0, ring: int = R, max_draft: int = 0, rule=gdn):
+        self.rule = rule
         self.batch = S0.shape[0]
         self.ckpt = np.asarray(S0, dtype=np.float64).copy()
         self.ring = RingModel(self.batch, ring, max_draft)
@@ -218,7 +224,7 @@ class GDNReplay:
                 continue
             for s, d in zip(slots, dr):
                 self.entries[b][s] = d
-            os_ = [gdn.replay_output(self.ckpt[b:b + 1], held + dr[:i + 1], dr[i]["q"]) for i in range(K)]
+            os_ = [self.rule.replay_output(self.ckpt[b:b + 1], held + dr[:i + 1], dr[i]["q"]) for i in range(K)]
             out.append(np.stack(os_))
         return np.concatenate(out, axis=1)
 
@@ -229,7 +235,7 @@ class GDNReplay:
             folded = self.ring.spec_commit(b, int(k))
             if folded:
                 ents = [self.entries[b][s] for s in folded]
-                self.ckpt[b:b + 1] = gdn.replay_fold(self.ckpt[b:b + 1], ents)
+                self.ckpt[b:b + 1] = self.rule.replay_fold(self.ckpt[b:b + 1], ents)
 
     def step(self, tok, force_flush: bool = False) -> np.ndarray:
         outs = []
@@ -240,7 +246,7 @@ class GDNReplay:
                 if self.ring.flush(b) is None:
                     outs.append(np.full((1,) + tb["v"].shape[1:], np.nan))
                     continue
-                Sn = gdn.replay_fold(self.ckpt[b:b + 1], held + [tb])
+                Sn = self.rule.replay_fold(self.ckpt[b:b + 1], held + [tb])
                 o = np.einsum("bhvk,bhk->bhv", Sn, gdn.expand_qk(tb["q"], Sn.shape[1]))
                 self.ckpt[b:b + 1] = Sn
             else:
@@ -249,7 +255,7 @@ class GDNReplay:
                     outs.append(np.full((1,) + tb["v"].shape[1:], np.nan))
                     continue
                 self.entries[b][s] = tb
-                o = gdn.replay_output(self.ckpt[b:b + 1], held + [tb], tb["q"])
+                o = self.rule.replay_output(self.ckpt[b:b + 1], held + [tb], tb["q"])
             outs.append(o)
         return np.concatenate(outs)
 
@@ -258,5 +264,5 @@ class GDNReplay:
         for b in range(self.batch):
             held = [self.entries[b][s] for s in self.ring.committed_slots(b)]
             if held:
-                out[b] = gdn.replay_fold(self.ckpt[b:b + 1], held)[0]
+                out[b] = self.rule.replay_fold(self.ckpt[b:b + 1], held)[0]
         return out

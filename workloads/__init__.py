@@ -115,6 +115,7 @@ class GDNWorkload:
     steps: int
     seed: int
     max_draft: int = 0
+    gate: str = "head"   # "head": one decay per value head (Gated DeltaNet); "channel": per key channel (KDA)
 
     def with_(self, **kw) -> "GDNWorkload":
         return replace(self, **kw)
@@ -137,6 +138,9 @@ M2_SPEC = Mamba2Workload("mamba2_spec_b512", batch=512, nheads=128, headdim=64, 
 # Speculative decode on the Qwen-style GDN shapes: batch 256, 4 drafts per round, 64 rounds.
 GDN_SPEC = GDNWorkload("gdn_qwen_spec_b256", batch=256, n_qk=16, n_v=32, dk=128, dv=128,
                        in_dtype="bf16", init_std=0.1, steps=64, seed=7, max_draft=4)
+# Kimi Delta Attention (per-key-channel decay) on the Qwen-style GDN shapes at batch 256.
+KDA_B256 = GDNWorkload("kda_b256", batch=256, n_qk=16, n_v=32, dk=128, dv=128, in_dtype="bf16",
+                       init_std=0.1, steps=256, seed=8, gate="channel")
 # Low-precision reads on the Nemotron-style shapes at batch 64 (zero initial state).
 M2_LOWPREC = Mamba2Workload("mamba2_lowprec_b64", batch=64, nheads=128, headdim=64,
                             dstate=128, ngroups=8, in_dtype="bf16", init_std=0.0,
@@ -144,6 +148,9 @@ M2_LOWPREC = Mamba2Workload("mamba2_lowprec_b64", batch=64, nheads=128, headdim=
 # Tiny Gated DeltaNet layer for brute-force checks: fp32, zero initial state.
 TINY_GDN = GDNWorkload("tiny_gdn", batch=4, n_qk=2, n_v=4, dk=16, dv=16, in_dtype="f32",
                        init_std=0.0, steps=64, seed=6)
+# Tiny KDA layer for brute-force checks: fp32, zero initial state, per-channel gate.
+TINY_KDA = GDNWorkload("tiny_kda", batch=4, n_qk=2, n_v=4, dk=16, dv=16, in_dtype="f32",
+                       init_std=0.0, steps=64, seed=9, gate="channel")
 
 
 def _as_in(x: np.ndarray, in_dtype: str) -> np.ndarray:
@@ -232,7 +239,7 @@ def gdn_token(w: GDNWorkload, t: int, b: int, params: Dict[str, np.ndarray] | No
     """Inputs (q, k, v, g, beta) of sequence b at step t.
 
     q, k: [n_qk, dk] (in_dtype values); v: [n_v, dv] (in_dtype values);
-    g, beta: [n_v] fp32.
+    g: [n_v] fp32, or [n_v, dk] for a per-channel gate; beta: [n_v] fp32.
     """
     if params is None:
         params = gdn_params(w)
@@ -241,7 +248,10 @@ def gdn_token(w: GDNWorkload, t: int, b: int, params: Dict[str, np.ndarray] | No
     k = _l2n(gen.standard_normal((w.n_qk, w.dk)))
     v = gen.standard_normal((w.n_v, w.dv))
     beta = _sigmoid(gen.standard_normal(w.n_v))
-    gate = -np.exp(params["a"].astype(np.float64)) * _softplus(gen.standard_normal(w.n_v))
+    if w.gate == "channel":
+        gate = -np.exp(params["a"].astype(np.float64))[:, None] * _softplus(gen.standard_normal((w.n_v, w.dk)))
+    else:
+        gate = -np.exp(params["a"].astype(np.float64)) * _softplus(gen.standard_normal(w.n_v))
     return {"q": _as_in(q, w.in_dtype), "k": _as_in(k, w.in_dtype), "v": _as_in(v, w.in_dtype),
             "g": gate.astype(np.float32), "beta": beta.astype(np.float32)}
 
