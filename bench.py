@@ -81,12 +81,14 @@ def m2_bytes(w: W.Mamba2Workload, ckpt_bytes_per_elem: float = 4.0, read_bytes_p
 def gdn_bytes(w: W.GDNWorkload):
     """Per-sequence bytes of each Gated DeltaNet step. A held entry is re-read
     as its k, its decay g and its solved row u (fp32); each non-flush step
-    appends the record (q, k, v, g, beta) and the new entry's u."""
+    appends the record (q, k, v, g, beta) and the new entry's u. A per-channel
+    gate (Kimi Delta Attention) is dk floats per value head instead of one."""
     s_in = 2 if w.in_dtype == "bf16" else 4
+    gw = w.dk if w.gate == "channel" else 1
     S = w.n_v * w.dv * w.dk * 4
-    E_in = 2 * w.n_qk * w.dk * s_in + w.n_v * w.dv * s_in + 2 * w.n_v * 4   # q, k, v, g, beta
+    E_in = 2 * w.n_qk * w.dk * s_in + w.n_v * w.dv * s_in + w.n_v * gw * 4 + w.n_v * 4   # q, k, v, g, beta
     Urow = w.n_v * w.dv * 4
-    E_old = w.n_qk * w.dk * s_in + Urow + w.n_v * 4                          # k, u, g of a held entry
+    E_old = w.n_qk * w.dk * s_in + Urow + w.n_v * gw * 4                    # k, u, g of a held entry
     O = w.n_v * w.dv * 4
     nonflush = {j: S + (j - 1) * E_old + 2 * E_in + Urow + O for j in range(1, RING)}
     flush = 2 * S + (RING - 1) * E_old + E_in + O
@@ -347,15 +349,17 @@ def bench_sweep(args, torch, rs):
             "rows": rows}
 
 
-def bench_gdn(args, torch, rs):
-    w = W.GDN_QWEN
+def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
+    """A delta-rule layer (Gated DeltaNet, or Kimi Delta Attention for a per-channel
+    gate) at batch 256: ReplaySSM windows vs the conventional kernel."""
     dev = "cuda"
     B = w.batch
     gp = W.gdn_params(w)
+    kda_layer = w.gate == "channel"
 
     def mk(mode):
-        cfg = rs.make_config(rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk, n_v_heads=w.n_v, head_k_dim=w.dk,
-                             head_v_dim=w.dv, in_dtype=rs.RS_BF16)
+        cfg = rs.make_config(rs.RS_KDA if kda_layer else rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk,
+                             n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv, in_dtype=rs.RS_BF16)
         _, layer = rs.rs_init(cfg)
         return layer, rs.alloc_buffers(layer, dev)
 
@@ -398,7 +402,7 @@ def bench_gdn(args, torch, rs):
     value = ntok / (total_r * 1e-3)
     conv_value = ntok / (total_c * 1e-3)
     return {
-        "metric": "GDN-layer decode tokens/s at batch 256 + achieved HBM GB/s vs conventional",
+        "metric": ("KDA" if kda_layer else "GDN") + "-layer decode tokens/s at batch 256 + achieved HBM GB/s vs conventional",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm, "ms_per_step": total_r / K,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_qk": w.n_qk, "n_v": w.n_v, "dk": w.dk, "dv": w.dv,
@@ -660,7 +664,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--workload", action="append", choices=["mamba2", "gdn", "spec", "gdn_spec", "lowprec", "copy", "sweep"],
+    ap.add_argument("--workload", action="append",
+                    choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "lowprec", "copy", "sweep"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
@@ -679,6 +684,7 @@ def main():
     for wl in (args.workload or ["mamba2"]):
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
               "sweep": bench_sweep, "gdn_spec": bench_gdn_spec,
+              "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
         if wl == "mamba2":

@@ -76,6 +76,13 @@
  *               g (= log alpha) and beta: float [batch][Hv]; drafts stack K
  *               tokens in front: [K][batch][...].
  *   output      o: float [batch][Hv][dv]; for drafts [K][batch][Hv][dv].
+ * Kimi Delta Attention (RS_KDA; Kimi Linear, Moonshot AI 2025; named as an SSM
+ *   layer type on the news.hamidun.com ReplaySSM page, "Why hybrid models
+ *   became the norm"): S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T)
+ *   + beta_t v_t k_t^T, o_t = S_t q_t, with alpha_t = exp(g_t) a vector over
+ *   the dk key channels. Everything as for Gated DeltaNet except g: float
+ *   [batch][Hv][dk] per token, and the ring's g float [batch][Hv][R][dk].
+ *   Speculative calls are Gated DeltaNet / Mamba-2 only (max_draft must be 0).
  * NVFP4 block (read copy, or the uniform NVFP4 checkpoint), for the stored
  *   matrices M[b][h] of rows x cols (rows = N or dk, cols = P or dv):
  *     codes   uint8 [batch][heads][rows][cols/2]: two E2M1 codes per byte,
@@ -116,6 +123,7 @@ typedef int32_t rs_status;
 /* layer kinds */
 #define RS_MAMBA2 1
 #define RS_GDN 2
+#define RS_KDA 3   /* Kimi Delta Attention: the Gated DeltaNet layout, gate per key channel */
 
 /* modes */
 #define RS_REPLAY 0          /* checkpoint + ring (ReplaySSM) */
@@ -136,7 +144,7 @@ typedef int32_t rs_status;
 #define RS_ERR_PENDING 8     /* plain step while drafts are pending */
 
 typedef struct rs_config {
-  int32_t kind;          /* RS_MAMBA2 | RS_GDN */
+  int32_t kind;          /* RS_MAMBA2 | RS_GDN | RS_KDA */
   int32_t mode;          /* RS_REPLAY | RS_CONVENTIONAL */
   int32_t batch;         /* sequences, >= 1 */
   int32_t nheads, headdim, dstate, ngroups;              /* Mamba-2 */

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librs.so")
 
 # status codes, kinds, modes, dtypes, device error bits (include/rs.h)
 RS_OK, RS_E_ARG, RS_E_DTYPE, RS_E_ALIGN, RS_E_MODE, RS_E_LAUNCH, RS_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
-RS_MAMBA2, RS_GDN = 1, 2
+RS_MAMBA2, RS_GDN, RS_KDA = 1, 2, 3
 RS_REPLAY, RS_CONVENTIONAL = 0, 1
 RS_NONE, RS_F32, RS_BF16, RS_F16, RS_FP8E4M3, RS_NVFP4 = 0, 1, 2, 3, 4, 5
 RS_ERR_FULL, RS_ERR_OVERFLOW, RS_ERR_COMMIT, RS_ERR_PENDING = 1, 2, 4, 8
@@ -240,7 +240,8 @@ def ckpt_f32_view(layer: RsLayer, bufs: Buffers):
 
 def ring_view(layer: RsLayer, bufs: Buffers, name: str):
     """One ring array as a typed tensor: Mamba-2 x [b,H,16,P], B/C [b,G,16,N], dt [b,H,16];
-    GDN q/k [b,Hk,16,dk], v [b,Hv,16,dv], g/beta [b,Hv,16], u [b,Hv,16,dv] (fp32)."""
+    GDN q/k [b,Hk,16,dk], v [b,Hv,16,dv], g/beta [b,Hv,16], u [b,Hv,16,dv] (fp32);
+    KDA as GDN with g [b,Hv,16,dk]."""
     import torch
     c = layer.cfg
     b = c.batch
@@ -253,6 +254,8 @@ def ring_view(layer: RsLayer, bufs: Buffers, name: str):
         shapes = {"q": (b, c.n_qk_heads, 16, c.head_k_dim), "k": (b, c.n_qk_heads, 16, c.head_k_dim),
                   "v": (b, c.n_v_heads, 16, c.head_v_dim), "g": (b, c.n_v_heads, 16),
                   "beta": (b, c.n_v_heads, 16), "u": (b, c.n_v_heads, 16, c.head_v_dim)}
+        if c.kind == RS_KDA:
+            shapes["g"] = (b, c.n_v_heads, 16, c.head_k_dim)
     shp = shapes[name]
     dt, sz = (torch.float32, 4) if name in ("g", "beta", "u") else (edt, esz)
     off = getattr(layer, f"ring_{name}_off")

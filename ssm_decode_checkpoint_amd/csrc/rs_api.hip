@@ -222,6 +222,7 @@ GDNLaunch gdn_launch_cfg(const rs_layer* L) {
   l.dk = c.head_k_dim;
   l.dv = c.head_v_dim;
   l.in_bf16 = c.in_dtype == RS_BF16;
+  l.vg = c.kind == RS_KDA;
   l.grid = c.batch * c.n_v_heads;
   return l;
 }
@@ -233,7 +234,7 @@ extern "C" {
 rs_status rs_init(const rs_config* cfg, rs_layer* out) {
   if (!cfg || !out) return RS_E_ARG;
   const rs_config c = *cfg;
-  if (c.kind != RS_MAMBA2 && c.kind != RS_GDN) return RS_E_ARG;
+  if (c.kind != RS_MAMBA2 && c.kind != RS_GDN && c.kind != RS_KDA) return RS_E_ARG;
   if (c.mode != RS_REPLAY && c.mode != RS_CONVENTIONAL) return RS_E_MODE;
   if (c.batch < 1 || c.batch > (1 << 20)) return RS_E_ARG;
   if (c.ring != kRing) return RS_E_ARG;
@@ -266,6 +267,7 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
     if (static_cast<uint64_t>(c.batch) * c.n_v_heads > (1u << 30)) return RS_E_ARG;
     if (!gdn_shape_supported(c.head_k_dim, c.head_v_dim)) return RS_E_UNSUPPORTED;
     if (c.ckpt_dtype != RS_F32 || c.read_copy != RS_NONE) return RS_E_DTYPE;
+    if (c.kind == RS_KDA && c.max_draft != 0) return RS_E_MODE;
     L.heads = c.n_v_heads;
     L.in_heads = c.n_qk_heads;
     L.rows = c.head_k_dim;
@@ -289,7 +291,8 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
       L.ring_q_off = off; off = align_up(off + B * c.n_qk_heads * kRing * c.head_k_dim * sin);
       L.ring_k_off = off; off = align_up(off + B * c.n_qk_heads * kRing * c.head_k_dim * sin);
       L.ring_v_off = off; off = align_up(off + B * c.n_v_heads * kRing * c.head_v_dim * sin);
-      L.ring_g_off = off; off = align_up(off + B * c.n_v_heads * kRing * 4);
+      const uint64_t gw = c.kind == RS_KDA ? static_cast<uint64_t>(c.head_k_dim) : 1;   // gate width
+      L.ring_g_off = off; off = align_up(off + B * c.n_v_heads * kRing * gw * 4);
       L.ring_beta_off = off; off = align_up(off + B * c.n_v_heads * kRing * 4);
       L.ring_u_off = off; off = align_up(off + B * c.n_v_heads * kRing * c.head_v_dim * 4);
     }
@@ -317,7 +320,7 @@ rs_status rs_step_conventional(const rs_layer* L, const rs_buffers* buf, const r
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (L->cfg.kind == RS_GDN) {
+  if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(GDNOp::Conv, a, gdn_launch_cfg(L), st);
@@ -339,7 +342,7 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (L->cfg.kind == RS_GDN) {
+  if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(flush ? GDNOp::Flush : GDNOp::NonFlush, a, gdn_launch_cfg(L), st);
@@ -371,7 +374,7 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
   if (K < 1 || K > L->cfg.max_draft) return RS_E_ARG;
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
-  if (L->cfg.kind == RS_GDN) {
+  if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, drafts, y, &a)) return s;
     a.K = K;
@@ -409,7 +412,7 @@ rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t
   if (!accepted) return RS_E_ARG;
   if (!aligned16(accepted)) return RS_E_ALIGN;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (L->cfg.kind == RS_GDN) {
+  if (L->cfg.kind != RS_MAMBA2) {
     if (!buf || !buf->ckpt) return RS_E_ARG;
     if (L->cfg.mode == RS_REPLAY && (!buf->ring || !buf->meta)) return RS_E_ARG;
     if (!aligned16(buf->ckpt)) return RS_E_ALIGN;

@@ -39,20 +39,31 @@ namespace {
 template <int NV>
 constexpr int gdn_slices() { return NV >= 128 ? 2 : 1; }
 
-template <int NK, int NVS>
+// VG: Kimi Delta Attention, the decay is a vector over the dk key channels
+// (a per-channel gate) instead of one scalar per head.
+template <int NK, int NVS, bool VG = false>
 struct GSmem {
+  static constexpr int kNK = NK;
+  static constexpr int kNVS = NVS;
+  static constexpr bool kVG = VG;
   float K[kRing][NK];    // k of entries 0..m-1
   float W[4][NK];        // matvec weights: k_cur, q, 0, 0
   float U[kRing][NVS];   // u of entries 0..m-1 (the current one computed here), own columns
   float vc[NVS];         // v of the current token, own columns
   float out[4][NVS];     // S0 k_cur, S0 q
-  float red[4 * 4 * NVS];
+  float red[VG ? 1 : 4 * 4 * NVS];   // matvec scratch (VG: lives in A, dead by then)
   float kk[kRing];       // beta_cur r_{cur,i} (k_cur . k_i), i < cur
   float kq[kRing];       // r_{cur,i} (k_i . q), i <= cur
   float rr[kRing];       // r_{cur,i}
   float al[kRing];
   float gam, bet;
   float s4[4];
+  // VG: per-channel log decays of entries 0..m-1, then in place the products
+  // r_{cur,e} = prod_{e<l<=cur} alpha_l; gv = gamma_cur per channel
+  float A[VG ? kRing : 1][NK];
+  float gv[VG ? NK : 1];
+  static_assert(!VG || 4 * 4 * NVS <= kRing * NK, "matvec scratch fits in the decay table");
+  __device__ __forceinline__ float* redp() { if constexpr (VG) return &A[0][0]; else return red; }
 };
 
 struct GPtrs {
@@ -122,7 +133,7 @@ struct GSlice {
 // weights [k_cur, q, 0, 0]. Loads go to registers first (load), so the caller
 // can issue the state tile after them and still have the records while the
 // tile streams in (vector loads return in order); store moves them to LDS.
-template <typename TIN, int NK, int NV, int NVS>
+template <typename TIN, int NK, int NV, int NVS, bool VG = false>
 struct GStage {
   static constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
   static_assert(NK % VK == 0 && NVS % VK == 0 && NVS % 4 == 0, "records are whole 16-byte chunks");
@@ -130,10 +141,12 @@ struct GStage {
   static constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
   static constexpr int CQ = (NK / VK + kThreads - 1) / kThreads;
   static constexpr int CV = (NVS / VK + kThreads - 1) / kThreads;
+  static constexpr int CG = VG ? (kRing * NK / 4 + kThreads - 1) / kThreads : 1;
   RegChunks<TIN, CK> k;
   RegChunks<float, CU> u;
   RegChunks<TIN, CQ> q, kc;
   RegChunks<TIN, CV> v;
+  RegChunks<float, CG> gr;   // VG: per-channel gate rows of entries 0..m-1
   float g, beta;
 
   __device__ __forceinline__ void load(const GDNArgs& a, const GPtrs& p, long long nck, int m) {
@@ -152,11 +165,17 @@ struct GStage {
     q.load(EntrySrc<TIN>{iq, iq, 0, 0, 0, NK}, 1, NK);
     kc.load(EntrySrc<TIN>{ik, ik, 0, 0, 0, NK}, 1, NK);
     v.load(EntrySrc<TIN>{iv, iv, 0, 0, 0, NVS}, 1, NVS);
-    const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
-    g = *(e < held ? rg + slot_of(nck, e) : a.g + p.st);
+    if constexpr (VG) {
+      const float* rgv = static_cast<const float*>(a.rg) + p.st * kRing * NK;
+      gr.load(EntrySrc<float>{rgv, a.g + p.st * NK, 0, nck, held, NK}, m, NK);
+      g = 0.0f;
+    } else {
+      const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+      g = *(e < held ? rg + slot_of(nck, e) : a.g + p.st);
+    }
     beta = a.beta[p.st];
   }
-  __device__ __forceinline__ void store(GSmem<NK, NVS>& s, int m) const {
+  __device__ __forceinline__ void store(GSmem<NK, NVS, VG>& s, int m) const {
     const int held = m - 1;
     k.to_lds(&s.K[0][0], NK, m, NK);
     u.to_lds(&s.U[0][0], NVS, held, NVS);
@@ -167,29 +186,66 @@ struct GStage {
       s.W[2][n] = 0.0f;
       s.W[3][n] = 0.0f;
     }
-    if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(g);
+    if constexpr (VG) gr.to_lds(&s.A[0][0], NK, m, NK);
+    else if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(g);
     if (threadIdx.x == 0) s.bet = beta;
   }
 };
 
+// VG only, after staging is visible: per key channel c, the decay products
+// r_{cur,e}[c] = prod_{e<l<=cur} alpha_l[c] replace the staged log decays (the
+// same descending order as the definition's direct products), gamma_cur[c] goes
+// to gv, and the matvec weights become gamma * k_cur and gamma * q (the plain q
+// is kept in W[2] for the dots). The scalar gamma of the common code is 1.
+template <typename SM>
+__device__ __forceinline__ void kda_decays(SM& s, int m) {
+  const int cur = m - 1;
+  for (int c = threadIdx.x; c < SM::kNK; c += kThreads) {
+    float acc = 1.0f;
+#pragma unroll
+    for (int e = kRing - 1; e >= 0; --e) {
+      if (e <= cur) {
+        const float al = expf(s.A[e][c]);
+        s.A[e][c] = acc;
+        acc *= al;
+      }
+    }
+    s.gv[c] = acc;
+    const float qv = s.W[1][c];
+    s.W[2][c] = qv;
+    s.W[0][c] *= acc;
+    s.W[1][c] = qv * acc;
+  }
+  if (threadIdx.x == 0) s.gam = 1.0f;
+}
+
 // Dots and decays for the current entry cur = m-1 (after staging is visible):
 //   kk[i] = beta_cur r_{cur,i} (k_cur . k_i) for i < cur
 //   kq[i] = r_{cur,i} (k_i . q) for i <= cur;  rr[i] = r_{cur,i};  gam = gamma_cur
-template <int NK, int NVS>
-__device__ __forceinline__ void gdn_dots(GSmem<NK, NVS>& s, int m) {
+// VG: the decays are per channel and weight the dots instead (r = 1):
+//   kk[i] = beta_cur <k_cur, r_{cur,i} * k_i>,  kq[i] = <q, r_{cur,i} * k_i>
+template <typename SM>
+__device__ __forceinline__ void gdn_dots(SM& s, int m) {
+  constexpr int NK = SM::kNK;
   const int cur = m - 1;
   const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
   for (int pr = grp; pr < 2 * m - 1; pr += kThreads / 16) {
     const bool isq = pr >= cur;
     const int i = isq ? pr - cur : pr;
-    const float* other = isq ? &s.W[1][0] : &s.K[cur][0];
+    const float* other = isq ? &s.W[SM::kVG ? 2 : 1][0] : &s.K[cur][0];
     float part = 0.0f;
-    for (int n = ln; n < NK; n += 16) part += s.K[i][n] * other[n];
+    if constexpr (SM::kVG) {
+      for (int n = ln; n < NK; n += 16) part += s.K[i][n] * s.A[i][n] * other[n];
+    } else {
+      for (int n = ln; n < NK; n += 16) part += s.K[i][n] * other[n];
+    }
     part = group_sum16(part);
     if (ln == 0) {
       float r = 1.0f;
+      if constexpr (!SM::kVG) {
 #pragma unroll
-      for (int l = 1; l < kRing; ++l) r *= (l > i && l <= cur) ? s.al[l] : 1.0f;
+        for (int l = 1; l < kRing; ++l) r *= (l > i && l <= cur) ? s.al[l] : 1.0f;
+      }
       if (isq) {
         s.kq[i] = r * part;
         s.rr[i] = r;
@@ -198,18 +254,20 @@ __device__ __forceinline__ void gdn_dots(GSmem<NK, NVS>& s, int m) {
       }
     }
   }
-  if (threadIdx.x == 0) {
-    float gm = 1.0f;
+  if constexpr (!SM::kVG) {
+    if (threadIdx.x == 0) {
+      float gm = 1.0f;
 #pragma unroll
-    for (int e = 0; e < kRing; ++e) gm *= e <= cur ? s.al[e] : 1.0f;
-    s.gam = gm;
+      for (int e = 0; e < kRing; ++e) gm *= e <= cur ? s.al[e] : 1.0f;
+      s.gam = gm;
+    }
   }
 }
 
 // u_cur[v] = beta (v_cur - gamma S0 k_cur) - sum_{i<cur} kk[i] u_i, stored in U[cur];
 // returns o[v] = gamma S0 q + sum_{i<=cur} kq[i] u_i for the thread's column v.
-template <int NK, int NVS>
-__device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NVS>& s, int m, int v) {
+template <typename SM>
+__device__ __forceinline__ float gdn_row_and_output(SM& s, int m, int v) {
   const int cur = m - 1;
   float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]);
   // fixed-length loops with selects: every LDS load is unconditional and in
@@ -223,12 +281,25 @@ __device__ __forceinline__ float gdn_row_and_output(GSmem<NK, NVS>& s, int m, in
   return o;
 }
 
+// S <- S Diag(f) for a [dk][dv] tile: row r (key channel r) times f[r].
+template <int NK, int NVS>
+__device__ __forceinline__ void tile_scale_rows(RegTile<4, NK, NVS>& S, const float* f) {
+#pragma unroll
+  for (int k = 0; k < RegTile<4, NK, NVS>::P; ++k) {
+    const int row = RegTile<4, NK, NVS>::row(k);
+    const float x = f[row < NK ? row : NK - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S.v[k][i] *= x;
+  }
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------------------
-// conventional step (baseline)
+// conventional step (baseline). VG (KDA): S <- S Diag(alpha) first, then the
+// delta update with no further decay.
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV>
+template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
   constexpr int NVS = NV;   // whole state per workgroup (measured faster for read + write)
   __shared__ GSmem<NK, NVS> s;
@@ -243,7 +314,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
   for (int i = threadIdx.x; i < NK; i += kThreads) {
     s.W[0][i] = to_f(ik[i]);
     s.W[1][i] = to_f(iq[i]);
-    s.W[2][i] = 0.0f;
+    s.W[2][i] = VG ? expf(a.g[p.st * NK + i]) : 0.0f;   // VG: the channel decays
     s.W[3][i] = 0.0f;
   }
   for (int i = threadIdx.x; i < NVS; i += kThreads) s.vc[i] = to_f(iv[i]);
@@ -255,10 +326,11 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
     part = group_sum16(part);
     if (threadIdx.x == 0) s.kq[0] = part;
   }
-  const float alpha = expf(a.g[p.st]);
+  const float alpha = VG ? 1.0f : expf(a.g[p.st]);
   const float beta = a.beta[p.st];
   RegTile<4, NK, NVS> S;
   raw.decode(S);
+  if constexpr (VG) tile_scale_rows(S, &s.W[2][0]);
   tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // out[0] = S k, out[1] = S q
   for (int v = threadIdx.x; v < NVS; v += kThreads) s.U[0][v] = beta * (s.vc[v] - alpha * s.out[0][v]);
   __syncthreads();
@@ -272,10 +344,10 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 // non-flush step: o from checkpoint + buffer, append (with its u row), no state write
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV>
+template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   constexpr int NVS = NV / gdn_slices<NV>();
-  __shared__ GSmem<NK, NVS> s;
+  __shared__ GSmem<NK, NVS, VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * gdn_slices<NV>() + p.half;
@@ -288,17 +360,22 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
     arr.arrive(actr, wg, nck, len, nd);
   } else {
     const int j = len + 1;
-    GStage<TIN, NK, NV, NVS> stg;
+    GStage<TIN, NK, NV, NVS, VG> stg;
     stg.load(a, p, nck, j);            // records first, then the state tile
     GSlice<NK, NV, NVS> raw;
     raw.issue(static_cast<const float*>(a.ck.data), p.st, p.c0);
     arr.arrive(actr, wg, nck, len, nd);
     stg.store(s, j);
     __syncthreads();
+    if constexpr (VG) {
+      kda_decays(s, j);
+      __syncthreads();
+    }
     gdn_dots(s, j);
+    if constexpr (VG) __syncthreads();   // dots done: the decay table becomes matvec scratch
     RegTile<4, NK, NVS> S;
     raw.decode(S);
-    tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);   // barriers inside publish the dots
+    tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);   // barriers inside publish the dots
     const int slot = slot_of(nck, len);
     float* ru = static_cast<float*>(a.ru) + (p.st * kRing + slot) * NV + p.c0;
     for (int v = threadIdx.x; v < NVS; v += kThreads) {
@@ -310,10 +387,13 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
     const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
     for (int v = threadIdx.x; v < NVS; v += kThreads) rv[v] = iv[v];
     if (p.half == 0) {
-      if (threadIdx.x == 0) {
+      if constexpr (VG) {
+        float* rgv = static_cast<float*>(a.rg) + (p.st * kRing + slot) * NK;
+        for (int n = threadIdx.x; n < NK; n += kThreads) rgv[n] = a.g[p.st * NK + n];
+      } else if (threadIdx.x == 0) {
         static_cast<float*>(a.rg)[p.st * kRing + slot] = a.g[p.st];
-        static_cast<float*>(a.rbeta)[p.st * kRing + slot] = a.beta[p.st];
       }
+      if (threadIdx.x == 0) static_cast<float*>(a.rbeta)[p.st * kRing + slot] = a.beta[p.st];
       if (p.h % a.vpk == 0) {
         const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
         TIN* rk = static_cast<TIN*>(a.rk) + bk * kRing * NK;
@@ -333,10 +413,10 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 // flush step: fold the len held entries and the current token, write once, o
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV>
+template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
   constexpr int NVS = NV / gdn_slices<NV>();
-  __shared__ GSmem<NK, NVS> s;
+  __shared__ GSmem<NK, NVS, VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * gdn_slices<NV>() + p.half;
@@ -350,26 +430,48 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
     arr.arrive(actr, wg, nck, len, nd);
   } else {
     float* ck = static_cast<float*>(a.ck.data);
-    GStage<TIN, NK, NV, NVS> stg;
+    GStage<TIN, NK, NV, NVS, VG> stg;
     stg.load(a, p, nck, m);            // records first, then the state tile
     GSlice<NK, NV, NVS> raw;
     raw.issue(ck, p.st, p.c0);
     arr.arrive(actr, wg, nck, len, nd);
     stg.store(s, m);
     __syncthreads();
+    if constexpr (VG) {
+      kda_decays(s, m);
+      __syncthreads();
+    }
     gdn_dots(s, m);
+    if constexpr (VG) {
+      // the fold's decayed k rows r_{m,i} * k_i, made now so that the decay table
+      // can serve as matvec scratch
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) {
+        const int i = idx / NK, c = idx - i * NK;
+        s.K[i][c] *= s.A[i][c];
+      }
+      __syncthreads();
+    }
     RegTile<4, NK, NVS> S;
     raw.decode(S);
-    tile_matvec<2>(S, &s.W[0][0], NK, s.red, &s.out[0][0]);
+    tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
     for (int v = threadIdx.x; v < NVS; v += kThreads) {
       a.o[p.st * NV + p.c0 + v] = gdn_row_and_output(s, m, v);
-      // fold columns r_{cur,i} u_i (same thread, same column v)
+      if constexpr (!VG) {
+        // fold columns r_{cur,i} u_i (same thread, same column v)
 #pragma unroll
-      for (int i = 0; i < kRing; ++i)
-        if (i < m) s.U[i][v] *= s.rr[i];
+        for (int i = 0; i < kRing; ++i)
+          if (i < m) s.U[i][v] *= s.rr[i];
+      }
     }
     __syncthreads();
-    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    if constexpr (VG) {
+      // S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T (k rows decayed above)
+      tile_scale_rows(S, s.gv);
+      tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    } else {
+      tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    }
     GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
   }
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
@@ -735,6 +837,22 @@ __global__ __launch_bounds__(kThreads) void gdn_restore_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
+template <int NK, int NV, bool VG>
+struct gdn_step_kernels {
+  static void conv(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
+    if (bf) gdn_conv_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    else gdn_conv_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+  }
+  static void nonflush(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
+    if (bf) gdn_nonflush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    else gdn_nonflush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+  }
+  static void flush(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
+    if (bf) gdn_flush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    else gdn_flush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+  }
+};
+
 template <typename TIN, int NK, int NV>
 void gdn_spec_append(const GDNArgs& a, int grid, hipStream_t st) {
   if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2><<<grid, kThreads, 0, st>>>(a);
@@ -757,16 +875,16 @@ void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
     l.grid *= gdn_slices<NV>();
   switch (op) {
     case GDNOp::Conv:
-      if (bf) gdn_conv_kernel<bf16, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
-      else gdn_conv_kernel<float, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
+      if (l.vg) gdn_step_kernels<NK, NV, true>::conv(bf, a, l.grid, st);
+      else gdn_step_kernels<NK, NV, false>::conv(bf, a, l.grid, st);
       break;
     case GDNOp::NonFlush:
-      if (bf) gdn_nonflush_kernel<bf16, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
-      else gdn_nonflush_kernel<float, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
+      if (l.vg) gdn_step_kernels<NK, NV, true>::nonflush(bf, a, l.grid, st);
+      else gdn_step_kernels<NK, NV, false>::nonflush(bf, a, l.grid, st);
       break;
     case GDNOp::Flush:
-      if (bf) gdn_flush_kernel<bf16, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
-      else gdn_flush_kernel<float, NK, NV><<<l.grid, kThreads, 0, st>>>(a);
+      if (l.vg) gdn_step_kernels<NK, NV, true>::flush(bf, a, l.grid, st);
+      else gdn_step_kernels<NK, NV, false>::flush(bf, a, l.grid, st);
       break;
     case GDNOp::SpecAppend:
       if (bf) gdn_spec_append<bf16, NK, NV>(a, l.grid, st);

@@ -157,6 +157,7 @@ enum class GDNOp { Conv, NonFlush, Flush, SpecAppend, CommitFold, ConvSpec, Rest
 struct GDNLaunch {
   int dk, dv;
   bool in_bf16;
+  bool vg;        // Kimi Delta Attention: per-key-channel gate
   int grid;
 };
 

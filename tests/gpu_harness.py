@@ -71,7 +71,9 @@ def m2_layer(w: W.Mamba2Workload, mode=rs.RS_REPLAY, ckpt_dtype=rs.RS_F32, read_
 
 
 def gdn_layer(w: W.GDNWorkload, mode=rs.RS_REPLAY, batch=None, max_draft=None):
-    cfg = rs.make_config(rs.RS_GDN, w.batch if batch is None else batch, mode=mode, n_qk_heads=w.n_qk,
+    """A Gated DeltaNet layer, or a Kimi Delta Attention layer for a per-channel gate."""
+    kind = rs.RS_KDA if w.gate == "channel" else rs.RS_GDN
+    cfg = rs.make_config(kind, w.batch if batch is None else batch, mode=mode, n_qk_heads=w.n_qk,
                          n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv,
                          max_draft=w.max_draft if max_draft is None else max_draft,
                          in_dtype=rs.RS_BF16 if w.in_dtype == "bf16" else rs.RS_F32)
