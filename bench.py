@@ -349,6 +349,48 @@ def bench_sweep(args, torch, rs):
             "rows": rows}
 
 
+def bench_serve(args, torch, rs):
+    """Continuous-batching schedule on the Nemotron-style Mamba-2 layer at batch
+    256: slots are reused at staggered times (rs_reset_slots) so that the buffer
+    fills differ, then every step is one self-scheduling call (rs_step) in which
+    the sequences whose buffers are full (1/16 of them) flush and the others take
+    a non-flush step. Reports throughput and the per-step time spread, beside the
+    lockstep schedule (15 non-flush calls, then one flush call for everyone)."""
+    w = W.M2_NEMOTRON
+    dev = "cuda"
+    B = w.batch
+    p = W.m2_params(w)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    layer, bufs = _m2_layer(rs, w, B, rs.RS_REPLAY, dev)
+    _m2_load_init(torch, rs, w, layer, bufs, dev)
+    pool = _m2_pool(torch, w, B, dev)
+    y = torch.empty(B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    groups = [torch.tensor([b for b in range(B) if b % RING == t], dtype=torch.int32, device=dev) for t in range(RING)]
+    for t in range(RING):                      # stagger: group t starts t steps later
+        rs.rs_reset_slots(layer, bufs, groups[t], len(groups[t]))
+        rs.rs_step(layer, bufs, pool[t], A, D, y)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+
+    def window(ev):
+        for t in range(RING):
+            _marked(ev, t, tm.stream, lambda: rs.rs_step(layer, bufs, pool[t], A, D, y))
+
+    total, per = tm.run(window, args.steps, args.warmup, RING)
+    ntok = B * RING * args.steps
+    steps_ms = per.reshape(-1)
+    return {"metric": "continuous-batching decode tokens/s at batch 256, staggered fills (self-scheduling step)",
+            "value": ntok / (total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": total / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "mamba2_nemotron_b256_staggered", "batch": B, "nheads": w.nheads,
+                       "headdim": w.headdim, "dstate": w.dstate, "fills": "sequence b at fill (15 - b mod 16) "
+                       "after the staggering phase", "step": "16 self-scheduling steps per timed window"},
+            "step_ms": {"mean": float(steps_ms.mean()), "max": float(steps_ms.max()), "min": float(steps_ms.min()),
+                        "p99": float(np.percentile(steps_ms, 99))}}
+
+
 def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
     """A delta-rule layer (Gated DeltaNet, or Kimi Delta Attention for a per-channel
     gate) at batch 256: ReplaySSM windows vs the conventional kernel."""
@@ -665,7 +707,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--workload", action="append",
-                    choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "lowprec", "copy", "sweep"],
+                    choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "lowprec", "copy", "sweep", "serve"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
@@ -683,7 +725,7 @@ def main():
     torch.cuda.set_device(0)
     for wl in (args.workload or ["mamba2"]):
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
-              "sweep": bench_sweep, "gdn_spec": bench_gdn_spec,
+              "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve,
               "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)

@@ -230,6 +230,25 @@ rs_status rs_step_nonflush(const rs_layer* L, const rs_buffers* buf, const rs_in
 rs_status rs_step_flush(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in,
                         const rs_params* prm, float* y, void* stream);
 
+/* Self-scheduling step (continuous batching; the flush rule of sitech.ge,
+ * "How ReplaySSM works", applied per sequence): in one launch, a sequence
+ * whose buffer is full (len == 15) takes the flush step and every other
+ * sequence the non-flush step, so sequences at different fills share a batch
+ * and a lockstep batch's flush work is spread over steps once fills differ.
+ * Same arguments, outputs and device errors as the two calls above. Replay
+ * mode. */
+rs_status rs_step(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in,
+                  const rs_params* prm, float* y, void* stream);
+
+/* Reuse sequence slots (continuous batching): clears the counters of the
+ * listed sequences (n_ckpt = len = nd = 0, error bits cleared), so each starts
+ * with an empty buffer; the sequences' checkpoint rows then hold whatever the
+ * caller writes there as the new initial state (call rs_requant_read_copy
+ * afterwards if a read copy is configured). seqs: device int32[count]; entries
+ * outside [0, batch) are skipped; count == 0 launches nothing. Replay mode. */
+rs_status rs_reset_slots(const rs_layer* L, const rs_buffers* buf, const int32_t* seqs, int32_t count,
+                         void* stream);
+
 /* Speculative append (same page, "Reducing state traffic and simplifying
  * rollback": draft inputs enter the buffer until verification; verification
  * reads outputs only, as a small matrix product, without forming

@@ -335,8 +335,10 @@ rs_status rs_step_conventional(const rs_layer* L, const rs_buffers* buf, const r
   return launched();
 }
 
+enum class StepKind { NonFlush, Flush, Auto };
+
 static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in, const rs_params* prm,
-                             float* y, void* stream, bool flush) {
+                             float* y, void* stream, StepKind kind) {
   if (rs_status s = check_layer(L)) return s;
   if (L->cfg.mode != RS_REPLAY) return RS_E_MODE;
   if (!y) return RS_E_ARG;
@@ -345,7 +347,8 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
-    gdn_launch(flush ? GDNOp::Flush : GDNOp::NonFlush, a, gdn_launch_cfg(L), st);
+    gdn_launch(kind == StepKind::Flush ? GDNOp::Flush : kind == StepKind::Auto ? GDNOp::Auto : GDNOp::NonFlush, a,
+               gdn_launch_cfg(L), st);
     return launched();
   }
   M2Args a;
@@ -353,18 +356,33 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (rs_status s = m2_args(L, buf, &a, &l)) return s;
   if (rs_status s = m2_inputs(in, prm, &a)) return s;
   a.y = y;
-  m2_launch(flush ? M2Op::Flush : M2Op::NonFlush, a, l, st);
+  m2_launch(kind == StepKind::Flush ? M2Op::Flush : kind == StepKind::Auto ? M2Op::Auto : M2Op::NonFlush, a, l, st);
   return launched();
 }
 
 rs_status rs_step_nonflush(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in, const rs_params* prm,
                            float* y, void* stream) {
-  return replay_step(L, buf, in, prm, y, stream, false);
+  return replay_step(L, buf, in, prm, y, stream, StepKind::NonFlush);
 }
 
 rs_status rs_step_flush(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in, const rs_params* prm, float* y,
                         void* stream) {
-  return replay_step(L, buf, in, prm, y, stream, true);
+  return replay_step(L, buf, in, prm, y, stream, StepKind::Flush);
+}
+
+rs_status rs_step(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in, const rs_params* prm, float* y,
+                  void* stream) {
+  return replay_step(L, buf, in, prm, y, stream, StepKind::Auto);
+}
+
+rs_status rs_reset_slots(const rs_layer* L, const rs_buffers* buf, const int32_t* seqs, int32_t count, void* stream) {
+  if (rs_status s = check_layer(L)) return s;
+  if (L->cfg.mode != RS_REPLAY) return RS_E_MODE;
+  if (!buf || !buf->meta || count < 0 || (count > 0 && !seqs)) return RS_E_ARG;
+  if (!aligned16(buf->meta)) return RS_E_ALIGN;
+  if (count == 0) return RS_OK;
+  reset_slots(static_cast<rs_meta*>(buf->meta), L->cfg.batch, seqs, count, static_cast<hipStream_t>(stream));
+  return launched();
 }
 
 rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inputs* drafts, int32_t K,

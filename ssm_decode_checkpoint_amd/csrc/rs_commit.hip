@@ -1,4 +1,4 @@
-// Speculative commit, counter part, for both layer kinds (sitech.ge ReplaySSM
+// Speculative commit, counter part, for every layer kind (sitech.ge ReplaySSM
 // page, "Reducing state traffic and simplifying rollback": the accepted prefix
 // of the drafts is committed by moving the buffer pointer, no snapshot is
 // saved or restored). Per sequence: len += accepted, nd = 0; a commit that
@@ -69,5 +69,24 @@ __global__ __launch_bounds__(1024) void commit_meta_kernel(CommitArgs a) {
 }
 
 void commit_meta(const CommitArgs& a, hipStream_t st) { commit_meta_kernel<<<1, 1024, 0, st>>>(a); }
+
+// Slot reuse: a sequence slot that starts a new sequence gets empty counters
+// (its buffer is empty; the caller writes the new checkpoint). The arrival
+// counts are zero between calls and stay untouched.
+__global__ __launch_bounds__(256) void reset_slots_kernel(rs_meta* meta, int batch, const int32_t* seqs, int count) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= count) return;
+  const int b = seqs[i];
+  if (b < 0 || b >= batch) return;
+  rs_meta* m = meta + b;
+  m->n_ckpt = 0;
+  m->len = 0;
+  m->nd = 0;
+  m->err = 0;
+}
+
+void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, hipStream_t st) {
+  reset_slots_kernel<<<(count + 255) / 256, 256, 0, st>>>(meta, batch, seqs, count);
+}
 
 }  // namespace rs

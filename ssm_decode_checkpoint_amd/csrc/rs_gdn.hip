@@ -345,9 +345,8 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
 // non-flush step: o from checkpoint + buffer, append (with its u row), no state write
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV, bool VG>
-__global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
+__device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
   constexpr int NVS = NV / gdn_slices<NV>();
-  __shared__ GSmem<NK, NVS, VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * gdn_slices<NV>() + p.half;
@@ -410,13 +409,18 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::NonFlush, 0, nck, len, nd);
 }
 
+template <typename TIN, int NK, int NV, bool VG>
+__global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
+  __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
+  gdn_nonflush_body<TIN, NK, NV, VG>(a, s);
+}
+
 // ----------------------------------------------------------------------------
 // flush step: fold the len held entries and the current token, write once, o
 // ----------------------------------------------------------------------------
 template <typename TIN, int NK, int NV, bool VG>
-__global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
+__device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
   constexpr int NVS = NV / gdn_slices<NV>();
-  __shared__ GSmem<NK, NVS, VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * gdn_slices<NV>() + p.half;
@@ -475,6 +479,23 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
     GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
   }
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
+}
+
+template <typename TIN, int NK, int NV, bool VG>
+__global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
+  __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
+  gdn_flush_body<TIN, NK, NV, VG>(a, s);
+}
+
+// self-scheduling step (continuous batching): a sequence whose buffer is full
+// takes the flush, every other one a non-flush step, in one launch (the branch
+// is uniform per workgroup)
+template <typename TIN, int NK, int NV, bool VG>
+__global__ __launch_bounds__(kThreads) void gdn_auto_kernel(GDNArgs a) {
+  __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
+  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+  if (a.meta[p.b].len == kRing - 1) gdn_flush_body<TIN, NK, NV, VG>(a, s);
+  else gdn_nonflush_body<TIN, NK, NV, VG>(a, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -851,6 +872,10 @@ struct gdn_step_kernels {
     if (bf) gdn_flush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     else gdn_flush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
   }
+  static void auto_step(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
+    if (bf) gdn_auto_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    else gdn_auto_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+  }
 };
 
 template <typename TIN, int NK, int NV>
@@ -871,7 +896,8 @@ template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   const bool bf = l.in_bf16;
   // replay steps and appends: one workgroup per column slice of each state
-  if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::SpecAppend || op == GDNOp::ConvSpec)
+  if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
+      op == GDNOp::ConvSpec)
     l.grid *= gdn_slices<NV>();
   switch (op) {
     case GDNOp::Conv:
@@ -885,6 +911,10 @@ void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
     case GDNOp::Flush:
       if (l.vg) gdn_step_kernels<NK, NV, true>::flush(bf, a, l.grid, st);
       else gdn_step_kernels<NK, NV, false>::flush(bf, a, l.grid, st);
+      break;
+    case GDNOp::Auto:
+      if (l.vg) gdn_step_kernels<NK, NV, true>::auto_step(bf, a, l.grid, st);
+      else gdn_step_kernels<NK, NV, false>::auto_step(bf, a, l.grid, st);
       break;
     case GDNOp::SpecAppend:
       if (bf) gdn_spec_append<bf16, NK, NV>(a, l.grid, st);

@@ -37,7 +37,7 @@ struct M2Args {
   const int32_t* accepted;
 };
 
-enum class M2Op { Conv, NonFlush, Flush, SpecAppend, CommitFold, ConvSpec, Restore, Requant };
+enum class M2Op { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore, Requant };
 
 struct M2Launch {
   int rows, cols;   // dstate, headdim
@@ -135,6 +135,10 @@ struct CommitArgs {
 };
 void commit_meta(const CommitArgs& a, hipStream_t st);
 
+// Clear the counters of the listed sequences (slot reuse); entries outside
+// [0, batch) are skipped.
+void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, hipStream_t st);
+
 // Gated DeltaNet
 struct GDNArgs {
   int batch, nv, nqk, vpk;   // vpk = value heads per qk head
@@ -152,7 +156,7 @@ struct GDNArgs {
   float* o;                  // [batch][nv][dv], or [K][batch][nv][dv]
 };
 
-enum class GDNOp { Conv, NonFlush, Flush, SpecAppend, CommitFold, ConvSpec, Restore };
+enum class GDNOp { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore };
 
 struct GDNLaunch {
   int dk, dv;

@@ -145,14 +145,13 @@ struct M2NfSmem {
 };
 
 template <typename TIN, int RDF, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
+__device__ __forceinline__ void m2_nonflush_body(const M2Args& a, M2NfSmem<NR, NC>& s) {
   constexpr int E = (RDF == FMT_F32) ? 4 : 8;
   constexpr int V = 16 / static_cast<int>(sizeof(TIN));
   static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
   constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
   constexpr int CX = (kRing * NC / V + kThreads - 1) / kThreads;
   constexpr int CC = (NR / V + kThreads - 1) / kThreads;
-  __shared__ M2NfSmem<NR, NC> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const float Ah = a.A[h], Dh = a.D[h];
@@ -242,6 +241,12 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
   arr.finish(mp, actr, h, a.nheads, MetaOp::NonFlush, 0, nck, len, nd);
 }
 
+template <typename TIN, int RDF, int NR, int NC>
+__global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
+  __shared__ M2NfSmem<NR, NC> s;
+  m2_nonflush_body<TIN, RDF, NR, NC>(a, s);
+}
+
 // ----------------------------------------------------------------------------
 // fold body shared by the flush step and the commit fold
 // H <- l_m H + sum_e B_e xt_e^T with xt_e = w_{m,e} dt_e x_e (entries staged)
@@ -304,15 +309,17 @@ __device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTi
 // ----------------------------------------------------------------------------
 // flush step: fold len stored entries + the current token, write once, y
 // ----------------------------------------------------------------------------
+template <int NR, int NC>
+using M2FlSmem = M2Smem<NR, NC, kRing, 1, true>;
+
 template <typename TIN, int CKF, bool RC, int NR, int NC>
-__global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
+__device__ __forceinline__ void m2_flush_body(const M2Args& a, M2FlSmem<NR, NC>& s) {
   constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
   constexpr int V = 16 / static_cast<int>(sizeof(TIN));
   static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
   constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
   constexpr int CX = (kRing * NC / V + kThreads - 1) / kThreads;
   constexpr int CC = (NR / V + kThreads - 1) / kThreads;
-  __shared__ M2Smem<NR, NC, kRing, 1, true> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const float Ah = a.A[h];
@@ -364,6 +371,34 @@ __global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
     store_folded<CKF, RC>(a, tile, H, s.s4);
   }
   arr.finish(mp, actr, h, a.nheads, MetaOp::Flush, 0, nck, len, nd);
+}
+
+template <typename TIN, int CKF, bool RC, int NR, int NC>
+__global__ __launch_bounds__(kThreads) void m2_flush_kernel(M2Args a) {
+  __shared__ M2FlSmem<NR, NC> s;
+  m2_flush_body<TIN, CKF, RC, NR, NC>(a, s);
+}
+
+// ----------------------------------------------------------------------------
+// self-scheduling step (continuous batching): each sequence takes the flush
+// when its buffer is full and a non-flush step otherwise, in one launch, so
+// sequences at different fills share a batch and the flush work spreads over
+// steps. The branch is uniform per workgroup (one sequence, one head).
+// ----------------------------------------------------------------------------
+template <int NR, int NC>
+union M2AutoSmem {
+  M2NfSmem<NR, NC> nf;
+  M2FlSmem<NR, NC> fl;
+};
+
+template <typename TIN, int CKF, bool RC, int NR, int NC>
+__global__ __launch_bounds__(kThreads) void m2_auto_kernel(M2Args a) {
+  constexpr int RDF = RC ? FMT_NVFP4 : CKF;   // what a non-flush step reads
+  __shared__ M2AutoSmem<NR, NC> s;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = tile / a.nheads;
+  if (a.meta[b].len == kRing - 1) m2_flush_body<TIN, CKF, RC, NR, NC>(a, s.fl);
+  else m2_nonflush_body<TIN, RDF, NR, NC>(a, s.nf);
 }
 
 // ----------------------------------------------------------------------------
@@ -623,6 +658,20 @@ struct M2Shape {
     if (rc) flush_rc<TIN, true>(a, ckf, grid, st);
     else flush_rc<TIN, false>(a, ckf, grid, st);
   }
+  template <typename TIN, bool RC>
+  static void auto_rc(const M2Args& a, int ckf, int grid, hipStream_t st) {
+    switch (ckf) {
+      case FMT_F32: m2_auto_kernel<TIN, FMT_F32, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+      case FMT_F16: m2_auto_kernel<TIN, FMT_F16, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+      case FMT_FP8: m2_auto_kernel<TIN, FMT_FP8, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+      default: m2_auto_kernel<TIN, FMT_NVFP4, RC, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
+    }
+  }
+  template <typename TIN>
+  static void auto_step(const M2Args& a, int ckf, bool rc, int grid, hipStream_t st) {
+    if (rc) auto_rc<TIN, true>(a, ckf, grid, st);
+    else auto_rc<TIN, false>(a, ckf, grid, st);
+  }
   template <typename TIN, int KQ>
   static void spec_append_k(const M2Args& a, int rdf, int grid, hipStream_t st) {
     switch (rdf) {
@@ -685,6 +734,10 @@ void m2_launch_shape(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st
       break;
     case M2Op::Flush:
       if (bf) Sh::template flush<bf16>(a, l.ckf, l.rc, l.grid, st); else Sh::template flush<float>(a, l.ckf, l.rc, l.grid, st);
+      break;
+    case M2Op::Auto:
+      if (bf) Sh::template auto_step<bf16>(a, l.ckf, l.rc, l.grid, st);
+      else Sh::template auto_step<float>(a, l.ckf, l.rc, l.grid, st);
       break;
     case M2Op::SpecAppend:
       if (bf) Sh::template spec_append<bf16>(a, l.rdf, l.grid, st); else Sh::template spec_append<float>(a, l.rdf, l.grid, st);

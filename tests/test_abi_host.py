@@ -69,6 +69,22 @@ def test_gdn_layout_sizes():
         assert L.ckpt_bytes == 256 * 32 * 128 * 128 * 4
 
 
+def test_reset_slots_host_checks():
+    """rs_reset_slots: argument and mode checks happen on the host; count == 0 launches nothing."""
+    lib = rs.lib()
+    _, L = rs.rs_init(_m2(batch=2, nheads=8, headdim=16, dstate=16, ngroups=1))
+    bufs = rs.RsBuffers(0x1000, 0x2000, None, 0x3000, None)
+    assert lib.rs_reset_slots(C.byref(L), C.byref(bufs), C.c_void_p(0x1000), 0, None) == rs.RS_OK
+    assert lib.rs_reset_slots(C.byref(L), C.byref(bufs), None, 2, None) == rs.RS_E_ARG
+    assert lib.rs_reset_slots(C.byref(L), C.byref(bufs), C.c_void_p(0x1000), -1, None) == rs.RS_E_ARG
+    nometa = rs.RsBuffers(0x1000, 0x2000, None, None, None)
+    assert lib.rs_reset_slots(C.byref(L), C.byref(nometa), C.c_void_p(0x1000), 1, None) == rs.RS_E_ARG
+    _, Lc = rs.rs_init(_m2(batch=2, nheads=8, headdim=16, dstate=16, ngroups=1, mode=rs.RS_CONVENTIONAL))
+    assert lib.rs_reset_slots(C.byref(Lc), C.byref(bufs), C.c_void_p(0x1000), 1, None) == rs.RS_E_MODE
+    assert lib.rs_step(C.byref(Lc), C.byref(bufs), C.byref(rs.RsInputs()), C.byref(rs.RsParams()), C.c_void_p(0x1000),
+                       None) == rs.RS_E_MODE
+
+
 def test_kda_layout_sizes():
     """Kimi Delta Attention: the GDN layout with a dk-wide gate per ring entry;
     speculative configs are refused."""
