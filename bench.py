@@ -593,6 +593,10 @@ LOWPREC_VARIANTS = [("f32", None), ("f32", "nvfp4"), ("f16", "nvfp4"), ("fp8", "
 
 def bench_lowprec(args, torch, rs):
     w = W.M2_LOWPREC
+    if args.lowprec_batch:
+        # the same layer at another batch (256: the step is HBM-bound there, the 256 MB
+        # last-level cache no longer holds the state)
+        w = w.with_(name=f"mamba2_lowprec_b{args.lowprec_batch}", batch=args.lowprec_batch)
     dev = "cuda"
     B = w.batch
     p = W.m2_params(w)
@@ -603,11 +607,12 @@ def bench_lowprec(args, torch, rs):
     pool = _m2_pool(torch, w, B, dev)
     y = torch.empty(B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
     tm = Timer(torch)
-    out = {"metric": "low-precision-read decode tokens/s, Mamba-2 batch 64 (per checkpoint / read-copy format)",
+    out = {"metric": f"low-precision-read decode tokens/s, Mamba-2 batch {B} (per checkpoint / read-copy format)",
            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "batch": B, "nheads": w.nheads, "headdim": w.headdim, "dstate": w.dstate,
-                      "note": "state 256 MiB at batch 64 fits the 256 MB last-level cache; GB/s are effective"},
+                      "note": (f"fp32 state {B * 4} MiB" + ("; fits the 256 MB last-level cache, GB/s are effective"
+                                                             if B <= 64 else ""))},
            "variants": {}}
     for fmt, rc in LOWPREC_VARIANTS:
         layer, bufs = _m2_layer(rs, w, B, rs.RS_REPLAY, dev, ckpt=code[fmt],
@@ -712,6 +717,7 @@ def main():
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
     ap.add_argument("--lowprec-error-seqs", type=int, default=2)
+    ap.add_argument("--lowprec-batch", type=int, default=0, help="batch of the low-precision workload (0: 64)")
     ap.add_argument("--lowprec-slow-decay", action="store_true",
                     help="error run with slowly decaying heads (outside the C5 configuration)")
     args = ap.parse_args()

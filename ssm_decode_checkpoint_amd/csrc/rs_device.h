@@ -100,6 +100,8 @@ typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float4 nt_load(const float4* p) {
   const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
@@ -205,13 +207,28 @@ __device__ __forceinline__ void decode_chunk(const Raw<FMT, E>& r, float ms, flo
       v[2 * i + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
     }
   } else if constexpr (FMT == FMT_FP8) {
+    // gfx950 converts two E4M3FN codes per instruction, exactly (the scale operand
+    // only contributes its exponent, so it is 1 and the scale is applied after)
     const uint32_t w[2] = {r.v.x, r.v.y};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e4m3_value((w[i >> 2] >> ((i & 3) * 8)) & 0xFFu) * ms;
+    for (int h = 0; h < 2; ++h) {
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[h], 1.0f, false);   // bytes 0, 1
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[h], 1.0f, true);    // bytes 2, 3
+      v[4 * h + 0] = lo.x * ms;
+      v[4 * h + 1] = lo.y * ms;
+      v[4 * h + 2] = hi.x * ms;
+      v[4 * h + 3] = hi.y * ms;
+    }
   } else {
+    // two E2M1 codes per instruction (low nibble first), exactly; block and tensor
+    // scale applied after
     const float sd = e4m3_value(r.s) * ms;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = e2m1_value((r.v >> (4 * i)) & 15u) * sd;
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 3);
+    v[0] = p0.x * sd; v[1] = p0.y * sd; v[2] = p1.x * sd; v[3] = p1.y * sd;
+    v[4] = p2.x * sd; v[5] = p2.y * sd; v[6] = p3.x * sd; v[7] = p3.y * sd;
   }
 }
 
