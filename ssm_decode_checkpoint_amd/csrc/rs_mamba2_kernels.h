@@ -248,6 +248,177 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
 }
 
 // ----------------------------------------------------------------------------
+// non-flush step for FP8 / NVFP4 reads: one wavefront per head, kHPB heads of
+// one B/C group per workgroup. A low-precision tile (4.6 KiB in NVFP4) is
+// smaller than the buffer records a head needs, so the group's B rows, C and
+// the B.C dots are staged and computed once for kHPB heads, and each head's
+// output is reduced inside its wavefront: lane l owns the 8 columns
+// 8 (l mod 8) .. +7 of rows l/8 + 8k of the tile and of the held x rows l/8 and
+// l/8 + 8, so the buffer term and D x join the lane's partial sums before one
+// 3-step shuffle reduction over the 8 lanes that share those columns.
+// ----------------------------------------------------------------------------
+constexpr int kHPB = 4;
+
+template <int NR, int NC>
+struct M2WaveSmem {
+  float B[kRing][NR];
+  float C[NR];
+  float bc[kRing];            // B_e . C_cur
+  float dt[kHPB][kRing];
+  float a[kHPB][kRing];       // exp(dt A) per head and entry
+  float w[kHPB][kRing];       // w_{j,e} dt_e (B_e . C_cur) per head
+  float L[kHPB];
+};
+
+template <typename TIN, int RDF, int NR, int NC>
+__global__ __launch_bounds__(kThreads) void m2_nonflush_wave_kernel(M2Args a) {
+  static_assert(RDF == FMT_FP8 || RDF == FMT_NVFP4, "low-precision reads only");
+  static_assert(NC == 64 && NR % 8 == 0, "8 lanes per 64-column row");
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  constexpr int XCH = 8 / V;                 // 16-byte chunks per lane per x row (8 columns)
+  constexpr int RPP = 8, PASSES = NR / RPP;   // tile rows per pass, passes per head
+  constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
+  constexpr int CC = (NR / V + kThreads - 1) / kThreads;
+  __shared__ M2WaveSmem<NR, NC> s;
+  const int nblk = a.nheads / kHPB;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);          // (sequence, head block)
+  const int b = tile / nblk, hb = tile - b * nblk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h = hb * kHPB + wave, g = (hb * kHPB) / a.hpg;
+  rs_meta* mp = a.meta + b;
+  uint32_t* actr = a.arrive + static_cast<size_t>(b) * arrive_groups(nblk) * kArriveStride;
+  const int len = mp->len, nd = mp->nd;
+  const long long nck = mp->n_ckpt;
+  const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, hb, nck, len, nd);
+    arr.finish(mp, actr, hb, nblk, MetaOp::NonFlush, 0, nck, len, nd);
+    return;
+  }
+  const int j = len + 1;
+  const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
+  const size_t mat = static_cast<size_t>(b) * a.nheads + h;
+  const TIN* inB = static_cast<const TIN*>(a.B) + bg * NR;
+  const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
+  const TIN* inX = static_cast<const TIN*>(a.x) + mat * NC;
+  TIN* rB = static_cast<TIN*>(a.rB) + bg * kRing * NR;
+  TIN* rC = static_cast<TIN*>(a.rC) + bg * kRing * NR;
+  TIN* rX = static_cast<TIN*>(a.rx) + mat * kRing * NC;
+  const size_t hdt = static_cast<size_t>(b) * a.nheads + hb * kHPB;   // first head of the block
+  // 1. records into registers: group B rows and C (whole block), this head's x
+  //    rows of entries lane/8 and lane/8 + 8 (8 columns), the block's dt
+  RegChunks<TIN, CB> cb;
+  RegChunks<TIN, CC> cc;
+  cb.load(EntrySrc<TIN>{rB, inB, 0, nck, len, NR}, j, NR);
+  cc.load(EntrySrc<TIN>{inC, inC, 0, 0, 0, NR}, 1, NR);
+  const EntrySrc<TIN> xs{rX, inX, 0, nck, len, NC};
+  const int ce = lane & 7, e0 = lane >> 3, e1 = e0 + 8;
+  uint4 xr[2][XCH];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = q == 0 ? e0 : e1;
+    const int ec = e < j ? e : j - 1;         // unconditional load from a valid entry
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) xr[q][c] = *reinterpret_cast<const uint4*>(xs.at(ec) + ce * 8 + c * V);
+  }
+  float dtv = 0.0f;
+  {
+    const int t = threadIdx.x, hw = t >> 4, e = t & 15;
+    const int ec = e < j ? e : j - 1;
+    const TIN* rD = static_cast<const TIN*>(a.rdt) + (hdt + (hw < kHPB ? hw : 0)) * kRing;
+    const TIN* iD = static_cast<const TIN*>(a.dt) + hdt + (hw < kHPB ? hw : 0);
+    dtv = to_f(*(ec < len ? rD + ((nck + ec) & (kRing - 1)) : iD));
+  }
+  // 2. this head's tile, then the arrival count
+  Raw<RDF, 8> raw[PASSES];
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) raw[k] = load_chunk<RDF, 8, NC>(a.rd, mat, NR, k * RPP + (lane >> 3), ce);
+  const float ms = mat_scale<RDF>(a.rd, mat);
+  arr.arrive(actr, hb, nck, len, nd);
+  // 3. records to LDS; dots, decays and weights (state-independent)
+  cb.to_lds(&s.B[0][0], NR, j, NR);
+  cc.to_lds(s.C, NR, 1, NR);
+  if (threadIdx.x < kHPB * 16) {
+    const int hw = threadIdx.x >> 4, e = threadIdx.x & 15;
+    s.dt[hw][e] = dtv;
+    s.a[hw][e] = expf(dtv * a.A[hb * kHPB + hw]);
+  }
+  __syncthreads();
+  {
+    const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+    if (grp < j) {
+      float part = 0.0f;
+      for (int n = ln; n < NR; n += 16) part += s.B[grp][n] * s.C[n];
+      part = group_sum16(part);
+      if (ln == 0) s.bc[grp] = part;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kHPB * 16) {
+    const int hw = threadIdx.x >> 4, e = threadIdx.x & 15;
+    if (e < j) {
+      float wv = 1.0f;
+      for (int l = e + 1; l < j; ++l) wv *= s.a[hw][l];
+      s.w[hw][e] = wv * s.dt[hw][e] * s.bc[e];
+    }
+    if (e == 0) {
+      float L = 1.0f;
+      for (int l = 0; l < j; ++l) L *= s.a[hw][l];
+      s.L[hw] = L;
+    }
+  }
+  __syncthreads();
+  // 4. this head's output inside its wavefront
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < PASSES; ++k) {
+    float t[8];
+    decode_chunk<RDF, 8>(raw[k], ms, t);
+    const float cr = s.C[k * RPP + (lane >> 3)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += t[i] * cr;
+  }
+  const float L = s.L[wave], Dh = a.D[h];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] *= L;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = q == 0 ? e0 : e1;
+    float xv[8];
+#pragma unroll
+    for (int c = 0; c < XCH; ++c) unpack16(xr[q][c], static_cast<const TIN*>(nullptr), xv + c * V);
+    const float we = e < j ? s.w[wave][e] + (e == j - 1 ? Dh : 0.0f) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += e < j ? we * xv[i] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i] += __shfl_xor(acc[i], 8, 64);
+    acc[i] += __shfl_xor(acc[i], 16, 64);
+    acc[i] += __shfl_xor(acc[i], 32, 64);
+  }
+  if (lane < 8) {
+    float4* yp = reinterpret_cast<float4*>(a.y + mat * NC + lane * 8);
+    nt_store(make_float4(acc[0], acc[1], acc[2], acc[3]), yp);
+    nt_store(make_float4(acc[4], acc[5], acc[6], acc[7]), yp + 1);
+  }
+  // 5. append the current record (bit copies)
+  const int slot = static_cast<int>((nck + len) & (kRing - 1));
+  if (lane < NC / V) reinterpret_cast<uint4*>(rX + slot * NC)[lane] = reinterpret_cast<const uint4*>(inX)[lane];
+  if (lane == 0) static_cast<TIN*>(a.rdt)[mat * kRing + slot] = static_cast<const TIN*>(a.dt)[mat];
+  if (wave == 0 && (hb * kHPB) % a.hpg == 0) {
+    if (lane < NR / V) {
+      reinterpret_cast<uint4*>(rB + slot * NR)[lane] = reinterpret_cast<const uint4*>(inB)[lane];
+      reinterpret_cast<uint4*>(rC + slot * NR)[lane] = reinterpret_cast<const uint4*>(inC)[lane];
+    }
+  }
+  arr.finish(mp, actr, hb, nblk, MetaOp::NonFlush, 0, nck, len, nd);
+}
+
+// ----------------------------------------------------------------------------
 // fold body shared by the flush step and the commit fold
 // H <- l_m H + sum_e B_e xt_e^T with xt_e = w_{m,e} dt_e x_e (entries staged)
 // ----------------------------------------------------------------------------
@@ -637,6 +808,14 @@ struct M2Shape {
   }
   template <typename TIN>
   static void nonflush(const M2Args& a, int rdf, int grid, hipStream_t st) {
+    if constexpr (NC == 64 && NR % 8 == 0) {
+      if ((rdf == FMT_FP8 || rdf == FMT_NVFP4) && a.hpg % kHPB == 0) {
+        const int g = grid / kHPB;   // one workgroup per kHPB heads
+        if (rdf == FMT_FP8) m2_nonflush_wave_kernel<TIN, FMT_FP8, NR, NC><<<g, kThreads, 0, st>>>(a);
+        else m2_nonflush_wave_kernel<TIN, FMT_NVFP4, NR, NC><<<g, kThreads, 0, st>>>(a);
+        return;
+      }
+    }
     switch (rdf) {
       case FMT_F32: m2_nonflush_kernel<TIN, FMT_F32, NR, NC><<<grid, kThreads, 0, st>>>(a); break;
       case FMT_F16: m2_nonflush_kernel<TIN, FMT_F16, NR, NC><<<grid, kThreads, 0, st>>>(a); break;

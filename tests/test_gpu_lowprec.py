@@ -111,8 +111,16 @@ def _run(w, layer, bufs, A, D, steps, t0=0):
     return ys
 
 
-def test_nonflush_reads_copy_and_isolation():
-    w = W.TINY_M2.with_(init_std=0.5, seed=61)
+# tiny layer; 128 x 64 heads four to a group (the wavefront-per-head read kernel), fp32 and
+# bf16 inputs; 128 x 64 heads two to a group (the workgroup-per-head kernel)
+READ_SHAPES = [dict(), dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64),
+               dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64, in_dtype="bf16"),
+               dict(batch=3, nheads=6, ngroups=3, dstate=128, headdim=64)]
+
+
+@pytest.mark.parametrize("shape", READ_SHAPES)
+def test_nonflush_reads_copy_and_isolation(shape):
+    w = W.TINY_M2.with_(init_std=0.5, seed=61, **shape)
     p = W.m2_params(w)
     A, D = params_dev(p)
     H0 = W.m2_init_states(w, range(w.batch))
@@ -158,10 +166,11 @@ def bufs_ck(layer, bufs):
 
 @pytest.mark.parametrize("fmt,rc,gate", [("f16", None, 1e-4), ("fp8", None, 2e-2), ("nvfp4", None, 2e-2),
                                          ("f16", "nvfp4", 2e-2), ("fp8", "nvfp4", 2e-2)])
-def test_low_precision_checkpoints(fmt, rc, gate):
+@pytest.mark.parametrize("shape", READ_SHAPES[:2])
+def test_low_precision_checkpoints(fmt, rc, gate, shape):
     """Zero initial state, 48 steps (3 flushes): GPU vs the oracle running the
     same storage formats; the error vs exact fp64 decoding is reported."""
-    w = W.TINY_M2.with_(seed=70)
+    w = W.TINY_M2.with_(seed=70, **shape)
     p = W.m2_params(w)
     A, D = params_dev(p)
     code = {"f16": rs.RS_F16, "fp8": rs.RS_FP8E4M3, "nvfp4": rs.RS_NVFP4}[fmt]
