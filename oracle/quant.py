@@ -56,7 +56,9 @@ E4M3_MAG = _e4m3_table()          # E4M3_MAG[126] = 448
 def _nearest_even(mag: np.ndarray, table: np.ndarray) -> np.ndarray:
     """Index of the nearest table entry to each |value|; ties go to the even index;
     values beyond the last entry take the last entry (saturation)."""
-    mag = np.asarray(mag, dtype=np.float64)
+    # Clamping first is the saturation itself; it also keeps the distances below
+    # from losing every table entry to float64 rounding for huge magnitudes.
+    mag = np.minimum(np.asarray(mag, dtype=np.float64), table[-1])
     d = np.abs(mag[..., None] - table.astype(np.float64))
     best = d.min(axis=-1, keepdims=True)
     hit = d == best

@@ -139,3 +139,14 @@ def test_fp8_checkpoint_format():
     assert np.all((codes >> 7) == np.signbit(x))
     xh = quant.fp8_dequantize(codes, scale)
     assert np.all(np.abs(xh - x) <= np.abs(x) / 16 + 2.0 ** -9 * scale)
+
+
+def test_saturation_over_the_whole_float32_range():
+    """Both encoders saturate at their largest finite code for every magnitude
+    above it, up to the largest float32 and infinity (the formats' saturating
+    conversion); the sign is kept."""
+    big = np.array([6.0, 6.5, 1e6, 1e16, 1e20, 1e30, 3.4e38, np.inf], np.float32)
+    assert quant.e2m1_encode(big).tolist() == [7] * big.size
+    assert quant.e2m1_encode(-big).tolist() == [15] * big.size
+    big8 = np.array([448.0, 464.0, 1e6, 1e17, 1e20, 1e30, 3.4e38, np.inf], np.float32)
+    assert quant.e4m3_encode_mag(big8).tolist() == [126] * big8.size
