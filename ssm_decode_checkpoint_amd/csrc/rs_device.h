@@ -45,27 +45,13 @@ template <>
 __device__ __forceinline__ bf16 from_f<bf16>(float v) { return bf16{static_cast<uint16_t>(__float_as_uint(v) >> 16)}; }
 
 // ----------------------------------------------------------------------------
-// E4M3FN and E2M1 codecs (round to nearest, ties to even, saturating)
+// E4M3FN and E2M1 code values (the encoders sit with the tile stores)
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
   const uint32_t e = (code >> 3) & 15u, m = code & 7u;
   float mag = (e == 0) ? static_cast<float>(m) * 0.001953125f  // m * 2^-9
                        : __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
   return (code & 0x80u) ? -mag : mag;
-}
-
-// Non-negative finite float -> E4M3FN code 0..126.
-__device__ __forceinline__ uint32_t e4m3_encode_mag(float x) {
-  if (!(x < 448.0f)) return 0x7Eu;                       // saturate (also 448 itself)
-  if (x < 0.015625f) {                                   // below 2^-6: subnormal grid 2^-9
-    return static_cast<uint32_t>(rintf(x * 512.0f));     // 8 -> code 8 = 2^-6, still right
-  }
-  const uint32_t bits = __float_as_uint(x);
-  int e = static_cast<int>((bits >> 23) & 255u) - 127;   // 2^e <= x < 2^(e+1), e in [-6, 8]
-  const float mant = __uint_as_float((bits & 0x7FFFFFu) | 0x3F800000u);  // [1, 2)
-  uint32_t m = static_cast<uint32_t>(rintf((mant - 1.0f) * 8.0f));
-  if (m == 8u) { m = 0u; ++e; }
-  return (static_cast<uint32_t>(e + 7) << 3) | m;
 }
 
 __device__ __forceinline__ float e2m1_value(uint32_t code) {
@@ -75,22 +61,6 @@ __device__ __forceinline__ float e2m1_value(uint32_t code) {
   float mag = (i < 4u) ? 0.5f * static_cast<float>(i)
                        : static_cast<float>(1u << (((i - 4u) >> 1) + 1u)) * ((i & 1u) ? 1.5f : 1.0f);
   return (code & 8u) ? -mag : mag;
-}
-
-// float -> E2M1 code (sign in bit 3), nearest-even, saturating at 6.
-__device__ __forceinline__ uint32_t e2m1_encode(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 31) << 3;
-  const float m = fabsf(q);
-  uint32_t c;
-  if (m <= 0.25f) c = 0;
-  else if (m < 0.75f) c = 1;
-  else if (m <= 1.25f) c = 2;
-  else if (m < 1.75f) c = 3;
-  else if (m <= 2.5f) c = 4;
-  else if (m < 3.5f) c = 5;
-  else if (m <= 5.0f) c = 6;
-  else c = 7;
-  return sign | c;
 }
 
 // ----------------------------------------------------------------------------

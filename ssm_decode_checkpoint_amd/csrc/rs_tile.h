@@ -150,9 +150,42 @@ __device__ __forceinline__ float tile_absmax(const RegTile<E, NR, NC>& M, float*
   return fmaxf(fmaxf(scratch4[0], scratch4[1]), fmaxf(scratch4[2], scratch4[3]));
 }
 
-// FP8 (E4M3, one scale per matrix) code of x given the matrix scale.
-__device__ __forceinline__ uint32_t fp8_code(float x, float sc) {
-  return e4m3_encode_mag(fabsf(x) / sc) | ((__float_as_uint(x) >> 31) << 7);
+// ----------------------------------------------------------------------------
+// Encoders. Each element is divided by its scale first (correctly rounded, the
+// order the format definitions use), the quotient is clamped to the format's
+// largest finite magnitude (saturation: the E4M3FN conversion instruction would
+// give the NaN code above about 464), then converted by gfx950's packed
+// conversion at unit scale, which rounds to nearest with ties to even.
+// ----------------------------------------------------------------------------
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float clamp_mag(float q, float m) { return fminf(fmaxf(q, -m), m); }
+
+// Four E4M3FN codes of x[0..3] / sc, element i in byte i.
+__device__ __forceinline__ uint32_t fp8_codes4(const float* x, float sc) {
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(x[0] / sc, 448.0f), clamp_mag(x[1] / sc, 448.0f), 1.0f,
+                                               false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(x[2] / sc, 448.0f), clamp_mag(x[3] / sc, 448.0f), 1.0f,
+                                               true);
+  return static_cast<uint32_t>(static_cast<uint16_t>(r.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(r.y)) << 16);
+}
+
+// E4M3FN code of a non-negative quotient q (an NVFP4 block scale).
+__device__ __forceinline__ uint32_t e4m3_code_of(float q) {
+  s16x2 r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(q, 448.0f), 0.0f, 1.0f, false);
+  return static_cast<uint32_t>(r.x) & 0xFFu;
+}
+
+// Eight E2M1 codes of x[0..7] / sd, element i in nibble i (all 0 when sd = 0).
+__device__ __forceinline__ uint32_t nvfp4_codes8(const float* x, float sd) {
+  uint32_t w = 0u;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[0] / sd, 6.0f), clamp_mag(x[1] / sd, 6.0f), 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[2] / sd, 6.0f), clamp_mag(x[3] / sd, 6.0f), 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[4] / sd, 6.0f), clamp_mag(x[5] / sd, 6.0f), 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[6] / sd, 6.0f), clamp_mag(x[7] / sd, 6.0f), 1.0f, 3);
+  return sd == 0.0f ? 0u : w;
 }
 
 __device__ __forceinline__ float fp8_scale_of(float amax) {
@@ -165,10 +198,15 @@ __device__ __forceinline__ float nvfp4_tscale_of(float amax) {
   return ts == 0.0f ? 1.0f : ts;
 }
 
-// NVFP4 block scale code and its decoded scale for a block whose |max| is bm.
-__device__ __forceinline__ uint32_t nvfp4_block_code(float bm, float ts) { return e4m3_encode_mag(bm / (6.0f * ts)); }
-
-__device__ __forceinline__ uint32_t nvfp4_code(float x, float sd) { return (sd == 0.0f) ? 0u : e2m1_encode(x / sd); }
+// NVFP4 block scale code for a block whose |max| is bm (the pair of threads
+// holding the block's sixteen columns exchange their halves' maxima).
+__device__ __forceinline__ uint32_t nvfp4_block_code(const float* x, float ts) {
+  float bm = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(x[i]));
+  bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+  return e4m3_code_of(bm / (6.0f * ts));
+}
 
 // Replace M by the value it reads back as after being stored in FMT (scales
 // computed from M itself, as tile_store does). All threads must call.
@@ -180,23 +218,23 @@ __device__ __forceinline__ void tile_round_trip(RegTile<E, NR, NC>& M, float* sc
 #pragma unroll
       for (int i = 0; i < E; ++i) M.v[k][i] = __half2float(__float2half_rn(M.v[k][i]));
   } else if constexpr (FMT == FMT_FP8) {
+    static_assert(E == 8, "fp8 state chunks are eight elements");
     const float sc = fp8_scale_of(tile_absmax(M, scratch4));
 #pragma unroll
-    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k)
-#pragma unroll
-      for (int i = 0; i < E; ++i) M.v[k][i] = e4m3_value(fp8_code(M.v[k][i], sc)) * sc;
+    for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
+      Raw<FMT_FP8, 8> r;
+      r.v = make_uint2(fp8_codes4(M.v[k], sc), fp8_codes4(M.v[k] + 4, sc));
+      decode_chunk<FMT_FP8, 8>(r, sc, M.v[k]);
+    }
   } else if constexpr (FMT == FMT_NVFP4) {
     static_assert(E == 8, "NVFP4 blocks span two threads of eight columns");
     const float ts = nvfp4_tscale_of(tile_absmax(M, scratch4));
 #pragma unroll
     for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
-      float bm = 0.0f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) bm = fmaxf(bm, fabsf(M.v[k][i]));
-      bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
-      const float sd = e4m3_value(nvfp4_block_code(bm, ts)) * ts;
-#pragma unroll
-      for (int i = 0; i < E; ++i) M.v[k][i] = e2m1_value(nvfp4_code(M.v[k][i], sd)) * sd;
+      Raw<FMT_NVFP4, 8> r;
+      r.s = nvfp4_block_code(M.v[k], ts);
+      r.v = nvfp4_codes8(M.v[k], e4m3_value(r.s) * ts);
+      decode_chunk<FMT_NVFP4, 8>(r, ts, M.v[k]);
     }
   }
 }
@@ -245,12 +283,9 @@ __device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
       const int row = RegTile<E, NR, NC>::row(k);
-      if (row < NR) {
-        uint32_t w[2] = {0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i >> 2] |= fp8_code(M.v[k][i], sc) << ((i & 3) * 8);
-        nt_store(make_uint2(w[0], w[1]), reinterpret_cast<uint2*>(base + row * NC + c * E));
-      }
+      if (row < NR)
+        nt_store(make_uint2(fp8_codes4(M.v[k], sc), fp8_codes4(M.v[k] + 4, sc)),
+                 reinterpret_cast<uint2*>(base + row * NC + c * E));
     }
     if (threadIdx.x == 0) sb.tscale[mat] = sc;
   } else {
@@ -261,15 +296,8 @@ __device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
       const int row = RegTile<E, NR, NC>::row(k);
-      float bm = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(M.v[k][i]));
-      bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
-      const uint32_t s = nvfp4_block_code(bm, ts);
-      const float sd = e4m3_value(s) * ts;
-      uint32_t w = 0u;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w |= nvfp4_code(M.v[k][i], sd) << (4 * i);
+      const uint32_t s = nvfp4_block_code(M.v[k], ts);
+      const uint32_t w = nvfp4_codes8(M.v[k], e4m3_value(s) * ts);
       if (row < NR) {
         nt_store(w, reinterpret_cast<uint32_t*>(base + (row * NC + c * 8) / 2));
         if ((c & 1) == 0) sbase[(row * NC + c * 8) / 16] = static_cast<uint8_t>(s);
