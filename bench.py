@@ -519,17 +519,19 @@ def bench_spec(args, torch, rs):
     }
 
 
-def bench_gdn_spec(args, torch, rs):
-    """Speculative decoding on the Qwen-style GDN layer: batch 256, 4 drafts per
-    round, seeded acceptance U{0..4}; ReplaySSM (append with cached u rows, commit
-    by pointer move, folds when room runs short) vs the snapshot/restore baseline."""
-    w = W.GDN_SPEC
+def bench_gdn_spec(args, torch, rs, w=None):
+    """Speculative decoding on the Qwen-style GDN layer (or KDA on its shapes):
+    batch 256, 4 drafts per round, seeded acceptance U{0..4}; ReplaySSM (append
+    with cached u rows, commit by pointer move, folds when room runs short) vs the
+    snapshot/restore baseline."""
+    w = W.GDN_SPEC if w is None else w
+    layer_name = "KDA" if w.gate == "channel" else "GDN"
     dev = "cuda"
     B, K = w.batch, w.max_draft
     gp = W.gdn_params(w)
 
     def mk(mode):
-        cfg = rs.make_config(rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk, n_v_heads=w.n_v, head_k_dim=w.dk,
+        cfg = rs.make_config(rs.RS_KDA if w.gate == "channel" else rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk, n_v_heads=w.n_v, head_k_dim=w.dk,
                              head_v_dim=w.dv, in_dtype=rs.RS_BF16, max_draft=K)
         _, layer = rs.rs_init(cfg)
         return layer, rs.alloc_buffers(layer, dev)
@@ -570,7 +572,8 @@ def bench_gdn_spec(args, torch, rs):
     total_c, per_c = tm.run(snap_all, 1, 1, 2 * rounds)
     S = w.n_v * w.dv * w.dk * 4
     return {
-        "metric": "GDN speculative decode committed tokens/s at batch 256, 4 drafts (ReplaySSM vs snapshot/restore)",
+        "metric": f"{layer_name} speculative decode committed tokens/s at batch {B}, {K} drafts "
+                  "(ReplaySSM vs snapshot/restore)",
         "value": committed / (total_r * 1e-3), "unit": "committed tokens/s", "n_gpus": 1, "steps": 1,
         "warmup": 1, "ms_per_step": total_r, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -712,7 +715,8 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--workload", action="append",
-                    choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "lowprec", "copy", "sweep", "serve"],
+                    choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "kda_spec", "lowprec", "copy", "sweep",
+                             "serve"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
@@ -733,6 +737,8 @@ def main():
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
               "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve,
               "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
+              "kda_spec": lambda a, t, r: bench_gdn_spec(a, t, r,
+                                                         W.KDA_B256.with_(name="kda_spec_b256", max_draft=4)),
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
         if wl == "mamba2":

@@ -81,8 +81,9 @@
  *   became the norm"): S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T)
  *   + beta_t v_t k_t^T, o_t = S_t q_t, with alpha_t = exp(g_t) a vector over
  *   the dk key channels. Everything as for Gated DeltaNet except g: float
- *   [batch][Hv][dk] per token, and the ring's g float [batch][Hv][R][dk].
- *   Speculative calls are Gated DeltaNet / Mamba-2 only (max_draft must be 0).
+ *   [batch][Hv][dk] per token (drafts [K][batch][Hv][dk]), and the ring's g
+ *   float [batch][Hv][R][dk]. The speculative calls work as for Gated
+ *   DeltaNet (the draft records are verified inside the KDA layer).
  * NVFP4 block (read copy, or the uniform NVFP4 checkpoint), for the stored
  *   matrices M[b][h] of rows x cols (rows = N or dk, cols = P or dv):
  *     codes   uint8 [batch][heads][rows][cols/2]: two E2M1 codes per byte,
@@ -257,7 +258,7 @@ rs_status rs_reset_slots(const rs_layer* L, const rs_buffers* buf, const int32_t
  * slots after the committed entries, nd = K, no state write (device error
  * RS_ERR_OVERFLOW when nd != 0 or len + K > 16). Conventional mode: the
  * snapshot baseline; steps the live state through the drafts and writes the
- * state after each draft to snap[d]. Both layer kinds (for Gated DeltaNet
+ * state after each draft to snap[d]. Every layer kind (for the delta rules
  * prm may be NULL; each draft's solved row u is written beside it in the
  * ring, and it stays valid for an accepted prefix because it depends only on
  * the checkpoint and earlier entries); 1 <= K <= max_draft. */
@@ -270,8 +271,8 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
  * entries are folded into the checkpoint (one write), n_ckpt += len, len = 0.
  * Device error RS_ERR_COMMIT when accepted[b] is outside [0, nd].
  * Conventional mode: live state = snap[accepted[b] - 1] where accepted[b] >= 1
- * (values outside [0, max_draft] leave the sequence unchanged). Both layer
- * kinds; prm (A, D) is required for Mamba-2 only. */
+ * (values outside [0, max_draft] leave the sequence unchanged). Every layer
+ * kind; prm (A, D) is required for Mamba-2 only. */
 rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted,
                          const rs_params* prm, void* stream);
 

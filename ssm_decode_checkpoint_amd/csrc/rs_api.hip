@@ -267,7 +267,6 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
     if (static_cast<uint64_t>(c.batch) * c.n_v_heads > (1u << 30)) return RS_E_ARG;
     if (!gdn_shape_supported(c.head_k_dim, c.head_v_dim)) return RS_E_UNSUPPORTED;
     if (c.ckpt_dtype != RS_F32 || c.read_copy != RS_NONE) return RS_E_DTYPE;
-    if (c.kind == RS_KDA && c.max_draft != 0) return RS_E_MODE;
     L.heads = c.n_v_heads;
     L.in_heads = c.n_qk_heads;
     L.rows = c.head_k_dim;

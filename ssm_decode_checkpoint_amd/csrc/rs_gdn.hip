@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void gdn_auto_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int NK, int NVS, int KQ>
+template <int NK, int NVS, int KQ, bool VG>
 struct GSpecSmem {
   // k of window entries 0..n-1 (held, then drafts) for the dots; once they are
   // done, the same space is the matvec scratch (4 KQ NVS floats), and after the
@@ -525,13 +525,17 @@ struct GSpecSmem {
   float kq[KQ][kRing];         // r_{e,i} (k_i . q_d) for i <= e
   float rt[KQ][kRing];         // r_{e,i} for i <= e
   float al[kRing];             // alpha of window entry e
-  float gam[KQ];               // gamma of draft d's entry
+  float gam[KQ];               // gamma of draft d's entry (VG: 1, the decays weight the dots)
   float bet[KQ];
+  // VG: r_{e,i} per key channel for the draft being dotted (e = len + d), and
+  // gamma_e per channel for each draft
+  float R[VG ? kRing : 1][NK];
+  float G[VG ? KQ : 1][NK];
 };
 
 }  // namespace
 
-template <typename TIN, int NK, int NV, int KQ>
+template <typename TIN, int NK, int NV, int KQ, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
   constexpr int NS = gdn_slices<NV>();
   constexpr int NVS = NV / NS;
@@ -541,9 +545,10 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
   constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
   constexpr int CD = (KQ * NK / VK + kThreads - 1) / kThreads;
   constexpr int CV = (KQ * NVS / VK + kThreads - 1) / kThreads;
-  __shared__ GSpecSmem<NK, NVS, KQ> s;
+  __shared__ GSpecSmem<NK, NVS, KQ, VG> s;
   const GPtrs p = gdn_tile<NV, NS>(a);
   const int K = a.K;
+  static_assert(!VG || NK <= kThreads, "one thread per key channel");
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * NS + p.half;
   uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * NS) * kArriveStride;
@@ -575,8 +580,21 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
     cq.load(EntrySrc<TIN>{iq, iq, kstride, 0, 0, NK}, K, NK);
     cd.load(EntrySrc<TIN>{ik, ik, kstride, 0, 0, NK}, K, NK);
     cv.load(EntrySrc<TIN>{iv, iv, vstride, 0, 0, NVS}, K, NVS);
-    const int e = static_cast<int>(threadIdx.x) < n ? static_cast<int>(threadIdx.x) : n - 1;
-    const float gv = *(e < len ? rg + slot_of(nck, e) : a.g + static_cast<size_t>(e - len) * gstride + p.st);
+    float gv = 0.0f;
+    float lg[kRing];   // VG: the log decays of window entries 0..n-1 of this thread's key channel
+    if constexpr (VG) {
+      const int c = static_cast<int>(threadIdx.x) < NK ? static_cast<int>(threadIdx.x) : NK - 1;
+      const float* rgc = static_cast<const float*>(a.rg) + p.st * kRing * NK + c;
+      const float* igc = a.g + p.st * NK + c;
+#pragma unroll
+      for (int e = 0; e < kRing; ++e) {
+        const int ee = e < n ? e : n - 1;
+        lg[e] = ee < len ? rgc[slot_of(nck, ee) * NK] : igc[static_cast<size_t>(ee - len) * gstride * NK];
+      }
+    } else {
+      const int e = static_cast<int>(threadIdx.x) < n ? static_cast<int>(threadIdx.x) : n - 1;
+      gv = *(e < len ? rg + slot_of(nck, e) : a.g + static_cast<size_t>(e - len) * gstride + p.st);
+    }
     const int dd = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
     const float bv = a.beta[static_cast<size_t>(dd) * gstride + p.st];
     GSlice<NK, NV, NVS> raw;
@@ -588,22 +606,65 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
     cq.to_lds(&s.W[1][0], 2 * NK, K, NK);
     for (int idx = 2 * K * NK + threadIdx.x; idx < 2 * KQ * NK; idx += kThreads) (&s.W[0][0])[idx] = 0.0f;
     cv.to_lds(&s.V[0][0], NVS, K, NVS);
-    if (static_cast<int>(threadIdx.x) < n) s.al[threadIdx.x] = expf(gv);
+    if constexpr (!VG)
+      if (static_cast<int>(threadIdx.x) < n) s.al[threadIdx.x] = expf(gv);
     if (static_cast<int>(threadIdx.x) < K) s.bet[threadIdx.x] = bv;
     __syncthreads();
-    // decays r_{e,i} (direct products), one (draft, entry) pair per thread, and gamma
-    for (int idx = threadIdx.x; idx < K * kRing; idx += kThreads) {
-      const int d = idx / kRing, i = idx - d * kRing, ee = len + d;
-      if (i <= ee) {
-        float r = 1.0f;
-        for (int l = i + 1; l <= ee; ++l) r *= s.al[l];
-        s.rt[d][i] = r;
-        if (i == 0) s.gam[d] = r * s.al[0];
+    if constexpr (VG) {
+      // per draft d: channel owners write r_{e,i} (descending direct products)
+      // and gamma_e, then the decay-weighted dots
+      //   kk[d][i] = beta_d <k_e, r_{e,i} * k_i>,  kq[d][i] = <q_d, r_{e,i} * k_i>
+      const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+#pragma unroll
+      for (int e = 0; e < kRing; ++e) lg[e] = expf(lg[e]);   // alpha per entry
+      for (int d = 0; d < K; ++d) {
+        const int ee = len + d;
+        if (static_cast<int>(threadIdx.x) < NK) {
+          float acc = 1.0f;
+#pragma unroll
+          for (int i = kRing - 1; i >= 0; --i) {
+            if (i <= ee) {
+              s.R[i][threadIdx.x] = acc;
+              acc *= lg[i];
+            }
+          }
+          s.G[d][threadIdx.x] = acc;
+        }
+        if (threadIdx.x == 0) s.gam[d] = 1.0f;
+        __syncthreads();
+        for (int pr = grp; pr < 2 * ee + 1; pr += kThreads / 16) {
+          const bool isq = pr >= ee;
+          const int i = isq ? pr - ee : pr;
+          const float* other = isq ? &s.W[2 * d + 1][0] : &s.K[ee][0];
+          float part = 0.0f;
+          for (int c = ln; c < NK; c += 16) part += s.K[i][c] * s.R[i][c] * other[c];
+          part = group_sum16(part);
+          if (ln == 0) {
+            if (isq) s.kq[d][i] = part;
+            else s.kk[d][i] = s.bet[d] * part;
+          }
+        }
+        __syncthreads();
       }
-    }
-    __syncthreads();
-    // dots per draft d (entry e = len + d), 16-lane groups
-    {
+      // matvec weights gamma_e * k_e and gamma_e * q_d
+      for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) {
+        const int d = idx / NK, c = idx - d * NK;
+        s.W[2 * d][c] *= s.G[d][c];
+        s.W[2 * d + 1][c] *= s.G[d][c];
+      }
+    } else {
+      // decays r_{e,i} (direct products), one (draft, entry) pair per thread, and gamma
+      for (int idx = threadIdx.x; idx < K * kRing; idx += kThreads) {
+        const int d = idx / kRing, i = idx - d * kRing, ee = len + d;
+        if (i <= ee) {
+          float r = 1.0f;
+          for (int l = i + 1; l <= ee; ++l) r *= s.al[l];
+          s.rt[d][i] = r;
+          if (i == 0) s.gam[d] = r * s.al[0];
+        }
+      }
+      __syncthreads();
+      // dots per draft d (entry e = len + d), 16-lane groups
       const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
       for (int pr = grp; pr < K * 2 * kRing; pr += kThreads / 16) {
         const int d = pr / (2 * kRing), rem = pr - d * 2 * kRing;
@@ -676,8 +737,15 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
     if (p.half == 0) {
       if (static_cast<int>(threadIdx.x) < K) {
         const int d = threadIdx.x, sl = slot_of(nck, len + d);
-        static_cast<float*>(a.rg)[p.st * kRing + sl] = a.g[d * gstride + p.st];
+        if constexpr (!VG) static_cast<float*>(a.rg)[p.st * kRing + sl] = a.g[d * gstride + p.st];
         static_cast<float*>(a.rbeta)[p.st * kRing + sl] = a.beta[d * gstride + p.st];
+      }
+      if constexpr (VG) {
+        float* rgw = static_cast<float*>(a.rg) + p.st * kRing * NK;
+        for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) {
+          const int d = idx / NK, c = idx - d * NK;
+          rgw[slot_of(nck, len + d) * NK + c] = a.g[(d * gstride + p.st) * NK + c];
+        }
       }
       if (p.h % a.vpk == 0) {
         TIN* rkw = static_cast<TIN*>(a.rk) + bk * kRing * NK;
@@ -697,16 +765,18 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
 // speculative commit (ReplaySSM), fold part: for each sequence listed by
 // commit_meta, S <- gamma_m S0 + sum_i r_{m,i} u_i k_i^T over its m committed
 // entries (u rows from the ring), one column slice per work item, over a
-// fixed grid (every workgroup leaves when the list is done)
+// fixed grid (every workgroup leaves when the list is done). VG (KDA):
+// S <- S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T with per-channel decays.
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV>
+template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
   constexpr int NS = gdn_slices<NV>();
   constexpr int NVS = NV / NS;
   constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
   constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
   constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
-  __shared__ GSmem<NK, NVS> s;
+  static_assert(!VG || NK <= kThreads, "one thread per key channel");
+  __shared__ GSmem<NK, NVS, VG> s;
   const int per = a.nv * NS;
   const int total = *a.work_count * per;
   float* ckp = static_cast<float*>(a.ck.data);
@@ -718,40 +788,69 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
     const size_t bk = static_cast<size_t>(it.b) * a.nqk + h / a.vpk;
     const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
     const float* ru = static_cast<const float*>(a.ru) + st * kRing * NV + c0;
-    const float* rg = static_cast<const float*>(a.rg) + st * kRing;
     RegChunks<TIN, CK> ck;
     RegChunks<float, CU> cu;
     ck.load(EntrySrc<TIN>{rk, rk, 0, it.nck, m, NK}, m, NK);
     cu.load(EntrySrc<float>{ru, ru, 0, it.nck, m, NV}, m, NVS);
-    const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
-    const float gv = rg[slot_of(it.nck, e)];
+    float gv = 0.0f;
+    float lg[VG ? kRing : 1];   // VG: log decays of the m entries, this thread's key channel
+    if constexpr (VG) {
+      const int c = static_cast<int>(threadIdx.x) < NK ? static_cast<int>(threadIdx.x) : NK - 1;
+      const float* rgc = static_cast<const float*>(a.rg) + st * kRing * NK + c;
+#pragma unroll
+      for (int e = 0; e < kRing; ++e) lg[e] = rgc[slot_of(it.nck, e < m ? e : m - 1) * NK];
+    } else {
+      const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+      gv = static_cast<const float*>(a.rg)[st * kRing + slot_of(it.nck, e)];
+    }
     GSlice<NK, NV, NVS> raw;
     raw.issue(ckp, st, c0);
     ck.to_lds(&s.K[0][0], NK, m, NK);
     cu.to_lds(&s.U[0][0], NVS, m, NVS);
-    if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(gv);
+    if constexpr (!VG)
+      if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(gv);
     __syncthreads();
-    if (static_cast<int>(threadIdx.x) < m) {
-      float w = 1.0f;
+    if constexpr (VG) {
+      // channel owners: k rows times r_{m,i} (descending direct products), gamma_m
+      if (static_cast<int>(threadIdx.x) < NK) {
+        float acc = 1.0f;
 #pragma unroll
-      for (int l = 1; l < kRing; ++l) w *= (l > static_cast<int>(threadIdx.x) && l < m) ? s.al[l] : 1.0f;
-      s.rr[threadIdx.x] = w;
+        for (int i = kRing - 1; i >= 0; --i) {
+          if (i < m) {
+            s.K[i][threadIdx.x] *= acc;
+            acc *= expf(lg[i]);
+          }
+        }
+        s.gv[threadIdx.x] = acc;
+      }
+    } else {
+      if (static_cast<int>(threadIdx.x) < m) {
+        float w = 1.0f;
+#pragma unroll
+        for (int l = 1; l < kRing; ++l) w *= (l > static_cast<int>(threadIdx.x) && l < m) ? s.al[l] : 1.0f;
+        s.rr[threadIdx.x] = w;
+      }
+      if (threadIdx.x == 0) {
+        float gm = 1.0f;
+#pragma unroll
+        for (int l = 0; l < kRing; ++l) gm *= l < m ? s.al[l] : 1.0f;
+        s.gam = gm;
+      }
+      __syncthreads();
+      for (int v = threadIdx.x; v < NVS; v += kThreads)
+#pragma unroll
+        for (int i = 0; i < kRing; ++i)
+          if (i < m) s.U[i][v] *= s.rr[i];
     }
-    if (threadIdx.x == 0) {
-      float gm = 1.0f;
-#pragma unroll
-      for (int l = 0; l < kRing; ++l) gm *= l < m ? s.al[l] : 1.0f;
-      s.gam = gm;
-    }
-    __syncthreads();
-    for (int v = threadIdx.x; v < NVS; v += kThreads)
-#pragma unroll
-      for (int i = 0; i < kRing; ++i)
-        if (i < m) s.U[i][v] *= s.rr[i];
     __syncthreads();
     RegTile<4, NK, NVS> S;
     raw.decode(S);
-    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    if constexpr (VG) {
+      tile_scale_rows(S, s.gv);
+      tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    } else {
+      tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+    }
     GSlice<NK, NV, NVS>::store(ckp, st, c0, S);
     __syncthreads();
   }
@@ -764,8 +863,9 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int NK, int NVS, int KQ>
+template <int NK, int NVS, int KQ, bool VG>
 struct GConvSpecSmem {
+  float AL[VG ? KQ : 1][NK];   // VG: the channel decays of each draft
   float W[2 * KQ][NK];   // k_d, q_d
   float V[KQ][NVS];      // v_d, own columns
   float out[2][NVS];     // S k_d, S q_d
@@ -779,14 +879,15 @@ struct GConvSpecSmem {
 // One workgroup per column slice, as in the replay kernels (the delta rule is
 // column-independent in the stored layout): the whole 128 x 128 state in one
 // workgroup needs 132 registers per lane here and runs at 3 waves per SIMD.
-template <typename TIN, int NK, int NV, int KQ>
+template <typename TIN, int NK, int NV, int KQ, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_conv_spec_kernel(GDNArgs a) {
   constexpr int NS = gdn_slices<NV>();
   constexpr int NVS = NV / NS;
   constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
   constexpr int CD = (KQ * NK / VK + kThreads - 1) / kThreads;
   constexpr int CV = (KQ * NVS / VK + kThreads - 1) / kThreads;
-  __shared__ GConvSpecSmem<NK, NVS, KQ> s;
+  constexpr int CA = VG ? (KQ * NK / 4 + kThreads - 1) / kThreads : 1;
+  __shared__ GConvSpecSmem<NK, NVS, KQ, VG> s;
   const GPtrs p = gdn_tile<NV, NS>(a);
   const int K = a.K;
   const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
@@ -801,19 +902,29 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_spec_kernel(GDNArgs a) {
   cq.load(EntrySrc<TIN>{iq, iq, kstride, 0, 0, NK}, K, NK);
   cd.load(EntrySrc<TIN>{ik, ik, kstride, 0, 0, NK}, K, NK);
   cv.load(EntrySrc<TIN>{iv, iv, vstride, 0, 0, NVS}, K, NVS);
+  RegChunks<float, CA> ca;
+  if constexpr (VG) {
+    const float* ig = a.g + p.st * NK;
+    ca.load(EntrySrc<float>{ig, ig, gstride * NK, 0, 0, NK}, K, NK);
+  }
   const int dd = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
-  const float gv = a.g[dd * gstride + p.st], bv = a.beta[dd * gstride + p.st];
+  const float gv = VG ? 0.0f : a.g[dd * gstride + p.st], bv = a.beta[dd * gstride + p.st];
   float* ck = static_cast<float*>(a.ck.data);
   GSlice<NK, NV, NVS> raw;
   raw.issue(ck, p.st, p.c0);
   cd.to_lds(&s.W[0][0], 2 * NK, K, NK);
   cq.to_lds(&s.W[1][0], 2 * NK, K, NK);
   cv.to_lds(&s.V[0][0], NVS, K, NVS);
+  if constexpr (VG) ca.to_lds(&s.AL[0][0], NK, K, NK);
   if (static_cast<int>(threadIdx.x) < K) {
-    s.al[threadIdx.x] = expf(gv);
+    s.al[threadIdx.x] = VG ? 1.0f : expf(gv);   // VG: the decay is applied to the rows
     s.bet[threadIdx.x] = bv;
   }
   __syncthreads();
+  if constexpr (VG) {
+    for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) (&s.AL[0][0])[idx] = expf((&s.AL[0][0])[idx]);
+    __syncthreads();
+  }
   {
     const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
     for (int d = grp; d < K; d += kThreads / 16) {
@@ -826,6 +937,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_spec_kernel(GDNArgs a) {
   RegTile<4, NK, NVS> S;
   raw.decode(S);
   for (int d = 0; d < K; ++d) {
+    if constexpr (VG) tile_scale_rows(S, &s.AL[d][0]);        // S Diag(alpha_d)
     tile_matvec<2>(S, &s.W[2 * d][0], NK, s.red, &s.out[0][0]);   // S k_d, S q_d (barriers inside)
     const float al = s.al[d], be = s.bet[d], kq = s.kq[d];
     for (int v = threadIdx.x; v < NVS; v += kThreads) {
@@ -878,18 +990,32 @@ struct gdn_step_kernels {
   }
 };
 
-template <typename TIN, int NK, int NV>
+template <typename TIN, int NK, int NV, bool VG>
 void gdn_spec_append(const GDNArgs& a, int grid, hipStream_t st) {
-  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2><<<grid, kThreads, 0, st>>>(a);
-  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4><<<grid, kThreads, 0, st>>>(a);
-  else gdn_spec_append_kernel<TIN, NK, NV, 8><<<grid, kThreads, 0, st>>>(a);
+  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2, VG><<<grid, kThreads, 0, st>>>(a);
+  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4, VG><<<grid, kThreads, 0, st>>>(a);
+  else gdn_spec_append_kernel<TIN, NK, NV, 8, VG><<<grid, kThreads, 0, st>>>(a);
 }
 
-template <typename TIN, int NK, int NV>
+template <typename TIN, int NK, int NV, bool VG>
 void gdn_conv_spec(const GDNArgs& a, int grid, hipStream_t st) {
-  if (a.K <= 2) gdn_conv_spec_kernel<TIN, NK, NV, 2><<<grid, kThreads, 0, st>>>(a);
-  else if (a.K <= 4) gdn_conv_spec_kernel<TIN, NK, NV, 4><<<grid, kThreads, 0, st>>>(a);
-  else gdn_conv_spec_kernel<TIN, NK, NV, 8><<<grid, kThreads, 0, st>>>(a);
+  if (a.K <= 2) gdn_conv_spec_kernel<TIN, NK, NV, 2, VG><<<grid, kThreads, 0, st>>>(a);
+  else if (a.K <= 4) gdn_conv_spec_kernel<TIN, NK, NV, 4, VG><<<grid, kThreads, 0, st>>>(a);
+  else gdn_conv_spec_kernel<TIN, NK, NV, 8, VG><<<grid, kThreads, 0, st>>>(a);
+}
+
+template <int NK, int NV, bool VG>
+void gdn_spec_kernels(GDNOp op, bool bf, const GDNArgs& a, int grid, hipStream_t st) {
+  if (op == GDNOp::SpecAppend) {
+    if (bf) gdn_spec_append<bf16, NK, NV, VG>(a, grid, st);
+    else gdn_spec_append<float, NK, NV, VG>(a, grid, st);
+  } else if (op == GDNOp::ConvSpec) {
+    if (bf) gdn_conv_spec<bf16, NK, NV, VG>(a, grid, st);
+    else gdn_conv_spec<float, NK, NV, VG>(a, grid, st);
+  } else {
+    if (bf) gdn_commit_fold_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    else gdn_commit_fold_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+  }
 }
 
 template <int NK, int NV>
@@ -917,20 +1043,17 @@ void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
       else gdn_step_kernels<NK, NV, false>::auto_step(bf, a, l.grid, st);
       break;
     case GDNOp::SpecAppend:
-      if (bf) gdn_spec_append<bf16, NK, NV>(a, l.grid, st);
-      else gdn_spec_append<float, NK, NV>(a, l.grid, st);
+    case GDNOp::ConvSpec:
+      if (l.vg) gdn_spec_kernels<NK, NV, true>(op, bf, a, l.grid, st);
+      else gdn_spec_kernels<NK, NV, false>(op, bf, a, l.grid, st);
       break;
     case GDNOp::CommitFold: {
       const int items = l.grid * gdn_slices<NV>();   // upper bound of listed work items
       const int grid = items < 2048 ? items : 2048;
-      if (bf) gdn_commit_fold_kernel<bf16, NK, NV><<<grid, kThreads, 0, st>>>(a);
-      else gdn_commit_fold_kernel<float, NK, NV><<<grid, kThreads, 0, st>>>(a);
+      if (l.vg) gdn_spec_kernels<NK, NV, true>(op, bf, a, grid, st);
+      else gdn_spec_kernels<NK, NV, false>(op, bf, a, grid, st);
       break;
     }
-    case GDNOp::ConvSpec:
-      if (bf) gdn_conv_spec<bf16, NK, NV>(a, l.grid, st);
-      else gdn_conv_spec<float, NK, NV>(a, l.grid, st);
-      break;
     case GDNOp::Restore:
       gdn_restore_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a);
       break;

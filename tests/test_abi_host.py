@@ -87,7 +87,7 @@ def test_reset_slots_host_checks():
 
 def test_kda_layout_sizes():
     """Kimi Delta Attention: the GDN layout with a dk-wide gate per ring entry;
-    speculative configs are refused."""
+    speculative configs get the GDN snapshot area (conventional mode)."""
     kw = dict(n_qk_heads=16, n_v_heads=32, head_k_dim=128, head_v_dim=128)
     _, G = rs.rs_init(rs.make_config(rs.RS_GDN, 4, **kw))
     _, K = rs.rs_init(rs.make_config(rs.RS_KDA, 4, **kw))
@@ -95,8 +95,9 @@ def test_kda_layout_sizes():
     gdn_g = G.ring_beta_off - G.ring_g_off
     kda_g = K.ring_beta_off - K.ring_g_off
     assert gdn_g >= 4 * 32 * 16 * 4 and kda_g >= 4 * 32 * 16 * 128 * 4 and kda_g < 4 * 32 * 16 * 128 * 4 + 256
-    st, _ = rs.rs_init(rs.make_config(rs.RS_KDA, 4, max_draft=4, **kw), raise_on_error=False)
-    assert st == rs.RS_E_MODE
+    _, Ks = rs.rs_init(rs.make_config(rs.RS_KDA, 4, max_draft=4, mode=rs.RS_CONVENTIONAL, **kw))
+    _, Gs = rs.rs_init(rs.make_config(rs.RS_GDN, 4, max_draft=4, mode=rs.RS_CONVENTIONAL, **kw))
+    assert Ks.snap_bytes == Gs.snap_bytes == 4 * K.ckpt_bytes
     st, _ = rs.rs_init(rs.make_config(4, 4, **kw), raise_on_error=False)
     assert st == rs.RS_E_ARG
 

@@ -1,5 +1,6 @@
-"""GPU parity of Gated DeltaNet speculative decoding (append / verify, commit
-with folds, and the snapshot baseline) against the fp64 oracle: verify outputs
+"""GPU parity of Gated DeltaNet and Kimi Delta Attention speculative decoding
+(append / verify, commit with folds, and the snapshot baseline) against the
+fp64 oracle: verify outputs
 against both the same-method oracle and stepping the drafts with snapshots,
 counters bit-exact, draft records bit-exact in the ring, cached u rows against
 the oracle's triangular solve, device error bits."""
@@ -9,7 +10,7 @@ import torch
 
 import ssm_decode_checkpoint_amd as rs
 import workloads as W
-from oracle import decode, gdn
+from oracle import decode, gdn, kda
 from gpu_harness import (gdn_drafts_dev, gdn_layer, gdn_tok_dev, load_state_f32, read_meta, read_state_f32, rel_l2,
                          require_gpu, y_buf)
 
@@ -30,6 +31,10 @@ def _in_bits(arr, in_dtype):
     return W.bf16_bits(arr).view(np.int16) if in_dtype == "bf16" else arr.view(np.int32)
 
 
+def _rule(w):
+    return kda if w.gate == "channel" else gdn
+
+
 def _check_ring(layer, bufs, same, w, seqs):
     """Every live slot's record bits, and its u row against the oracle's solve over
     the live entries from the oracle's checkpoint."""
@@ -45,7 +50,7 @@ def _check_ring(layer, bufs, same, w, seqs):
             for n in ("g", "beta"):
                 assert np.array_equal(rings[n][b, :, s], e[n][0].astype(np.float32).view(np.int32)), (b, s, n)
         if ents:
-            us = gdn.ut_solve(same.ckpt[i:i + 1], ents)
+            us = _rule(w).ut_solve(same.ckpt[i:i + 1], ents)
             for s, u in zip(slots, us):
                 worst = max(worst, rel_l2(ug[b, :, s], u[0]))
     return worst
@@ -57,8 +62,8 @@ def _spec_run(w, rounds, Ks, seqs=None, t0=3000):
     S0 = W.gdn_init_states(w, range(w.batch))
     layer, bufs = gdn_layer(w)
     load_state_f32(layer, bufs, S0)
-    exact = decode.GDNConventional(S0[seqs])
-    same = decode.GDNReplay(S0[seqs], max_draft=w.max_draft)
+    exact = decode.GDNConventional(S0[seqs], rule=_rule(w))
+    same = decode.GDNReplay(S0[seqs], max_draft=w.max_draft, rule=_rule(w))
     worst_same = worst_exact = worst_u = 0.0
     t = t0
     folds = 0
@@ -115,14 +120,42 @@ def test_qwen_batch256_sampled():
     assert folds > 0
 
 
+@pytest.mark.parametrize("K,kmax", [(4, 4), (2, 4), (8, 8)])
+def test_kda_tiny(K, kmax):
+    """Kimi Delta Attention (a decay per key channel), dk = dv = 16."""
+    w = W.TINY_KDA.with_(max_draft=kmax, init_std=0.4, seed=170 + K)
+    ws, we, wu, wc, folds = _spec_run(w, 24, [K])
+    assert ws <= 1e-5 and we <= 1e-5 and wu <= 1e-5 and wc <= 1e-5, (ws, we, wu, wc)
+    assert folds > 0
+
+
+def test_kda_mixed_draft_counts_two_slices():
+    w = W.TINY_KDA.with_(batch=3, n_qk=2, n_v=4, dk=128, dv=128, in_dtype="bf16", init_std=0.3, max_draft=4,
+                         seed=175)
+    ws, we, wu, wc, folds = _spec_run(w, 20, [1, 2, 3, 4])
+    assert ws <= 1e-5 and we <= 1e-5 and wu <= 1e-5 and wc <= 1e-5, (ws, we, wu, wc)
+    assert folds > 0
+
+
+def test_kda_batch256_sampled():
+    """KDA on the Qwen-style shapes at batch 256 with 4 drafts, 8 sequences checked."""
+    w = W.KDA_B256.with_(max_draft=4)
+    seqs = [0, 37, 74, 111, 148, 185, 222, 255]
+    ws, we, wu, wc, folds = _spec_run(w, 10, [4], seqs=seqs)
+    print(f"kda spec b256: vs same-method {ws:.2e}, vs snapshots {we:.2e}, u rows {wu:.2e}, checkpoint {wc:.2e}")
+    assert ws <= 1e-5 and we <= 1e-5 and wu <= 1e-5 and wc <= 1e-5
+    assert folds > 0
+
+
+@pytest.mark.parametrize("gate", ["head", "channel"])
 @pytest.mark.parametrize("K", [2, 4])
-def test_snapshot_baseline(K):
-    w = W.TINY_GDN.with_(batch=3, n_qk=2, n_v=4, dk=128, dv=128, init_std=0.3, max_draft=4, seed=150)
+def test_snapshot_baseline(K, gate):
+    w = W.TINY_GDN.with_(batch=3, n_qk=2, n_v=4, dk=128, dv=128, init_std=0.3, max_draft=4, seed=150, gate=gate)
     gp = W.gdn_params(w)
     S0 = W.gdn_init_states(w, range(w.batch))
     layer, bufs = gdn_layer(w, mode=rs.RS_CONVENTIONAL)
     load_state_f32(layer, bufs, S0)
-    exact = decode.GDNConventional(S0)
+    exact = decode.GDNConventional(S0, rule=_rule(w))
     worst = 0.0
     for r in range(10):
         drafts = [W.gdn_step(w, 500 + r * K + d, range(w.batch), gp) for d in range(K)]

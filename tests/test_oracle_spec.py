@@ -1,5 +1,5 @@
-"""Pins for speculative rounds (Mamba-2 and Gated DeltaNet) and the low-precision
-read copy in the oracle.
+"""Pins for speculative rounds (Mamba-2, Gated DeltaNet and Kimi Delta
+Attention) and the low-precision read copy in the oracle.
 
 * commit(k) equals replaying the first k drafts: the replay driver's verify
   outputs and its effective state after each commit equal those of plain
@@ -11,9 +11,10 @@ read copy in the oracle.
   copy is really what the non-flush steps read).
 """
 import numpy as np
+import pytest
 
 import workloads as W
-from oracle import decode
+from oracle import decode, gdn, kda
 
 
 def _spec_case(batch=3, K=4, rounds=24):
@@ -80,20 +81,23 @@ def test_read_copy_isolation():
     assert differ > 1e-4
 
 
-def _gdn_spec_case(batch=3, kmax=4):
-    w = W.TINY_GDN.with_(batch=batch, seed=15, init_std=0.3)
+def _gdn_spec_case(gate, batch=3, kmax=4):
+    base = W.TINY_KDA if gate == "channel" else W.TINY_GDN
+    w = base.with_(batch=batch, seed=15, init_std=0.3)
     gp = W.gdn_params(w)
     S0 = W.gdn_init_states(w, range(batch))
-    return w, gp, S0, kmax
+    return w, gp, S0, kmax, (kda if gate == "channel" else gdn)
 
 
-def test_gdn_commit_equals_replaying_accepted_drafts():
-    """Gated DeltaNet: verify outputs from checkpoint + buffer equal stepping the
-    drafts with snapshots; after each commit the effective state equals the state
-    after the accepted drafts; rejected drafts leave the checkpoint bits alone."""
-    w, gp, S0, kmax = _gdn_spec_case()
-    conv = decode.GDNConventional(S0)
-    rep = decode.GDNReplay(S0, max_draft=kmax)
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_gdn_commit_equals_replaying_accepted_drafts(gate):
+    """Gated DeltaNet (per-head gate) and KDA (per-channel gate): verify outputs
+    from checkpoint + buffer equal stepping the drafts with snapshots; after each
+    commit the effective state equals the state after the accepted drafts;
+    rejected drafts leave the checkpoint bits alone."""
+    w, gp, S0, kmax, rule = _gdn_spec_case(gate)
+    conv = decode.GDNConventional(S0, rule=rule)
+    rep = decode.GDNReplay(S0, max_draft=kmax, rule=rule)
     folds = 0
     t = 0
     for rnd in range(30):
@@ -117,10 +121,11 @@ def test_gdn_commit_equals_replaying_accepted_drafts():
     assert rep.ring.err == [0] * w.batch
 
 
-def test_gdn_plain_steps_continue_after_spec():
-    w, gp, S0, kmax = _gdn_spec_case(batch=2)
-    conv = decode.GDNConventional(S0)
-    rep = decode.GDNReplay(S0, max_draft=kmax)
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_gdn_plain_steps_continue_after_spec(gate):
+    w, gp, S0, kmax, rule = _gdn_spec_case(gate, batch=2)
+    conv = decode.GDNConventional(S0, rule=rule)
+    rep = decode.GDNReplay(S0, max_draft=kmax, rule=rule)
     for rnd in range(6):
         drafts = [W.gdn_step(w, rnd * kmax + d, range(w.batch), gp) for d in range(kmax)]
         acc = W.accepted_counts(w.seed, rnd, w.batch, kmax)
