@@ -380,6 +380,21 @@ def bench_serve(args, torch, rs):
     total, per = tm.run(window, args.steps, args.warmup, RING)
     ntok = B * RING * args.steps
     steps_ms = per.reshape(-1)
+    # prefix cache: save 64 mid-window sequences into a 64-slot cache of the same
+    # layer and restore them into other slots (checkpoint rows + ring + counters)
+    nc = 64
+    cl, cb = _m2_layer(rs, w, nc, rs.RS_REPLAY, dev)
+    src = torch.arange(0, B, B // nc, dtype=torch.int32, device=dev)[:nc]
+    slots = torch.arange(nc, dtype=torch.int32, device=dev)
+    dst = (src + 1) % B
+
+    def cache_pass(ev):
+        _marked(ev, 0, tm.stream, lambda: rs.rs_copy_slots(layer, bufs, src, cl, cb, slots, nc))
+        _marked(ev, 1, tm.stream, lambda: rs.rs_copy_slots(cl, cb, slots, layer, bufs, dst, nc))
+
+    ctot, cper = tm.run(cache_pass, 4, 1, 2)
+    per_seq = (layer.ckpt_bytes + layer.ring_bytes) / B
+    copy_ms = float(cper.mean())
     return {"metric": "continuous-batching decode tokens/s at batch 256, staggered fills (self-scheduling step)",
             "value": ntok / (total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": total / args.steps, "higher_is_better": True,
@@ -388,7 +403,12 @@ def bench_serve(args, torch, rs):
                        "headdim": w.headdim, "dstate": w.dstate, "fills": "sequence b at fill (15 - b mod 16) "
                        "after the staggering phase", "step": "16 self-scheduling steps per timed window"},
             "step_ms": {"mean": float(steps_ms.mean()), "max": float(steps_ms.max()), "min": float(steps_ms.min()),
-                        "p99": float(np.percentile(steps_ms, 99))}}
+                        "p99": float(np.percentile(steps_ms, 99))},
+            "prefix_cache": {"seqs_per_copy": nc, "bytes_per_seq": per_seq, "save_ms": float(cper[:, 0].mean()),
+                             "restore_ms": float(cper[:, 1].mean()),
+                             "copy_gbs": 2 * nc * per_seq / (copy_ms * 1e-3) / 1e9,
+                             "note": "one call copies the sequences' checkpoint rows, 16 ring slots and counters; "
+                                     "GB/s counts read + write"}}
 
 
 def bench_gdn(args, torch, rs, w=W.GDN_QWEN):

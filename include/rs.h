@@ -250,6 +250,26 @@ rs_status rs_step(const rs_layer* L, const rs_buffers* buf, const rs_inputs* in,
 rs_status rs_reset_slots(const rs_layer* L, const rs_buffers* buf, const int32_t* seqs, int32_t count,
                          void* stream);
 
+/* Copy whole sequence states (prefix caching, forks). The state of a sequence
+ * at any token is its checkpoint, its buffer entries and its counters, with no
+ * per-token snapshot (sitech.ge ReplaySSM page, "Reducing state traffic and
+ * simplifying rollback"), so saving it, restoring it or forking it is a copy
+ * of those regions: for i < count, the state of sequence src_seqs[i] of `src`
+ * (layer Ls) replaces that of sequence dst_seqs[i] of `dst` (layer Ld) —
+ * checkpoint rows with their scales, read copy, all 16 ring slots of every
+ * ring array (GDN / KDA solved rows u included), and the counters n_ckpt, len,
+ * nd, err (the arrival count stays). A restored sequence continues exactly as
+ * the saved one would have: same outputs, same flush schedule. Ls and Ld must
+ * have identical configurations except batch (src and dst may be the same
+ * buffers of one layer, e.g. a cache of B_cache sequences beside a decode
+ * batch); pairs with an index outside its layer's batch are skipped.
+ * src_seqs, dst_seqs: device int32[count], count <= 65535. Destinations must
+ * be distinct and must not be sources of the same call (those copies would
+ * race). Conventional mode copies the checkpoint (live state) only. */
+rs_status rs_copy_slots(const rs_layer* Ls, const rs_buffers* src, const int32_t* src_seqs,
+                        const rs_layer* Ld, const rs_buffers* dst, const int32_t* dst_seqs,
+                        int32_t count, void* stream);
+
 /* Speculative append (same page, "Reducing state traffic and simplifying
  * rollback": draft inputs enter the buffer until verification; verification
  * reads outputs only, as a small matrix product, without forming

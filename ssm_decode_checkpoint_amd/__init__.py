@@ -28,7 +28,8 @@ RS_NONE, RS_F32, RS_BF16, RS_F16, RS_FP8E4M3, RS_NVFP4 = 0, 1, 2, 3, 4, 5
 RS_ERR_FULL, RS_ERR_OVERFLOW, RS_ERR_COMMIT, RS_ERR_PENDING = 1, 2, 4, 8
 
 EXPORTS = ("rs_init", "rs_step_conventional", "rs_step_nonflush", "rs_step_flush", "rs_step", "rs_spec_append",
-           "rs_spec_commit", "rs_requant_read_copy", "rs_reset_slots", "rs_status_string", "rs_version")
+           "rs_spec_commit", "rs_requant_read_copy", "rs_reset_slots", "rs_copy_slots", "rs_status_string",
+           "rs_version")
 
 
 class RsConfig(C.Structure):
@@ -87,6 +88,8 @@ def lib() -> C.CDLL:
         L.rs_spec_commit.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, P(RsParams), C.c_void_p]
         L.rs_requant_read_copy.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p]
         L.rs_reset_slots.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, C.c_int32, C.c_void_p]
+        L.rs_copy_slots.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, P(RsLayer), P(RsBuffers), C.c_void_p,
+                                    C.c_int32, C.c_void_p]
         for name in EXPORTS:
             if name not in ("rs_status_string", "rs_version"):
                 getattr(L, name).restype = C.c_int32
@@ -207,6 +210,13 @@ def rs_step(layer: RsLayer, bufs: Buffers, inputs: Dict[str, object], A, D, y, s
 def rs_reset_slots(layer: RsLayer, bufs: Buffers, seqs, count: int, stream=None, raise_on_error: bool = True) -> int:
     st = lib().rs_reset_slots(C.byref(layer), C.byref(bufs.c()), _ptr(seqs), int(count), _stream(stream))
     return _check("rs_reset_slots", st, raise_on_error)
+
+
+def rs_copy_slots(src_layer: RsLayer, src: Buffers, src_seqs, dst_layer: RsLayer, dst: Buffers, dst_seqs, count: int,
+                  stream=None, raise_on_error: bool = True) -> int:
+    st = lib().rs_copy_slots(C.byref(src_layer), C.byref(src.c()), _ptr(src_seqs), C.byref(dst_layer),
+                             C.byref(dst.c()), _ptr(dst_seqs), int(count), _stream(stream))
+    return _check("rs_copy_slots", st, raise_on_error)
 
 
 def rs_spec_append(layer: RsLayer, bufs: Buffers, drafts: Dict[str, object], K: int, A, D, y, stream=None,

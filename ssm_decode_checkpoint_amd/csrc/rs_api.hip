@@ -384,6 +384,102 @@ rs_status rs_reset_slots(const rs_layer* L, const rs_buffers* buf, const int32_t
   return launched();
 }
 
+namespace {
+
+// Per-sequence regions of a layer's buffers, in the order rs_copy_slots copies them.
+struct SeqRegion {
+  int buf;           // 0 checkpoint, 1 ring, 2 read copy
+  uint64_t off, per;
+};
+
+int seq_regions(const rs_layer* L, SeqRegion* out) {
+  const rs_config& c = L->cfg;
+  const uint64_t h = static_cast<uint64_t>(L->heads);
+  const uint64_t rc = static_cast<uint64_t>(L->rows) * L->cols;
+  const uint64_t sin = c.in_dtype == RS_BF16 ? 2 : 4;
+  int n = 0;
+  auto add = [&](int b, uint64_t off, uint64_t per) { out[n++] = SeqRegion{b, off, per}; };
+  switch (c.ckpt_dtype) {
+    case RS_F32: add(0, 0, h * rc * 4); break;
+    case RS_F16: add(0, 0, h * rc * 2); break;
+    case RS_FP8E4M3:
+      add(0, 0, h * rc);
+      add(0, L->ck_scale_off, h * 4);
+      break;
+    default:
+      add(0, 0, h * rc / 2);
+      add(0, L->ck_nv_scale_off, h * rc / 16);
+      add(0, L->ck_nv_tscale_off, h * 4);
+      break;
+  }
+  if (c.mode != RS_REPLAY) return n;
+  if (c.kind == RS_MAMBA2) {
+    add(1, L->ring_x_off, static_cast<uint64_t>(c.nheads) * kRing * c.headdim * sin);
+    add(1, L->ring_B_off, static_cast<uint64_t>(c.ngroups) * kRing * c.dstate * sin);
+    add(1, L->ring_C_off, static_cast<uint64_t>(c.ngroups) * kRing * c.dstate * sin);
+    add(1, L->ring_dt_off, static_cast<uint64_t>(c.nheads) * kRing * sin);
+  } else {
+    const uint64_t gw = c.kind == RS_KDA ? static_cast<uint64_t>(c.head_k_dim) : 1;
+    add(1, L->ring_q_off, static_cast<uint64_t>(c.n_qk_heads) * kRing * c.head_k_dim * sin);
+    add(1, L->ring_k_off, static_cast<uint64_t>(c.n_qk_heads) * kRing * c.head_k_dim * sin);
+    add(1, L->ring_v_off, static_cast<uint64_t>(c.n_v_heads) * kRing * c.head_v_dim * sin);
+    add(1, L->ring_g_off, static_cast<uint64_t>(c.n_v_heads) * kRing * gw * 4);
+    add(1, L->ring_beta_off, static_cast<uint64_t>(c.n_v_heads) * kRing * 4);
+    add(1, L->ring_u_off, static_cast<uint64_t>(c.n_v_heads) * kRing * c.head_v_dim * 4);
+  }
+  if (c.read_copy == RS_NVFP4) {
+    add(2, 0, h * rc / 2);
+    add(2, L->nv_scale_off, h * rc / 16);
+    add(2, L->nv_tscale_off, h * 4);
+  }
+  return n;
+}
+
+}  // namespace
+
+rs_status rs_copy_slots(const rs_layer* Ls, const rs_buffers* src, const int32_t* src_seqs, const rs_layer* Ld,
+                        const rs_buffers* dst, const int32_t* dst_seqs, int32_t count, void* stream) {
+  if (rs_status s = check_layer(Ls)) return s;
+  if (rs_status s = check_layer(Ld)) return s;
+  rs_config cs = Ls->cfg;
+  cs.batch = Ld->cfg.batch;
+  if (std::memcmp(&cs, &Ld->cfg, sizeof(rs_config)) != 0) return RS_E_ARG;
+  if (count < 0 || count > 65535 || (count > 0 && (!src_seqs || !dst_seqs))) return RS_E_ARG;
+  if (!src || !dst || !src->ckpt || !dst->ckpt) return RS_E_ARG;
+  const bool replay = Ls->cfg.mode == RS_REPLAY;
+  if (replay && (!src->ring || !dst->ring || !src->meta || !dst->meta)) return RS_E_ARG;
+  if (Ls->cfg.read_copy == RS_NVFP4 && (!src->read_copy || !dst->read_copy)) return RS_E_ARG;
+  const void* ptrs[8] = {src->ckpt, dst->ckpt, src->ring, dst->ring, src->read_copy, dst->read_copy, src->meta,
+                         dst->meta};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return RS_E_ALIGN;
+  if (count == 0) return RS_OK;
+  SeqRegion reg[kMaxCopyRegions], dreg[kMaxCopyRegions];
+  const int nreg = seq_regions(Ls, reg);
+  seq_regions(Ld, dreg);   // same regions and sizes; offsets of the other batch
+  CopyArgs a{};
+  uint64_t total = 0;
+  for (int i = 0; i < nreg; ++i) {
+    const char* sb = static_cast<const char*>(reg[i].buf == 0 ? src->ckpt : reg[i].buf == 1 ? src->ring
+                                                                                              : src->read_copy);
+    char* db = static_cast<char*>(reg[i].buf == 0 ? dst->ckpt : reg[i].buf == 1 ? dst->ring : dst->read_copy);
+    if (reg[i].per % 4 != 0) return RS_E_UNSUPPORTED;
+    a.r[i] = CopyRegion{sb + reg[i].off, db + dreg[i].off, reg[i].per};
+    total += reg[i].per;
+  }
+  a.nreg = nreg;
+  a.count = count;
+  a.src_batch = Ls->cfg.batch;
+  a.dst_batch = Ld->cfg.batch;
+  a.src_seqs = src_seqs;
+  a.dst_seqs = dst_seqs;
+  a.src_meta = replay ? static_cast<const rs_meta*>(src->meta) : nullptr;
+  a.dst_meta = replay ? static_cast<rs_meta*>(dst->meta) : nullptr;
+  const uint64_t bpp = (total + 16383) / 16384;   // about four 16-byte chunks per thread
+  copy_slots(a, static_cast<int>(bpp < 1 ? 1 : bpp > 1024 ? 1024 : bpp), static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inputs* drafts, int32_t K,
                          const rs_params* prm, float* y, void* stream) {
   if (rs_status s = check_layer(L)) return s;

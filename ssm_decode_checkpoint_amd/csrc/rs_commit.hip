@@ -1,4 +1,7 @@
-// Speculative commit, counter part, for every layer kind (sitech.ge ReplaySSM
+// Per-sequence operations shared by every layer kind: the speculative commit's
+// counter part, slot reuse and slot copies (prefix caching, forks).
+//
+// Speculative commit, counter part (sitech.ge ReplaySSM
 // page, "Reducing state traffic and simplifying rollback": the accepted prefix
 // of the drafts is committed by moving the buffer pointer, no snapshot is
 // saved or restored). Per sequence: len += accepted, nd = 0; a commit that
@@ -87,6 +90,44 @@ __global__ __launch_bounds__(256) void reset_slots_kernel(rs_meta* meta, int bat
 
 void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, hipStream_t st) {
   reset_slots_kernel<<<(count + 255) / 256, 256, 0, st>>>(meta, batch, seqs, count);
+}
+
+// Prefix caching and forks: the state of a sequence at any token is its
+// checkpoint, its buffer entries and its counters (sitech.ge ReplaySSM page,
+// "Reducing state traffic and simplifying rollback": no per-token snapshot is
+// kept), so saving or restoring it is a plain copy of those regions. One
+// row of the grid per listed pair, blockIdx.x strides over the bytes.
+__global__ __launch_bounds__(256) void copy_slots_kernel(CopyArgs a) {
+  const int i = blockIdx.y;
+  const int s = a.src_seqs[i], d = a.dst_seqs[i];
+  if (s < 0 || s >= a.src_batch || d < 0 || d >= a.dst_batch) return;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (int r = 0; r < a.nreg; ++r) {
+    const CopyRegion g = a.r[r];
+    const char* src = g.src + static_cast<uint64_t>(s) * g.per;
+    char* dst = g.dst + static_cast<uint64_t>(d) * g.per;
+    if (g.per % 16 == 0) {
+      const uint64_t n = g.per / 16;
+      for (uint64_t k = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; k < n; k += stride)
+        nt_store(nt_load(reinterpret_cast<const uint4*>(src) + k), reinterpret_cast<uint4*>(dst) + k);
+    } else {
+      const uint64_t n = g.per / 4;
+      for (uint64_t k = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; k < n; k += stride)
+        reinterpret_cast<uint32_t*>(dst)[k] = reinterpret_cast<const uint32_t*>(src)[k];
+    }
+  }
+  if (a.dst_meta && blockIdx.x == 0 && threadIdx.x == 0) {
+    const rs_meta* m = a.src_meta + s;
+    rs_meta* o = a.dst_meta + d;
+    o->n_ckpt = m->n_ckpt;
+    o->len = m->len;
+    o->nd = m->nd;
+    o->err = m->err;
+  }
+}
+
+void copy_slots(const CopyArgs& a, int blocks_per_pair, hipStream_t st) {
+  copy_slots_kernel<<<dim3(blocks_per_pair, a.count), 256, 0, st>>>(a);
 }
 
 }  // namespace rs

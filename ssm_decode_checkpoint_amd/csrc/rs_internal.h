@@ -139,6 +139,26 @@ void commit_meta(const CommitArgs& a, hipStream_t st);
 // [0, batch) are skipped.
 void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, hipStream_t st);
 
+// Copy the whole state of listed sequences between two buffer sets of one
+// layer configuration: every per-sequence region (checkpoint and its scales,
+// read copy, ring arrays) is `per` bytes at src + seq * per, and the counters
+// n_ckpt, len, nd, err of the meta record.
+constexpr int kMaxCopyRegions = 16;
+struct CopyRegion {
+  const char* src;
+  char* dst;
+  uint64_t per;
+};
+struct CopyArgs {
+  CopyRegion r[kMaxCopyRegions];
+  int nreg, count, src_batch, dst_batch;
+  const int32_t* src_seqs;
+  const int32_t* dst_seqs;
+  const rs_meta* src_meta;   // null in conventional mode
+  rs_meta* dst_meta;
+};
+void copy_slots(const CopyArgs& a, int blocks_per_pair, hipStream_t st);
+
 // Gated DeltaNet
 struct GDNArgs {
   int batch, nv, nqk, vpk;   // vpk = value heads per qk head

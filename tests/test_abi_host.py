@@ -85,6 +85,33 @@ def test_reset_slots_host_checks():
                        None) == rs.RS_E_MODE
 
 
+def test_copy_slots_host_checks():
+    """rs_copy_slots: configurations must match except batch; pointer, count and
+    alignment checks happen on the host; count == 0 launches nothing."""
+    lib = rs.lib()
+    kw = dict(nheads=8, headdim=16, dstate=16, ngroups=1)
+    _, L = rs.rs_init(_m2(batch=4, **kw))
+    _, Lc = rs.rs_init(_m2(batch=2, **kw))                      # a cache of another batch: fine
+    _, Lx = rs.rs_init(_m2(batch=2, nheads=4, headdim=16, dstate=16, ngroups=1))
+    _, Lf = rs.rs_init(_m2(batch=2, ckpt_dtype=rs.RS_F16, **kw))
+    bufs = rs.RsBuffers(0x1000, 0x2000, None, 0x3000, None)
+    seqs = C.c_void_p(0x4000)
+
+    def call(Ls, Ld, b1=bufs, b2=bufs, s1=seqs, s2=seqs, n=1):
+        return lib.rs_copy_slots(C.byref(Ls), C.byref(b1), s1, C.byref(Ld), C.byref(b2), s2, n, None)
+
+    assert call(L, Lc, n=0) == rs.RS_OK
+    assert call(L, Lx, n=0) == rs.RS_E_ARG and call(L, Lf, n=0) == rs.RS_E_ARG
+    assert call(L, Lc, s1=None) == rs.RS_E_ARG and call(L, Lc, n=-1) == rs.RS_E_ARG
+    assert call(L, Lc, n=65536) == rs.RS_E_ARG
+    assert call(L, Lc, b2=rs.RsBuffers(0x1000, None, None, 0x3000, None)) == rs.RS_E_ARG   # no ring
+    assert call(L, Lc, b2=rs.RsBuffers(0x1004, 0x2000, None, 0x3000, None)) == rs.RS_E_ALIGN
+    _, Lr = rs.rs_init(_m2(batch=4, read_copy=rs.RS_NVFP4, **kw))
+    assert call(Lr, Lr) == rs.RS_E_ARG                                                   # no read copy
+    L.magic = 0
+    assert call(L, Lc, n=0) == rs.RS_E_ARG
+
+
 def test_kda_layout_sizes():
     """Kimi Delta Attention: the GDN layout with a dk-wide gate per ring entry;
     speculative configs get the GDN snapshot area (conventional mode)."""
