@@ -270,6 +270,45 @@ rs_status rs_copy_slots(const rs_layer* Ls, const rs_buffers* src, const int32_t
                         const rs_layer* Ld, const rs_buffers* dst, const int32_t* dst_seqs,
                         int32_t count, void* stream);
 
+/* Mamba-2 block around the SSM step (Dao and Gu 2024; the ReplaySSM pages name
+ * the layer type only). Both calls take a Mamba-2 layer; K = 1 for a plain
+ * token, or the K drafts of a speculative round (K <= max_draft).
+ *
+ * Short causal convolution (depthwise, width W <= 4, bias, then SiLU) over the
+ * channels xBC = [x | B | C], C_ch = nheads*headdim + 2*ngroups*dstate:
+ *   out_t[c] = silu(bias[c] + sum_{k<W} weight[c][k] * xBC_{t-W+1+k}[c]).
+ * Its state, the last W-1 inputs, is a ring of recent inputs like the SSM
+ * buffer (sitech.ge ReplaySSM page, "Reducing state traffic and simplifying
+ * rollback"): conv_ring, in_dtype [batch][16][C_ch] (batch * 16 * C_ch *
+ * sizeof(in) bytes, caller-owned), holds the input of token position q in
+ * slot q mod 16, where the next position of sequence b is n_ckpt + len of the
+ * layer's meta (replay mode). Call it before the SSM call of the same tokens:
+ * it reads positions p-W+1..p-1, writes the K inputs at p..p+K-1 and the
+ * outputs x [K][batch][nheads][headdim], B and C [K][batch][ngroups][dstate]
+ * (in_dtype; bf16 rounded to nearest even), ready for the SSM call. A
+ * speculative commit needs nothing here (the SSM commit advances the
+ * position; slots of rejected drafts are overwritten later). A new sequence's
+ * caller writes its last W-1 prompt inputs, or zeros, at positions -W+1..-1
+ * (slots 16-W+1..15 when n_ckpt = len = 0); rs_copy_slots does not copy this
+ * buffer (copy the sequence's [16][C_ch] row with it). Sequences with drafts
+ * pending or without room for K entries (len + K > 16) are skipped, outputs
+ * untouched, as the SSM call refuses them. xbc: in_dtype [K][batch][C_ch];
+ * weight float [C_ch][W]; bias float [C_ch] or NULL. d_inner and
+ * ngroups*dstate must be multiples of 8; pointers 16-byte aligned. */
+rs_status rs_conv_step(const rs_layer* L, const rs_buffers* buf, void* conv_ring, const void* xbc,
+                       int32_t K, const float* weight, const float* bias, int32_t width,
+                       void* x, void* B, void* C, void* stream);
+
+/* Gated RMS norm of the SSM output (same block; gate applied before the norm):
+ *   v = y * silu(z);  out = v / sqrt(mean_group(v^2) + eps) * weight
+ * over norm_groups groups of d_inner / norm_groups consecutive channels of
+ * the flattened y [nheads*headdim]. y float [K][batch][d_inner] (the SSM
+ * call's output), z and out in_dtype [K][batch][d_inner] (bf16 rounded to
+ * nearest even), weight float [d_inner]. Either mode. */
+rs_status rs_gated_norm(const rs_layer* L, int32_t K, const float* y, const void* z,
+                        const float* weight, int32_t norm_groups, float eps, void* out,
+                        void* stream);
+
 /* Speculative append (same page, "Reducing state traffic and simplifying
  * rollback": draft inputs enter the buffer until verification; verification
  * reads outputs only, as a small matrix product, without forming

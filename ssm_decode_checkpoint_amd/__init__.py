@@ -28,8 +28,8 @@ RS_NONE, RS_F32, RS_BF16, RS_F16, RS_FP8E4M3, RS_NVFP4 = 0, 1, 2, 3, 4, 5
 RS_ERR_FULL, RS_ERR_OVERFLOW, RS_ERR_COMMIT, RS_ERR_PENDING = 1, 2, 4, 8
 
 EXPORTS = ("rs_init", "rs_step_conventional", "rs_step_nonflush", "rs_step_flush", "rs_step", "rs_spec_append",
-           "rs_spec_commit", "rs_requant_read_copy", "rs_reset_slots", "rs_copy_slots", "rs_status_string",
-           "rs_version")
+           "rs_spec_commit", "rs_requant_read_copy", "rs_reset_slots", "rs_copy_slots", "rs_conv_step",
+           "rs_gated_norm", "rs_status_string", "rs_version")
 
 
 class RsConfig(C.Structure):
@@ -90,6 +90,10 @@ def lib() -> C.CDLL:
         L.rs_reset_slots.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, C.c_int32, C.c_void_p]
         L.rs_copy_slots.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, P(RsLayer), P(RsBuffers), C.c_void_p,
                                     C.c_int32, C.c_void_p]
+        L.rs_conv_step.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, C.c_void_p, C.c_int32, C.c_void_p,
+                                   C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.rs_gated_norm.argtypes = [P(RsLayer), C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32, C.c_float,
+                                    C.c_void_p, C.c_void_p]
         for name in EXPORTS:
             if name not in ("rs_status_string", "rs_version"):
                 getattr(L, name).restype = C.c_int32
@@ -230,6 +234,30 @@ def rs_spec_commit(layer: RsLayer, bufs: Buffers, accepted, A, D, stream=None, r
     st = lib().rs_spec_commit(C.byref(layer), C.byref(bufs.c()), _ptr(accepted), C.byref(_params(A, D)),
                               _stream(stream))
     return _check("rs_spec_commit", st, raise_on_error)
+
+
+def rs_conv_step(layer: RsLayer, bufs: Buffers, conv_ring, xbc, K: int, weight, bias, width: int, x, B, Cm,
+                 stream=None, raise_on_error: bool = True) -> int:
+    st = lib().rs_conv_step(C.byref(layer), C.byref(bufs.c()), _ptr(conv_ring), _ptr(xbc), int(K), _ptr(weight),
+                            _ptr(bias), int(width), _ptr(x), _ptr(B), _ptr(Cm), _stream(stream))
+    return _check("rs_conv_step", st, raise_on_error)
+
+
+def rs_gated_norm(layer: RsLayer, K: int, y, z, weight, norm_groups: int, eps: float, out, stream=None,
+                  raise_on_error: bool = True) -> int:
+    st = lib().rs_gated_norm(C.byref(layer), int(K), _ptr(y), _ptr(z), _ptr(weight), int(norm_groups), float(eps),
+                             _ptr(out), _stream(stream))
+    return _check("rs_gated_norm", st, raise_on_error)
+
+
+def conv_channels(layer: RsLayer) -> int:
+    c = layer.cfg
+    return c.nheads * c.headdim + 2 * c.ngroups * c.dstate
+
+
+def conv_ring_bytes(layer: RsLayer) -> int:
+    """Bytes of the convolution ring: batch x 16 x channels inputs."""
+    return layer.cfg.batch * 16 * conv_channels(layer) * (2 if layer.cfg.in_dtype == RS_BF16 else 4)
 
 
 def rs_requant_read_copy(layer: RsLayer, bufs: Buffers, stream=None, raise_on_error: bool = True) -> int:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librs.so")
-SOURCES = ["rs_api.hip", "rs_commit.hip", "rs_mamba2.hip", "rs_m2_16x16.hip", "rs_m2_64x64.hip", "rs_m2_128x64.hip",
+SOURCES = ["rs_api.hip", "rs_commit.hip", "rs_block.hip", "rs_mamba2.hip", "rs_m2_16x16.hip", "rs_m2_64x64.hip", "rs_m2_128x64.hip",
            "rs_m2_128x128.hip", "rs_gdn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

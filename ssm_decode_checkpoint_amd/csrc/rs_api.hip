@@ -480,6 +480,61 @@ rs_status rs_copy_slots(const rs_layer* Ls, const rs_buffers* src, const int32_t
   return launched();
 }
 
+rs_status rs_conv_step(const rs_layer* L, const rs_buffers* buf, void* conv_ring, const void* xbc, int32_t K,
+                       const float* weight, const float* bias, int32_t width, void* x, void* Bo, void* Co,
+                       void* stream) {
+  if (rs_status s = check_layer(L)) return s;
+  const rs_config& c = L->cfg;
+  if (c.kind != RS_MAMBA2 || c.mode != RS_REPLAY) return RS_E_MODE;
+  if (K < 1 || K > (c.max_draft > 1 ? c.max_draft : 1)) return RS_E_ARG;
+  if (width < 1 || width > 4) return RS_E_ARG;
+  if (!buf || !buf->meta || !conv_ring || !xbc || !weight || !x || !Bo || !Co) return RS_E_ARG;
+  const int d_inner = c.nheads * c.headdim, gn = c.ngroups * c.dstate;
+  if (d_inner % 8 != 0 || gn % 8 != 0) return RS_E_UNSUPPORTED;
+  const void* ptrs[7] = {buf->meta, conv_ring, xbc, weight, x, Bo, Co};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return RS_E_ALIGN;
+  ConvArgs a{};
+  a.batch = c.batch;
+  a.channels = d_inner + 2 * gn;
+  a.width = width;
+  a.K = K;
+  a.d_inner = d_inner;
+  a.gn = gn;
+  a.meta = static_cast<const rs_meta*>(buf->meta);
+  a.ring = conv_ring;
+  a.xbc = xbc;
+  a.w = weight;
+  a.bias = bias;
+  a.x = x;
+  a.B = Bo;
+  a.C = Co;
+  conv_step(a, c.in_dtype == RS_BF16, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+rs_status rs_gated_norm(const rs_layer* L, int32_t K, const float* y, const void* z, const float* weight,
+                        int32_t norm_groups, float eps, void* out, void* stream) {
+  if (rs_status s = check_layer(L)) return s;
+  const rs_config& c = L->cfg;
+  if (c.kind != RS_MAMBA2) return RS_E_MODE;
+  const int d_inner = c.nheads * c.headdim;
+  if (K < 1 || K > (c.max_draft > 1 ? c.max_draft : 1)) return RS_E_ARG;
+  if (norm_groups < 1 || d_inner % norm_groups != 0 || !(eps >= 0.0f)) return RS_E_ARG;
+  if (!y || !z || !weight || !out) return RS_E_ARG;
+  NormArgs a{};
+  a.rows = K * c.batch;
+  a.d = d_inner;
+  a.gs = d_inner / norm_groups;
+  a.eps = eps;
+  a.y = y;
+  a.z = z;
+  a.w = weight;
+  a.out = out;
+  gated_norm(a, c.in_dtype == RS_BF16, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inputs* drafts, int32_t K,
                          const rs_params* prm, float* y, void* stream) {
   if (rs_status s = check_layer(L)) return s;

@@ -159,6 +159,32 @@ struct CopyArgs {
 };
 void copy_slots(const CopyArgs& a, int blocks_per_pair, hipStream_t st);
 
+// Mamba-2 block: short causal convolution with its ring of recent inputs, and
+// the gated RMS norm of the SSM output.
+struct ConvArgs {
+  int batch, channels, width, K;
+  int d_inner, gn;         // x channels, then ngroups * dstate each for B and C
+  const rs_meta* meta;     // positions n_ckpt + len
+  void* ring;              // [batch][16][channels]
+  const void* xbc;         // [K][batch][channels]
+  const float* w;          // [channels][width]
+  const float* bias;       // [channels] or null
+  void* x;                 // [K][batch][d_inner]
+  void* B;                 // [K][batch][gn]
+  void* C;                 // [K][batch][gn]
+};
+void conv_step(const ConvArgs& a, bool bf, hipStream_t st);
+
+struct NormArgs {
+  int rows, d, gs;         // rows = K * batch, d = d_inner, gs = channels per group
+  float eps;
+  const float* y;          // [rows][d]
+  const void* z;           // [rows][d], input type
+  const float* w;          // [d]
+  void* out;               // [rows][d], input type
+};
+void gated_norm(const NormArgs& a, bool bf, hipStream_t st);
+
 // Gated DeltaNet
 struct GDNArgs {
   int batch, nv, nqk, vpk;   // vpk = value heads per qk head

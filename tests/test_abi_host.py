@@ -112,6 +112,36 @@ def test_copy_slots_host_checks():
     assert call(L, Lc, n=0) == rs.RS_E_ARG
 
 
+def test_block_calls_host_checks():
+    """rs_conv_step / rs_gated_norm: kind, mode, K, width, group and pointer checks on the host."""
+    lib = rs.lib()
+    kw = dict(nheads=8, headdim=16, dstate=16, ngroups=1)
+    _, L = rs.rs_init(_m2(batch=2, **kw))
+    _, Ls = rs.rs_init(_m2(batch=2, max_draft=4, **kw))
+    _, Lc = rs.rs_init(_m2(batch=2, mode=rs.RS_CONVENTIONAL, **kw))
+    _, G = rs.rs_init(rs.make_config(rs.RS_GDN, 2, n_qk_heads=1, n_v_heads=2, head_k_dim=16, head_v_dim=16))
+    bufs = rs.RsBuffers(0x1000, 0x2000, None, 0x3000, None)
+    p = C.c_void_p(0x4000)
+
+    def conv(Lx, K=1, width=4, ring=p, x=p, bb=bufs):
+        return lib.rs_conv_step(C.byref(Lx), C.byref(bb), ring, p, K, p, None, width, x, p, p, None)
+
+    assert conv(Lc) == rs.RS_E_MODE and conv(G) == rs.RS_E_MODE
+    assert conv(L, K=2) == rs.RS_E_ARG and conv(Ls, K=5) == rs.RS_E_ARG and conv(L, K=0) == rs.RS_E_ARG
+    assert conv(L, width=5) == rs.RS_E_ARG and conv(L, width=0) == rs.RS_E_ARG
+    assert conv(L, ring=None) == rs.RS_E_ARG and conv(L, x=C.c_void_p(0x4004)) == rs.RS_E_ALIGN
+    assert conv(L, bb=rs.RsBuffers(0x1000, 0x2000, None, None, None)) == rs.RS_E_ARG
+
+    def norm(Lx, K=1, groups=1, eps=1e-5, out=p):
+        return lib.rs_gated_norm(C.byref(Lx), K, p, p, p, groups, C.c_float(eps), out, None)
+
+    assert norm(G) == rs.RS_E_MODE and norm(L, K=2) == rs.RS_E_ARG
+    assert norm(L, groups=3) == rs.RS_E_ARG and norm(L, groups=0) == rs.RS_E_ARG
+    assert norm(L, eps=-1.0) == rs.RS_E_ARG and norm(L, eps=float("nan")) == rs.RS_E_ARG
+    assert norm(L, out=None) == rs.RS_E_ARG
+    assert rs.conv_channels(L) == 8 * 16 + 2 * 16 and rs.conv_ring_bytes(L) == 2 * 16 * 160 * 2   # bf16
+
+
 def test_kda_layout_sizes():
     """Kimi Delta Attention: the GDN layout with a dk-wide gate per ring entry;
     speculative configs get the GDN snapshot area (conventional mode)."""

@@ -42,6 +42,7 @@ KEY_PARAMS = 2**31
 KEY_INIT = 2**31 + 1
 KEY_ACCEPT = 2**31 + 2
 KEY_TILE = 2**31 + 3
+KEY_BLOCK = 2**31 + 4
 
 
 def rng_for(*key: int) -> np.random.Generator:
@@ -203,6 +204,34 @@ def accepted_counts(seed: int, rnd: int, batch: int, max_draft: int) -> np.ndarr
     """Accepted draft count per sequence for speculative round rnd, uniform on {0..max_draft}."""
     g = rng_for(seed, KEY_ACCEPT, rnd)
     return g.integers(0, max_draft + 1, size=batch).astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Mamba-2 block draws (short convolution and gated norm around the SSM)
+# --------------------------------------------------------------------------
+
+def block_params(w: Mamba2Workload, width: int = 4) -> Dict[str, np.ndarray]:
+    """Convolution weights [channels, width] (~ 1/sqrt(width)), bias [channels] and
+    norm weights [d_inner], fp32; channels = d_inner + 2 ngroups dstate."""
+    g = rng_for(w.seed, KEY_BLOCK)
+    ch = w.nheads * w.headdim + 2 * w.ngroups * w.dstate
+    return {"conv_w": (g.standard_normal((ch, width)) / np.sqrt(width)).astype(np.float32),
+            "conv_b": (0.1 * g.standard_normal(ch)).astype(np.float32),
+            "norm_w": (1.0 + 0.1 * g.standard_normal(w.nheads * w.headdim)).astype(np.float32)}
+
+
+def block_token(w: Mamba2Workload, t: int, b: int) -> Dict[str, np.ndarray]:
+    """Pre-convolution channels xbc [channels] and gate z [d_inner] of sequence b at
+    step t, as float32 holding in_dtype values."""
+    g = rng_for(w.seed, KEY_BLOCK, t, b)
+    ch = w.nheads * w.headdim + 2 * w.ngroups * w.dstate
+    return {"xbc": _as_in(g.standard_normal(ch), w.in_dtype),
+            "z": _as_in(g.standard_normal(w.nheads * w.headdim), w.in_dtype)}
+
+
+def block_step(w: Mamba2Workload, t: int, seqs: Sequence[int]) -> Dict[str, np.ndarray]:
+    toks = [block_token(w, t, b) for b in seqs]
+    return {k: np.stack([tk[k] for tk in toks]) for k in ("xbc", "z")}
 
 
 # --------------------------------------------------------------------------
