@@ -411,6 +411,61 @@ def bench_serve(args, torch, rs):
                                      "GB/s counts read + write"}}
 
 
+def bench_block(args, torch, rs):
+    """The Nemotron-style Mamba-2 layer's per-token path at batch 256 beyond the
+    SSM step: short causal convolution (ring of recent inputs) -> self-scheduling
+    SSM step -> gated RMS norm, 16 tokens per window, vs the SSM step alone."""
+    w = W.M2_NEMOTRON
+    dev = "cuda"
+    B = w.batch
+    p = W.m2_params(w)
+    A = torch.from_numpy(p["A"]).to(dev)
+    D = torch.from_numpy(p["D"]).to(dev)
+    layer, bufs = _m2_layer(rs, w, B, rs.RS_REPLAY, dev)
+    _m2_load_init(torch, rs, w, layer, bufs, dev)
+    bp = W.block_params(w)
+    ch = rs.conv_channels(layer)
+    ring = torch.zeros(rs.conv_ring_bytes(layer), dtype=torch.uint8, device=dev)
+    cw = torch.from_numpy(bp["conv_w"]).to(dev)
+    cbias = torch.from_numpy(bp["conv_b"]).to(dev)
+    nw = torch.from_numpy(bp["norm_w"]).to(dev)
+    d = w.nheads * w.headdim
+    xbc, z = [], []
+    for t in range(RING):
+        bt = W.block_step(w, t, range(B))
+        xbc.append(_bf16_dev(torch, bt["xbc"], dev))
+        z.append(_bf16_dev(torch, bt["z"], dev))
+    dts = [_bf16_dev(torch, W.m2_step(w, t, range(B))["dt"], dev) for t in range(RING)]
+    x = torch.empty(B, w.nheads, w.headdim, dtype=torch.bfloat16, device=dev)
+    Bm = torch.empty(B, w.ngroups, w.dstate, dtype=torch.bfloat16, device=dev)
+    Cm = torch.empty(B, w.ngroups, w.dstate, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(B, w.nheads, w.headdim, dtype=torch.float32, device=dev)
+    out = torch.empty(B, d, dtype=torch.bfloat16, device=dev)
+    tm = Timer(torch)
+
+    def window(ev):
+        for t in range(RING):
+            _marked(ev, 3 * t, tm.stream,
+                    lambda: rs.rs_conv_step(layer, bufs, ring, xbc[t], 1, cw, cbias, 4, x, Bm, Cm))
+            _marked(ev, 3 * t + 1, tm.stream,
+                    lambda: rs.rs_step(layer, bufs, {"x": x, "B": Bm, "C": Cm, "dt": dts[t]}, A, D, y))
+            _marked(ev, 3 * t + 2, tm.stream, lambda: rs.rs_gated_norm(layer, 1, y, z[t], nw, w.ngroups, 1e-5, out))
+
+    total, per = tm.run(window, args.steps, args.warmup, 3 * RING)
+    conv_ms, ssm_ms, norm_ms = (float(per[:, i::3].mean()) for i in range(3))
+    conv_bytes = B * ch * 2 * 6          # 3 history reads, input, ring write, output (bf16)
+    norm_bytes = B * d * (4 + 2 + 2)     # y fp32, z and out bf16
+    ntok = B * RING * args.steps
+    return {"metric": "Mamba-2 layer per-token path (conv + SSM step + gated norm) tokens/s at batch 256",
+            "value": ntok / (total * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": total / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "mamba2_nemotron_b256_block", "batch": B, "conv_channels": ch, "conv_width": 4,
+                       "norm_groups": w.ngroups, "step": "16 tokens of conv -> rs_step -> gated norm"},
+            "per_call_ms": {"conv": conv_ms, "ssm_step": ssm_ms, "gated_norm": norm_ms},
+            "conv_gbs": conv_bytes / (conv_ms * 1e-3) / 1e9, "norm_gbs": norm_bytes / (norm_ms * 1e-3) / 1e9}
+
+
 def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
     """A delta-rule layer (Gated DeltaNet, or Kimi Delta Attention for a per-channel
     gate) at batch 256: ReplaySSM windows vs the conventional kernel."""
@@ -736,7 +791,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--workload", action="append",
                     choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "kda_spec", "lowprec", "copy", "sweep",
-                             "serve"],
+                             "serve", "block"],
                     help="workloads to run (default: mamba2 only); repeat for several")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
@@ -755,7 +810,7 @@ def main():
     torch.cuda.set_device(0)
     for wl in (args.workload or ["mamba2"]):
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
-              "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve,
+              "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve, "block": bench_block,
               "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
               "kda_spec": lambda a, t, r: bench_gdn_spec(a, t, r,
                                                          W.KDA_B256.with_(name="kda_spec_b256", max_draft=4)),

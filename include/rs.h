@@ -294,7 +294,8 @@ rs_status rs_copy_slots(const rs_layer* Ls, const rs_buffers* src, const int32_t
  * pending or without room for K entries (len + K > 16) are skipped, outputs
  * untouched, as the SSM call refuses them. xbc: in_dtype [K][batch][C_ch];
  * weight float [C_ch][W]; bias float [C_ch] or NULL. d_inner and
- * ngroups*dstate must be multiples of 8; pointers 16-byte aligned. */
+ * ngroups*dstate must be multiples of 8; pointers (bias included) 16-byte
+ * aligned. */
 rs_status rs_conv_step(const rs_layer* L, const rs_buffers* buf, void* conv_ring, const void* xbc,
                        int32_t K, const float* weight, const float* bias, int32_t width,
                        void* x, void* B, void* C, void* stream);
@@ -304,7 +305,8 @@ rs_status rs_conv_step(const rs_layer* L, const rs_buffers* buf, void* conv_ring
  * over norm_groups groups of d_inner / norm_groups consecutive channels of
  * the flattened y [nheads*headdim]. y float [K][batch][d_inner] (the SSM
  * call's output), z and out in_dtype [K][batch][d_inner] (bf16 rounded to
- * nearest even), weight float [d_inner]. Either mode. */
+ * nearest even), weight float [d_inner]; pointers 16-byte aligned, group size
+ * a multiple of 4 (RS_E_UNSUPPORTED otherwise). Either mode. */
 rs_status rs_gated_norm(const rs_layer* L, int32_t K, const float* y, const void* z,
                         const float* weight, int32_t norm_groups, float eps, void* out,
                         void* stream);

@@ -494,6 +494,7 @@ rs_status rs_conv_step(const rs_layer* L, const rs_buffers* buf, void* conv_ring
   const void* ptrs[7] = {buf->meta, conv_ring, xbc, weight, x, Bo, Co};
   for (const void* p : ptrs)
     if (!aligned16(p)) return RS_E_ALIGN;
+  if (bias && !aligned16(bias)) return RS_E_ALIGN;
   ConvArgs a{};
   a.batch = c.batch;
   a.channels = d_inner + 2 * gn;
@@ -522,6 +523,8 @@ rs_status rs_gated_norm(const rs_layer* L, int32_t K, const float* y, const void
   if (K < 1 || K > (c.max_draft > 1 ? c.max_draft : 1)) return RS_E_ARG;
   if (norm_groups < 1 || d_inner % norm_groups != 0 || !(eps >= 0.0f)) return RS_E_ARG;
   if (!y || !z || !weight || !out) return RS_E_ARG;
+  if ((d_inner / norm_groups) % 4 != 0) return RS_E_UNSUPPORTED;
+  if (!aligned16(y) || !aligned16(z) || !aligned16(weight) || !aligned16(out)) return RS_E_ALIGN;
   NormArgs a{};
   a.rows = K * c.batch;
   a.d = d_inner;
