@@ -248,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
 }
 
 // ----------------------------------------------------------------------------
-// non-flush step for FP8 / NVFP4 reads: one wavefront per head, kHPB heads of
-// one B/C group per workgroup. A low-precision tile (4.6 KiB in NVFP4) is
+// non-flush step for FP16 / FP8 / NVFP4 reads: one wavefront per head, kHPB heads
+// of one B/C group per workgroup. A low-precision tile (4.6 KiB in NVFP4) is
 // smaller than the buffer records a head needs, so the group's B rows, C and
 // the B.C dots are staged and computed once for kHPB heads, and each head's
 // output is reduced inside its wavefront: lane l owns the 8 columns
@@ -272,7 +272,8 @@ struct M2WaveSmem {
 
 template <typename TIN, int RDF, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_nonflush_wave_kernel(M2Args a) {
-  static_assert(RDF == FMT_FP8 || RDF == FMT_NVFP4, "low-precision reads only");
+  static_assert(RDF == FMT_F16 || RDF == FMT_FP8 || RDF == FMT_NVFP4,
+                "2-byte or smaller reads (an fp32 head needs 128 registers per lane here)");
   static_assert(NC == 64 && NR % 8 == 0, "8 lanes per 64-column row");
   constexpr int V = 16 / static_cast<int>(sizeof(TIN));
   constexpr int XCH = 8 / V;                 // 16-byte chunks per lane per x row (8 columns)
@@ -809,9 +810,12 @@ struct M2Shape {
   template <typename TIN>
   static void nonflush(const M2Args& a, int rdf, int grid, hipStream_t st) {
     if constexpr (NC == 64 && NR % 8 == 0) {
-      if ((rdf == FMT_FP8 || rdf == FMT_NVFP4) && a.hpg % kHPB == 0) {
+      // fp32 reads keep the 256-thread tile kernel: a whole fp32 head per wavefront
+      // needs 170 registers per lane, 2 waves per SIMD, and measured 270 vs 177 us
+      if (rdf != FMT_F32 && a.hpg % kHPB == 0) {
         const int g = grid / kHPB;   // one workgroup per kHPB heads
-        if (rdf == FMT_FP8) m2_nonflush_wave_kernel<TIN, FMT_FP8, NR, NC><<<g, kThreads, 0, st>>>(a);
+        if (rdf == FMT_F16) m2_nonflush_wave_kernel<TIN, FMT_F16, NR, NC><<<g, kThreads, 0, st>>>(a);
+        else if (rdf == FMT_FP8) m2_nonflush_wave_kernel<TIN, FMT_FP8, NR, NC><<<g, kThreads, 0, st>>>(a);
         else m2_nonflush_wave_kernel<TIN, FMT_NVFP4, NR, NC><<<g, kThreads, 0, st>>>(a);
         return;
       }
