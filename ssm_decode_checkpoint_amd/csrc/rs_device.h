@@ -211,6 +211,33 @@ __device__ __forceinline__ float wave_sum_stride(float v, int from) {
   return v;
 }
 
+// One lane's part of a length-N dot of LDS rows held by a 16-lane group: lane
+// ln takes the N/16 consecutive elements from ln*N/16, with 16-byte LDS loads
+// when that run is a whole number of float4 (rows then 16-byte aligned).
+// Optional third row w weights the products. Sum the parts with group_sum16.
+template <int N>
+__device__ __forceinline__ float lds_dot16(const float* a, const float* b, int ln, const float* w = nullptr) {
+  constexpr int R = N / 16;
+  float part = 0.0f;
+  if constexpr (N % 16 == 0 && R % 4 == 0) {
+    const float4* pa = reinterpret_cast<const float4*>(a + ln * R);
+    const float4* pb = reinterpret_cast<const float4*>(b + ln * R);
+#pragma unroll
+    for (int q = 0; q < R / 4; ++q) {
+      float4 x = pa[q];
+      const float4 y = pb[q];
+      if (w) {
+        const float4 z = reinterpret_cast<const float4*>(w + ln * R)[q];
+        x.x *= z.x; x.y *= z.y; x.z *= z.z; x.w *= z.w;
+      }
+      part += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+    }
+  } else {
+    for (int n = ln; n < N; n += 16) part += (w ? a[n] * w[n] : a[n]) * b[n];
+  }
+  return part;
+}
+
 __device__ __forceinline__ float group_sum16(float v) {
   // sum over aligned groups of 16 lanes
   v += __shfl_xor(v, 8, 64);

@@ -42,12 +42,12 @@ constexpr int gdn_slices() { return NV >= 128 ? 2 : 1; }
 // VG: Kimi Delta Attention, the decay is a vector over the dk key channels
 // (a per-channel gate) instead of one scalar per head.
 template <int NK, int NVS, bool VG = false>
-struct GSmem {
+struct alignas(16) GSmem {
   static constexpr int kNK = NK;
   static constexpr int kNVS = NVS;
   static constexpr bool kVG = VG;
-  float K[kRing][NK];    // k of entries 0..m-1
-  float W[4][NK];        // matvec weights: k_cur, q, 0, 0
+  alignas(16) float K[kRing][NK];    // k of entries 0..m-1
+  alignas(16) float W[4][NK];        // matvec weights: k_cur, q, 0, 0
   float U[kRing][NVS];   // u of entries 0..m-1 (the current one computed here), own columns
   float vc[NVS];         // v of the current token, own columns
   float out[4][NVS];     // S0 k_cur, S0 q
@@ -60,7 +60,7 @@ struct GSmem {
   float s4[4];
   // VG: per-channel log decays of entries 0..m-1, then in place the products
   // r_{cur,e} = prod_{e<l<=cur} alpha_l; gv = gamma_cur per channel
-  float A[VG ? kRing : 1][NK];
+  alignas(16) float A[VG ? kRing : 1][NK];
   float gv[VG ? NK : 1];
   static_assert(!VG || 4 * 4 * NVS <= kRing * NK, "matvec scratch fits in the decay table");
   __device__ __forceinline__ float* redp() { if constexpr (VG) return &A[0][0]; else return red; }
@@ -233,12 +233,7 @@ __device__ __forceinline__ void gdn_dots(SM& s, int m) {
     const bool isq = pr >= cur;
     const int i = isq ? pr - cur : pr;
     const float* other = isq ? &s.W[SM::kVG ? 2 : 1][0] : &s.K[cur][0];
-    float part = 0.0f;
-    if constexpr (SM::kVG) {
-      for (int n = ln; n < NK; n += 16) part += s.K[i][n] * s.A[i][n] * other[n];
-    } else {
-      for (int n = ln; n < NK; n += 16) part += s.K[i][n] * other[n];
-    }
+    float part = lds_dot16<NK>(&s.K[i][0], other, ln, SM::kVG ? &s.A[i][0] : nullptr);
     part = group_sum16(part);
     if (ln == 0) {
       float r = 1.0f;
@@ -511,13 +506,13 @@ __global__ __launch_bounds__(kThreads) void gdn_auto_kernel(GDNArgs a) {
 namespace {
 
 template <int NK, int NVS, int KQ, bool VG>
-struct GSpecSmem {
+struct alignas(16) GSpecSmem {
   // k of window entries 0..n-1 (held, then drafts) for the dots; once they are
   // done, the same space is the matvec scratch (4 KQ NVS floats), and after the
   // matvecs the held-entry sums HU, HO (KQ NVS floats each)
   static constexpr int KROWS = (4 * KQ * NVS + NK - 1) / NK > kRing ? (4 * KQ * NVS + NK - 1) / NK : kRing;
-  float K[KROWS][NK];
-  float W[2 * KQ][NK];         // matvec weights k_d, q_d per draft (zero past K)
+  alignas(16) float K[KROWS][NK];
+  alignas(16) float W[2 * KQ][NK];         // matvec weights k_d, q_d per draft (zero past K)
   float U[kRing][NVS];         // u rows, own columns (held from the ring, drafts solved here)
   float V[KQ][NVS];            // v of the drafts, own columns
   float out[2 * KQ][NVS];      // S0 k_d, S0 q_d
@@ -529,7 +524,7 @@ struct GSpecSmem {
   float bet[KQ];
   // VG: r_{e,i} per key channel for the draft being dotted (e = len + d), and
   // gamma_e per channel for each draft
-  float R[VG ? kRing : 1][NK];
+  alignas(16) float R[VG ? kRing : 1][NK];
   float G[VG ? KQ : 1][NK];
 };
 
@@ -636,8 +631,7 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
           const bool isq = pr >= ee;
           const int i = isq ? pr - ee : pr;
           const float* other = isq ? &s.W[2 * d + 1][0] : &s.K[ee][0];
-          float part = 0.0f;
-          for (int c = ln; c < NK; c += 16) part += s.K[i][c] * s.R[i][c] * other[c];
+          float part = lds_dot16<NK>(&s.K[i][0], other, ln, &s.R[i][0]);
           part = group_sum16(part);
           if (ln == 0) {
             if (isq) s.kq[d][i] = part;
@@ -673,8 +667,7 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
         const int ee = len + d;
         if (isq ? i > ee : i >= ee) continue;   // uniform over the group
         const float* other = isq ? &s.W[2 * d + 1][0] : &s.K[ee][0];
-        float part = 0.0f;
-        for (int c = ln; c < NK; c += 16) part += s.K[i][c] * other[c];
+        float part = lds_dot16<NK>(&s.K[i][0], other, ln);
         part = group_sum16(part);
         if (ln == 0) {
           if (isq) s.kq[d][i] = s.rt[d][i] * part;
@@ -692,7 +685,8 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
     // accumulator registers and half the scratch of one 2KQ-row pass)
     tile_matvec<KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);   // barriers inside publish the dots
     if (2 * K > KQ) tile_matvec<KQ>(S, &s.W[KQ][0], NK, red, &s.out[KQ][0]);
-    // the held entries' part of every draft's row and output, all (draft, column) pairs at once
+    // every (draft, column) pair at once: the parts of the draft's row and output
+    // that do not involve other drafts (checkpoint and held entries)
     for (int idx = threadIdx.x; idx < K * NVS; idx += kThreads) {
       const int d = idx / NVS, v = idx - d * NVS;
       float hu = 0.0f, ho = 0.0f;
@@ -702,31 +696,37 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
         hu += s.kk[d][i] * ui;
         ho += s.kq[d][i] * ui;
       }
-      HU[d * NVS + v] = hu;
-      HO[d * NVS + v] = ho;
+      HU[d * NVS + v] = s.bet[d] * (s.V[d][v] - s.gam[d] * s.out[2 * d][v]) - hu;
+      HO[d * NVS + v] = s.gam[d] * s.out[2 * d + 1][v] + ho;
     }
     __syncthreads();
-    // the drafts in order: each row also depends on the drafts before it
+    // the drafts' rows in order (each depends on the drafts before it), one
+    // thread per column with the earlier rows in registers
     float* ruw = static_cast<float*>(a.ru) + p.st * kRing * NV + p.c0;
     for (int v = threadIdx.x; v < NVS; v += kThreads) {
-      for (int d = 0; d < K; ++d) {
-        const int ee = len + d;
-        float u = s.bet[d] * (s.V[d][v] - s.gam[d] * s.out[2 * d][v]) - HU[d * NVS + v];
+      float ur[KQ];
 #pragma unroll
-        for (int j = 0; j < KQ; ++j) {   // earlier drafts: entries len .. ee-1
-          const int i = len + j < kRing ? len + j : kRing - 1;
-          u -= j < d ? s.kk[d][i] * s.U[i][v] : 0.0f;
-        }
-        s.U[ee][v] = u;
-        float o = s.gam[d] * s.out[2 * d + 1][v] + HO[d * NVS + v];
+      for (int d = 0; d < KQ; ++d) {
+        if (d < K) {
+          float u = HU[d * NVS + v];
 #pragma unroll
-        for (int j = 0; j < KQ; ++j) {   // drafts up to this one: entries len .. ee
-          const int i = len + j < kRing ? len + j : kRing - 1;
-          o += j <= d ? s.kq[d][i] * s.U[i][v] : 0.0f;
+          for (int j = 0; j < d; ++j) u -= s.kk[d][len + j] * ur[j];   // len + j < len + K <= 16
+          ur[d] = u;
+          s.U[len + d][v] = u;
+          ruw[slot_of(nck, len + d) * NV + v] = u;
         }
-        a.o[d * vstride + p.st * NV + p.c0 + v] = o;
-        ruw[slot_of(nck, ee) * NV + v] = u;
       }
+    }
+    __syncthreads();
+    // outputs, every (draft, column) pair at once
+    for (int idx = threadIdx.x; idx < K * NVS; idx += kThreads) {
+      const int d = idx / NVS, v = idx - d * NVS;
+      float o = HO[d * NVS + v];
+#pragma unroll
+      for (int j = 0; j < KQ; ++j)   // drafts up to this one: entries len .. len + d
+        o += j <= d ? s.kq[d][len + j < kRing ? len + j : kRing - 1] * s.U[len + j < kRing ? len + j : kRing - 1][v]
+                    : 0.0f;
+      a.o[d * vstride + p.st * NV + p.c0 + v] = o;
     }
     // drafts into the ring (bit copies); each slice its own v columns
     TIN* rv = static_cast<TIN*>(a.rv) + p.st * kRing * NV + p.c0;
