@@ -522,10 +522,11 @@ struct alignas(16) GSpecSmem {
   float al[kRing];             // alpha of window entry e
   float gam[KQ];               // gamma of draft d's entry (VG: 1, the decays weight the dots)
   float bet[KQ];
-  // VG: r_{e,i} per key channel for the draft being dotted (e = len + d), and
-  // gamma_e per channel for each draft
-  alignas(16) float R[VG ? kRing : 1][NK];
-  float G[VG ? KQ : 1][NK];
+  // VG (per-channel decays, e = len + d): WS = k_e * P_d and q_d * P_d with
+  // P_d = prod_{len<=l<=e} alpha_l; DW[d(d-1)/2 + j] = prod_{len+j<l<=e} alpha_l
+  // (the decay between draft j and draft d > j)
+  alignas(16) float WS[VG ? 2 * KQ : 1][NK];
+  alignas(16) float DW[VG && KQ > 1 ? KQ * (KQ - 1) / 2 : 1][NK];
 };
 
 }  // namespace
@@ -606,45 +607,79 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
     if (static_cast<int>(threadIdx.x) < K) s.bet[threadIdx.x] = bv;
     __syncthreads();
     if constexpr (VG) {
-      // per draft d: channel owners write r_{e,i} (descending direct products)
-      // and gamma_e, then the decay-weighted dots
-      //   kk[d][i] = beta_d <k_e, r_{e,i} * k_i>,  kq[d][i] = <q_d, r_{e,i} * k_i>
+      // The decay from entry i to draft entry e = len + d factors at the first
+      // draft: r_{e,i} = Rh_i * P_d for a held entry (Rh_i = prod_{i<l<len}
+      // alpha_l), and DW for a pair of drafts. Channel owners (one thread per
+      // key channel, window decays in registers) scale the held k rows by Rh in
+      // place and write WS and DW; then every dot of every draft in one pass:
+      //   kk[d][i] = beta_d <k_e, r_{e,i} * k_i>,  kq[d][i] = <q_d, r_{e,i} * k_i>.
+      // gamma_e = Gam * P_d with Gam = prod_{l<len} alpha_l.
       const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+      float gam_c = 1.0f;
+      if (static_cast<int>(threadIdx.x) < NK) {
+        const int c = threadIdx.x;
 #pragma unroll
-      for (int e = 0; e < kRing; ++e) lg[e] = expf(lg[e]);   // alpha per entry
-      for (int d = 0; d < K; ++d) {
-        const int ee = len + d;
-        if (static_cast<int>(threadIdx.x) < NK) {
-          float acc = 1.0f;
+        for (int e = 0; e < kRing; ++e) lg[e] = expf(lg[e]);   // alpha per entry
+        float acc = 1.0f;
 #pragma unroll
-          for (int i = kRing - 1; i >= 0; --i) {
-            if (i <= ee) {
-              s.R[i][threadIdx.x] = acc;
-              acc *= lg[i];
-            }
-          }
-          s.G[d][threadIdx.x] = acc;
-        }
-        if (threadIdx.x == 0) s.gam[d] = 1.0f;
-        __syncthreads();
-        for (int pr = grp; pr < 2 * ee + 1; pr += kThreads / 16) {
-          const bool isq = pr >= ee;
-          const int i = isq ? pr - ee : pr;
-          const float* other = isq ? &s.W[2 * d + 1][0] : &s.K[ee][0];
-          float part = lds_dot16<NK>(&s.K[i][0], other, ln, &s.R[i][0]);
-          part = group_sum16(part);
-          if (ln == 0) {
-            if (isq) s.kq[d][i] = part;
-            else s.kk[d][i] = s.bet[d] * part;
+        for (int i = kRing - 1; i >= 0; --i) {
+          if (i < len) {
+            s.K[i][c] *= acc;
+            acc *= lg[i];
           }
         }
-        __syncthreads();
+        gam_c = acc;
+        float pd = 1.0f;
+        for (int d = 0; d < K; ++d) {
+          pd *= lg[len + d];                      // len + d < 16; wave-uniform index
+          s.WS[2 * d][c] = s.W[2 * d][c] * pd;
+          s.WS[2 * d + 1][c] = s.W[2 * d + 1][c] * pd;
+          float q = 1.0f;
+          for (int j = d - 1; j >= 0; --j) {
+            q *= lg[len + j + 1];
+            s.DW[d * (d - 1) / 2 + j][c] = q;
+          }
+        }
       }
-      // matvec weights gamma_e * k_e and gamma_e * q_d
-      for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) {
-        const int d = idx / NK, c = idx - d * NK;
-        s.W[2 * d][c] *= s.G[d][c];
-        s.W[2 * d + 1][c] *= s.G[d][c];
+      if (static_cast<int>(threadIdx.x) < K) s.gam[threadIdx.x] = 1.0f;
+      __syncthreads();
+      // pairs of draft d: len held kk, len held kq, d draft kk, d + 1 draft kq
+      const int npairs = K * (2 * len + 1) + K * (K - 1);
+      for (int pr = grp; pr < npairs; pr += kThreads / 16) {
+        int d = 0, r = pr;
+        while (r >= 2 * (len + d) + 1) {          // uniform over the group
+          r -= 2 * (len + d) + 1;
+          ++d;
+        }
+        const int ee = len + d;
+        float part;
+        bool isq;
+        int i;
+        if (r < 2 * len) {                        // held entry i: k row already scaled by Rh_i
+          isq = r >= len;
+          i = isq ? r - len : r;
+          part = lds_dot16<NK>(&s.K[i][0], &s.WS[2 * d + (isq ? 1 : 0)][0], ln);
+        } else {                                  // earlier draft j (kk: j < d; kq: j <= d)
+          const int t = r - 2 * len;
+          isq = t >= d;
+          const int j = isq ? t - d : t;
+          i = len + j;
+          const float* w = j < d ? &s.DW[d * (d - 1) / 2 + j][0] : nullptr;
+          part = lds_dot16<NK>(&s.K[i][0], isq ? &s.W[2 * d + 1][0] : &s.K[ee][0], ln, w);
+        }
+        part = group_sum16(part);
+        if (ln == 0) {
+          if (isq) s.kq[d][i] = part;
+          else s.kk[d][i] = s.bet[d] * part;
+        }
+      }
+      __syncthreads();
+      // matvec weights gamma_e * k_e and gamma_e * q_d (owners: their channel)
+      if (static_cast<int>(threadIdx.x) < NK) {
+        for (int d = 0; d < K; ++d) {
+          s.W[2 * d][threadIdx.x] = s.WS[2 * d][threadIdx.x] * gam_c;
+          s.W[2 * d + 1][threadIdx.x] = s.WS[2 * d + 1][threadIdx.x] * gam_c;
+        }
       }
     } else {
       // decays r_{e,i} (direct products), one (draft, entry) pair per thread, and gamma
