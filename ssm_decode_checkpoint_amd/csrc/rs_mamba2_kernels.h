@@ -31,7 +31,7 @@ namespace rs {
 // LDS of one Mamba-2 workgroup: NE buffer entries, Q outputs, and (XT) the
 // fold coefficients. Sized per kernel so residency is not limited by LDS.
 template <int NR, int NC, int NE, int Q, bool XT>
-struct M2Smem {
+struct alignas(16) M2Smem {
   float B[NE][NR];
   float X[NE][NC];
   float Cw[Q][NR];        // C vectors the outputs are read with (current token, or drafts)
@@ -56,16 +56,19 @@ __device__ __forceinline__ void stage_decays(float* a, const float* dt, float A,
 template <typename SM>
 __device__ __forceinline__ void output_weights(SM& s, int j0, int nq) {
   const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
-  constexpr int NE = sizeof(s.dt) / sizeof(float);
   constexpr int NR = sizeof(s.B[0]) / sizeof(float);
-  for (int pair = grp; pair < nq * NE; pair += kThreads / 16) {
-    const int q = pair / NE, e = pair - q * NE;
+  // valid pairs only: output q has J_q = j0 + q of them, q-major
+  const int npairs = nq * j0 + nq * (nq - 1) / 2;
+  for (int pair = grp; pair < npairs; pair += kThreads / 16) {
+    int q = 0, e = pair;
+    while (e >= j0 + q) {                        // uniform over the group
+      e -= j0 + q;
+      ++q;
+    }
     const int J = j0 + q;
-    float part = 0.0f;
-    if (e < J)
-      for (int n = ln; n < NR; n += 16) part += s.B[e][n] * s.Cw[q][n];
+    float part = lds_dot16<NR>(&s.B[e][0], &s.Cw[q][0], ln);
     part = group_sum16(part);
-    if (ln == 0 && e < J) {
+    if (ln == 0) {
       float w = 1.0f;
       for (int l = e + 1; l < J; ++l) w *= s.a[l];
       s.w[q][e] = w * s.dt[e] * part;
@@ -132,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void m2_conv_kernel(M2Args a) {
 // the buffer part of y) runs while the tile streams in, and the tail after
 // its arrival is one reduction and the y store.
 template <int NR, int NC>
-struct M2NfSmem {
+struct alignas(16) M2NfSmem {
   float B[kRing][NR];
   float X[kRing][NC];
   float C[NR];
@@ -201,8 +204,7 @@ __device__ __forceinline__ void m2_nonflush_body(const M2Args& a, M2NfSmem<NR, N
   {
     const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
     for (int e = grp; e < j; e += kThreads / 16) {
-      float part = 0.0f;
-      for (int n = ln; n < NR; n += 16) part += s.B[e][n] * s.C[n];
+      float part = lds_dot16<NR>(&s.B[e][0], s.C, ln);
       part = group_sum16(part);
       if (ln == 0) {
         float w = 1.0f;
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_kernel(M2Args a) {
 constexpr int kHPB = 4;
 
 template <int NR, int NC>
-struct M2WaveSmem {
+struct alignas(16) M2WaveSmem {
   float B[kRing][NR];
   float C[NR];
   float bc[kRing];            // B_e . C_cur
@@ -349,8 +351,7 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_wave_kernel(M2Args a) {
   {
     const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
     if (grp < j) {
-      float part = 0.0f;
-      for (int n = ln; n < NR; n += 16) part += s.B[grp][n] * s.C[n];
+      float part = lds_dot16<NR>(&s.B[grp][0], s.C, ln);
       part = group_sum16(part);
       if (ln == 0) s.bc[grp] = part;
     }
