@@ -777,9 +777,18 @@ def bench_copy(args, torch, rs):
     tm = Timer(torch)
     total, per = tm.run(lambda ev: _marked(ev, 0, tm.stream, lambda: dst.copy_(src)), args.steps, args.warmup, 1)
     ms = float(per.mean())
+    # a plain read of the same 1 GiB (torch's sum over fp32): a reference for what a
+    # read-only stream reaches on this chip
+    srcf = src.view(torch.float32)
+    acc = torch.empty((), dtype=torch.float32, device="cuda")
+    rtot, rper = tm.run(lambda ev: _marked(ev, 0, tm.stream, lambda: torch.sum(srcf, out=acc)), args.steps,
+                        args.warmup, 1)
+    rms = float(rper.mean())
     return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
-            "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n}}
+            "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n},
+            "read_reference": {"what": "torch.sum over the same 1 GiB (read only)", "ms": rms,
+                               "gbs": n / (rms * 1e-3) / 1e9}}
 
 
 def main():
