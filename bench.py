@@ -781,7 +781,7 @@ def bench_copy(args, torch, rs):
     # read-only stream reaches on this chip
     srcf = src.view(torch.float32)
     acc = torch.empty((), dtype=torch.float32, device="cuda")
-    rtot, rper = tm.run(lambda ev: _marked(ev, 0, tm.stream, lambda: torch.sum(srcf, out=acc)), args.steps,
+    rtot, rper = tm.run(lambda ev: _marked(ev, 0, tm.stream, lambda: torch.sum(srcf, dim=0, out=acc)), args.steps,
                         args.warmup, 1)
     rms = float(rper.mean())
     return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
