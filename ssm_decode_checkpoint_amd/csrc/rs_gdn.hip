@@ -259,21 +259,30 @@ __device__ __forceinline__ void gdn_dots(SM& s, int m) {
   }
 }
 
-// u_cur[v] = beta (v_cur - gamma S0 k_cur) - sum_{i<cur} kk[i] u_i, stored in U[cur];
-// returns o[v] = gamma S0 q + sum_{i<=cur} kq[i] u_i for the thread's column v.
+// The held entries' part of row cur and of the output for column v: it needs
+// no state, so it is summed while the state tile streams in.
+//   hu = sum_{i<cur} kk[i] u_i[v],  ho = sum_{i<cur} kq[i] u_i[v]
 template <typename SM>
-__device__ __forceinline__ float gdn_row_and_output(SM& s, int m, int v) {
+__device__ __forceinline__ void gdn_held_sums(const SM& s, int m, int v, float& hu, float& ho) {
   const int cur = m - 1;
-  float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]);
-  // fixed-length loops with selects: every LDS load is unconditional and in
-  // bounds, so they issue together instead of one round trip per entry
+  hu = 0.0f;
+  ho = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kRing - 1; ++i) u -= i < cur ? s.kk[i] * s.U[i][v] : 0.0f;
+  for (int i = 0; i < kRing - 1; ++i) {   // selects keep every LDS load unconditional
+    const float ui = s.U[i][v];
+    hu += i < cur ? s.kk[i] * ui : 0.0f;
+    ho += i < cur ? s.kq[i] * ui : 0.0f;
+  }
+}
+
+// After the matvec: u_cur[v] = beta (v_cur - gamma S0 k_cur) - hu, stored in
+// U[cur]; returns o[v] = gamma S0 q + ho + kq[cur] u_cur.
+template <typename SM>
+__device__ __forceinline__ float gdn_finish_row(SM& s, int m, int v, float hu, float ho) {
+  const int cur = m - 1;
+  const float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]) - hu;
   s.U[cur][v] = u;
-  float o = s.gam * s.out[1][v];
-#pragma unroll
-  for (int i = 0; i < kRing; ++i) o += i <= cur ? s.kq[i] * s.U[i][v] : 0.0f;
-  return o;
+  return s.gam * s.out[1][v] + ho + s.kq[cur] * u;
 }
 
 // S <- S Diag(f) for a [dk][dv] tile: row r (key channel r) times f[r].
@@ -366,14 +375,18 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
       __syncthreads();
     }
     gdn_dots(s, j);
-    if constexpr (VG) __syncthreads();   // dots done: the decay table becomes matvec scratch
+    __syncthreads();   // dots visible; VG: the decay table becomes matvec scratch
+    static_assert(NVS <= kThreads, "one thread per column");
+    const int v = threadIdx.x;
+    float hu = 0.0f, ho = 0.0f;
+    if (v < NVS) gdn_held_sums(s, j, v, hu, ho);
     RegTile<4, NK, NVS> S;
     raw.decode(S);
-    tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);   // barriers inside publish the dots
+    tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
     const int slot = slot_of(nck, len);
     float* ru = static_cast<float*>(a.ru) + (p.st * kRing + slot) * NV + p.c0;
-    for (int v = threadIdx.x; v < NVS; v += kThreads) {
-      a.o[p.st * NV + p.c0 + v] = gdn_row_and_output(s, j, v);
+    if (v < NVS) {
+      a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, j, v, hu, ho);
       ru[v] = s.U[j - 1][v];
     }
     // append the current record (bit copies); each slice its own v columns
@@ -451,11 +464,16 @@ __device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, NV / 
       }
       __syncthreads();
     }
+    if constexpr (!VG) __syncthreads();   // dots visible (VG: the barrier above)
+    static_assert(NVS <= kThreads, "one thread per column");
+    const int v = threadIdx.x;
+    float hu = 0.0f, ho = 0.0f;
+    if (v < NVS) gdn_held_sums(s, m, v, hu, ho);
     RegTile<4, NK, NVS> S;
     raw.decode(S);
     tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
-    for (int v = threadIdx.x; v < NVS; v += kThreads) {
-      a.o[p.st * NV + p.c0 + v] = gdn_row_and_output(s, m, v);
+    if (v < NVS) {
+      a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, m, v, hu, ho);
       if constexpr (!VG) {
         // fold columns r_{cur,i} u_i (same thread, same column v)
 #pragma unroll
