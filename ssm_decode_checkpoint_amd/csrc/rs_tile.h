@@ -161,13 +161,30 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float clamp_mag(float q, float m) { return fminf(fmaxf(q, -m), m); }
 
-// Four E4M3FN codes of x[0..3] / sc, element i in byte i.
-__device__ __forceinline__ uint32_t fp8_codes4(const float* x, float sc) {
+// The correctly rounded quotient x / d from y = RN(1/d), by Markstein's
+// correction step (Markstein 1990; Muller et al., Handbook of Floating-Point
+// Arithmetic): q = RN(x y) is within one ulp of x / d, the remainder x - d q is
+// exact by FMA, and RN(q + (x - d q) y) = RN(x / d) when neither 1/d nor the
+// quotient overflows or underflows. A zero quotient takes the sign of x, as the
+// division gives it. Below the scale kRecipMin the callers divide: there 1/d
+// could overflow. Subnormal quotients (|x / d| < 2^-126) cannot change a code.
+constexpr float kRecipMin = 0x1p-125f;
+
+__device__ __forceinline__ float quot(float x, float d, float y, bool recip) {
+  if (!recip) return x / d;
+  const float q = x * y;
+  const float r = fmaf(-q, d, x);
+  return copysignf(fmaf(r, y, q), x);
+}
+
+// Four E4M3FN codes of x[0..3] / sc, element i in byte i (y = RN(1/sc)).
+__device__ __forceinline__ uint32_t fp8_codes4(const float* x, float sc, float y) {
+  const bool rc = sc >= kRecipMin;
   s16x2 r = {0, 0};
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(x[0] / sc, 448.0f), clamp_mag(x[1] / sc, 448.0f), 1.0f,
-                                               false);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(x[2] / sc, 448.0f), clamp_mag(x[3] / sc, 448.0f), 1.0f,
-                                               true);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(quot(x[0], sc, y, rc), 448.0f),
+                                               clamp_mag(quot(x[1], sc, y, rc), 448.0f), 1.0f, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(quot(x[2], sc, y, rc), 448.0f),
+                                               clamp_mag(quot(x[3], sc, y, rc), 448.0f), 1.0f, true);
   return static_cast<uint32_t>(static_cast<uint16_t>(r.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(r.y)) << 16);
 }
 
@@ -180,11 +197,16 @@ __device__ __forceinline__ uint32_t e4m3_code_of(float q) {
 
 // Eight E2M1 codes of x[0..7] / sd, element i in nibble i (all 0 when sd = 0).
 __device__ __forceinline__ uint32_t nvfp4_codes8(const float* x, float sd) {
+  const bool rc = sd >= kRecipMin;
+  const float y = 1.0f / sd;   // one correctly rounded division per eight codes
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = clamp_mag(quot(x[i], sd, y, rc), 6.0f);
   uint32_t w = 0u;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[0] / sd, 6.0f), clamp_mag(x[1] / sd, 6.0f), 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[2] / sd, 6.0f), clamp_mag(x[3] / sd, 6.0f), 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[4] / sd, 6.0f), clamp_mag(x[5] / sd, 6.0f), 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, clamp_mag(x[6] / sd, 6.0f), clamp_mag(x[7] / sd, 6.0f), 1.0f, 3);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
   return sd == 0.0f ? 0u : w;
 }
 
@@ -220,10 +242,11 @@ __device__ __forceinline__ void tile_round_trip(RegTile<E, NR, NC>& M, float* sc
   } else if constexpr (FMT == FMT_FP8) {
     static_assert(E == 8, "fp8 state chunks are eight elements");
     const float sc = fp8_scale_of(tile_absmax(M, scratch4));
+    const float y = 1.0f / sc;
 #pragma unroll
     for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
       Raw<FMT_FP8, 8> r;
-      r.v = make_uint2(fp8_codes4(M.v[k], sc), fp8_codes4(M.v[k] + 4, sc));
+      r.v = make_uint2(fp8_codes4(M.v[k], sc, y), fp8_codes4(M.v[k] + 4, sc, y));
       decode_chunk<FMT_FP8, 8>(r, sc, M.v[k]);
     }
   } else if constexpr (FMT == FMT_NVFP4) {
@@ -279,12 +302,13 @@ __device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const
   } else if constexpr (FMT == FMT_FP8) {
     static_assert(E == 8, "fp8 state chunks are eight elements");
     const float sc = fp8_scale_of(tile_absmax(M, scratch4));
+    const float y = 1.0f / sc;
     uint8_t* base = static_cast<uint8_t*>(sb.data) + mat * NR * NC;
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
       const int row = RegTile<E, NR, NC>::row(k);
       if (row < NR)
-        nt_store(make_uint2(fp8_codes4(M.v[k], sc), fp8_codes4(M.v[k] + 4, sc)),
+        nt_store(make_uint2(fp8_codes4(M.v[k], sc, y), fp8_codes4(M.v[k] + 4, sc, y)),
                  reinterpret_cast<uint2*>(base + row * NC + c * E));
     }
     if (threadIdx.x == 0) sb.tscale[mat] = sc;

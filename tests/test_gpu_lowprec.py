@@ -69,6 +69,57 @@ def test_requant_bit_exact_from_f32(shape, heavy):
     assert np.array_equal(got[0], want[0]), f"{np.count_nonzero(got[0] != want[0])} code bytes differ"
 
 
+def _boundary_tiles(b, h, rows, cols, seed):
+    """fp32 matrices whose elements sit on E2M1 rounding boundaries of their own
+    block scale (ties, and one and two float32 steps either side), so that the
+    codes depend on the quotient x / scale being rounded exactly as a float32
+    division rounds it. The matrix max and each block's max are placed first,
+    which fixes the tensor scale and every block scale (the oracle's formulas)."""
+    g = np.random.default_rng(seed)
+    F = np.float32
+    x = np.zeros((b, h, rows, cols), F)
+    bounds = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], F)
+    for i in range(b):
+        for j in range(h):
+            amax = F(np.exp(g.uniform(np.log(0.3), np.log(300.0))))
+            ts = F(amax / F(2688.0))
+            d = F(F(6.0) * ts)
+            for r in range(rows):
+                for k in range(cols // 16):
+                    bm = amax if (r == 0 and k == 0) else F(amax * F(g.uniform(0.02, 1.0)))
+                    s = quant.e4m3_encode_mag(F(bm / d))
+                    sd = F(quant.e4m3_decode(s) * ts)
+                    blk = np.zeros(16, F)
+                    blk[0] = bm
+                    for e in range(1, 16):
+                        q = F(bounds[g.integers(len(bounds))] * sd)
+                        q = np.nextafter(q, F(np.inf) if g.integers(2) else F(0.0)) if g.integers(3) == 0 else q
+                        if g.integers(4) == 0:
+                            q = np.nextafter(np.nextafter(q, F(np.inf)), F(np.inf))
+                        if abs(q) > bm:
+                            q = F(0.0)
+                        blk[e] = -q if g.integers(2) else q
+                    g.shuffle(blk)
+                    x[i, j, r, 16 * k: 16 * k + 16] = blk
+    return x
+
+
+def test_requant_codes_on_rounding_boundaries():
+    """The GPU forms each quotient from one reciprocal per block plus a
+    correction step; on values at and next to the code boundaries its codes must
+    still equal those of the oracle's float32 division."""
+    w = W.TINY_M2.with_(batch=2, nheads=8, dstate=128, headdim=64, ngroups=2)
+    layer, bufs = m2_layer(w, read_copy=rs.RS_NVFP4)
+    tiles = _boundary_tiles(w.batch, w.nheads, w.dstate, w.headdim, 47)
+    rs.ckpt_f32_view(layer, bufs).copy_(torch.from_numpy(tiles).cuda())
+    rs.rs_requant_read_copy(layer, bufs)
+    got = _read_copy(layer, bufs)
+    want = _oracle_copy(tiles)
+    assert np.array_equal(got[2].view(np.uint32), want[2].view(np.uint32))
+    assert np.array_equal(got[1], want[1])
+    assert np.array_equal(got[0], want[0]), f"{np.count_nonzero(got[0] != want[0])} code bytes differ"
+
+
 def test_requant_bit_exact_from_f16_and_fp8():
     w = W.TINY_M2.with_(batch=2, nheads=16, dstate=128, headdim=64, ngroups=2)
     # fp16 checkpoint (values rounded by torch's conversion)
