@@ -467,9 +467,21 @@ __device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, SM& s, int m) {
 }
 
 // Store the folded tile in the checkpoint format, and the NVFP4 read copy of
-// the stored values when asked.
+// the stored values when asked. For an fp32 checkpoint the read copy's maximum
+// is reduced before the checkpoint's stores go out: the reduction's workgroup
+// barriers would otherwise wait for those 32 KiB of stores (measured 476 ->
+// 454 us per flush at batch 256). For fp16 and fp8 checkpoints the stores go
+// out first and overlap the requantisation (reordering those measured slower).
 template <int CKF, bool RC, int E, int NR, int NC>
 __device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTile<E, NR, NC>& H, float* s4) {
+  if constexpr (RC && CKF == FMT_F32) {
+    if (a.fuse_rc) {
+      const float amax = tile_absmax(H, s4);
+      tile_store<FMT_F32>(a.ck, tile, H, s4);
+      tile_store_nvfp4(a.rc, tile, H, amax);
+      return;
+    }
+  }
   tile_store<CKF>(a.ck, tile, H, s4);
   if constexpr (RC) {
     if (a.fuse_rc) {

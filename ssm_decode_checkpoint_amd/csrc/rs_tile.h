@@ -262,6 +262,10 @@ __device__ __forceinline__ void tile_round_trip(RegTile<E, NR, NC>& M, float* sc
   }
 }
 
+template <int E, int NR, int NC>
+__device__ __forceinline__ void tile_store_nvfp4(const StateBuf& sb, size_t mat, const RegTile<E, NR, NC>& M,
+                                                 float amax);
+
 // Store M into sb in format FMT. FP8 and NVFP4 compute their scales from M.
 // All threads must call.
 template <int FMT, int E, int NR, int NC>
@@ -313,8 +317,19 @@ __device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const
     }
     if (threadIdx.x == 0) sb.tscale[mat] = sc;
   } else {
+    tile_store_nvfp4(sb, mat, M, tile_absmax(M, scratch4));
+  }
+}
+
+// NVFP4 store of M whose matrix |max| is amax (already reduced: no barrier here).
+template <int E, int NR, int NC>
+__device__ __forceinline__ void tile_store_nvfp4(const StateBuf& sb, size_t mat, const RegTile<E, NR, NC>& M,
+                                                 float amax) {
+  using TM = TileMap<E, NR, NC>;
+  const int c = static_cast<int>(threadIdx.x % TM::TPR);
+  {
     static_assert(E == 8, "NVFP4 blocks span two threads of eight columns");
-    const float ts = nvfp4_tscale_of(tile_absmax(M, scratch4));
+    const float ts = nvfp4_tscale_of(amax);
     uint8_t* base = static_cast<uint8_t*>(sb.data) + mat * NR * NC / 2;
     uint8_t* sbase = sb.nv_scale + mat * NR * NC / 16;
 #pragma unroll
