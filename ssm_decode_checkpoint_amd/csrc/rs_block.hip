@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void gated_norm_kernel(NormArgs a) {
       ss += t * t;
     }
   }
-  ss = wave_sum_stride(ss, 1);
+  ss = wave_sum_stride<1>(ss);
   const float rs_ = 1.0f / sqrtf(ss / static_cast<float>(a.gs) + a.eps);
 #pragma unroll
   for (int j = 0; j < kNormRuns; ++j) {

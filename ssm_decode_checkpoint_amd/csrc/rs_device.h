@@ -205,10 +205,45 @@ __device__ __forceinline__ void decode_chunk(const Raw<FMT, E>& r, float ms, flo
 // ----------------------------------------------------------------------------
 // wavefront helpers
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum_stride(float v, int from) {
-  // sum over lanes that agree on (lane mod from); from is a power of two < 64
-  for (int off = from; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Cross-lane reductions without the LDS path: inside a 16-lane row through
+// DPP operand modifiers (quad_perm, row rotations and mirrors fold into the
+// add), across rows through gfx950's permlane swaps, which exchange rows 0/1
+// and 2/3 (permlane16) or the two halves of the wavefront (permlane32).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRor4 = 0x124;       // row_ror:4
+constexpr int kDppRor8 = 0x128;       // row_ror:8
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+
+// v of this lane and of lane ^ 16 (respectively ^ 32), as the pair the swap returns
+__device__ __forceinline__ f32x2 swap16(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(q[0]), __uint_as_float(q[1])};
+}
+__device__ __forceinline__ f32x2 swap32(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2{__uint_as_float(q[0]), __uint_as_float(q[1])};
+}
+
+// Sum over the lanes that agree on (lane mod FROM); FROM a power of two <= 32.
+template <int FROM>
+__device__ __forceinline__ float wave_sum_stride(float v) {
+  static_assert(FROM >= 1 && FROM <= 32 && (FROM & (FROM - 1)) == 0, "power of two up to 32");
+  if constexpr (FROM == 1) v += dpp_mov<kDppXor1>(v);
+  if constexpr (FROM <= 2) v += dpp_mov<kDppXor2>(v);
+  if constexpr (FROM <= 4) v += dpp_mov<kDppRor4>(v);   // with ror 8: the row's lanes of one residue mod 4
+  if constexpr (FROM <= 8) v += dpp_mov<kDppRor8>(v);
+  if constexpr (FROM <= 16) {
+    const f32x2 p = swap16(v);
+    v = p.x + p.y;
+  }
+  const f32x2 p = swap32(v);
+  return p.x + p.y;
 }
 
 // One lane's part of a length-N dot of LDS rows held by a 16-lane group: lane
@@ -238,18 +273,25 @@ __device__ __forceinline__ float lds_dot16(const float* a, const float* b, int l
   return part;
 }
 
+// Sum over each aligned group of 16 lanes (a DPP row), in every lane of it.
 __device__ __forceinline__ float group_sum16(float v) {
-  // sum over aligned groups of 16 lanes
-  v += __shfl_xor(v, 8, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 1, 64);
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  v += dpp_mov<kDppHalfMirror>(v);
+  v += dpp_mov<kDppMirror>(v);
   return v;
 }
 
+// Maximum over the wavefront, in every lane.
 __device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppMirror>(v));
+  f32x2 p = swap16(v);
+  v = fmaxf(p.x, p.y);
+  p = swap32(v);
+  return fmaxf(p.x, p.y);
 }
 
 // Workgroups are handed to the eight XCDs round-robin; give each XCD a

@@ -398,9 +398,7 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_wave_kernel(M2Args a) {
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    acc[i] += __shfl_xor(acc[i], 8, 64);
-    acc[i] += __shfl_xor(acc[i], 16, 64);
-    acc[i] += __shfl_xor(acc[i], 32, 64);
+    acc[i] = wave_sum_stride<8>(acc[i]);
   }
   if (lane < 8) {
     float4* yp = reinterpret_cast<float4*>(a.y + mat * NC + lane * 8);

@@ -81,7 +81,7 @@ __device__ __forceinline__ void tile_matvec(const RegTile<E, NR, NC>& M, const f
 #pragma unroll
   for (int q = 0; q < Q; ++q)
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[q][i] = wave_sum_stride(acc[q][i], TM::TPR);
+    for (int i = 0; i < E; ++i) acc[q][i] = wave_sum_stride<TM::TPR>(acc[q][i]);
   if (lane < TM::TPR) {
 #pragma unroll
     for (int q = 0; q < Q; ++q)
@@ -121,7 +121,7 @@ __device__ __forceinline__ void tiles_matvec(const RegTile<E, NR, NC> (&M)[T], c
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
-    for (int i = 0; i < E; ++i) acc[t][i] = wave_sum_stride(acc[t][i], TM::TPR);
+    for (int i = 0; i < E; ++i) acc[t][i] = wave_sum_stride<TM::TPR>(acc[t][i]);
   if (lane < TM::TPR) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -226,7 +226,7 @@ __device__ __forceinline__ uint32_t nvfp4_block_code(const float* x, float ts) {
   float bm = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(x[i]));
-  bm = fmaxf(bm, __shfl_xor(bm, 1, 64));
+  bm = fmaxf(bm, dpp_mov<kDppXor1>(bm));
   return e4m3_code_of(bm / (6.0f * ts));
 }
 
