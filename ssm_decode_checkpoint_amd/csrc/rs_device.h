@@ -45,22 +45,14 @@ template <>
 __device__ __forceinline__ bf16 from_f<bf16>(float v) { return bf16{static_cast<uint16_t>(__float_as_uint(v) >> 16)}; }
 
 // ----------------------------------------------------------------------------
-// E4M3FN and E2M1 code values (the encoders sit with the tile stores)
+// E4M3FN code values (decoding and encoding otherwise use the gfx950
+// conversion instructions, with the tile loads and stores)
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
   const uint32_t e = (code >> 3) & 15u, m = code & 7u;
   float mag = (e == 0) ? static_cast<float>(m) * 0.001953125f  // m * 2^-9
                        : __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
   return (code & 0x80u) ? -mag : mag;
-}
-
-__device__ __forceinline__ float e2m1_value(uint32_t code) {
-  // magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}
-  const uint32_t i = code & 7u;
-  // i < 4: 0.5 i;  i >= 4: 2^(1 + (i-4)/2) * (1.5 if i odd else 1)
-  float mag = (i < 4u) ? 0.5f * static_cast<float>(i)
-                       : static_cast<float>(1u << (((i - 4u) >> 1) + 1u)) * ((i & 1u) ? 1.5f : 1.0f);
-  return (code & 8u) ? -mag : mag;
 }
 
 // ----------------------------------------------------------------------------

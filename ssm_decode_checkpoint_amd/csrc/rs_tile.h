@@ -373,19 +373,6 @@ __device__ __forceinline__ void tile_rank_update(RegTile<E, NR, NC>& H, float L,
   }
 }
 
-// Copy `n` input elements (a record row) between global buffers, 16 bytes per
-// lane where the length allows; used for ring appends (bit copies).
-template <typename T>
-__device__ __forceinline__ void copy_row(T* dst, const T* src, int n) {
-  constexpr int V = 16 / static_cast<int>(sizeof(T));
-  if (n % V == 0) {
-    for (int i = threadIdx.x; i < n / V; i += kThreads)
-      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
-  } else {
-    for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = src[i];
-  }
-}
-
 // Write n LDS floats that came from T back to a global T row (exact), 16 bytes
 // per lane where the length allows (n % (16/sizeof(T)) == 0, dst 16-byte aligned).
 template <typename T>
