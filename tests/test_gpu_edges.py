@@ -2,8 +2,8 @@
 
 * Largest sizes: 4096 sequences of the Nemotron-style Mamba-2 layer (a 16 GiB
   fp32 checkpoint: element offsets pass 2^31, byte offsets 2^34) and of the
-  Qwen-style GDN layer (8 GiB), replay and conventional; sampled sequences
-  include the last.
+  Qwen-style GDN and KDA layers (8 GiB), replay and conventional; sampled
+  sequences include the last. Slot copies at the same size.
   Sequences other than the sampled ones reuse the sampled ones' inputs (their
   values do not matter here); the sampled sequences get exactly their own.
 * Degenerate gates and steps: dt = 0 (no input, no decay) and decays that
@@ -16,7 +16,7 @@ import torch
 
 import ssm_decode_checkpoint_amd as rs
 import workloads as W
-from oracle import decode, kda
+from oracle import decode, gdn, kda
 from gpu_harness import (DEV, dev_in, gdn_layer, gdn_tok_dev, load_state_f32, m2_layer, m2_tok_dev, params_dev,
                          read_meta, read_state_f32, rel_l2, require_gpu, y_buf)
 
@@ -71,15 +71,17 @@ def test_mamba2_4096_sequences_past_32bit_offsets():
     assert worst <= 1e-5 and worst_c <= 1e-5, (worst, worst_c)
 
 
-def test_gdn_4096_sequences():
-    w = W.GDN_QWEN.with_(batch=BIG, seed=181)
+@pytest.mark.parametrize("gate", ["head", "channel"])
+def test_gdn_4096_sequences(gate):
+    """Gated DeltaNet, and KDA (per-channel gate: a 1 GiB gate ring beside the 8 GiB state)."""
+    w = W.GDN_QWEN.with_(batch=BIG, seed=181, gate=gate)
     gp = W.gdn_params(w)
     S0 = W.gdn_init_states(w, SEQS)
     layer, bufs = gdn_layer(w)
     ck = rs.ckpt_f32_view(layer, bufs)
     for i, b in enumerate(SEQS):
         ck[b].copy_(torch.from_numpy(np.ascontiguousarray(S0[i].transpose(0, 2, 1))).to(DEV))
-    ref = decode.GDNConventional(S0)
+    ref = decode.GDNConventional(S0, rule=kda if gate == "channel" else gdn)
     worst = 0.0
     for t in range(17):
         tok = W.gdn_step(w, t, SEQS, gp)
@@ -92,6 +94,31 @@ def test_gdn_4096_sequences():
     nck, ln, nd, err, arrive = read_meta(layer, bufs)
     assert (nck == 16).all() and (ln == 1).all() and not err.any() and not arrive.any()
     assert worst <= 1e-5, worst
+
+
+def test_copy_slots_past_32bit_offsets():
+    """Slot copies at 4096 Nemotron-style sequences (checkpoint row offsets past 2^34
+    bytes): the last sequence is forked into the first and the first into a middle
+    slot; copies are bit-exact and untouched slots keep their bits."""
+    w = W.M2_NEMOTRON.with_(batch=BIG, seed=186)
+    layer, bufs = m2_layer(w)
+    ck = rs.ckpt_f32_view(layer, bufs)
+    g = torch.Generator(device=DEV).manual_seed(186)
+    for b in (0, 1, 2047, 4095):
+        ck[b].copy_(torch.randn(ck[b].shape, generator=g, device=DEV))
+    ring = rs.ring_view(layer, bufs, "x")
+    ring[4095].copy_(torch.randn(ring[4095].shape, generator=g, device=DEV).to(ring.dtype))
+    meta_before = read_meta(layer, bufs)
+    src_rows = {b: ck[b].clone() for b in (0, 1, 4095)}
+    ring_src = ring[4095].clone()
+    rs.rs_copy_slots(layer, bufs, torch.tensor([4095, 0], dtype=torch.int32, device=DEV), layer, bufs,
+                     torch.tensor([1, 2047], dtype=torch.int32, device=DEV), 2)
+    torch.cuda.synchronize()
+    assert torch.equal(ck[1], src_rows[4095]) and torch.equal(ck[2047], src_rows[0])
+    assert torch.equal(ck[0], src_rows[0]) and torch.equal(ck[4095], src_rows[4095])
+    assert torch.equal(ring[1], ring_src)
+    nck, ln, nd, err, arrive = read_meta(layer, bufs)
+    assert (ln == meta_before[1]).all() and not arrive.any()
 
 
 def test_mamba2_degenerate_steps():
