@@ -784,11 +784,30 @@ def bench_copy(args, torch, rs):
     rtot, rper = tm.run(lambda ev: _marked(ev, 0, tm.stream, lambda: torch.sum(srcf, dim=0, out=acc)), args.steps,
                         args.warmup, 1)
     rms = float(rper.mean())
+    # the read-only stream with the decode kernels' tile shapes (librs_probe.so)
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "ssm_decode_checkpoint_amd", "librs_probe.so"))
+    probe.rs_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p]
+    probe.rs_probe_read.restype = ctypes.c_int32
+    sums = torch.empty(n // (16 * 256 * 4), dtype=torch.float32, device="cuda")   # tiles of the smallest shape
+    tiles = {}
+    for threads, per in ((256, 8), (256, 4), (128, 16)):
+        def call(threads=threads, per=per):
+            st = probe.rs_probe_read(src.data_ptr(), sums.data_ptr(), n, threads, per, tm.stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError(f"rs_probe_read returned {st}")
+        _, pper = tm.run(lambda ev: _marked(ev, 0, tm.stream, call), args.steps, args.warmup, 1)
+        pms = float(pper.mean())
+        tiles[f"{threads}x{per}"] = {"tile_kib": threads * per * 16 // 1024, "ms": pms, "gbs": n / (pms * 1e-3) / 1e9}
     return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n},
             "read_reference": {"what": "torch.sum over the same 1 GiB (read only)", "ms": rms,
-                               "gbs": n / (rms * 1e-3) / 1e9}}
+                               "gbs": n / (rms * 1e-3) / 1e9},
+            "read_probe": {"what": "1 GiB read as tiles of threads x 16-byte non-temporal loads per workgroup "
+                                   "(rs_probe_read); 256x8 is the decode kernels' 32 KiB state tile",
+                           "tiles": tiles}}
 
 
 def main():

@@ -1,0 +1,29 @@
+/* Measurement helper beside the decode library (librs_probe.so), not part of
+ * the decode ABI: a read-only stream with the decode kernels' access pattern,
+ * the reference for how much of the chip's read bandwidth a kernel that
+ * streams such tiles can reach. */
+#ifndef RS_PROBE_H
+#define RS_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` of device memory at `src` (16-byte aligned) as tiles of
+ * threads x per_thread 16-byte non-temporal loads, one tile per workgroup of
+ * `threads` threads; each workgroup writes the sum of its tile to
+ * out[tile] (device float[bytes / tile bytes], caller-owned). Shapes offered:
+ * 256 x 8 (32 KiB tiles, the decode kernels' state tile), 256 x 4 (16 KiB),
+ * 128 x 16 (32 KiB). Returns 0 when launched on `stream` (a hipStream_t, may
+ * be NULL); -1 bad pointer, -2 bytes not a positive multiple of the tile (or
+ * too many tiles), -3 launch error, -4 shape not offered. Asynchronous. */
+int32_t rs_probe_read(const void* src, float* out, uint64_t bytes, int32_t threads, int32_t per_thread,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

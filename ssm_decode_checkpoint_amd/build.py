@@ -20,6 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librs.so")
+PROBE_LIB = os.path.join(PKG, "librs_probe.so")   # measurement helper, separate from the decode library
 SOURCES = ["rs_api.hip", "rs_commit.hip", "rs_block.hip", "rs_mamba2.hip", "rs_m2_16x16.hip", "rs_m2_64x64.hip", "rs_m2_128x64.hip",
            "rs_m2_128x128.hip", "rs_gdn.hip"]
 
@@ -55,8 +56,15 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     shutil.move(tmp, LIB)
+    probe = _compile("rs_probe.hip")
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", probe, "-o", PROBE_LIB + ".tmp"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    shutil.move(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
         print(f"built {LIB}")
+        print(f"built {PROBE_LIB}")
     return LIB
 
 

@@ -29,6 +29,24 @@ def test_exports_every_declared_symbol():
     assert rs.status_string(rs.RS_E_ALIGN).startswith("pointer")
 
 
+def test_probe_library_exports_and_checks_arguments():
+    """librs_probe.so (the read-stream measurement helper) exports what
+    include/rs_probe.h declares and rejects bad arguments before launching."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    hdr = open(os.path.join(root, "include", "rs_probe.h")).read()
+    names = re.findall(r"^\s*int32_t\s+(rs_\w+)\s*\(", hdr, re.M)
+    assert names == ["rs_probe_read"]
+    lib = C.CDLL(os.path.join(root, "ssm_decode_checkpoint_amd", "librs_probe.so"))
+    f = lib.rs_probe_read
+    f.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_void_p]
+    f.restype = C.c_int32
+    p = C.c_void_p(0x10000)
+    assert f(None, p, 1 << 20, 256, 8, None) == -1
+    assert f(C.c_void_p(0x10004), p, 1 << 20, 256, 8, None) == -1
+    assert f(p, p, (1 << 20) + 16, 256, 8, None) == -2 and f(p, p, 0, 256, 4, None) == -2
+    assert f(p, p, 1 << 20, 64, 8, None) == -4
+
+
 def test_struct_sizes_match_header():
     assert C.sizeof(rs.RsConfig) == 17 * 4
     assert C.sizeof(rs.RsBuffers) == 5 * 8
