@@ -260,6 +260,8 @@ def bench_mamba2(args, torch, rs):
     fl_ms = float(per_r[:, RING - 1].mean())
     cv_ms = float(per_c.mean())
     win_bytes = nf_bytes + byt["flush"] * B
+    # what a plain stream of the same 32 KiB tiles reads on this chip, after the timed runs
+    probe_gbs = probe_read_gbs(torch, tm)
     win_ms = total_r / K
     return {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm,
@@ -271,7 +273,8 @@ def bench_mamba2(args, torch, rs):
         "roofline": {"bound": "hbm", "achieved": nf_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": nf_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile("m2_nonflush_b256"),
                      "kernel": "m2_nonflush_kernel", "avg_launch_ms": nf_avg_ms,
-                     "alg_bytes_per_launch": nf_bytes / (RING - 1)},
+                     "alg_bytes_per_launch": nf_bytes / (RING - 1),
+                     "read_stream_gbs": probe_gbs, "frac_of_read_stream": nf_gbs / probe_gbs},
         "replay": {"tokens_per_s": value, "window_ms": win_ms, "window_alg_bytes": win_bytes,
                    "window_gbs": win_bytes / (win_ms * 1e-3) / 1e9,
                    "nonflush_avg_ms": nf_avg_ms, "nonflush_gbs": nf_gbs,
@@ -768,6 +771,26 @@ def lowprec_error(args, torch, rs):
             "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
 
 
+def probe_read_gbs(torch, tm, nbytes=1 << 30, threads=256, per=8, steps=10, warmup=2):
+    """Read bandwidth of a plain stream of the decode kernels' 32 KiB tiles
+    (rs_probe_read in librs_probe.so) over nbytes of device memory."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "ssm_decode_checkpoint_amd", "librs_probe.so"))
+    probe.rs_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_void_p]
+    probe.rs_probe_read.restype = ctypes.c_int32
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sums = torch.empty(nbytes // (16 * threads * per), dtype=torch.float32, device="cuda")
+
+    def call():
+        st = probe.rs_probe_read(src.data_ptr(), sums.data_ptr(), nbytes, threads, per, tm.stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"rs_probe_read returned {st}")
+
+    _, per_ms = tm.run(lambda ev: _marked(ev, 0, tm.stream, call), steps, warmup, 1)
+    return nbytes / (float(per_ms.mean()) * 1e-3) / 1e9
+
+
 def bench_copy(args, torch, rs):
     """A plain 1 GiB device copy (torch's copy kernel): the known-size reference
     that HBM traffic counters are scaled by."""
@@ -785,21 +808,11 @@ def bench_copy(args, torch, rs):
                         args.warmup, 1)
     rms = float(rper.mean())
     # the read-only stream with the decode kernels' tile shapes (librs_probe.so)
-    import ctypes
-    probe = ctypes.CDLL(os.path.join(ROOT, "ssm_decode_checkpoint_amd", "librs_probe.so"))
-    probe.rs_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
-                                    ctypes.c_int32, ctypes.c_void_p]
-    probe.rs_probe_read.restype = ctypes.c_int32
-    sums = torch.empty(n // (16 * 256 * 4), dtype=torch.float32, device="cuda")   # tiles of the smallest shape
+    del dst
     tiles = {}
     for threads, per in ((256, 8), (256, 4), (128, 16)):
-        def call(threads=threads, per=per):
-            st = probe.rs_probe_read(src.data_ptr(), sums.data_ptr(), n, threads, per, tm.stream.cuda_stream)
-            if st != 0:
-                raise RuntimeError(f"rs_probe_read returned {st}")
-        _, pper = tm.run(lambda ev: _marked(ev, 0, tm.stream, call), args.steps, args.warmup, 1)
-        pms = float(pper.mean())
-        tiles[f"{threads}x{per}"] = {"tile_kib": threads * per * 16 // 1024, "ms": pms, "gbs": n / (pms * 1e-3) / 1e9}
+        tiles[f"{threads}x{per}"] = {"tile_kib": threads * per * 16 // 1024,
+                                     "gbs": probe_read_gbs(torch, tm, n, threads, per, args.steps, args.warmup)}
     return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n},
