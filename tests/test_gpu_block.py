@@ -79,7 +79,7 @@ def _split(w, v):
             v[..., d + gn:].reshape(*lead, w.ngroups, w.dstate).astype(np.float32))
 
 
-@pytest.mark.parametrize("in_dtype,width", [("f32", 4), ("bf16", 4), ("bf16", 2)])
+@pytest.mark.parametrize("in_dtype,width", [("f32", 4), ("bf16", 4), ("bf16", 2), ("f32", 3), ("bf16", 1)])
 def test_conv_then_ssm_steps(in_dtype, width):
     w = W.TINY_M2.with_(batch=4, init_std=0.4, seed=210, in_dtype=in_dtype)
     bp = W.block_params(w)

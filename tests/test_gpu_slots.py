@@ -149,11 +149,14 @@ def test_delta_rule_fork_with_cached_rows(gate):
     assert worst <= 1e-5, worst
 
 
-def test_low_precision_fork_copies_scales_and_read_copy():
-    """FP8 checkpoint (per-matrix scales) with an NVFP4 read copy (codes, block
-    and tensor scales): the fork reads exactly what its source reads."""
+@pytest.mark.parametrize("ckpt,rc", [("fp8", True), ("nvfp4", False), ("f16", True)])
+def test_low_precision_fork_copies_scales_and_read_copy(ckpt, rc):
+    """Low-precision checkpoints (FP8 with its per-matrix scales, uniform NVFP4
+    with block and tensor scales, FP16), with or without an NVFP4 read copy: the
+    fork reads exactly what its source reads."""
     w = W.TINY_M2.with_(batch=4, init_std=0.0, seed=203)
-    p, A, D, layer, bufs, _ = _m2_case(w, ckpt_dtype=rs.RS_FP8E4M3, read_copy=rs.RS_NVFP4)
+    code = {"fp8": rs.RS_FP8E4M3, "nvfp4": rs.RS_NVFP4, "f16": rs.RS_F16}[ckpt]
+    p, A, D, layer, bufs, _ = _m2_case(w, ckpt_dtype=code, read_copy=rs.RS_NVFP4 if rc else rs.RS_NONE)
     for t in range(20):
         tok = W.m2_step(w, t, range(w.batch))
         rs.rs_step(layer, bufs, m2_tok_dev(tok, w.in_dtype), A, D, y_buf(w.batch, w.nheads, w.headdim))
