@@ -260,8 +260,11 @@ def bench_mamba2(args, torch, rs):
     fl_ms = float(per_r[:, RING - 1].mean())
     cv_ms = float(per_c.mean())
     win_bytes = nf_bytes + byt["flush"] * B
-    # what a plain stream of the same 32 KiB tiles reads on this chip, after the timed runs
+    # what a plain stream of the same 32 KiB tiles reaches on this chip, after the timed
+    # runs: read only, and with the step's writes per tile (y and the appended record)
     probe_gbs = probe_read_gbs(torch, tm)
+    wtile = m2_writes_per_tile(w)
+    probe_rw_gbs = probe_read_gbs(torch, tm, write_bytes=wtile)
     win_ms = total_r / K
     return {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm,
@@ -274,7 +277,9 @@ def bench_mamba2(args, torch, rs):
                      "frac": nf_gbs / HBM_PEAK_GBS, "traffic": traffic_from_profile("m2_nonflush_b256"),
                      "kernel": "m2_nonflush_kernel", "avg_launch_ms": nf_avg_ms,
                      "alg_bytes_per_launch": nf_bytes / (RING - 1),
-                     "read_stream_gbs": probe_gbs, "frac_of_read_stream": nf_gbs / probe_gbs},
+                     "read_stream_gbs": probe_gbs, "frac_of_read_stream": nf_gbs / probe_gbs,
+                     "read_write_stream_gbs": probe_rw_gbs, "write_bytes_per_tile": wtile,
+                     "frac_of_read_write_stream": nf_gbs / probe_rw_gbs},
         "replay": {"tokens_per_s": value, "window_ms": win_ms, "window_alg_bytes": win_bytes,
                    "window_gbs": win_bytes / (win_ms * 1e-3) / 1e9,
                    "nonflush_avg_ms": nf_avg_ms, "nonflush_gbs": nf_gbs,
@@ -771,24 +776,45 @@ def lowprec_error(args, torch, rs):
             "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
 
 
-def probe_read_gbs(torch, tm, nbytes=1 << 30, threads=256, per=8, steps=10, warmup=2):
-    """Read bandwidth of a plain stream of the decode kernels' 32 KiB tiles
-    (rs_probe_read in librs_probe.so) over nbytes of device memory."""
+def probe_read_gbs(torch, tm, nbytes=1 << 30, threads=256, per=8, steps=10, warmup=2, write_bytes=0):
+    """Bandwidth of a plain stream of the decode kernels' 32 KiB tiles over
+    nbytes of device memory (librs_probe.so): read only (rs_probe_read), or
+    with write_bytes written per tile after its sum (rs_probe_read_write),
+    counting the bytes read plus the bytes written."""
     import ctypes
     probe = ctypes.CDLL(os.path.join(ROOT, "ssm_decode_checkpoint_amd", "librs_probe.so"))
     probe.rs_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_void_p]
     probe.rs_probe_read.restype = ctypes.c_int32
+    probe.rs_probe_read_write.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    probe.rs_probe_read_write.restype = ctypes.c_int32
+    tiles = nbytes // (16 * threads * per)
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
-    sums = torch.empty(nbytes // (16 * threads * per), dtype=torch.float32, device="cuda")
+    if write_bytes:
+        dst = torch.empty(tiles * write_bytes, dtype=torch.uint8, device="cuda")
+    else:
+        dst = torch.empty(tiles, dtype=torch.float32, device="cuda")
 
     def call():
-        st = probe.rs_probe_read(src.data_ptr(), sums.data_ptr(), nbytes, threads, per, tm.stream.cuda_stream)
+        if write_bytes:
+            st = probe.rs_probe_read_write(src.data_ptr(), dst.data_ptr(), nbytes, threads, per, write_bytes,
+                                           tm.stream.cuda_stream)
+        else:
+            st = probe.rs_probe_read(src.data_ptr(), dst.data_ptr(), nbytes, threads, per, tm.stream.cuda_stream)
         if st != 0:
-            raise RuntimeError(f"rs_probe_read returned {st}")
+            raise RuntimeError(f"librs_probe returned {st}")
 
     _, per_ms = tm.run(lambda ev: _marked(ev, 0, tm.stream, call), steps, warmup, 1)
-    return nbytes / (float(per_ms.mean()) * 1e-3) / 1e9
+    return (nbytes + tiles * write_bytes) / (float(per_ms.mean()) * 1e-3) / 1e9
+
+
+def m2_writes_per_tile(w, s_in=2):
+    """Bytes a Mamba-2 non-flush step writes per (sequence, head) tile: y in
+    fp32, the appended x row and dt, and the head's share of the group's B and
+    C rows; rounded to a whole number of 16-byte stores."""
+    b = w.headdim * 4 + w.headdim * s_in + s_in + 2 * w.ngroups * w.dstate * s_in // w.nheads
+    return 16 * max(1, round(b / 16))
 
 
 def bench_copy(args, torch, rs):
@@ -813,6 +839,11 @@ def bench_copy(args, torch, rs):
     for threads, per in ((256, 8), (256, 4), (128, 16)):
         tiles[f"{threads}x{per}"] = {"tile_kib": threads * per * 16 // 1024,
                                      "gbs": probe_read_gbs(torch, tm, n, threads, per, args.steps, args.warmup)}
+    # the 32 KiB tile stream with a write per tile after its sum, as a decode step
+    # writes its output and appended record: what those writes cost in a read stream
+    writes = {}
+    for wb in (128, 256, 416, 1024, 4096):
+        writes[str(wb)] = probe_read_gbs(torch, tm, n, 256, 8, args.steps, args.warmup, write_bytes=wb)
     return {"metric": "device copy GB/s (read + write)", "value": 2 * n / (ms * 1e-3) / 1e9, "unit": "GB/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
             "config": {"workload": "copy_1GiB", "bytes_read": n, "bytes_written": n},
@@ -820,7 +851,10 @@ def bench_copy(args, torch, rs):
                                "gbs": n / (rms * 1e-3) / 1e9},
             "read_probe": {"what": "1 GiB read as tiles of threads x 16-byte non-temporal loads per workgroup "
                                    "(rs_probe_read); 256x8 is the decode kernels' 32 KiB state tile",
-                           "tiles": tiles}}
+                           "tiles": tiles},
+            "read_write_probe": {"what": "the 256x8 tile read with write_bytes written per tile after its sum "
+                                         "(rs_probe_read_write); GB/s of bytes read plus written",
+                                 "gbs_by_write_bytes": writes}}
 
 
 def main():

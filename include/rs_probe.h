@@ -1,7 +1,9 @@
 /* Measurement helper beside the decode library (librs_probe.so), not part of
  * the decode ABI: a read-only stream with the decode kernels' access pattern,
  * the reference for how much of the chip's read bandwidth a kernel that
- * streams such tiles can reach. */
+ * streams such tiles can reach, and the same stream with a small write per
+ * tile, which prices the output and append writes a decode step mixes into
+ * its read stream. */
 #ifndef RS_PROBE_H
 #define RS_PROBE_H
 
@@ -21,6 +23,16 @@ extern "C" {
  * too many tiles), -3 launch error, -4 shape not offered. Asynchronous. */
 int32_t rs_probe_read(const void* src, float* out, uint64_t bytes, int32_t threads, int32_t per_thread,
                       void* stream);
+
+/* The same tiled read of `bytes` at `src`; after its tile is summed, each
+ * workgroup writes `write_bytes` bytes (a positive multiple of 16, at most
+ * threads x 16) to dst + tile * write_bytes as 16-byte non-temporal stores
+ * (device memory of bytes / tile bytes x write_bytes bytes, caller-owned,
+ * 16-byte aligned; the values are sums, only the traffic matters). Same
+ * shapes and return codes as rs_probe_read, plus -5 for a write size out of
+ * range. Asynchronous. */
+int32_t rs_probe_read_write(const void* src, void* dst, uint64_t bytes, int32_t threads, int32_t per_thread,
+                            int32_t write_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_probe_library_exports_and_checks_arguments():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     hdr = open(os.path.join(root, "include", "rs_probe.h")).read()
     names = re.findall(r"^\s*int32_t\s+(rs_\w+)\s*\(", hdr, re.M)
-    assert names == ["rs_probe_read"]
+    assert names == ["rs_probe_read", "rs_probe_read_write"]
     lib = C.CDLL(os.path.join(root, "ssm_decode_checkpoint_amd", "librs_probe.so"))
     f = lib.rs_probe_read
     f.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_void_p]
@@ -45,6 +45,16 @@ def test_probe_library_exports_and_checks_arguments():
     assert f(C.c_void_p(0x10004), p, 1 << 20, 256, 8, None) == -1
     assert f(p, p, (1 << 20) + 16, 256, 8, None) == -2 and f(p, p, 0, 256, 4, None) == -2
     assert f(p, p, 1 << 20, 64, 8, None) == -4
+    g = lib.rs_probe_read_write
+    g.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_int32, C.c_void_p]
+    g.restype = C.c_int32
+    assert g(p, None, 1 << 20, 256, 8, 256, None) == -1
+    assert g(p, C.c_void_p(0x10008), 1 << 20, 256, 8, 256, None) == -1
+    assert g(p, p, (1 << 20) + 16, 256, 8, 256, None) == -2
+    for wb in (0, -16, 8, 24, 256 * 16 + 16):
+        assert g(p, p, 1 << 20, 256, 8, wb, None) == -5, wb
+    assert g(p, p, 1 << 20, 128, 16, 128 * 16 + 16, None) == -5
+    assert g(p, p, 1 << 20, 64, 8, 256, None) == -4
 
 
 def test_struct_sizes_match_header():
