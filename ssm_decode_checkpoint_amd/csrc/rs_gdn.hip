@@ -783,10 +783,8 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
     }
     // drafts into the ring (bit copies); each slice its own v columns
     TIN* rv = static_cast<TIN*>(a.rv) + p.st * kRing * NV + p.c0;
-    for (int idx = threadIdx.x; idx < K * NVS; idx += kThreads) {
-      const int d = idx / NVS, v = idx - d * NVS;
-      rv[slot_of(nck, len + d) * NV + v] = iv[d * vstride + v];
-    }
+    const auto dslot = [&](int d) { return slot_of(nck, len + d); };
+    copy_rows16(rv, NV, iv, vstride, K, NVS, dslot);
     if (p.half == 0) {
       if (static_cast<int>(threadIdx.x) < K) {
         const int d = threadIdx.x, sl = slot_of(nck, len + d);
@@ -795,19 +793,13 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
       }
       if constexpr (VG) {
         float* rgw = static_cast<float*>(a.rg) + p.st * kRing * NK;
-        for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) {
-          const int d = idx / NK, c = idx - d * NK;
-          rgw[slot_of(nck, len + d) * NK + c] = a.g[(d * gstride + p.st) * NK + c];
-        }
+        copy_rows16(rgw, NK, a.g + p.st * NK, gstride * NK, K, NK, dslot);
       }
       if (p.h % a.vpk == 0) {
         TIN* rkw = static_cast<TIN*>(a.rk) + bk * kRing * NK;
         TIN* rqw = static_cast<TIN*>(a.rq) + bk * kRing * NK;
-        for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) {
-          const int d = idx / NK, c = idx - d * NK, sl = slot_of(nck, len + d);
-          rkw[sl * NK + c] = ik[d * kstride + c];
-          rqw[sl * NK + c] = iq[d * kstride + c];
-        }
+        copy_rows16(rkw, NK, ik, kstride, K, NK, dslot);
+        copy_rows16(rqw, NK, iq, kstride, K, NK, dslot);
       }
     }
   }

@@ -649,30 +649,27 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
     raw.decode(H);
     tile_matvec<KQ>(H, &s.Cw[0][0], NR, s.red, s.out);
     const float Dh = a.D[h];
-    for (int idx = threadIdx.x; idx < K * NC; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < K * NC; idx += kThreads) {   // in place: s.out[idx] is this thread's
       const int d = idx / NC, p = idx - d * NC;
       const int J = len + d + 1;
-      float yv = s.L[d] * s.out[d * NC + p];
+      float yv = s.L[d] * s.out[idx];
       for (int e = 0; e < J; ++e) yv += s.w[d][e] * s.X[e][p];
-      a.y[d * xstride + static_cast<size_t>(tile) * NC + p] = yv + Dh * s.X[J - 1][p];
+      s.out[idx] = yv + Dh * s.X[J - 1][p];
     }
-    // drafts into the ring (bit copies)
-    for (int idx = threadIdx.x; idx < K * NC; idx += kThreads) {
-      const int d = idx / NC, p = idx - d * NC;
-      const int slot = static_cast<int>((nck + len + d) & (kRing - 1));
-      rX[slot * NC + p] = inX[d * xstride + p];
+    __syncthreads();
+    for (int i = threadIdx.x; i < K * NC / 4; i += kThreads) {
+      const int d = i / (NC / 4), c = i - d * (NC / 4);
+      const float* o = &s.out[d * NC + 4 * c];
+      nt_store(make_float4(o[0], o[1], o[2], o[3]),
+               reinterpret_cast<float4*>(a.y + d * xstride + static_cast<size_t>(tile) * NC) + c);
     }
-    if (static_cast<int>(threadIdx.x) < K) {
-      const int d = threadIdx.x;
-      rDt[(nck + len + d) & (kRing - 1)] = inDt[d * dstride];
-    }
+    // drafts into the ring from their staged copies (bit copies: the values came from TIN)
+    const auto draft_slot = [&](int d) { return static_cast<int>((nck + len + d) & (kRing - 1)); };
+    store_rows_as(rX, &s.X[len][0], NC, K, NC, draft_slot);
+    if (static_cast<int>(threadIdx.x) < K) rDt[draft_slot(threadIdx.x)] = from_f<TIN>(s.dt[len + threadIdx.x]);
     if (h % a.hpg == 0) {
-      for (int idx = threadIdx.x; idx < K * NR; idx += kThreads) {
-        const int d = idx / NR, r = idx - d * NR;
-        const int slot = static_cast<int>((nck + len + d) & (kRing - 1));
-        rB[slot * NR + r] = inB[d * gstride + r];
-        rC[slot * NR + r] = inC[d * gstride + r];
-      }
+      store_rows_as(rB, &s.B[len][0], NR, K, NR, draft_slot);
+      store_rows_as(rC, &s.Cw[0][0], NR, K, NR, draft_slot);
     }
   }
   arr.finish(mp, actr, h, a.nheads, MetaOp::Append, K, nck, len, nd);

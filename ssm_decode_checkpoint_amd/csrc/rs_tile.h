@@ -373,6 +373,22 @@ __device__ __forceinline__ void tile_rank_update(RegTile<E, NR, NC>& H, float L,
   }
 }
 
+// The 16 / sizeof(T) floats at src as 16 bytes of T. Exact for values that
+// came from T (bf16 keeps the upper half of the float's bits).
+template <typename T>
+__device__ __forceinline__ uint4 pack16(const float* src) {
+  if constexpr (sizeof(T) == 4) {
+    return make_uint4(__float_as_uint(src[0]), __float_as_uint(src[1]), __float_as_uint(src[2]),
+                      __float_as_uint(src[3]));
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (__float_as_uint(src[2 * k]) >> 16) | (__float_as_uint(src[2 * k + 1]) & 0xFFFF0000u);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 // Write n LDS floats that came from T back to a global T row (exact), 16 bytes
 // per lane where the length allows (n % (16/sizeof(T)) == 0, dst 16-byte aligned).
 template <typename T>
@@ -380,17 +396,36 @@ __device__ __forceinline__ void store_row_as(T* dst, const float* src, int n) {
   constexpr int V = 16 / static_cast<int>(sizeof(T));
   if (n % V != 0) {
     for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = from_f<T>(src[i]);
-  } else if constexpr (sizeof(T) == 4) {
-    for (int i = threadIdx.x; i < n / 4; i += kThreads)
-      reinterpret_cast<float4*>(dst)[i] = make_float4(src[4 * i], src[4 * i + 1], src[4 * i + 2], src[4 * i + 3]);
   } else {
-    for (int i = threadIdx.x; i < n / 8; i += kThreads) {
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w[k] = (__float_as_uint(src[8 * i + 2 * k]) >> 16) | (__float_as_uint(src[8 * i + 2 * k + 1]) & 0xFFFF0000u);
-      reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+    for (int i = threadIdx.x; i < n / V; i += kThreads) reinterpret_cast<uint4*>(dst)[i] = pack16<T>(src + V * i);
+  }
+}
+
+// Rows r = 0..nrows-1 of n floats each (LDS, src + r * sstride) that came from
+// T, to global T rows at dst + slot(r) * n, as one pass of 16-byte stores over
+// all threads (n % (16/sizeof(T)) == 0, rows 16-byte aligned).
+template <typename T, typename SLOT>
+__device__ __forceinline__ void store_rows_as(T* dst, const float* src, int sstride, int nrows, int n, SLOT slot) {
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  const int per = n / V;
+  for (int i = threadIdx.x; i < nrows * per; i += kThreads) {
+    const int r = i / per, c = i - r * per;
+    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot(r)) * n + c * V) = pack16<T>(src + r * sstride + c * V);
+  }
+}
+
+// Copy nrows rows of n T elements from global src (row r at src + r * sstride)
+// to global dst rows (row r at dst + slot(r) * dstride), 16 bytes per lane over
+// all threads (n % (16/sizeof(T)) == 0, rows 16-byte aligned).
+template <typename T, typename SLOT>
+__device__ __forceinline__ void copy_rows16(T* dst, size_t dstride, const T* src, size_t sstride, int nrows, int n,
+                                            SLOT slot) {
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  const int per = n / V;
+  for (int i = threadIdx.x; i < nrows * per; i += kThreads) {
+    const int r = i / per, c = i - r * per;
+    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(slot(r)) * dstride + c * V) =
+        *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * sstride + c * V);
   }
 }
 
