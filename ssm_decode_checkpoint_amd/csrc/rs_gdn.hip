@@ -98,7 +98,9 @@ struct GSlice {
   __device__ __forceinline__ static size_t off(size_t st, int c0, int row) {
     return (st * NK + row) * NV + c0 + RegTile<4, NK, NVS>::col0();
   }
+  // (loads written before the slice stay ahead of it, as for RawTile::issue)
   __device__ __forceinline__ void issue(const float* base, size_t st, int c0) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
       int row = RegTile<4, NK, NVS>::row(k);
@@ -309,19 +311,27 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NVS> s;
   const GPtrs p = gdn_tile<NV, 1>(a);
   float* ck = static_cast<float*>(a.ck.data);
-  GSlice<NK, NV, NVS> raw;
-  raw.issue(ck, p.st, p.c0);
+  static_assert(NK <= kThreads && NVS <= kThreads, "one input element per thread");
+  // the token's inputs into registers first, then the state (returns come back
+  // in issue order), then the inputs to LDS while the state streams in
   const size_t bk = static_cast<size_t>(p.b) * a.nqk + p.kh;
   const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
   const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
   const TIN* iv = static_cast<const TIN*>(a.v) + p.st * NV + p.c0;
-  for (int i = threadIdx.x; i < NK; i += kThreads) {
-    s.W[0][i] = to_f(ik[i]);
-    s.W[1][i] = to_f(iq[i]);
-    s.W[2][i] = VG ? expf(a.g[p.st * NK + i]) : 0.0f;   // VG: the channel decays
-    s.W[3][i] = 0.0f;
+  const int ti = static_cast<int>(threadIdx.x);
+  const int ik_ = ti < NK ? ti : 0, iv_ = ti < NVS ? ti : 0;
+  const float kv = to_f(ik[ik_]), qv = to_f(iq[ik_]), vv = to_f(iv[iv_]);
+  const float gvv = VG ? a.g[p.st * NK + ik_] : 0.0f;
+  const float gs = VG ? 0.0f : a.g[p.st], beta = a.beta[p.st];
+  GSlice<NK, NV, NVS> raw;
+  raw.issue(ck, p.st, p.c0);
+  if (ti < NK) {
+    s.W[0][ti] = kv;
+    s.W[1][ti] = qv;
+    s.W[2][ti] = VG ? expf(gvv) : 0.0f;   // VG: the channel decays
+    s.W[3][ti] = 0.0f;
   }
-  for (int i = threadIdx.x; i < NVS; i += kThreads) s.vc[i] = to_f(iv[i]);
+  if (ti < NVS) s.vc[ti] = vv;
   __syncthreads();
   // k . q (one 16-lane group)
   if (threadIdx.x < 16) {
@@ -330,8 +340,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
     part = group_sum16(part);
     if (threadIdx.x == 0) s.kq[0] = part;
   }
-  const float alpha = VG ? 1.0f : expf(a.g[p.st]);
-  const float beta = a.beta[p.st];
+  const float alpha = VG ? 1.0f : expf(gs);
   RegTile<4, NK, NVS> S;
   raw.decode(S);
   if constexpr (VG) tile_scale_rows(S, &s.W[2][0]);

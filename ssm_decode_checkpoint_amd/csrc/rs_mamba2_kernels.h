@@ -45,11 +45,6 @@ struct alignas(16) M2Smem {
   float s4[4];
 };
 
-// a[e] = exp(dt_e * A) for e < n.
-__device__ __forceinline__ void stage_decays(float* a, const float* dt, float A, int n) {
-  if (static_cast<int>(threadIdx.x) < n) a[threadIdx.x] = expf(dt[threadIdx.x] * A);
-}
-
 // For outputs q = 0..nq-1 reading entries 0..J_q-1 (J_q = j0 + q):
 //   L[q] = prod_{l<J_q} a_l;  w[q][e] = prod_{e<l<J_q} a_l * dt_e * (B_e . C_q)
 // Dots use groups of 16 lanes (one per (q, e) pair per round).
@@ -91,19 +86,26 @@ __global__ __launch_bounds__(kThreads) void m2_conv_kernel(M2Args a) {
   __shared__ M2Smem<NR, NC, 1, 1, false> s;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  RawTile<FMT_F32, E, NR, NC> raw;
-  raw.issue(a.ck, tile);
+  static_assert(NR <= kThreads && NC <= kThreads, "one input element per thread");
+  // the token's inputs into registers first, then the state (returns come back
+  // in issue order), then the inputs to LDS while the state streams in
   const TIN* inB = static_cast<const TIN*>(a.B) + (static_cast<size_t>(b) * a.ngroups + g) * NR;
   const TIN* inC = static_cast<const TIN*>(a.C) + (static_cast<size_t>(b) * a.ngroups + g) * NR;
   const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
-  for (int i = threadIdx.x; i < NR; i += kThreads) {
-    s.B[0][i] = to_f(inB[i]);
-    s.Cw[0][i] = to_f(inC[i]);
-  }
-  for (int i = threadIdx.x; i < NC; i += kThreads) s.X[0][i] = to_f(inX[i]);
-  __syncthreads();
+  const int ti = static_cast<int>(threadIdx.x);
+  const int ir = ti < NR ? ti : 0, ic = ti < NC ? ti : 0;
+  const float bv = to_f(inB[ir]), cv = to_f(inC[ir]), xv = to_f(inX[ic]);
   const float dt = to_f(static_cast<const TIN*>(a.dt)[tile]);
-  const float decay = expf(dt * a.A[h]);
+  const float Ah = a.A[h];
+  RawTile<FMT_F32, E, NR, NC> raw;
+  raw.issue(a.ck, tile);
+  if (ti < NR) {
+    s.B[0][ti] = bv;
+    s.Cw[0][ti] = cv;
+  }
+  if (ti < NC) s.X[0][ti] = xv;
+  __syncthreads();
+  const float decay = expf(dt * Ah);
   RegTile<E, NR, NC> H;
   raw.decode(H);
   const int c0 = RegTile<E, NR, NC>::col0();
@@ -325,16 +327,20 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_wave_kernel(M2Args a) {
 #pragma unroll
     for (int c = 0; c < XCH; ++c) xr[q][c] = *reinterpret_cast<const uint4*>(xs.at(ec) + ce * 8 + c * V);
   }
-  float dtv = 0.0f;
+  // the block's dt and A with the records: a load issued after the tile would
+  // return after all of it (in-order returns) and hold the first barrier there
+  float dtv = 0.0f, Av = 0.0f;
   {
     const int t = threadIdx.x, hw = t >> 4, e = t & 15;
     const int ec = e < j ? e : j - 1;
     const TIN* rD = static_cast<const TIN*>(a.rdt) + (hdt + (hw < kHPB ? hw : 0)) * kRing;
     const TIN* iD = static_cast<const TIN*>(a.dt) + hdt + (hw < kHPB ? hw : 0);
     dtv = to_f(*(ec < len ? rD + ((nck + ec) & (kRing - 1)) : iD));
+    Av = a.A[hb * kHPB + (hw < kHPB ? hw : 0)];
   }
   // 2. this head's tile, then the arrival count
   Raw<RDF, 8> raw[PASSES];
+  __builtin_amdgcn_sched_barrier(0);           // the record loads stay ahead of the tile
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) raw[k] = load_chunk<RDF, 8, NC>(a.rd, mat, NR, k * RPP + (lane >> 3), ce);
   const float ms = mat_scale<RDF>(a.rd, mat);
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void m2_nonflush_wave_kernel(M2Args a) {
   if (threadIdx.x < kHPB * 16) {
     const int hw = threadIdx.x >> 4, e = threadIdx.x & 15;
     s.dt[hw][e] = dtv;
-    s.a[hw][e] = expf(dtv * a.A[hb * kHPB + hw]);
+    s.a[hw][e] = expf(dtv * Av);
   }
   __syncthreads();
   {
@@ -706,13 +712,14 @@ __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
     cx.load(EntrySrc<TIN>{rX, rX, 0, it.nck, m, NC}, m, NC);
     const int de = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
     const float dtv = to_f(*EntrySrc<TIN>{rDt, rDt, 0, it.nck, m, 1}.at(de));
+    const float Ah = a.A[h];   // before the tile: a load behind it would wait for all of it
     RawTile<CKF, E, NR, NC> raw;
     raw.issue(a.ck, tile);
     cb.to_lds(&s.B[0][0], NR, m, NR);
     cx.to_lds(&s.X[0][0], NC, m, NC);
     if (static_cast<int>(threadIdx.x) < m) {
       s.dt[threadIdx.x] = dtv;
-      s.a[threadIdx.x] = expf(dtv * a.A[h]);
+      s.a[threadIdx.x] = expf(dtv * Ah);
     }
     __syncthreads();
     RegTile<E, NR, NC> H;
@@ -734,8 +741,10 @@ __global__ __launch_bounds__(kThreads) void m2_conv_spec_kernel(M2Args a) {
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
   const int K = a.K;
-  RawTile<FMT_F32, E, NR, NC> raw;
-  raw.issue(a.ck, tile);
+  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
+  static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
+  constexpr int CB = (KMAX * NR / V + kThreads - 1) / kThreads;
+  constexpr int CX = (KMAX * NC / V + kThreads - 1) / kThreads;
   const size_t bg = static_cast<size_t>(b) * a.ngroups + g;
   const size_t gstride = static_cast<size_t>(a.batch) * a.ngroups * NR;
   const size_t xstride = static_cast<size_t>(a.batch) * a.nheads * NC;
@@ -744,12 +753,24 @@ __global__ __launch_bounds__(kThreads) void m2_conv_spec_kernel(M2Args a) {
   const TIN* inC = static_cast<const TIN*>(a.C) + bg * NR;
   const TIN* inX = static_cast<const TIN*>(a.x) + static_cast<size_t>(tile) * NC;
   const TIN* inDt = static_cast<const TIN*>(a.dt) + tile;
-  stage_rows(&s.B[0][0], NR, EntrySrc<TIN>{inB, inB, gstride, 0, 0, NR}, K);
-  stage_rows(&s.Cw[0][0], NR, EntrySrc<TIN>{inC, inC, gstride, 0, 0, NR}, K);
-  stage_rows(&s.X[0][0], NC, EntrySrc<TIN>{inX, inX, xstride, 0, 0, NC}, K);
-  stage_rows(&s.dt[0], 1, EntrySrc<TIN>{inDt, inDt, dstride, 0, 0, 1}, K);
-  __syncthreads();
-  stage_decays(s.a, s.dt, a.A[h], K);
+  // the drafts' inputs into registers, then the state, then the inputs to LDS
+  RegChunks<TIN, CB> cb, cc;
+  RegChunks<TIN, CX> cx;
+  cb.load(EntrySrc<TIN>{inB, inB, gstride, 0, 0, NR}, K, NR);
+  cc.load(EntrySrc<TIN>{inC, inC, gstride, 0, 0, NR}, K, NR);
+  cx.load(EntrySrc<TIN>{inX, inX, xstride, 0, 0, NC}, K, NC);
+  const int de = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
+  const float dtv = to_f(inDt[de * dstride]);
+  const float Ah = a.A[h];
+  RawTile<FMT_F32, E, NR, NC> raw;
+  raw.issue(a.ck, tile);
+  cb.to_lds(&s.B[0][0], NR, K, NR);
+  cc.to_lds(&s.Cw[0][0], NR, K, NR);
+  cx.to_lds(&s.X[0][0], NC, K, NC);
+  if (static_cast<int>(threadIdx.x) < K) {
+    s.dt[threadIdx.x] = dtv;
+    s.a[threadIdx.x] = expf(dtv * Ah);
+  }
   __syncthreads();
   RegTile<E, NR, NC> H;
   raw.decode(H);

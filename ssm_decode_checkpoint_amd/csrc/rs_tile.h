@@ -30,8 +30,11 @@ struct RawTile {
   // Every thread issues all its loads unconditionally (rows past a matrix
   // smaller than one pass are clamped to its last row and ignored when
   // decoding): loads under a branch would be merged through a wait, which
-  // serialises the stream.
+  // serialises the stream. The scheduling barrier keeps every load written
+  // before the tile (the buffer records) ahead of it: returns come back in
+  // issue order, so a record load moved behind the tile would wait for all of it.
   __device__ __forceinline__ void issue(const StateBuf& sb, size_t mat) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
       int row = static_cast<int>(threadIdx.x / TM::TPR) + k * TM::RPP;
@@ -462,30 +465,6 @@ __device__ __forceinline__ void unpack16(const uint4& u, const bf16*, float* d) 
   for (int i = 0; i < 4; ++i) {
     d[2 * i] = __uint_as_float(w[i] << 16);
     d[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-  }
-}
-
-// Copy n records of src.width elements into LDS rows (stride floats apart),
-// 16 bytes per load when the record length allows it.
-template <typename TIN>
-__device__ __forceinline__ void stage_rows(float* dst, int stride, const EntrySrc<TIN>& src, int n) {
-  constexpr int V = 16 / static_cast<int>(sizeof(TIN));
-  if (src.width % V == 0) {
-    const int per = src.width / V;
-    for (int idx = threadIdx.x; idx < n * per; idx += kThreads) {
-      const int e = idx / per, c = idx - e * per;
-      const uint4 u = *reinterpret_cast<const uint4*>(src.at(e) + c * V);
-      float t[V];
-      unpack16(u, static_cast<const TIN*>(nullptr), t);
-      float* d = dst + e * stride + c * V;
-#pragma unroll
-      for (int i = 0; i < V; ++i) d[i] = t[i];
-    }
-  } else {
-    for (int idx = threadIdx.x; idx < n * src.width; idx += kThreads) {
-      const int e = idx / src.width, r = idx - e * src.width;
-      dst[e * stride + r] = to_f(src.at(e)[r]);
-    }
   }
 }
 
