@@ -44,15 +44,17 @@ __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <>
 __device__ __forceinline__ bf16 from_f<bf16>(float v) { return bf16{static_cast<uint16_t>(__float_as_uint(v) >> 16)}; }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 // ----------------------------------------------------------------------------
 // E4M3FN code values (decoding and encoding otherwise use the gfx950
 // conversion instructions, with the tile loads and stores)
 // ----------------------------------------------------------------------------
+// Value of an E4M3FN code (a block scale): the packed FP8 conversion at unit
+// scale, exact for every finite code (0x7F and 0xFF are NaN, as the format
+// defines them; the encoders here never produce them).
 __device__ __forceinline__ float e4m3_value(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  float mag = (e == 0) ? static_cast<float>(m) * 0.001953125f  // m * 2^-9
-                       : __uint_as_float(((e + 120u) << 23) | (m << 20));  // (1 + m/8) 2^(e-7)
-  return (code & 0x80u) ? -mag : mag;
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code & 0xFFu, 1.0f, false)[0];
 }
 
 // ----------------------------------------------------------------------------
@@ -61,8 +63,6 @@ __device__ __forceinline__ float e4m3_value(uint32_t code) {
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float4 nt_load(const float4* p) {
   const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
