@@ -272,6 +272,7 @@ struct alignas(16) M2WaveSmem {
   float a[kHPB][kRing];       // exp(dt A) per head and entry
   float w[kHPB][kRing];       // w_{j,e} dt_e (B_e . C_cur) per head
   float L[kHPB];
+  uint8_t scl[kHPB][NR * NC / 16];   // NVFP4 reads: each head's block scales
 };
 
 // FP8 and NVFP4 reads with bf16 records fit in 80 registers, which gives 6
@@ -342,16 +343,40 @@ void m2_nonflush_wave_kernel(M2Args a) {
     dtv = to_f(*(ec < len ? rD + ((nck + ec) & (kRing - 1)) : iD));
     Av = a.A[hb * kHPB + (hw < kHPB ? hw : 0)];
   }
+  const float Dh = a.D[h];                     // per-wave values ahead of the tile too
+  const float ms = mat_scale<RDF>(a.rd, mat);   // FP8 / NVFP4 matrix scale
   // 2. this head's tile, then the arrival count
+  // NVFP4: the head's block scales come as one 4- or 8-byte load per lane
+  // (not a byte load per chunk) and go to LDS with the records; each chunk's
+  // scale is read back from there when it is decoded
+  constexpr int SPL = NR * NC / 16 / 64;       // scale bytes per lane
+  static_assert(RDF != FMT_NVFP4 || SPL == 4 || SPL == 8, "whole-lane scale loads");
+  uint2 scv = make_uint2(0u, 0u);
   Raw<RDF, 8> raw[PASSES];
   __builtin_amdgcn_sched_barrier(0);           // the record loads stay ahead of the tile
+  if constexpr (RDF == FMT_NVFP4) {
+    const uint8_t* sp = a.rd.nv_scale + mat * (NR * NC / 16) + lane * SPL;
+    if constexpr (SPL == 8) scv = nt_load(reinterpret_cast<const uint2*>(sp));
+    else scv.x = nt_load(reinterpret_cast<const uint32_t*>(sp));
+  }
 #pragma unroll
-  for (int k = 0; k < PASSES; ++k) raw[k] = load_chunk<RDF, 8, NC>(a.rd, mat, NR, k * RPP + (lane >> 3), ce);
-  const float ms = mat_scale<RDF>(a.rd, mat);
+  for (int k = 0; k < PASSES; ++k) {
+    if constexpr (RDF == FMT_NVFP4) {
+      const size_t elem = (mat * NR + k * RPP + (lane >> 3)) * NC + static_cast<size_t>(ce) * 8;
+      raw[k].v = nt_load(reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.rd.data) + elem / 2));
+      raw[k].s = 0u;
+    } else {
+      raw[k] = load_chunk<RDF, 8, NC>(a.rd, mat, NR, k * RPP + (lane >> 3), ce);
+    }
+  }
   arr.arrive(actr, hb, nck, len, nd);
   // 3. records to LDS; dots, decays and weights (state-independent)
   cb.to_lds(&s.B[0][0], NR, j, NR);
   cc.to_lds(s.C, NR, 1, NR);
+  if constexpr (RDF == FMT_NVFP4) {
+    if constexpr (SPL == 8) *reinterpret_cast<uint2*>(&s.scl[wave][lane * 8]) = scv;
+    else *reinterpret_cast<uint32_t*>(&s.scl[wave][lane * 4]) = scv.x;
+  }
   if (threadIdx.x < kHPB * 16) {
     const int hw = threadIdx.x >> 4, e = threadIdx.x & 15;
     s.dt[hw][e] = dtv;
@@ -388,12 +413,13 @@ void m2_nonflush_wave_kernel(M2Args a) {
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
     float t[8];
+    if constexpr (RDF == FMT_NVFP4) raw[k].s = s.scl[wave][(k * RPP + (lane >> 3)) * (NC / 16) + (ce >> 1)];
     decode_chunk<RDF, 8>(raw[k], ms, t);
     const float cr = s.C[k * RPP + (lane >> 3)];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += t[i] * cr;
   }
-  const float L = s.L[wave], Dh = a.D[h];
+  const float L = s.L[wave];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] *= L;
 #pragma unroll
