@@ -293,7 +293,11 @@ void m2_nonflush_wave_kernel(M2Args a) {
   const int nblk = a.nheads / kHPB;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);          // (sequence, head block)
   const int b = tile / nblk, hb = tile - b * nblk;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the wave index is uniform per wavefront: as a scalar, everything derived
+  // from it (head, matrix, record pointers, D, matrix scale) stays in scalar
+  // registers and its loads are scalar loads, which do not queue behind the tile
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
   const int h = hb * kHPB + wave, g = (hb * kHPB) / a.hpg;
   rs_meta* mp = a.meta + b;
   uint32_t* actr = a.arrive + static_cast<size_t>(b) * arrive_groups(nblk) * kArriveStride;
