@@ -11,15 +11,27 @@ i.e. 16 decode tokens for all 256 sequences; `value` is decode tokens/s over
 the K timed windows. The conventional read-modify-write kernel is timed on
 the same windows for comparison. The JSON line carries the roofline of the
 dominant kernel (the non-flush step) measured with HIP events on the launch
-stream, and the fp64 CPU oracle timed on a bounded sample of the workload.
+stream, beside two plain streams of the same tiles (read only, and with the
+step's writes per tile) timed in the same process, and the fp64 CPU oracle
+timed on a bounded sample of the workload.
 
 Other workloads (each one more JSON line, only when asked with --workload):
-  gdn      Qwen3.5-style Gated DeltaNet layer, batch 256 (UT-form non-flush)
-  spec     speculative decode on 120B-class Mamba-2 shapes, batch 512, 4 drafts
-           per round: ReplaySSM append + commit vs snapshot / restore
-  lowprec  Nemotron shapes at batch 64: fp32 / fp16 / fp8 checkpoints with and
-           without the NVFP4 read copy, and the uniform NVFP4 checkpoint;
-           optionally (--lowprec-error-steps) y error vs fp64 over length
+  gdn       Qwen3.5-style Gated DeltaNet layer, batch 256 (UT-form non-flush)
+  kda       the same shapes with Kimi Delta Attention's per-key-channel gate
+  spec      speculative decode on 120B-class Mamba-2 shapes, batch 512, 4 drafts
+            per round: ReplaySSM append + commit vs snapshot / restore
+  gdn_spec  speculative decode on the Gated DeltaNet layer, batch 256, 4 drafts
+  kda_spec  the same for Kimi Delta Attention
+  lowprec   Nemotron shapes at batch 64 (or --lowprec-batch): fp32 / fp16 / fp8
+            checkpoints with and without the NVFP4 read copy, and the uniform
+            NVFP4 checkpoint; optionally (--lowprec-error-steps) y error vs fp64
+            over length
+  serve     continuous batching (staggered buffer fills, one self-scheduling
+            launch per step) and prefix-cache save / restore of 64 sequences
+  block     the Mamba-2 block per token: short convolution, SSM step, gated norm
+  sweep     the Nemotron layer at batch 1 .. 512, ReplaySSM vs conventional
+  copy      a 1 GiB device copy, a read-only sum and the tile probes (the
+            references the HBM counters and the roofline are read against)
 """
 from __future__ import annotations
 
