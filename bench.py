@@ -308,6 +308,31 @@ def bench_mamba2(args, torch, rs):
 SWEEP_BATCHES = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512)
 
 
+def _graph_window_ms(torch, window, K, warm):
+    """Milliseconds per window when the window's launches are captured once in a
+    HIP graph (torch.cuda.CUDAGraph) and replayed K times. The library calls
+    allocate, synchronise and memset nothing, and the buffer counters advance on
+    the device, so each replay continues the window sequence; a graph's first
+    replays are warm-up."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        window()
+    for _ in range(max(1, warm)):
+        g.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(K):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / K
+    del g
+    return ms
+
+
 def bench_sweep(args, torch, rs):
     """Conventional vs ReplaySSM decode over batch sizes on the Nemotron-style
     Mamba-2 layer shapes (128 heads, 64 x 128 fp32 state, bf16 inputs). Each
@@ -342,6 +367,9 @@ def bench_sweep(args, torch, rs):
 
         total_r, per_r = tm.run(replay_window, args.steps, args.warmup, RING)
         total_c, _ = tm.run(conv_window, args.steps, args.warmup, RING)
+        # the same windows captured once as HIP graphs and replayed (no host launch cost)
+        graph_r = _graph_window_ms(torch, lambda: replay_window(None), args.steps, args.warmup)
+        graph_c = _graph_window_ms(torch, lambda: conv_window(None), args.steps, args.warmup)
         ntok = B * RING * args.steps
         win_bytes = (sum(byt["nonflush"].values()) + byt["flush"]) * B
         rows.append({"batch": B,
@@ -353,7 +381,10 @@ def bench_sweep(args, torch, rs):
                      "replay_nonflush_ms": float(per_r[:, :RING - 1].mean()),
                      "replay_flush_ms": float(per_r[:, RING - 1].mean()),
                      "replay_window_gbs": win_bytes / (total_r / args.steps * 1e-3) / 1e9,
-                     "conventional_gbs": byt["conv"] * B * RING / (total_c / args.steps * 1e-3) / 1e9})
+                     "conventional_gbs": byt["conv"] * B * RING / (total_c / args.steps * 1e-3) / 1e9,
+                     "graph_replay_tokens_per_s": B * RING / (graph_r * 1e-3),
+                     "graph_conventional_tokens_per_s": B * RING / (graph_c * 1e-3),
+                     "graph_speedup": graph_c / graph_r})
         print(f"sweep: batch {B} done", file=sys.stderr, flush=True)
         del rl, rb, cl, cb, y
         torch.cuda.empty_cache()
