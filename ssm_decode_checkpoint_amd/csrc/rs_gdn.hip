@@ -556,10 +556,70 @@ struct alignas(16) GSpecSmem {
   alignas(16) float DW[VG && KQ > 1 ? KQ * (KQ - 1) / 2 : 1][NK];
 };
 
+// The dots of a speculative round on the matrix cores, for bf16 records (their
+// products are exact in fp32; only the accumulation order differs from the
+// lane-group dots). One wavefront forms G = A Bt^T with A's rows 0..K-1 the
+// drafts' k (window entries len + d), rows 8..8+K-1 their q, the rest zero, and
+// Bt's rows the window's 16 k rows, in steps of 32 of v_mfma_f32_16x16x32_bf16
+// (a short last step zero-padded). Operand lane layout of that instruction: lane l
+// holds row l % 16 of A (of Bt) at k = 8 (l / 16) .. + 7 of each 32-wide step;
+// the result lane l holds column l % 16, rows 4 (l / 16) .. + 3 (checked against
+// a host product before use). Then kk[d][i] = beta_d r_{e,i} (k_e . k_i) for
+// i < e and kq[d][i] = r_{e,i} (k_i . q_d) for i <= e, e = len + d; entries past
+// the window are garbage in G and never read. Called by lanes 0..63 only.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t bf16x8_of(const float* p) {
+  const float4 u = *reinterpret_cast<const float4*>(p), v = *reinterpret_cast<const float4*>(p + 4);
+  const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+  bf16x8_t r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)   // the values are bf16 already: keep the upper half
+    r[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(__float_as_uint(f[i]) >> 16));
+  return r;
+}
+
+template <int NK, int KQ, typename SM>
+__device__ __forceinline__ void spec_gram_bf16(SM& s, int K, int len) {
+  static_assert(NK % 8 == 0 && KQ <= 8, "8-element lane chunks; at most 8 drafts");
+  const int l = threadIdx.x, row = l & 15, k8 = 8 * (l >> 4);
+  const bool isk = row < 8;
+  const int d = isk ? row : row - 8;
+  const bool live = d < K;
+  const float* arow = isk ? &s.K[(len + d) & (kRing - 1)][0] : &s.W[2 * (d < KQ ? d : 0) + 1][0];
+  const float* brow = &s.K[row][0];
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8_t zero;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) zero[i] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(0));
+#pragma unroll
+  for (int st = 0; st < (NK + 31) / 32; ++st) {
+    const bool in = 32 * st + k8 < NK;   // a short last step is zero-padded
+    const bf16x8_t av = live && in ? bf16x8_of(arow + 32 * st + k8) : zero;
+    const bf16x8_t bv = in ? bf16x8_of(brow + 32 * st + k8) : zero;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+  const int i = l & 15;           // window entry (column)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = 4 * (l >> 4) + j;  // A row
+    if (m < 8) {
+      if (m < K && i < len + m) s.kk[m][i] = s.bet[m] * s.rt[m][i] * acc[j];
+    } else if (m - 8 < K && i <= len + m - 8) {
+      s.kq[m - 8][i] = s.rt[m - 8][i] * acc[j];
+    }
+  }
+}
+
 }  // namespace
 
+// bf16 records without the per-channel gate: 7 waves per SIMD with the matrix-core
+// dots' accumulator (the register budget the lane-group dots had)
 template <typename TIN, int NK, int NV, int KQ, bool VG>
-__global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu((!VG && sizeof(TIN) == 2 && KQ <= 4) ? 7 : 1, 8)))
+void gdn_spec_append_kernel(GDNArgs a) {
   constexpr int NS = gdn_slices<NV>();
   constexpr int NVS = NV / NS;
   constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
@@ -720,6 +780,12 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
         }
       }
       __syncthreads();
+      if constexpr (sizeof(TIN) == 2) {
+        // bf16 records: all the round's dots are one 16 x 16 block of a small
+        // GEMM, [k of the drafts; q of the drafts] times the window's k rows,
+        // taken by one wavefront on the matrix cores
+        if (threadIdx.x < 64) spec_gram_bf16<NK, KQ>(s, K, len);
+      } else {
       // dots per draft d (entry e = len + d), 16-lane groups
       const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
       for (int pr = grp; pr < K * 2 * kRing; pr += kThreads / 16) {
@@ -735,6 +801,7 @@ __global__ __launch_bounds__(kThreads) void gdn_spec_append_kernel(GDNArgs a) {
           if (isq) s.kq[d][i] = s.rt[d][i] * part;
           else s.kk[d][i] = s.bet[d] * s.rt[d][i] * part;
         }
+      }
       }
     }
     float* red = &s.K[0][0];

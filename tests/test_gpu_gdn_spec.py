@@ -92,9 +92,12 @@ def _spec_run(w, rounds, Ks, seqs=None, t0=3000):
     return worst_same, worst_exact, worst_u, worst_ck, folds
 
 
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("K,kmax", [(4, 4), (2, 4), (8, 8)])
-def test_tiny(K, kmax):
-    w = W.TINY_GDN.with_(max_draft=kmax, init_std=0.4, seed=130 + K)
+def test_tiny(K, kmax, in_dtype):
+    """dk = dv = 16. With bf16 records the round's dots run on the matrix cores
+    (one zero-padded 32-wide step; 8 drafts fill all 16 rows)."""
+    w = W.TINY_GDN.with_(max_draft=kmax, init_std=0.4, seed=130 + K, in_dtype=in_dtype)
     ws, we, wu, wc, folds = _spec_run(w, 24, [K])
     assert ws <= 1e-5 and we <= 1e-5 and wu <= 1e-5 and wc <= 1e-5, (ws, we, wu, wc)
     assert folds > 0
