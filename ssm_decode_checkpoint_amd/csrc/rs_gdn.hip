@@ -612,13 +612,57 @@ __device__ __forceinline__ void spec_gram_bf16(SM& s, int K, int len) {
   }
 }
 
+// out[m][col] = sum_rows S[row][col] * w[m * ws + row] for m < Q <= 16, the
+// state slice held as RegTile<4, NK, 64> (16 threads per row, four columns
+// each), on the matrix cores: in a wavefront, lane l holds rows
+// 4 wave + l / 16 + 16 k and columns 4 (l % 16) + c, which is, for each pass k
+// and column offset c, the B operand of v_mfma_f32_16x16x4f32 (B[l / 16][l % 16]);
+// the A operand is w[l % 16][that row]. Each wavefront sums its 32 rows inside
+// the instruction; the four wavefronts' partials meet in `red` (4 Q 64 floats of
+// LDS). fp32 products and sums: only the order of the additions differs from
+// tile_matvec. Barriers inside; all threads must call.
+template <int Q, int NK, int NVS>
+__device__ __forceinline__ void tile_matvec_mfma(const RegTile<4, NK, NVS>& S, const float* w, int ws, float* red,
+                                                 float* out) {
+  static_assert(NVS == 64 && Q <= 16, "16 lanes per row of four columns; at most 16 weight rows");
+  constexpr int P = RegTile<4, NK, NVS>::P;
+  const int l = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = l & 15;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int k = 0; k < P; ++k) {
+    const int row = RegTile<4, NK, NVS>::row(k);
+    const float a = (m < Q && row < NK) ? w[m * ws + row] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, row < NK ? S.v[k][c] : 0.0f,
+                                                                              acc[c], 0, 0, 0);
+  }
+  // lane l: column 4 (l % 16) + c, rows 4 (l / 16) + i of the wavefront's partial
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int mr = 4 * (l >> 4) + i;
+    if (mr < Q) {
+      float* dst = red + (wave * Q + mr) * NVS + 4 * (l & 15);
+      *reinterpret_cast<float4*>(dst) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < Q * NVS; idx += kThreads)
+    out[idx] = (red[idx] + red[Q * NVS + idx]) + (red[2 * Q * NVS + idx] + red[3 * Q * NVS + idx]);
+  __syncthreads();
+}
+
 }  // namespace
 
-// bf16 records without the per-channel gate: 7 waves per SIMD with the matrix-core
-// dots' accumulator (the register budget the lane-group dots had)
+// Without the per-channel gate and up to 4 drafts: 7 waves per SIMD with the
+// matrix-core accumulators, the register budget the VALU dots and matvecs had;
+// otherwise the compiler puts the accumulators in separate registers and
+// occupancy drops.
 template <typename TIN, int NK, int NV, int KQ, bool VG>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu((!VG && sizeof(TIN) == 2 && KQ <= 4) ? 7 : 1, 8)))
+__attribute__((amdgpu_waves_per_eu((!VG && KQ <= 4) ? 7 : 1, 8)))
 void gdn_spec_append_kernel(GDNArgs a) {
   constexpr int NS = gdn_slices<NV>();
   constexpr int NVS = NV / NS;
@@ -810,10 +854,18 @@ void gdn_spec_append_kernel(GDNArgs a) {
     __syncthreads();                 // dots done: the k rows become scratch
     RegTile<4, NK, NVS> S;
     raw.decode(S);
-    // S0 [k_d, q_d]: weight rows 0..KQ-1, then KQ..2KQ-1 if drafts reach them (fewer
-    // accumulator registers and half the scratch of one 2KQ-row pass)
-    tile_matvec<KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);   // barriers inside publish the dots
-    if (2 * K > KQ) tile_matvec<KQ>(S, &s.W[KQ][0], NK, red, &s.out[KQ][0]);
+    // S0 [k_d, q_d]: all 2 KQ weight rows in one pass on the matrix cores where the
+    // slice has 64 columns and the scratch holds it (without the per-channel gate:
+    // with it the accumulators cost a wave of occupancy); otherwise on the VALU, rows
+    // 0..KQ-1, then KQ..2KQ-1 if drafts reach them (fewer accumulator registers and
+    // half the scratch of one 2KQ-row pass). Barriers inside publish the dots.
+    constexpr bool kMfmaMv = !VG && NVS == 64 && 4 * 2 * KQ * NVS <= GSpecSmem<NK, NVS, KQ, VG>::KROWS * NK;
+    if constexpr (kMfmaMv) {
+      tile_matvec_mfma<2 * KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);
+    } else {
+      tile_matvec<KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);
+      if (2 * K > KQ) tile_matvec<KQ>(S, &s.W[KQ][0], NK, red, &s.out[KQ][0]);
+    }
     // every (draft, column) pair at once: the parts of the draft's row and output
     // that do not involve other drafts (checkpoint and held entries)
     for (int idx = threadIdx.x; idx < K * NVS; idx += kThreads) {
