@@ -112,6 +112,16 @@ def test_mixed_draft_counts_two_slices():
     assert folds > 0
 
 
+def test_eight_drafts_two_slices():
+    """dk = dv = 128, bf16 records, up to 8 drafts per round: all 16 rows of the
+    matrix-core dot block live (8 draft k, 8 draft q), the matvec on the VALU."""
+    w = W.TINY_GDN.with_(batch=3, n_qk=2, n_v=4, dk=128, dv=128, in_dtype="bf16", init_std=0.3, max_draft=8,
+                         seed=141)
+    ws, we, wu, wc, folds = _spec_run(w, 12, [8, 5, 8, 3])
+    assert ws <= 1e-5 and we <= 1e-5 and wu <= 1e-5 and wc <= 1e-5, (ws, we, wu, wc)
+    assert folds > 0
+
+
 def test_qwen_batch256_sampled():
     """The speculative Qwen-style workload at full size (256 sequences x 32 value
     heads of 128 x 128), 8 sequences spread over the batch checked each round."""
