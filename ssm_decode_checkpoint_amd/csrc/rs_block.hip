@@ -154,7 +154,8 @@ void conv_step_t(const ConvArgs& a, hipStream_t st) {
   }
 }
 
-void conv_step(const ConvArgs& a, bool bf, hipStream_t st) {
+void conv_step(const ConvArgs& a, bool bf, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (bf) conv_step_t<bf16>(a, st);
   else conv_step_t<float>(a, st);
 }
@@ -255,7 +256,8 @@ __global__ __launch_bounds__(kThreads) void gated_norm_kernel(NormArgs a) {
   }
 }
 
-void gated_norm(const NormArgs& a, bool bf, hipStream_t st) {
+void gated_norm(const NormArgs& a, bool bf, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   const long long items = static_cast<long long>(a.rows) * (a.d / a.gs);
   const int grid = static_cast<int>((items + kThreads / 64 - 1) / (kThreads / 64));
   if (bf) gated_norm_kernel<bf16><<<grid, kThreads, 0, st>>>(a);

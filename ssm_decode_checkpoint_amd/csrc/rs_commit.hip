@@ -71,7 +71,9 @@ __global__ __launch_bounds__(1024) void commit_meta_kernel(CommitArgs a) {
   if (threadIdx.x == 0) *a.work_count = base;
 }
 
-void commit_meta(const CommitArgs& a, hipStream_t st) { commit_meta_kernel<<<1, 1024, 0, st>>>(a); }
+void commit_meta(const CommitArgs& a, void* stream) {
+  commit_meta_kernel<<<1, 1024, 0, static_cast<hipStream_t>(stream)>>>(a);
+}
 
 // Slot reuse: a sequence slot that starts a new sequence gets empty counters
 // (its buffer is empty; the caller writes the new checkpoint). The arrival
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(256) void reset_slots_kernel(rs_meta* meta, int bat
   m->err = 0;
 }
 
-void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, hipStream_t st) {
+void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   reset_slots_kernel<<<(count + 255) / 256, 256, 0, st>>>(meta, batch, seqs, count);
 }
 
@@ -126,8 +129,11 @@ __global__ __launch_bounds__(256) void copy_slots_kernel(CopyArgs a) {
   }
 }
 
-void copy_slots(const CopyArgs& a, int blocks_per_pair, hipStream_t st) {
+void copy_slots(const CopyArgs& a, int blocks_per_pair, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   copy_slots_kernel<<<dim3(blocks_per_pair, a.count), 256, 0, st>>>(a);
 }
+
+rs_status launch_status() { return hipGetLastError() == hipSuccess ? RS_OK : RS_E_LAUNCH; }
 
 }  // namespace rs

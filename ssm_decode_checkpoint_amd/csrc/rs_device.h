@@ -18,13 +18,11 @@
 #include <stdint.h>
 
 #include "rs.h"
+#include "rs_host.h"
 
 namespace rs {
 
 constexpr int kThreads = 256;
-constexpr int kRing = 16;
-
-enum Fmt { FMT_F32 = 0, FMT_F16 = 1, FMT_FP8 = 2, FMT_NVFP4 = 3 };
 
 // ----------------------------------------------------------------------------
 // input element types
@@ -95,14 +93,6 @@ __device__ __forceinline__ void nt_store(uint32_t v, uint32_t* p) { __builtin_no
 // ----------------------------------------------------------------------------
 // stored-state access
 // ----------------------------------------------------------------------------
-// One layer's state buffer in a given format. `data` points at matrix 0;
-// matrix t (t = b*heads + h) starts at t*rows*cols elements.
-struct StateBuf {
-  void* data;          // f32 / f16 values, E4M3 codes, or packed E2M1 codes
-  uint8_t* nv_scale;   // NVFP4 block scales [t][rows][cols/16]
-  float* tscale;       // FP8 per-matrix scale or NVFP4 tensor scale [t]
-};
-
 // Thread -> (row, column chunk) mapping of a rows x cols matrix: each thread
 // owns E consecutive columns of one row per pass.
 template <int E_, int NR, int NC>

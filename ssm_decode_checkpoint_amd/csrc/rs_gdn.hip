@@ -1235,11 +1235,9 @@ void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
 
 }  // namespace
 
-bool gdn_shape_supported(int dk, int dv) {
-  return (dk == 16 && dv == 16) || (dk == 64 && dv == 64) || (dk == 128 && dv == 128);
-}
-
-void gdn_launch(GDNOp op, const GDNArgs& a, const GDNLaunch& l, hipStream_t st) {
+// The compiled shapes are the ones gdn_shape_supported (rs_host.cpp) accepts.
+void gdn_launch(GDNOp op, const GDNArgs& a, const GDNLaunch& l, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (l.dk == 16 && l.dv == 16) gdn_launch_shape<16, 16>(op, a, l, st);
   else if (l.dk == 64 && l.dv == 64) gdn_launch_shape<64, 64>(op, a, l, st);
   else if (l.dk == 128 && l.dv == 128) gdn_launch_shape<128, 128>(op, a, l, st);

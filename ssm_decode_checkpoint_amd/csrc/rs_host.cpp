@@ -1,12 +1,12 @@
-// Host side of the C ABI: configuration checks, buffer layout, and kernel
-// dispatch. Every entry point validates what the host can see, enqueues its
-// kernels on the caller's stream and returns without synchronising.
-#include <hip/hip_runtime.h>
-
+// Host side of the C ABI: configuration checks, buffer layout, and the
+// argument blocks of the kernels. Every entry point validates what the host
+// can see, then hands its arguments to the dispatch functions of the kernel
+// files (rs_host.h), which enqueue the kernels on the caller's stream and
+// return without synchronising. Plain C++: no GPU header is included here.
 #include <cstring>
 
 #include "rs.h"
-#include "rs_internal.h"
+#include "rs_host.h"
 
 using namespace rs;
 
@@ -71,9 +71,8 @@ rs_status check_layer(const rs_layer* L) {
   return RS_OK;
 }
 
-rs_status launched() {
-  return hipGetLastError() == hipSuccess ? RS_OK : RS_E_LAUNCH;
-}
+rs_status launched() { return launch_status(); }
+
 
 StateBuf ck_buf(const rs_layer* L, void* ckpt) {
   StateBuf s{ckpt, nullptr, nullptr};
@@ -229,6 +228,16 @@ GDNLaunch gdn_launch_cfg(const rs_layer* L) {
 
 }  // namespace
 
+// The shapes the kernel files instantiate (rs_m2_<rows>x<cols>.hip; rs_gdn.hip).
+bool rs::m2_shape_supported(int dstate, int headdim) {
+  return (dstate == 16 && headdim == 16) || (dstate == 64 && headdim == 64) || (dstate == 128 && headdim == 64) ||
+         (dstate == 128 && headdim == 128);
+}
+
+bool rs::gdn_shape_supported(int dk, int dv) {
+  return (dk == 16 && dv == 16) || (dk == 64 && dv == 64) || (dk == 128 && dv == 128);
+}
+
 extern "C" {
 
 rs_status rs_init(const rs_config* cfg, rs_layer* out) {
@@ -318,7 +327,7 @@ rs_status rs_step_conventional(const rs_layer* L, const rs_buffers* buf, const r
   if (L->cfg.mode != RS_CONVENTIONAL) return RS_E_MODE;
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* st = stream;
   if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
@@ -342,7 +351,7 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
   if (L->cfg.mode != RS_REPLAY) return RS_E_MODE;
   if (!y) return RS_E_ARG;
   if (!aligned16(y)) return RS_E_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* st = stream;
   if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
@@ -380,7 +389,7 @@ rs_status rs_reset_slots(const rs_layer* L, const rs_buffers* buf, const int32_t
   if (!buf || !buf->meta || count < 0 || (count > 0 && !seqs)) return RS_E_ARG;
   if (!aligned16(buf->meta)) return RS_E_ALIGN;
   if (count == 0) return RS_OK;
-  reset_slots(static_cast<rs_meta*>(buf->meta), L->cfg.batch, seqs, count, static_cast<hipStream_t>(stream));
+  reset_slots(static_cast<rs_meta*>(buf->meta), L->cfg.batch, seqs, count, stream);
   return launched();
 }
 
@@ -476,7 +485,7 @@ rs_status rs_copy_slots(const rs_layer* Ls, const rs_buffers* src, const int32_t
   a.src_meta = replay ? static_cast<const rs_meta*>(src->meta) : nullptr;
   a.dst_meta = replay ? static_cast<rs_meta*>(dst->meta) : nullptr;
   const uint64_t bpp = (total + 16383) / 16384;   // about four 16-byte chunks per thread
-  copy_slots(a, static_cast<int>(bpp < 1 ? 1 : bpp > 1024 ? 1024 : bpp), static_cast<hipStream_t>(stream));
+  copy_slots(a, static_cast<int>(bpp < 1 ? 1 : bpp > 1024 ? 1024 : bpp), stream);
   return launched();
 }
 
@@ -510,7 +519,7 @@ rs_status rs_conv_step(const rs_layer* L, const rs_buffers* buf, void* conv_ring
   a.x = x;
   a.B = Bo;
   a.C = Co;
-  conv_step(a, c.in_dtype == RS_BF16, static_cast<hipStream_t>(stream));
+  conv_step(a, c.in_dtype == RS_BF16, stream);
   return launched();
 }
 
@@ -534,7 +543,7 @@ rs_status rs_gated_norm(const rs_layer* L, int32_t K, const float* y, const void
   a.z = z;
   a.w = weight;
   a.out = out;
-  gated_norm(a, c.in_dtype == RS_BF16, static_cast<hipStream_t>(stream));
+  gated_norm(a, c.in_dtype == RS_BF16, stream);
   return launched();
 }
 
@@ -549,7 +558,7 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
     GDNArgs a;
     if (rs_status s = gdn_common(L, buf, drafts, y, &a)) return s;
     a.K = K;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* st = stream;
     if (L->cfg.mode == RS_CONVENTIONAL) {
       if (!buf->snap) return RS_E_ARG;
       if (!aligned16(buf->snap)) return RS_E_ALIGN;
@@ -565,7 +574,7 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
   if (rs_status s = m2_inputs(drafts, prm, &a)) return s;
   a.y = y;
   a.K = K;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* st = stream;
   if (L->cfg.mode == RS_CONVENTIONAL) {
     if (!buf->snap) return RS_E_ARG;
     if (!aligned16(buf->snap)) return RS_E_ALIGN;
@@ -582,7 +591,7 @@ rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t
   if (L->cfg.max_draft == 0) return RS_E_MODE;
   if (!accepted) return RS_E_ARG;
   if (!aligned16(accepted)) return RS_E_ALIGN;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* st = stream;
   if (L->cfg.kind != RS_MAMBA2) {
     if (!buf || !buf->ckpt) return RS_E_ARG;
     if (L->cfg.mode == RS_REPLAY && (!buf->ring || !buf->meta)) return RS_E_ARG;
@@ -597,7 +606,7 @@ rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t
       gdn_launch(GDNOp::Restore, a, l, st);
     } else {
       commit_meta(commit_args(L, buf, accepted), st);
-      if (hipGetLastError() != hipSuccess) return RS_E_LAUNCH;
+      if (rs_status s = launch_status()) return s;
       gdn_launch(GDNOp::CommitFold, a, l, st);
     }
     return launched();
@@ -615,7 +624,7 @@ rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t
     m2_launch(M2Op::Restore, a, l, st);
   } else {
     commit_meta(commit_args(L, buf, accepted), st);
-    if (hipGetLastError() != hipSuccess) return RS_E_LAUNCH;
+    if (rs_status s = launch_status()) return s;
     const int tiles = L->cfg.batch * L->cfg.nheads;
     l.grid = tiles < 2048 ? tiles : 2048;
     m2_launch(M2Op::CommitFold, a, l, st);
@@ -640,7 +649,7 @@ rs_status rs_requant_read_copy(const rs_layer* L, const rs_buffers* buf, void* s
   l.rdf = FMT_NVFP4;
   l.rc = true;
   l.grid = L->cfg.batch * L->heads;
-  m2_launch(M2Op::Requant, a, l, static_cast<hipStream_t>(stream));
+  m2_launch(M2Op::Requant, a, l, stream);
   return launched();
 }
 

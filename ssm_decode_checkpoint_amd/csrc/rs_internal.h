@@ -1,4 +1,5 @@
-// Library-internal declarations shared by the host API and the kernel files.
+// Library-internal declarations of the kernel files: the host interface
+// (rs_host.h) and the device-side arrival protocol of the step kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -6,46 +7,9 @@
 
 #include "rs.h"
 #include "rs_device.h"
+#include "rs_host.h"
 
 namespace rs {
-
-constexpr int kMaxDraft = 8;
-constexpr uint32_t kLayerMagic = 0x52534C31u;  // "RSL1"
-
-// One sequence whose committed buffer entries a speculative commit folds.
-struct FoldItem {
-  int32_t b;      // sequence
-  int32_t m;      // entries folded
-  int64_t nck;    // n_ckpt before the fold (gives the ring slots)
-};
-
-// Kernel arguments for every Mamba-2 kernel (passed by value).
-struct M2Args {
-  int batch, nheads, ngroups, hpg, kmax, K, fuse_rc;
-  StateBuf ck;          // checkpoint, or live state (conventional)
-  StateBuf rc;          // NVFP4 read copy
-  StateBuf rd;          // what non-flush / append read: rc or ck
-  float* snap;          // snapshot baseline states
-  void *rx, *rB, *rC, *rdt;
-  rs_meta* meta;
-  uint32_t* arrive;     // first-level arrival counters, arrive_groups(nheads) per sequence
-  FoldItem* work;
-  int* work_count;
-  const void *x, *B, *C, *dt;
-  const float *A, *D;
-  float* y;
-  const int32_t* accepted;
-};
-
-enum class M2Op { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore, Requant };
-
-struct M2Launch {
-  int rows, cols;   // dstate, headdim
-  bool in_bf16;
-  int ckf, rdf;     // checkpoint format, format read by non-flush / append
-  bool rc;          // read copy configured
-  int grid;
-};
 
 // Per-sequence buffer counters, advanced inside the step kernels (sitech.ge
 // ReplaySSM page, "How ReplaySSM works": append on a non-flush step; fold and
@@ -65,11 +29,6 @@ struct M2Launch {
 // launch. The first-level atomic is issued after the state loads and its
 // result is needed only at the end, so it costs the workgroup no wait.
 enum class MetaOp { NonFlush = 0, Flush = 1, Append = 2 };
-
-constexpr int kArriveGroup = 32;   // workgroups per first-level counter
-constexpr int kArriveStride = 32;  // uint32 per first-level counter (128 bytes)
-
-__host__ __device__ constexpr int arrive_groups(int nwg) { return (nwg + kArriveGroup - 1) / kArriveGroup; }
 
 struct Arrival {
   uint32_t c;
@@ -120,98 +79,5 @@ struct Arrival {
     }
   }
 };
-
-bool m2_shape_supported(int dstate, int headdim);
-void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st);
-
-// Speculative commit, counter part (both layer kinds): len += accepted[b], nd = 0,
-// and the ordered list of sequences whose committed entries must be folded now.
-struct CommitArgs {
-  int batch, kmax;
-  rs_meta* meta;
-  const int32_t* accepted;
-  FoldItem* work;
-  int* work_count;
-};
-void commit_meta(const CommitArgs& a, hipStream_t st);
-
-// Clear the counters of the listed sequences (slot reuse); entries outside
-// [0, batch) are skipped.
-void reset_slots(rs_meta* meta, int batch, const int32_t* seqs, int count, hipStream_t st);
-
-// Copy the whole state of listed sequences between two buffer sets of one
-// layer configuration: every per-sequence region (checkpoint and its scales,
-// read copy, ring arrays) is `per` bytes at src + seq * per, and the counters
-// n_ckpt, len, nd, err of the meta record.
-constexpr int kMaxCopyRegions = 16;
-struct CopyRegion {
-  const char* src;
-  char* dst;
-  uint64_t per;
-};
-struct CopyArgs {
-  CopyRegion r[kMaxCopyRegions];
-  int nreg, count, src_batch, dst_batch;
-  const int32_t* src_seqs;
-  const int32_t* dst_seqs;
-  const rs_meta* src_meta;   // null in conventional mode
-  rs_meta* dst_meta;
-};
-void copy_slots(const CopyArgs& a, int blocks_per_pair, hipStream_t st);
-
-// Mamba-2 block: short causal convolution with its ring of recent inputs, and
-// the gated RMS norm of the SSM output.
-struct ConvArgs {
-  int batch, channels, width, K;
-  int d_inner, gn;         // x channels, then ngroups * dstate each for B and C
-  const rs_meta* meta;     // positions n_ckpt + len
-  void* ring;              // [batch][16][channels]
-  const void* xbc;         // [K][batch][channels]
-  const float* w;          // [channels][width]
-  const float* bias;       // [channels] or null
-  void* x;                 // [K][batch][d_inner]
-  void* B;                 // [K][batch][gn]
-  void* C;                 // [K][batch][gn]
-};
-void conv_step(const ConvArgs& a, bool bf, hipStream_t st);
-
-struct NormArgs {
-  int rows, d, gs;         // rows = K * batch, d = d_inner, gs = channels per group
-  float eps;
-  const float* y;          // [rows][d]
-  const void* z;           // [rows][d], input type
-  const float* w;          // [d]
-  void* out;               // [rows][d], input type
-};
-void gated_norm(const NormArgs& a, bool bf, hipStream_t st);
-
-// Gated DeltaNet
-struct GDNArgs {
-  int batch, nv, nqk, vpk;   // vpk = value heads per qk head
-  int K, kmax;               // speculative: drafts in this call, configured maximum
-  StateBuf ck;               // checkpoint, or live state (conventional)
-  float* snap;               // snapshot baseline states [kmax][batch][nv][dk][dv]
-  void *rq, *rk, *rv, *rg, *rbeta, *ru;
-  rs_meta* meta;
-  uint32_t* arrive;     // first-level arrival counters, arrive_groups(workgroups per sequence) each
-  FoldItem* work;
-  int* work_count;
-  const int32_t* accepted;
-  const void *q, *k, *v;     // one token, or K drafts stacked [K][batch][...]
-  const float *g, *beta;
-  float* o;                  // [batch][nv][dv], or [K][batch][nv][dv]
-};
-
-enum class GDNOp { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore };
-
-struct GDNLaunch {
-  int dk, dv;
-  bool in_bf16;
-  bool vg;        // Kimi Delta Attention: per-key-channel gate
-  int grid;
-};
-
-bool gdn_shape_supported(int dk, int dv);
-void gdn_launch(GDNOp op, const GDNArgs& a, const GDNLaunch& l, hipStream_t st);
 
 }  // namespace rs

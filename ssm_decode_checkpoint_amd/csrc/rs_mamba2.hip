@@ -12,12 +12,9 @@ extern template void m2_launch_shape<64, 64>(M2Op, const M2Args&, const M2Launch
 extern template void m2_launch_shape<128, 64>(M2Op, const M2Args&, const M2Launch&, hipStream_t);
 extern template void m2_launch_shape<128, 128>(M2Op, const M2Args&, const M2Launch&, hipStream_t);
 
-bool m2_shape_supported(int dstate, int headdim) {
-  return (dstate == 16 && headdim == 16) || (dstate == 64 && headdim == 64) || (dstate == 128 && headdim == 64) ||
-         (dstate == 128 && headdim == 128);
-}
-
-void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, hipStream_t st) {
+// The compiled shapes are the ones m2_shape_supported (rs_host.cpp) accepts.
+void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (l.rows == 16 && l.cols == 16) m2_launch_shape<16, 16>(op, a, l, st);
   else if (l.rows == 64 && l.cols == 64) m2_launch_shape<64, 64>(op, a, l, st);
   else if (l.rows == 128 && l.cols == 64) m2_launch_shape<128, 64>(op, a, l, st);
