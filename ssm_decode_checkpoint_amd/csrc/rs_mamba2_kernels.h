@@ -21,6 +21,7 @@
 
 #include "rs_device.h"
 #include "rs_tile.h"
+#include "rs_mtile.h"
 #include "rs_internal.h"
 
 namespace rs {
@@ -41,7 +42,7 @@ struct alignas(16) M2Smem {
   float L[Q];             // l_j per output
   float red[4 * Q * NC];  // reduction scratch
   float out[Q * NC];      // matvec results
-  float xt[XT ? NE : 1][NC];  // fold coefficients w_{m,i} dt_i x_i
+  alignas(16) float xt[XT ? NE : 1][NC];  // fold coefficients w_{m,i} dt_i x_i
   float s4[4];
 };
 
@@ -462,9 +463,11 @@ void m2_nonflush_wave_kernel(M2Args a) {
 // fold body shared by the flush step and the commit fold
 // H <- l_m H + sum_e B_e xt_e^T with xt_e = w_{m,e} dt_e x_e (entries staged)
 // ----------------------------------------------------------------------------
-template <int E, int NR, int NC, typename SM>
-__device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, SM& s, int m) {
-  // coefficients
+// Coefficients of the fold into LDS: L = l_m and xt_e = w_{m,e} dt_e x_e.
+// Barriers inside; all threads must call.
+template <typename SM>
+__device__ __forceinline__ void fold_coeffs(SM& s, int m) {
+  constexpr int NC = sizeof(s.X[0]) / sizeof(float);
   if (static_cast<int>(threadIdx.x) < m) {
     const int e = threadIdx.x;
     float w = 1.0f;
@@ -477,11 +480,19 @@ __device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, SM& s, int m) {
     s.L[0] = L;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < m * NC; idx += kThreads) {
-    const int e = idx / NC, p = idx - e * NC;
-    s.xt[e][p] = s.w[0][e] * s.X[e][p];
+  static_assert(NC % 4 == 0, "float4 rows");
+  for (int idx = threadIdx.x; idx < m * (NC / 4); idx += kThreads) {
+    const int e = idx / (NC / 4), p = 4 * (idx - e * (NC / 4));
+    const float w = s.w[0][e];
+    const float4 x = *reinterpret_cast<const float4*>(&s.X[e][p]);
+    *reinterpret_cast<float4*>(&s.xt[e][p]) = make_float4(w * x.x, w * x.y, w * x.z, w * x.w);
   }
   __syncthreads();
+}
+
+template <int E, int NR, int NC, typename SM>
+__device__ __forceinline__ void fold_tile(RegTile<E, NR, NC>& H, SM& s, int m) {
+  fold_coeffs(s, m);
   const float L = s.L[0];
   const int c0 = RegTile<E, NR, NC>::col0();
 #pragma unroll
@@ -529,6 +540,79 @@ __device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTi
   }
 }
 
+// The fold, the output matvec and the store of the flush and commit-fold, on
+// one of two tile layouts: the streaming layout (each thread owns E
+// consecutive columns of rows spaced a pass apart; rank-m update on fp32 FMAs)
+// or the matrix-core layout of rs_mtile.h (rank-m update on
+// v_mfma_f32_16x16x4f32; each lane owns 16 consecutive columns of a row).
+template <int CKF, bool RC, int NR, int NC>
+struct ValuFold {
+  static constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
+  using Raw = RawTile<CKF, E, NR, NC>;
+  using Tile = RegTile<E, NR, NC>;
+  template <typename SM>
+  __device__ __forceinline__ static void fold(const Raw& raw, Tile& H, SM& s, int m) {
+    raw.decode(H);
+    fold_tile(H, s, m);
+  }
+  __device__ __forceinline__ static void matvec(const Tile& H, const float* w, float* red, float* out) {
+    tile_matvec<1>(H, w, NR, red, out);
+  }
+  __device__ __forceinline__ static void store(const M2Args& a, size_t tile, Tile& H, float* s4) {
+    store_folded<CKF, RC>(a, tile, H, s4);
+  }
+};
+
+template <int CKF, bool RC, int NR, int NC>
+struct MfmaFold {
+  using Raw = MRaw<CKF, NR, NC>;
+  using Tile = MTile<NR, NC>;
+  // the decay product l_m is applied as the tile is decoded
+  template <typename SM>
+  __device__ __forceinline__ static void fold(const Raw& raw, Tile& H, SM& s, int m) {
+    fold_coeffs(s, m);
+    raw.decode(H, s.L[0]);
+    mtile_rank_update(H, &s.B[0][0], NR, &s.xt[0][0], NC, m);
+  }
+  __device__ __forceinline__ static void matvec(const Tile& H, const float* w, float* red, float* out) {
+    mtile_matvec(H, w, red, out);
+  }
+  // as store_folded: for an fp32 checkpoint the copy's maximum is reduced
+  // before the checkpoint's stores go out
+  __device__ __forceinline__ static void store(const M2Args& a, size_t tile, Tile& H, float* s4) {
+    if constexpr (RC && CKF == FMT_F32) {
+      if (a.fuse_rc) {
+        const float amax = mtile_absmax(H, s4);
+        mtile_store<FMT_F32>(a.ck, tile, H, s4);
+        mtile_store<FMT_NVFP4>(a.rc, tile, H, s4, amax);
+        return;
+      }
+    }
+    mtile_store<CKF>(a.ck, tile, H, s4);
+    if constexpr (RC) {
+      if (a.fuse_rc) {
+        mtile_round_trip<CKF>(H, s4);
+        mtile_store<FMT_NVFP4>(a.rc, tile, H, s4);
+      }
+    }
+  }
+};
+
+// Which layout folds a (format, shape), by measurement at batch 256 on the
+// 128 x 64 state (flush times, streaming vs matrix-core layout): fp32 374.9
+// vs 437.1 us and fp32 + NVFP4 copy 455.9 vs 515.4 (the fp32 flush is bound
+// by its traffic, which the streaming layout moves in whole 1 KiB rows per
+// instruction); fp16 214.1 vs 240.9; fp16 + copy 284.0 vs 271.2; fp8 246.7
+// vs 199.7; fp8 + copy 358.5 vs 341.5; uniform NVFP4 261.0 vs 210.1 (these
+// are bound by the fold's arithmetic on the streaming layout).
+template <int CKF, bool RC, int NR, int NC>
+constexpr bool kMfmaFold =
+    NR % 64 == 0 && NC % 64 == 0 && (CKF == FMT_FP8 || CKF == FMT_NVFP4 || (CKF == FMT_F16 && RC));
+
+template <int CKF, bool RC, int NR, int NC>
+using FoldOps = typename std::conditional<kMfmaFold<CKF, RC, NR, NC>, MfmaFold<CKF, RC, NR, NC>,
+                                          ValuFold<CKF, RC, NR, NC>>::type;
+
 // ----------------------------------------------------------------------------
 // flush step: fold len stored entries + the current token, write once, y
 // ----------------------------------------------------------------------------
@@ -537,7 +621,7 @@ using M2FlSmem = M2Smem<NR, NC, kRing, 1, true>;
 
 template <typename TIN, int CKF, bool RC, int NR, int NC>
 __device__ __forceinline__ void m2_flush_body(const M2Args& a, M2FlSmem<NR, NC>& s) {
-  constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
+  using Ops = FoldOps<CKF, RC, NR, NC>;
   constexpr int V = 16 / static_cast<int>(sizeof(TIN));
   static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
   constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
@@ -545,7 +629,7 @@ __device__ __forceinline__ void m2_flush_body(const M2Args& a, M2FlSmem<NR, NC>&
   constexpr int CC = (NR / V + kThreads - 1) / kThreads;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / a.nheads, h = tile - b * a.nheads, g = h / a.hpg;
-  const float Ah = a.A[h];
+  const float Ah = a.A[h], Dh = a.D[h];   // before the tile: a load behind it would wait for all of it
   rs_meta* mp = a.meta + b;
   uint32_t* actr = a.arrive + static_cast<size_t>(b) * arrive_groups(a.nheads) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
@@ -573,7 +657,7 @@ __device__ __forceinline__ void m2_flush_body(const M2Args& a, M2FlSmem<NR, NC>&
     cc.load(EntrySrc<TIN>{inC, inC, 0, 0, 0, NR}, 1, NR);
     const int de = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
     const float dtv = to_f(*EntrySrc<TIN>{rDt, inDt, 0, nck, len, 1}.at(de));
-    RawTile<CKF, E, NR, NC> raw;
+    typename Ops::Raw raw;
     raw.issue(a.ck, tile);
     arr.arrive(actr, h, nck, len, nd);
     cb.to_lds(&s.B[0][0], NR, m, NR);
@@ -584,14 +668,12 @@ __device__ __forceinline__ void m2_flush_body(const M2Args& a, M2FlSmem<NR, NC>&
       s.a[threadIdx.x] = expf(dtv * Ah);
     }
     __syncthreads();
-    RegTile<E, NR, NC> H;
-    raw.decode(H);
-    fold_tile(H, s, m);
-    tile_matvec<1>(H, &s.Cw[0][0], NR, s.red, s.out);
-    const float Dh = a.D[h];
+    typename Ops::Tile H;
+    Ops::fold(raw, H, s, m);
+    Ops::matvec(H, &s.Cw[0][0], s.red, s.out);
     for (int p = threadIdx.x; p < NC; p += kThreads)
       a.y[static_cast<size_t>(tile) * NC + p] = s.out[p] + Dh * s.X[m - 1][p];
-    store_folded<CKF, RC>(a, tile, H, s.s4);
+    Ops::store(a, tile, H, s.s4);
   }
   arr.finish(mp, actr, h, a.nheads, MetaOp::Flush, 0, nck, len, nd);
 }
@@ -723,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void m2_spec_append_kernel(M2Args a) {
 // item, over a fixed grid (every workgroup leaves when the list is done)
 template <typename TIN, int CKF, bool RC, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
-  constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
+  using Ops = FoldOps<CKF, RC, NR, NC>;
   constexpr int V = 16 / static_cast<int>(sizeof(TIN));
   static_assert(NR % V == 0 && NC % V == 0, "records are whole 16-byte chunks");
   constexpr int CB = (kRing * NR / V + kThreads - 1) / kThreads;
@@ -747,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
     const int de = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
     const float dtv = to_f(*EntrySrc<TIN>{rDt, rDt, 0, it.nck, m, 1}.at(de));
     const float Ah = a.A[h];   // before the tile: a load behind it would wait for all of it
-    RawTile<CKF, E, NR, NC> raw;
+    typename Ops::Raw raw;
     raw.issue(a.ck, tile);
     cb.to_lds(&s.B[0][0], NR, m, NR);
     cx.to_lds(&s.X[0][0], NC, m, NC);
@@ -756,10 +838,9 @@ __global__ __launch_bounds__(kThreads) void m2_commit_fold_kernel(M2Args a) {
       s.a[threadIdx.x] = expf(dtv * Ah);
     }
     __syncthreads();
-    RegTile<E, NR, NC> H;
-    raw.decode(H);
-    fold_tile(H, s, m);
-    store_folded<CKF, RC>(a, tile, H, s.s4);
+    typename Ops::Tile H;
+    Ops::fold(raw, H, s, m);
+    Ops::store(a, tile, H, s.s4);
     __syncthreads();
   }
 }

@@ -173,22 +173,39 @@ __device__ __forceinline__ float clamp_mag(float q, float m) { return fminf(fmax
 // could overflow. Subnormal quotients (|x / d| < 2^-126) cannot change a code.
 constexpr float kRecipMin = 0x1p-125f;
 
-__device__ __forceinline__ float quot(float x, float d, float y, bool recip) {
-  if (!recip) return x / d;
-  const float q = x * y;
-  const float r = fmaf(-q, d, x);
-  return copysignf(fmaf(r, y, q), x);
+// q[i] = RN(x[i] / d) for i < N, with y = RN(1/d) when d >= kRecipMin. The
+// choice between the correction step and the division depends on d alone, so
+// it is taken once for all N quotients (those sharing a scale).
+template <int N>
+__device__ __forceinline__ void quot_n(const float* x, float d, float y, float* q) {
+  if (d >= kRecipMin) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float q0 = x[i] * y;
+      const float r = fmaf(-q0, d, x[i]);
+      q[i] = copysignf(fmaf(r, y, q0), x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) q[i] = x[i] / d;
+  }
 }
 
-// Four E4M3FN codes of x[0..3] / sc, element i in byte i (y = RN(1/sc)).
-__device__ __forceinline__ uint32_t fp8_codes4(const float* x, float sc, float y) {
-  const bool rc = sc >= kRecipMin;
-  s16x2 r = {0, 0};
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(quot(x[0], sc, y, rc), 448.0f),
-                                               clamp_mag(quot(x[1], sc, y, rc), 448.0f), 1.0f, false);
-  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(quot(x[2], sc, y, rc), 448.0f),
-                                               clamp_mag(quot(x[3], sc, y, rc), 448.0f), 1.0f, true);
-  return static_cast<uint32_t>(static_cast<uint16_t>(r.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(r.y)) << 16);
+// E4M3FN codes of x[0..N) / sc, element i in byte i of w (N a multiple of 4;
+// y = RN(1/sc)).
+template <int N>
+__device__ __forceinline__ void fp8_codes(const float* x, float sc, float y, uint32_t* w) {
+  float q[N];
+  quot_n<N>(x, sc, y, q);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    s16x2 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(q[4 * i], 448.0f), clamp_mag(q[4 * i + 1], 448.0f),
+                                                 1.0f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(q[4 * i + 2], 448.0f), clamp_mag(q[4 * i + 3], 448.0f),
+                                                 1.0f, true);
+    w[i] = static_cast<uint32_t>(static_cast<uint16_t>(r.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(r.y)) << 16);
+  }
 }
 
 // E4M3FN code of a non-negative quotient q (an NVFP4 block scale).
@@ -198,19 +215,23 @@ __device__ __forceinline__ uint32_t e4m3_code_of(float q) {
   return static_cast<uint32_t>(r.x) & 0xFFu;
 }
 
-// Eight E2M1 codes of x[0..7] / sd, element i in nibble i (all 0 when sd = 0).
-__device__ __forceinline__ uint32_t nvfp4_codes8(const float* x, float sd) {
-  const bool rc = sd >= kRecipMin;
-  const float y = 1.0f / sd;   // one correctly rounded division per eight codes
-  float q[8];
+// E2M1 codes of x[0..N) / sd (one block scale), element i in nibble i of w
+// (N a multiple of 8; all 0 when sd = 0). One correctly rounded division per
+// call gives the reciprocal.
+template <int N>
+__device__ __forceinline__ void nvfp4_codes(const float* x, float sd, uint32_t* w) {
+  float q[N];
+  quot_n<N>(x, sd, 1.0f / sd, q);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = clamp_mag(quot(x[i], sd, y, rc), 6.0f);
-  uint32_t w = 0u;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[0], q[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[2], q[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[4], q[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, q[6], q[7], 1.0f, 3);
-  return sd == 0.0f ? 0u : w;
+  for (int j = 0; j < N / 8; ++j) {
+    const float* p = q + 8 * j;
+    uint32_t v = 0u;
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, clamp_mag(p[0], 6.0f), clamp_mag(p[1], 6.0f), 1.0f, 0);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, clamp_mag(p[2], 6.0f), clamp_mag(p[3], 6.0f), 1.0f, 1);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, clamp_mag(p[4], 6.0f), clamp_mag(p[5], 6.0f), 1.0f, 2);
+    v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, clamp_mag(p[6], 6.0f), clamp_mag(p[7], 6.0f), 1.0f, 3);
+    w[j] = sd == 0.0f ? 0u : v;
+  }
 }
 
 __device__ __forceinline__ float fp8_scale_of(float amax) {
@@ -249,7 +270,9 @@ __device__ __forceinline__ void tile_round_trip(RegTile<E, NR, NC>& M, float* sc
 #pragma unroll
     for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
       Raw<FMT_FP8, 8> r;
-      r.v = make_uint2(fp8_codes4(M.v[k], sc, y), fp8_codes4(M.v[k] + 4, sc, y));
+      uint32_t w[2];
+      fp8_codes<8>(M.v[k], sc, y, w);
+      r.v = make_uint2(w[0], w[1]);
       decode_chunk<FMT_FP8, 8>(r, sc, M.v[k]);
     }
   } else if constexpr (FMT == FMT_NVFP4) {
@@ -259,7 +282,7 @@ __device__ __forceinline__ void tile_round_trip(RegTile<E, NR, NC>& M, float* sc
     for (int k = 0; k < RegTile<E, NR, NC>::P; ++k) {
       Raw<FMT_NVFP4, 8> r;
       r.s = nvfp4_block_code(M.v[k], ts);
-      r.v = nvfp4_codes8(M.v[k], e4m3_value(r.s) * ts);
+      nvfp4_codes<8>(M.v[k], e4m3_value(r.s) * ts, &r.v);
       decode_chunk<FMT_NVFP4, 8>(r, ts, M.v[k]);
     }
   }
@@ -314,9 +337,11 @@ __device__ __forceinline__ void tile_store(const StateBuf& sb, size_t mat, const
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
       const int row = RegTile<E, NR, NC>::row(k);
-      if (row < NR)
-        nt_store(make_uint2(fp8_codes4(M.v[k], sc, y), fp8_codes4(M.v[k] + 4, sc, y)),
-                 reinterpret_cast<uint2*>(base + row * NC + c * E));
+      if (row < NR) {
+        uint32_t w[2];
+        fp8_codes<8>(M.v[k], sc, y, w);
+        nt_store(make_uint2(w[0], w[1]), reinterpret_cast<uint2*>(base + row * NC + c * E));
+      }
     }
     if (threadIdx.x == 0) sb.tscale[mat] = sc;
   } else {
@@ -339,7 +364,8 @@ __device__ __forceinline__ void tile_store_nvfp4(const StateBuf& sb, size_t mat,
     for (int k = 0; k < TM::PASSES; ++k) {
       const int row = RegTile<E, NR, NC>::row(k);
       const uint32_t s = nvfp4_block_code(M.v[k], ts);
-      const uint32_t w = nvfp4_codes8(M.v[k], e4m3_value(s) * ts);
+      uint32_t w;
+      nvfp4_codes<8>(M.v[k], e4m3_value(s) * ts, &w);
       if (row < NR) {
         nt_store(w, reinterpret_cast<uint32_t*>(base + (row * NC + c * 8) / 2));
         if ((c & 1) == 0) sbase[(row * NC + c * 8) / 16] = static_cast<uint8_t>(s);

@@ -119,3 +119,24 @@ def test_dominant_kernels_keep_their_occupancy(isa):
     # wave-per-head kernel, FP8 (2) and NVFP4 (3) reads with bf16 records
     for k, v in _usage(usage, r"m2_nonflush_wave_kernelINS_4bf16ELi[23]ELi128ELi64E").items():
         assert v["Occupancy [waves/SIMD]"] >= 6, (k, v)
+
+
+def test_fold_layout_per_format(isa):
+    """The rank-16 fold runs on the matrix cores (v_mfma_f32_16x16x4_f32) for the
+    FP8 and NVFP4 checkpoints and for FP16 with the read copy, and on the
+    streaming layout's VALU FMAs for fp32 checkpoints (traffic-bound there)."""
+    kernels, _ = isa
+
+    def has_mfma(pat):
+        hits = [k for k in kernels if re.search(pat, k)]
+        assert hits, pat
+        return all(any("v_mfma_f32_16x16x4" in l for l in kernels[k]) for k in hits), \
+            any(any("v_mfma_f32_16x16x4" in l for l in kernels[k]) for k in hits)
+
+    for fmt_rc in ("Li2ELb0", "Li2ELb1", "Li3ELb0", "Li1ELb1"):
+        for kern in ("m2_flush_kernel", "m2_commit_fold_kernel"):
+            every, _ = has_mfma(rf"{kern}INS_4bf16E{fmt_rc}ELi128ELi64E")
+            assert every, (kern, fmt_rc)
+    for fmt_rc in ("Li0ELb0", "Li0ELb1", "Li1ELb0"):
+        _, some = has_mfma(rf"m2_flush_kernelINS_4bf16E{fmt_rc}ELi128ELi64E")
+        assert not some, fmt_rc
