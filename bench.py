@@ -51,6 +51,7 @@ import workloads as W  # noqa: E402
 
 RING = 16
 HBM_PEAK_GBS = 8000.0
+POOL_MAX = 16            # worker processes of the CPU oracle leg (the host's CPU share per GPU)
 METRIC = "SSM-layer decode tokens/s at batch 256 + achieved HBM GB/s (% of peak) vs conventional"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["ssm_decode_checkpoint_amd/csrc/rs_mamba2_kernels.h", "ssm_decode_checkpoint_amd/csrc/rs_tile.h",
@@ -112,30 +113,88 @@ def gdn_bytes(w: W.GDNWorkload):
 # CPU baseline: the fp64 oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(w: W.Mamba2Workload, nseq: int, windows: int = 1):
+def _conv_window(w: W.Mamba2Workload, seqs, steps: int) -> float:
+    """Seconds the fp64 conventional recurrence (the oracle) takes for `steps`
+    decode steps of the listed sequences, one thread; inputs drawn beforehand."""
     from oracle import decode
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
-    except Exception:  # pragma: no cover
-        limiter = None
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        p = W.m2_params(w)
+        ref = decode.M2Conventional(W.m2_init_states(w, seqs), p["A"], p["D"])
+        toks = [W.m2_step(w, t, seqs) for t in range(steps)]
+        t0 = time.perf_counter()
+        for tk in toks:
+            ref.step(tk)
+        return time.perf_counter() - t0
+
+
+def _pool_worker(w, seqs, steps, ready, go, out):
+    """One shard of the pool leg: draw inputs, wait for every shard, then time."""
+    from oracle import decode
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        p = W.m2_params(w)
+        ref = decode.M2Conventional(W.m2_init_states(w, seqs), p["A"], p["D"])
+        toks = [W.m2_step(w, t, seqs) for t in range(steps)]
+        ready.wait()
+        go.wait()
+        t0 = time.perf_counter()
+        for tk in toks:
+            ref.step(tk)
+        out.put(time.perf_counter() - t0)
+
+
+def cpu_baseline(w: W.Mamba2Workload, single_seqs: int = 48, replay_seqs: int = 64):
+    """The fp64 CPU oracle timed on this host's cores on one 16-step window of
+    the workload: the conventional recurrence single-process (a sample of
+    sequences) and as a process pool over every core this process may run on,
+    one shard of sequences per core, the whole batch (the value); and, as a
+    separate figure, the oracle's ReplaySSM form on one thread. A reported
+    baseline, not the target. Runs before the GPU is touched (the pool forks)."""
+    import multiprocessing as mp
+    from oracle import decode
+    from threadpoolctl import threadpool_limits
+    host = len(os.sched_getaffinity(0))
+    n = min(host, POOL_MAX)
+    # single process, one thread
+    single = _conv_window(w, list(range(single_seqs)), RING)
+    # pool: one process per core, sequences dealt round-robin
+    ctx = mp.get_context("fork")
+    ready, go, out = ctx.Barrier(n + 1), ctx.Barrier(n + 1), ctx.Queue()
+    shards = [list(range(i, w.batch, n)) for i in range(n)]
+    procs = [ctx.Process(target=_pool_worker, args=(w, sh, RING, ready, go, out)) for sh in shards if sh]
+    for pr in procs:
+        pr.start()
+    ready.wait()
+    t0 = time.perf_counter()
+    go.wait()
+    times = [out.get() for _ in procs]
+    pool_wall = time.perf_counter() - t0
+    for pr in procs:
+        pr.join()
+    # ReplaySSM form of the oracle, one thread
     p = W.m2_params(w)
-    seqs = list(range(nseq))
-    H0 = W.m2_init_states(w, seqs)
-    toks = [W.m2_step(w, t, seqs) for t in range(RING * windows)]
-    rep = decode.M2Replay(H0, p["A"], p["D"])
-    c0, t0 = time.process_time(), time.perf_counter()
-    for tk in toks:
-        rep.step(tk)
-    wall = time.perf_counter() - t0
-    cpu = time.process_time() - c0
-    if limiter is not None:
-        limiter.unregister()
-    ntok = nseq * RING * windows
-    return {"value": ntok / wall, "unit": "tokens/s", "cores": max(1, int(round(cpu / wall))), "kind": "oracle",
-            "sample": f"fp64 ReplaySSM oracle (checkpoint + buffer, plain numpy) on {nseq} of {w.batch} sequences "
-                      f"x {RING * windows} decode steps ({windows} windows) of the {w.name} workload; "
-                      f"{wall:.1f} s wall, {cpu:.1f} s CPU"}
+    seqs = list(range(replay_seqs))
+    with threadpool_limits(1):
+        rep = decode.M2Replay(W.m2_init_states(w, seqs), p["A"], p["D"])
+        toks = [W.m2_step(w, t, seqs) for t in range(RING)]
+        t1 = time.perf_counter()
+        for tk in toks:
+            rep.step(tk)
+        rwall = time.perf_counter() - t1
+    return {"value": w.batch * RING / pool_wall, "unit": "tokens/s", "cores": len(procs), "kind": "oracle",
+            "label": "baseline, not target", "host_cores": host,
+            "sample": (f"fp64 conventional recurrence (the oracle, plain numpy, one thread per process) on all "
+                       f"{w.batch} sequences x {RING} decode steps (one window) of the {w.name} workload, "
+                       f"{len(procs)} processes ({host} cores in os.sched_getaffinity(0), at most {POOL_MAX} used), "
+                       f"sequences dealt "
+                       f"round-robin; {pool_wall:.1f} s wall (slowest shard {max(times):.1f} s)"),
+            "single_process": {"value": single_seqs * RING / single, "unit": "tokens/s", "cores": 1,
+                               "sample": f"{single_seqs} sequences x {RING} steps, conventional recurrence; "
+                                         f"{single:.1f} s"},
+            "replay_oracle_one_thread": {"value": replay_seqs * RING / rwall, "unit": "tokens/s", "cores": 1,
+                                         "sample": f"fp64 ReplaySSM form of the oracle (checkpoint + buffer), "
+                                                   f"{replay_seqs} sequences x {RING} steps; {rwall:.1f} s"}}
 
 
 # ---------------------------------------------------------------------------
@@ -905,7 +964,6 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20, help="timed windows")
     ap.add_argument("--warmup", type=int, default=3, help="untimed windows")
-    ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the CPU oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--workload", action="append",
                     choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "kda_spec", "lowprec", "copy", "sweep",
@@ -923,10 +981,13 @@ def main():
               f"collective, so N GPUs would each run this single-GPU workload on their own batch shard.",
               file=sys.stderr)
         sys.exit(2)
+    wls = args.workload or ["mamba2"]
+    # the CPU oracle leg forks worker processes: before anything touches the GPU
+    cpu = cpu_baseline(W.M2_NEMOTRON) if ("mamba2" in wls and not args.no_cpu) else None
     import torch
     import ssm_decode_checkpoint_amd as rs
     torch.cuda.set_device(0)
-    for wl in (args.workload or ["mamba2"]):
+    for wl in wls:
         fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
               "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve, "block": bench_block,
               "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
@@ -935,7 +996,7 @@ def main():
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
         if wl == "mamba2":
-            out["cpu_baseline"] = None if args.no_cpu else cpu_baseline(W.M2_NEMOTRON, args.cpu_seqs, windows=2)
+            out["cpu_baseline"] = cpu
         print(json.dumps(out), flush=True)
         torch.cuda.empty_cache()
 
