@@ -199,15 +199,38 @@ class GDNConventional:
 
 
 class GDNReplay:
-    """ReplaySSM decode of a delta-rule layer in fp64 (fp64 checkpoint); rule = gdn
-    or kda as for GDNConventional."""
+    """ReplaySSM decode of a delta-rule layer in fp64; rule = gdn or kda as for
+    GDNConventional.
 
-    def __init__(self, S0, ring: int = R, max_draft: int = 0, rule=gdn):
+    ckpt_fmt: "f32_exact" (fp64 checkpoint, the method without storage
+    rounding) or "f32" (the checkpoint rounded to float32 at every write).
+    read_copy: None or "nvfp4". With a read copy, every output (non-flush
+    steps and speculative verify) is computed from the NVFP4 copy of the stored
+    checkpoint, the solved rows u included, while every fold (flush, commit)
+    solves its rows from the checkpoint itself, so read error never enters the
+    recurrence (sitech.ge ReplaySSM page, "Bounding quantization error"). The
+    copy quantizes the stored matrix [dk][dv] (value index innermost, the
+    layout the checkpoint is stored in), so its 16-element blocks run along dv.
+    """
+
+    def __init__(self, S0, ring: int = R, max_draft: int = 0, rule=gdn, ckpt_fmt: str = "f32_exact",
+                 read_copy=None):
         self.rule = rule
+        self.ckpt_fmt, self.read_copy = ckpt_fmt, read_copy
         self.batch = S0.shape[0]
-        self.ckpt = np.asarray(S0, dtype=np.float64).copy()
+        self.ckpt = _stored(ckpt_fmt, S0)
+        self.view = self._read_view(self.ckpt)
         self.ring = RingModel(self.batch, ring, max_draft)
         self.entries: List[Dict[int, dict]] = [dict() for _ in range(self.batch)]
+
+    def _read_view(self, ckpt):
+        if self.read_copy == "nvfp4":
+            return _stored("nvfp4", ckpt)
+        return ckpt
+
+    def _set_ckpt(self, b, Sn):
+        self.ckpt[b:b + 1] = _stored(self.ckpt_fmt, Sn)
+        self.view[b:b + 1] = self._read_view(self.ckpt[b:b + 1])
 
     def spec_append(self, drafts: Sequence[dict]) -> np.ndarray:
         """Append K drafts after the committed entries and return their verify outputs
@@ -224,7 +247,7 @@ class GDNReplay:
                 continue
             for s, d in zip(slots, dr):
                 self.entries[b][s] = d
-            os_ = [self.rule.replay_output(self.ckpt[b:b + 1], held + dr[:i + 1], dr[i]["q"]) for i in range(K)]
+            os_ = [self.rule.replay_output(self.view[b:b + 1], held + dr[:i + 1], dr[i]["q"]) for i in range(K)]
             out.append(np.stack(os_))
         return np.concatenate(out, axis=1)
 
@@ -235,7 +258,7 @@ class GDNReplay:
             folded = self.ring.spec_commit(b, int(k))
             if folded:
                 ents = [self.entries[b][s] for s in folded]
-                self.ckpt[b:b + 1] = self.rule.replay_fold(self.ckpt[b:b + 1], ents)
+                self._set_ckpt(b, self.rule.replay_fold(self.ckpt[b:b + 1], ents))
 
     def step(self, tok, force_flush: bool = False) -> np.ndarray:
         outs = []
@@ -248,14 +271,14 @@ class GDNReplay:
                     continue
                 Sn = self.rule.replay_fold(self.ckpt[b:b + 1], held + [tb])
                 o = np.einsum("bhvk,bhk->bhv", Sn, gdn.expand_qk(tb["q"], Sn.shape[1]))
-                self.ckpt[b:b + 1] = Sn
+                self._set_ckpt(b, Sn)
             else:
                 s = self.ring.nonflush(b)
                 if s is None:
                     outs.append(np.full((1,) + tb["v"].shape[1:], np.nan))
                     continue
                 self.entries[b][s] = tb
-                o = self.rule.replay_output(self.ckpt[b:b + 1], held + [tb], tb["q"])
+                o = self.rule.replay_output(self.view[b:b + 1], held + [tb], tb["q"])
             outs.append(o)
         return np.concatenate(outs)
 
