@@ -26,8 +26,9 @@
  * Conventions shared by every entry point
  * ---------------------------------------------------------------------------
  * Ownership. The caller allocates and owns every device buffer, sized from
- *   the rs_layer that rs_init fills. The library allocates nothing, keeps no
- *   global state and never synchronises; there is nothing to destroy.
+ *   the rs_layer that rs_init fills. The library allocates nothing and never
+ *   synchronises; there is nothing to destroy. Its only global state is the
+ *   static device array of rs_spec_commit_static (one per device).
  * Pointers. Device pointers (hipMalloc'd or equivalent), 16-byte aligned.
  *   rs_layer, rs_buffers, rs_inputs and rs_params structs themselves are host
  *   memory, read during the call only.
@@ -336,6 +337,20 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
  * kind; prm (A, D) is required for Mamba-2 only. */
 rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted,
                          const rs_params* prm, void* stream);
+
+/* rs_spec_commit for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops that forbid allocation): identical
+ * arguments, results and errors, but the commit's fold list (the ordered list
+ * of sequences whose committed entries are folded, and its count) lives in a
+ * static device array inside the library instead of the meta buffer's work
+ * space. Nothing is allocated, here or at set-up; the array (128 KiB per
+ * device, held until the process ends) is resolved on the first call on each
+ * device. Limit: batch <= 8192 (RS_E_ARG beyond it). Every call on one device
+ * shares that array: calls that overlap on one device, from any stream or
+ * layer, race; order them. RS_E_LAUNCH if the runtime cannot give the
+ * array's address. */
+rs_status rs_spec_commit_static(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted,
+                                const rs_params* prm, void* stream);
 
 /* Rewrite the whole NVFP4 read copy from the stored checkpoint (same page,
  * "Bounding quantization error"). Needs read_copy == RS_NVFP4. Bit-identical

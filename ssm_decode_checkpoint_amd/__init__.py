@@ -28,7 +28,7 @@ RS_NONE, RS_F32, RS_BF16, RS_F16, RS_FP8E4M3, RS_NVFP4 = 0, 1, 2, 3, 4, 5
 RS_ERR_FULL, RS_ERR_OVERFLOW, RS_ERR_COMMIT, RS_ERR_PENDING = 1, 2, 4, 8
 
 EXPORTS = ("rs_init", "rs_step_conventional", "rs_step_nonflush", "rs_step_flush", "rs_step", "rs_spec_append",
-           "rs_spec_commit", "rs_requant_read_copy", "rs_reset_slots", "rs_copy_slots", "rs_conv_step",
+           "rs_spec_commit", "rs_spec_commit_static", "rs_requant_read_copy", "rs_reset_slots", "rs_copy_slots", "rs_conv_step",
            "rs_gated_norm", "rs_status_string", "rs_version")
 
 
@@ -86,6 +86,7 @@ def lib() -> C.CDLL:
         L.rs_spec_append.argtypes = [P(RsLayer), P(RsBuffers), P(RsInputs), C.c_int32, P(RsParams), C.c_void_p,
                                      C.c_void_p]
         L.rs_spec_commit.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, P(RsParams), C.c_void_p]
+        L.rs_spec_commit_static.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, P(RsParams), C.c_void_p]
         L.rs_requant_read_copy.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p]
         L.rs_reset_slots.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, C.c_int32, C.c_void_p]
         L.rs_copy_slots.argtypes = [P(RsLayer), P(RsBuffers), C.c_void_p, P(RsLayer), P(RsBuffers), C.c_void_p,
@@ -234,6 +235,13 @@ def rs_spec_commit(layer: RsLayer, bufs: Buffers, accepted, A, D, stream=None, r
     st = lib().rs_spec_commit(C.byref(layer), C.byref(bufs.c()), _ptr(accepted), C.byref(_params(A, D)),
                               _stream(stream))
     return _check("rs_spec_commit", st, raise_on_error)
+
+
+def rs_spec_commit_static(layer: RsLayer, bufs: Buffers, accepted, A, D, stream=None,
+                          raise_on_error: bool = True) -> int:
+    st = lib().rs_spec_commit_static(C.byref(layer), C.byref(bufs.c()), _ptr(accepted), C.byref(_params(A, D)),
+                                     _stream(stream))
+    return _check("rs_spec_commit_static", st, raise_on_error)
 
 
 def rs_conv_step(layer: RsLayer, bufs: Buffers, conv_ring, xbc, K: int, weight, bias, width: int, x, B, Cm,

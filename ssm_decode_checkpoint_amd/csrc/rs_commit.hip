@@ -8,6 +8,8 @@
 // leaves less room than the largest draft count folds the committed entries
 // (n_ckpt += len, len = 0), and those sequences are listed, in ascending order,
 // for the layer's fold kernel.
+#include <atomic>
+
 #include "rs_internal.h"
 
 namespace rs {
@@ -135,5 +137,34 @@ void copy_slots(const CopyArgs& a, int blocks_per_pair, void* stream) {
 }
 
 rs_status launch_status() { return hipGetLastError() == hipSuccess ? RS_OK : RS_E_LAUNCH; }
+
+// Fold list of rs_spec_commit_static: FoldItem[kStaticFoldSeqs] (128 KiB), then
+// the count. Each device holds its own copy for the life of the process. In
+// host code `scratch` names a host-side stand-in, so its device address is
+// taken with hipGetSymbolAddress once per device (with that device current)
+// and only that address is handed to kernels. commit_meta_kernel writes the
+// count and the listed items on every call before the fold kernel reads them,
+// so nothing needs clearing between calls; calls that overlap on one device
+// share the array and race.
+constexpr size_t kStaticListBytes = static_cast<size_t>(kStaticFoldSeqs) * sizeof(FoldItem);
+static __device__ __align__(256) unsigned char scratch[kStaticListBytes + 256];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+rs_status static_fold_list(FoldItem** list, int** count) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RS_E_LAUNCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return RS_E_LAUNCH;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *list = static_cast<FoldItem*>(p);
+  *count = reinterpret_cast<int*>(static_cast<char*>(p) + kStaticListBytes);
+  return RS_OK;
+}
 
 }  // namespace rs

@@ -585,18 +585,29 @@ rs_status rs_spec_append(const rs_layer* L, const rs_buffers* buf, const rs_inpu
   return launched();
 }
 
-rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted, const rs_params* prm,
-                         void* stream) {
+// The speculative commit; the fold list lives in the meta buffer's work space,
+// or, with use_static, in the library's static device array.
+static rs_status spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted, const rs_params* prm,
+                             void* stream, bool use_static) {
   if (rs_status s = check_layer(L)) return s;
   if (L->cfg.max_draft == 0) return RS_E_MODE;
   if (!accepted) return RS_E_ARG;
   if (!aligned16(accepted)) return RS_E_ALIGN;
+  if (use_static && L->cfg.batch > kStaticFoldSeqs) return RS_E_ARG;
   void* st = stream;
   if (L->cfg.kind != RS_MAMBA2) {
     if (!buf || !buf->ckpt) return RS_E_ARG;
     if (L->cfg.mode == RS_REPLAY && (!buf->ring || !buf->meta)) return RS_E_ARG;
     if (!aligned16(buf->ckpt)) return RS_E_ALIGN;
     if (L->cfg.mode == RS_REPLAY && (!aligned16(buf->ring) || !aligned16(buf->meta))) return RS_E_ALIGN;
+  } else if (!prm || !prm->A || !prm->D) {
+    return RS_E_ARG;
+  }
+  FoldItem* list = nullptr;
+  int* count = nullptr;
+  if (use_static && L->cfg.mode == RS_REPLAY)
+    if (rs_status s = static_fold_list(&list, &count)) return s;
+  if (L->cfg.kind != RS_MAMBA2) {
     GDNArgs a = gdn_args(L, buf);
     a.accepted = accepted;
     GDNLaunch l = gdn_launch_cfg(L);
@@ -605,13 +616,17 @@ rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t
       if (!aligned16(buf->snap)) return RS_E_ALIGN;
       gdn_launch(GDNOp::Restore, a, l, st);
     } else {
-      commit_meta(commit_args(L, buf, accepted), st);
+      CommitArgs ca = commit_args(L, buf, accepted);
+      if (list) {
+        ca.work = a.work = list;
+        ca.work_count = a.work_count = count;
+      }
+      commit_meta(ca, st);
       if (rs_status s = launch_status()) return s;
       gdn_launch(GDNOp::CommitFold, a, l, st);
     }
     return launched();
   }
-  if (!prm || !prm->A || !prm->D) return RS_E_ARG;
   M2Args a;
   M2Launch l;
   if (rs_status s = m2_args(L, buf, &a, &l)) return s;
@@ -623,13 +638,28 @@ rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t
     if (!aligned16(buf->snap)) return RS_E_ALIGN;
     m2_launch(M2Op::Restore, a, l, st);
   } else {
-    commit_meta(commit_args(L, buf, accepted), st);
+    CommitArgs ca = commit_args(L, buf, accepted);
+    if (list) {
+      ca.work = a.work = list;
+      ca.work_count = a.work_count = count;
+    }
+    commit_meta(ca, st);
     if (rs_status s = launch_status()) return s;
     const int tiles = L->cfg.batch * L->cfg.nheads;
     l.grid = tiles < 2048 ? tiles : 2048;
     m2_launch(M2Op::CommitFold, a, l, st);
   }
   return launched();
+}
+
+rs_status rs_spec_commit(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted, const rs_params* prm,
+                         void* stream) {
+  return spec_commit(L, buf, accepted, prm, stream, false);
+}
+
+rs_status rs_spec_commit_static(const rs_layer* L, const rs_buffers* buf, const int32_t* accepted,
+                                const rs_params* prm, void* stream) {
+  return spec_commit(L, buf, accepted, prm, stream, true);
 }
 
 rs_status rs_requant_read_copy(const rs_layer* L, const rs_buffers* buf, void* stream) {

@@ -161,6 +161,14 @@ struct GDNLaunch {
 bool gdn_shape_supported(int dk, int dv);
 void gdn_launch(GDNOp op, const GDNArgs& a, const GDNLaunch& l, void* stream);
 
+// The speculative commit's fold list without caller memory: a static device
+// array in rs_commit.hip holding FoldItem[kStaticFoldSeqs] and the list's
+// count, one copy per device. Sets *list and *count to its address on the
+// current device (resolved once per device); RS_E_LAUNCH if the runtime
+// cannot give it.
+constexpr int kStaticFoldSeqs = 8192;
+rs_status static_fold_list(FoldItem** list, int** count);
+
 // RS_OK if every launch so far succeeded, RS_E_LAUNCH otherwise (the runtime's
 // last error, read and cleared; no synchronisation).
 rs_status launch_status();

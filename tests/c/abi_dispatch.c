@@ -13,7 +13,7 @@
 
 int rs_stub_calls(int kind);
 void rs_stub_reset(void);
-enum { STUB_M2, STUB_GDN, STUB_COMMIT, STUB_RESET, STUB_COPY, STUB_CONV, STUB_NORM, STUB_KINDS };
+enum { STUB_M2, STUB_GDN, STUB_COMMIT, STUB_RESET, STUB_COPY, STUB_CONV, STUB_NORM, STUB_STATIC, STUB_KINDS };
 
 static int fails = 0;
 
@@ -71,14 +71,15 @@ static rs_config delta_cfg(int kind, int mode) {
 }
 
 int main(void) {
-  const int M2[STUB_KINDS] = {1, 0, 0, 0, 0, 0, 0};
-  const int GD[STUB_KINDS] = {0, 1, 0, 0, 0, 0, 0};
-  const int M2C[STUB_KINDS] = {1, 0, 1, 0, 0, 0, 0};
-  const int GDC[STUB_KINDS] = {0, 1, 1, 0, 0, 0, 0};
-  const int RST[STUB_KINDS] = {0, 0, 0, 1, 0, 0, 0};
-  const int CPY[STUB_KINDS] = {0, 0, 0, 0, 1, 0, 0};
-  const int CNV[STUB_KINDS] = {0, 0, 0, 0, 0, 1, 0};
-  const int NRM[STUB_KINDS] = {0, 0, 0, 0, 0, 0, 1};
+  const int M2[STUB_KINDS] = {1, 0, 0, 0, 0, 0, 0, 0};
+  const int GD[STUB_KINDS] = {0, 1, 0, 0, 0, 0, 0, 0};
+  const int M2C[STUB_KINDS] = {1, 0, 1, 0, 0, 0, 0, 0};
+  const int GDC[STUB_KINDS] = {0, 1, 1, 0, 0, 0, 0, 0};
+  const int M2S[STUB_KINDS] = {1, 0, 1, 0, 0, 0, 0, 1};
+  const int RST[STUB_KINDS] = {0, 0, 0, 1, 0, 0, 0, 0};
+  const int CPY[STUB_KINDS] = {0, 0, 0, 0, 1, 0, 0, 0};
+  const int CNV[STUB_KINDS] = {0, 0, 0, 0, 0, 1, 0, 0};
+  const int NRM[STUB_KINDS] = {0, 0, 0, 0, 0, 0, 1, 0};
   rs_stub_reset();
 
   /* ---- Mamba-2, replay mode, fp32 checkpoint with an NVFP4 read copy ---- */
@@ -106,6 +107,18 @@ int main(void) {
   }
   {
     SNAP(b); expect_call(rs_spec_commit(&L, &buf, acc, &prm, NULL), RS_OK, M2C, b, "commit: counters, then fold");
+  }
+  {
+    SNAP(b); expect_call(rs_spec_commit_static(&L, &buf, acc, &prm, NULL), RS_OK, M2S, b,
+                         "commit with the static fold list");
+  }
+  {
+    rs_config big = c;
+    big.batch = 8193;
+    rs_layer LB;
+    expect(rs_init(&big, &LB) == RS_OK, "a layer of 8193 sequences");
+    SNAP(b); expect_call(rs_spec_commit_static(&LB, &buf, acc, &prm, NULL), RS_E_ARG, NULL, b,
+                         "static fold list refused beyond 8192 sequences");
   }
   {
     SNAP(b); expect_call(rs_requant_read_copy(&L, &buf, NULL), RS_OK, M2, b, "requant dispatches");
