@@ -154,9 +154,15 @@ typedef struct rs_config {
   int32_t ring;          /* buffer entries; must be 16 */
   int32_t max_draft;     /* 0 = no speculative decoding; else 1..ring/2 */
   int32_t in_dtype;      /* RS_F32 | RS_BF16 (GDN g and beta are always float) */
-  int32_t ckpt_dtype;    /* RS_F32 | RS_F16 | RS_FP8E4M3 | RS_NVFP4 (uniform comparator) */
-  int32_t read_copy;     /* RS_NONE | RS_NVFP4 */
-  int32_t fuse_requant;  /* 1: flush and commit-fold rewrite the read copy in their epilogue */
+  int32_t ckpt_dtype;    /* RS_F32 | RS_F16 | RS_FP8E4M3 | RS_NVFP4 (uniform comparator);
+                            Gated DeltaNet and KDA: RS_F32 only */
+  int32_t read_copy;     /* RS_NONE | RS_NVFP4 (replay mode). Gated DeltaNet and KDA:
+                            with an RS_F32 checkpoint; every fold rewrites the copy of the
+                            sequences it folded in a second launch on the same stream
+                            (one tensor scale spans the whole matrix, which the fold
+                            writes in slices), whatever fuse_requant says */
+  int32_t fuse_requant;  /* Mamba-2: 1: flush and commit-fold rewrite the read copy in
+                            their epilogue; 0: the caller calls rs_requant_read_copy */
 } rs_config;
 
 /* Per-sequence buffer counters (32 bytes). */

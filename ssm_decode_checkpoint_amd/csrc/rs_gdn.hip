@@ -24,6 +24,8 @@
 // slice of a (sequence, value head) state in the ReplaySSM steps: dv = 128 is
 // split into two slices of 64 columns (32 KiB of fp32 each), smaller states
 // are one slice; the conventional step takes the whole state.
+#include <type_traits>
+
 #include "rs_device.h"
 #include "rs_tile.h"
 #include "rs_internal.h"
@@ -127,7 +129,56 @@ struct GSlice {
                  reinterpret_cast<float4*>(base + off(st, c0, row)));
     }
   }
+  // the checkpoint slice a step reads
+  __device__ __forceinline__ void issue_read(const GDNArgs& a, size_t st, int c0) {
+    issue(static_cast<const float*>(a.ck.data), st, c0);
+  }
 };
+
+// The same slice read from the NVFP4 read copy (sitech.ge ReplaySSM page,
+// "Bounding quantization error": reads go to a low-precision copy), decoded into
+// the same register layout: a thread's four columns are two bytes of E2M1 codes
+// and its block's E4M3 scale (the block's 16 columns span four threads), times
+// the matrix's tensor scale. The value is e2m1(code) * (e4m3(scale) * tscale),
+// the product rounded as the format defines it.
+template <int NK, int NV, int NVS>
+struct GSliceNv {
+  using TM = TileMap<4, NK, NVS>;
+  uint32_t c[TM::PASSES];   // four codes (two bytes)
+  uint32_t s[TM::PASSES];   // block scale code
+  float ts;
+  __device__ __forceinline__ void issue_read(const GDNArgs& a, size_t st, int c0) {
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* codes = static_cast<const uint8_t*>(a.rc.data);
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      int row = RegTile<4, NK, NVS>::row(k);
+      if constexpr (NK % TM::RPP != 0 || TM::RPP > NK) row = row < NK ? row : NK - 1;
+      const size_t elem = GSlice<NK, NV, NVS>::off(st, c0, row);
+      c[k] = *reinterpret_cast<const uint16_t*>(codes + elem / 2);
+      s[k] = a.rc.nv_scale[elem / 16];
+    }
+    ts = a.rc.tscale[st];
+  }
+  __device__ __forceinline__ void decode(RegTile<4, NK, NVS>& d) const {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const bool in = (NK % TM::RPP == 0 && TM::RPP <= NK) || RegTile<4, NK, NVS>::row(k) < NK;
+      const float sd = e4m3_value(s[k]) * ts;
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 0);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 1);
+      d.v[k][0] = in ? lo.x * sd : 0.0f;
+      d.v[k][1] = in ? lo.y * sd : 0.0f;
+      d.v[k][2] = in ? hi.x * sd : 0.0f;
+      d.v[k][3] = in ? hi.y * sd : 0.0f;
+    }
+  }
+};
+
+// What the non-flush step and the speculative append read: the checkpoint, or
+// its read copy.
+template <bool RC, int NK, int NV, int NVS>
+using ReadSlice = typename std::conditional<RC, GSliceNv<NK, NV, NVS>, GSlice<NK, NV, NVS>>::type;
 
 // Stage the window's entries 0..m-1 (entry m-1 is the current token, the
 // others come from the ring): k rows, the own columns of the held entries' u
@@ -357,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 // non-flush step: o from checkpoint + buffer, append (with its u row), no state write
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV, bool VG>
+template <typename TIN, int NK, int NV, bool VG, bool RC>
 __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
   constexpr int NVS = NV / gdn_slices<NV>();
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
@@ -374,8 +425,8 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
     const int j = len + 1;
     GStage<TIN, NK, NV, NVS, VG> stg;
     stg.load(a, p, nck, j);            // records first, then the state tile
-    GSlice<NK, NV, NVS> raw;
-    raw.issue(static_cast<const float*>(a.ck.data), p.st, p.c0);
+    ReadSlice<RC, NK, NV, NVS> raw;   // the checkpoint slice, or the read copy's
+    raw.issue_read(a, p.st, p.c0);
     arr.arrive(actr, wg, nck, len, nd);
     stg.store(s, j);
     __syncthreads();
@@ -426,10 +477,10 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::NonFlush, 0, nck, len, nd);
 }
 
-template <typename TIN, int NK, int NV, bool VG>
+template <typename TIN, int NK, int NV, bool VG, bool RC>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
-  gdn_nonflush_body<TIN, NK, NV, VG>(a, s);
+  gdn_nonflush_body<TIN, NK, NV, VG, RC>(a, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -517,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void gdn_auto_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
   if (a.meta[p.b].len == kRing - 1) gdn_flush_body<TIN, NK, NV, VG>(a, s);
-  else gdn_nonflush_body<TIN, NK, NV, VG>(a, s);
+  else gdn_nonflush_body<TIN, NK, NV, VG, false>(a, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -660,7 +711,7 @@ __device__ __forceinline__ void tile_matvec_mfma(const RegTile<4, NK, NVS>& S, c
 // matrix-core accumulators, the register budget the VALU dots and matvecs had;
 // otherwise the compiler puts the accumulators in separate registers and
 // occupancy drops.
-template <typename TIN, int NK, int NV, int KQ, bool VG>
+template <typename TIN, int NK, int NV, int KQ, bool VG, bool RC>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu((!VG && KQ <= 4) ? 7 : 1, 8)))
 void gdn_spec_append_kernel(GDNArgs a) {
@@ -724,8 +775,8 @@ void gdn_spec_append_kernel(GDNArgs a) {
     }
     const int dd = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
     const float bv = a.beta[static_cast<size_t>(dd) * gstride + p.st];
-    GSlice<NK, NV, NVS> raw;
-    raw.issue(static_cast<const float*>(a.ck.data), p.st, p.c0);
+    ReadSlice<RC, NK, NV, NVS> raw;   // the checkpoint slice, or the read copy's
+    raw.issue_read(a, p.st, p.c0);
     arr.arrive(actr, wg, nck, len, nd);
     ck.to_lds(&s.K[0][0], NK, n, NK);
     cu.to_lds(&s.U[0][0], NVS, len, NVS);
@@ -932,6 +983,290 @@ void gdn_spec_append_kernel(GDNArgs a) {
     }
   }
   arr.finish(mp, actr, wg, a.nv * NS, MetaOp::Append, K, nck, len, nd);
+}
+
+// ----------------------------------------------------------------------------
+// Folds with a read copy. The non-flush steps and appends solved their rows u
+// from the read copy, so a fold re-solves the rows of its m entries from the
+// fp32 checkpoint before folding (sitech.ge ReplaySSM page, "Bounding
+// quantization error": the read error must not enter the recurrence):
+//   (I + L) U = diag(beta) (V - diag(gamma) K S0^T),  L_{t,i} = beta_t r_{t,i} (k_t . k_i)
+// (KDA: the per-channel decays weight the dots, L_{t,i} = beta_t <k_t, r_{t,i} * k_i>,
+// and the matvec rows, S0 (gamma_t * k_t)). S0 times all the rows in one pass
+// (on the matrix cores for 64-column slices), forward substitution per column,
+// then the fold as in the steps without a copy.
+// ----------------------------------------------------------------------------
+namespace {
+
+template <int NK, int NVS, bool VG>
+struct alignas(16) GRcSmem {
+  alignas(16) float K[kRing][NK];            // k rows of entries 0..m-1 (VG: then times r_{m-1,i})
+  alignas(16) float Wt[VG ? kRing : 1][NK];  // VG: matvec rows gamma_t * k_t
+  alignas(16) float q[NK];                   // flush: q of the current token
+  float U[kRing][NVS];                       // v rows, then the solved rows u (own columns)
+  float out[kRing][NVS];                     // S0 times the matvec rows
+  float red[4 * kRing * NVS];                // matvec scratch
+  float kk[kRing][kRing];                    // L_{t,i}, i < t
+  float al[kRing], bt[kRing], gam[kRing], rr[kRing];
+  alignas(16) float A[VG ? kRing : 1][NK];   // VG: alpha of entry e on channel c
+  float gv[VG ? NK : 1];                     // VG: gamma_{m-1} per channel
+  float s4[4];
+};
+
+// The entries of a fold in registers, then LDS: entries 0..held-1 from the
+// ring, and, with cur, entry held the current token. Own columns of v.
+template <typename TIN, int NK, int NV, int NVS, bool VG>
+struct GRcStage {
+  static constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  static constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
+  static constexpr int CV = (kRing * NVS / VK + kThreads - 1) / kThreads;
+  static constexpr int CQ = (NK / VK + kThreads - 1) / kThreads;
+  static constexpr int CG = VG ? (kRing * NK / 4 + kThreads - 1) / kThreads : 1;
+  RegChunks<TIN, CK> k;
+  RegChunks<TIN, CV> v;
+  RegChunks<TIN, CQ> q;
+  RegChunks<float, CG> gr;
+  float g = 0.0f, beta = 0.0f;
+
+  __device__ __forceinline__ void load(const GDNArgs& a, size_t st, int b, int kh, int c0, long long nck, int held,
+                                       bool cur) {
+    const int m = held + (cur ? 1 : 0);
+    const size_t bk = static_cast<size_t>(b) * a.nqk + kh;
+    const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
+    const TIN* rv = static_cast<const TIN*>(a.rv) + st * kRing * NV + c0;
+    const TIN* ik = static_cast<const TIN*>(a.k) + bk * NK;
+    const TIN* iv = static_cast<const TIN*>(a.v) + st * NV + c0;
+    k.load(EntrySrc<TIN>{rk, ik, 0, nck, held, NK}, m, NK);
+    v.load(EntrySrc<TIN>{rv, iv, 0, nck, held, NV}, m, NVS);
+    const TIN* iq = static_cast<const TIN*>(a.q) + bk * NK;
+    if (cur) q.load(EntrySrc<TIN>{iq, iq, 0, 0, 0, NK}, 1, NK);
+    const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+    if constexpr (VG) {
+      const float* rgv = static_cast<const float*>(a.rg) + st * kRing * NK;
+      gr.load(EntrySrc<float>{rgv, a.g + st * NK, 0, nck, held, NK}, m, NK);
+    } else {
+      g = e < held ? static_cast<const float*>(a.rg)[st * kRing + slot_of(nck, e)] : a.g[st];
+    }
+    beta = e < held ? static_cast<const float*>(a.rbeta)[st * kRing + slot_of(nck, e)] : a.beta[st];
+  }
+  template <typename SM>
+  __device__ __forceinline__ void store(SM& s, int m, bool cur) const {
+    k.to_lds(&s.K[0][0], NK, m, NK);
+    v.to_lds(&s.U[0][0], NVS, m, NVS);
+    if (cur) q.to_lds(s.q, NK, 1, NK);
+    if constexpr (VG) gr.to_lds(&s.A[0][0], NK, m, NK);
+    if (static_cast<int>(threadIdx.x) < m) {
+      if constexpr (!VG) s.al[threadIdx.x] = expf(g);
+      s.bt[threadIdx.x] = beta;
+    }
+  }
+};
+
+// After the staging is visible: gates, the matvec rows and L. Rows past m are
+// zeroed (the matvec takes all 16). Barrier at the end.
+template <int NK, int NVS, bool VG>
+__device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m) {
+  if constexpr (VG) {
+    // alpha per entry and channel, then gamma_t * k_t (direct products in entry order)
+    for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) (&s.A[0][0])[idx] = expf((&s.A[0][0])[idx]);
+    __syncthreads();
+    for (int c = threadIdx.x; c < NK; c += kThreads) {
+      float acc = 1.0f;
+      for (int t = 0; t < m; ++t) {
+        acc *= s.A[t][c];
+        s.Wt[t][c] = acc * s.K[t][c];
+      }
+      s.gv[c] = acc;
+    }
+    for (int idx = m * NK + threadIdx.x; idx < kRing * NK; idx += kThreads) (&s.Wt[0][0])[idx] = 0.0f;
+  } else {
+    if (static_cast<int>(threadIdx.x) < m) {
+      const int t = threadIdx.x;
+      float g = 1.0f, r = 1.0f;
+      for (int l = 0; l < m; ++l) {
+        if (l <= t) g *= s.al[l];
+        if (l > t) r *= s.al[l];
+      }
+      s.gam[t] = g;
+      s.rr[t] = r;   // r_{m-1,t}
+    }
+    for (int idx = m * NK + threadIdx.x; idx < kRing * NK; idx += kThreads) (&s.K[0][0])[idx] = 0.0f;
+  }
+  // L_{t,i} for i < t < m, one pair per 16-lane group
+  const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
+  const int npairs = m * (m - 1) / 2;
+  for (int pr = grp; pr < npairs; pr += kThreads / 16) {
+    int t = 1, i = pr;
+    while (i >= t) {   // uniform over the group
+      i -= t;
+      ++t;
+    }
+    float part = 0.0f;
+    if constexpr (VG) {
+      for (int c = ln; c < NK; c += 16) {
+        float r = 1.0f;
+        for (int l = i + 1; l <= t; ++l) r *= s.A[l][c];
+        part += s.K[t][c] * (r * s.K[i][c]);
+      }
+    } else {
+      part = lds_dot16<NK>(&s.K[t][0], &s.K[i][0], ln);
+    }
+    part = group_sum16(part);
+    if (ln == 0) {
+      float r = 1.0f;
+      if constexpr (!VG)
+        for (int l = i + 1; l <= t; ++l) r *= s.al[l];
+      s.kk[t][i] = s.bt[t] * r * part;
+    }
+  }
+  __syncthreads();
+}
+
+// S0 times the matvec rows, the forward substitution per own column, and the
+// fold into S. Barriers inside; all threads call.
+template <int NK, int NVS, bool VG>
+__device__ __forceinline__ void rc_solve_and_fold(RegTile<4, NK, NVS>& S, GRcSmem<NK, NVS, VG>& s, int m) {
+  const float* W = VG ? &s.Wt[0][0] : &s.K[0][0];
+  if constexpr (NVS == 64) tile_matvec_mfma<kRing>(S, W, NK, s.red, &s.out[0][0]);
+  else tile_matvec<kRing>(S, W, NK, s.red, &s.out[0][0]);
+  for (int v = threadIdx.x; v < NVS; v += kThreads) {
+    float ur[kRing];
+#pragma unroll
+    for (int t = 0; t < kRing; ++t) {
+      if (t < m) {
+        float u = VG ? s.bt[t] * (s.U[t][v] - s.out[t][v]) : s.bt[t] * (s.U[t][v] - s.gam[t] * s.out[t][v]);
+#pragma unroll
+        for (int i = 0; i < t; ++i) u -= s.kk[t][i] * ur[i];
+        ur[t] = u;
+        s.U[t][v] = VG ? u : u * s.rr[t];   // fold columns: r_{m-1,t} u_t (VG: the decay goes on k)
+      }
+    }
+  }
+  if constexpr (VG) {
+    // fold rows r_{m-1,i} * k_i (descending direct products)
+    for (int c = threadIdx.x; c < NK; c += kThreads) {
+      float acc = 1.0f;
+      for (int i = m - 1; i >= 0; --i) {
+        s.K[i][c] *= acc;
+        acc *= s.A[i][c];
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (VG) {
+    tile_scale_rows(S, s.gv);
+    tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  } else {
+    tile_rank_update(S, s.gam[m - 1], &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  }
+}
+
+}  // namespace
+
+// flush step with a read copy: the rows of the len held entries and the
+// current token re-solved from the checkpoint, the fold, one write, o = S q
+// (the read copy is refreshed by the requant that follows)
+template <typename TIN, int NK, int NV, bool VG>
+__device__ __forceinline__ void gdn_flush_rc_body(const GDNArgs& a, GRcSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
+  constexpr int NVS = NV / gdn_slices<NV>();
+  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+  rs_meta* mp = a.meta + p.b;
+  const int wg = p.h * gdn_slices<NV>() + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * gdn_slices<NV>()) * kArriveStride;
+  const int len = mp->len, nd = mp->nd;
+  const long long nck = mp->n_ckpt;
+  const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
+  const int m = len + 1;
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, wg, nck, len, nd);
+  } else {
+    float* ck = static_cast<float*>(a.ck.data);
+    GRcStage<TIN, NK, NV, NVS, VG> stg;
+    stg.load(a, p.st, p.b, p.kh, p.c0, nck, len, true);   // records first, then the state tile
+    GSlice<NK, NV, NVS> raw;
+    raw.issue(ck, p.st, p.c0);
+    arr.arrive(actr, wg, nck, len, nd);
+    stg.store(s, m, true);
+    __syncthreads();
+    rc_gates_and_gram(s, m);
+    RegTile<4, NK, NVS> S;
+    raw.decode(S);
+    rc_solve_and_fold(S, s, m);
+    GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
+    tile_matvec<1>(S, s.q, NK, s.red, &s.out[0][0]);   // o = S_m q (barriers inside)
+    for (int v = threadIdx.x; v < NVS; v += kThreads) a.o[p.st * NV + p.c0 + v] = s.out[0][v];
+  }
+  arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
+}
+
+template <typename TIN, int NK, int NV, bool VG>
+__global__ __launch_bounds__(kThreads) void gdn_flush_rc_kernel(GDNArgs a) {
+  __shared__ GRcSmem<NK, NV / gdn_slices<NV>(), VG> s;
+  gdn_flush_rc_body<TIN, NK, NV, VG>(a, s);
+}
+
+template <int NK, int NV, bool VG>
+union GAutoRcSmem {
+  GSmem<NK, NV / gdn_slices<NV>(), VG> nf;
+  GRcSmem<NK, NV / gdn_slices<NV>(), VG> fl;
+};
+
+template <typename TIN, int NK, int NV, bool VG>
+__global__ __launch_bounds__(kThreads) void gdn_auto_rc_kernel(GDNArgs a) {
+  __shared__ GAutoRcSmem<NK, NV, VG> s;
+  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+  if (a.meta[p.b].len == kRing - 1) gdn_flush_rc_body<TIN, NK, NV, VG>(a, s.fl);
+  else gdn_nonflush_body<TIN, NK, NV, VG, true>(a, s.nf);
+}
+
+// speculative commit with a read copy, fold part: as gdn_commit_fold_kernel,
+// with the rows of the m committed entries re-solved from the checkpoint
+template <typename TIN, int NK, int NV, bool VG>
+__global__ __launch_bounds__(kThreads) void gdn_commit_fold_rc_kernel(GDNArgs a) {
+  constexpr int NS = gdn_slices<NV>();
+  constexpr int NVS = NV / NS;
+  __shared__ GRcSmem<NK, NVS, VG> s;
+  const int per = a.nv * NS;
+  const int total = *a.work_count * per;
+  float* ckp = static_cast<float*>(a.ck.data);
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    const FoldItem it = a.work[item / per];
+    const int r = item - (item / per) * per;
+    const int h = r / NS, half = r - h * NS, c0 = half * NVS, m = it.m;
+    const size_t st = static_cast<size_t>(it.b) * a.nv + h;
+    GRcStage<TIN, NK, NV, NVS, VG> stg;
+    stg.load(a, st, it.b, h / a.vpk, c0, it.nck, m, false);
+    GSlice<NK, NV, NVS> raw;
+    raw.issue(ckp, st, c0);
+    stg.store(s, m, false);
+    __syncthreads();
+    rc_gates_and_gram(s, m);
+    RegTile<4, NK, NVS> S;
+    raw.decode(S);
+    rc_solve_and_fold(S, s, m);
+    GSlice<NK, NV, NVS>::store(ckp, st, c0, S);
+    __syncthreads();
+  }
+}
+
+// The NVFP4 read copy of whole states from the fp32 checkpoint, one workgroup
+// per state: every state, or (folded) those of sequences whose buffer is empty
+// and holds no drafts. Bytes identical to the Mamba-2 quantizer's for the same
+// matrix (same tile layout and encoder).
+template <int NK, int NV>
+__global__ __launch_bounds__(kThreads) void gdn_requant_kernel(GDNArgs a, int folded) {
+  __shared__ float s4[4];
+  const int mat = xcd_tile(blockIdx.x, gridDim.x);
+  if (folded) {
+    const rs_meta* mp = a.meta + mat / a.nv;
+    if (mp->len != 0 || mp->nd != 0) return;   // uniform over the workgroup
+  }
+  RawTile<FMT_F32, 8, NK, NV> raw;
+  raw.issue(a.ck, mat);
+  RegTile<8, NK, NV> H;
+  raw.decode(H);
+  tile_store<FMT_NVFP4>(a.rc, mat, H, s4);
 }
 
 // ----------------------------------------------------------------------------
@@ -1143,31 +1478,41 @@ __global__ __launch_bounds__(kThreads) void gdn_restore_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int NK, int NV, bool VG>
+template <int NK, int NV, bool VG, bool RC>
 struct gdn_step_kernels {
   static void conv(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
     if (bf) gdn_conv_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     else gdn_conv_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
   }
   static void nonflush(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
-    if (bf) gdn_nonflush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
-    else gdn_nonflush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    if (bf) gdn_nonflush_kernel<bf16, NK, NV, VG, RC><<<grid, kThreads, 0, st>>>(a);
+    else gdn_nonflush_kernel<float, NK, NV, VG, RC><<<grid, kThreads, 0, st>>>(a);
   }
   static void flush(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
-    if (bf) gdn_flush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
-    else gdn_flush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    if constexpr (RC) {
+      if (bf) gdn_flush_rc_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+      else gdn_flush_rc_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    } else {
+      if (bf) gdn_flush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+      else gdn_flush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    }
   }
   static void auto_step(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
-    if (bf) gdn_auto_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
-    else gdn_auto_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    if constexpr (RC) {
+      if (bf) gdn_auto_rc_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+      else gdn_auto_rc_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    } else {
+      if (bf) gdn_auto_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+      else gdn_auto_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    }
   }
 };
 
-template <typename TIN, int NK, int NV, bool VG>
+template <typename TIN, int NK, int NV, bool VG, bool RC>
 void gdn_spec_append(const GDNArgs& a, int grid, hipStream_t st) {
-  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2, VG><<<grid, kThreads, 0, st>>>(a);
-  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4, VG><<<grid, kThreads, 0, st>>>(a);
-  else gdn_spec_append_kernel<TIN, NK, NV, 8, VG><<<grid, kThreads, 0, st>>>(a);
+  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2, VG, RC><<<grid, kThreads, 0, st>>>(a);
+  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4, VG, RC><<<grid, kThreads, 0, st>>>(a);
+  else gdn_spec_append_kernel<TIN, NK, NV, 8, VG, RC><<<grid, kThreads, 0, st>>>(a);
 }
 
 template <typename TIN, int NK, int NV, bool VG>
@@ -1177,59 +1522,57 @@ void gdn_conv_spec(const GDNArgs& a, int grid, hipStream_t st) {
   else gdn_conv_spec_kernel<TIN, NK, NV, 8, VG><<<grid, kThreads, 0, st>>>(a);
 }
 
-template <int NK, int NV, bool VG>
+template <int NK, int NV, bool VG, bool RC>
 void gdn_spec_kernels(GDNOp op, bool bf, const GDNArgs& a, int grid, hipStream_t st) {
   if (op == GDNOp::SpecAppend) {
-    if (bf) gdn_spec_append<bf16, NK, NV, VG>(a, grid, st);
-    else gdn_spec_append<float, NK, NV, VG>(a, grid, st);
+    if (bf) gdn_spec_append<bf16, NK, NV, VG, RC>(a, grid, st);
+    else gdn_spec_append<float, NK, NV, VG, RC>(a, grid, st);
   } else if (op == GDNOp::ConvSpec) {
     if (bf) gdn_conv_spec<bf16, NK, NV, VG>(a, grid, st);
     else gdn_conv_spec<float, NK, NV, VG>(a, grid, st);
+  } else if constexpr (RC) {
+    if (bf) gdn_commit_fold_rc_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    else gdn_commit_fold_rc_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
   } else {
     if (bf) gdn_commit_fold_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     else gdn_commit_fold_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
   }
 }
 
+template <int NK, int NV, bool VG, bool RC>
+void gdn_launch_kind(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
+  const bool bf = l.in_bf16;
+  using Steps = gdn_step_kernels<NK, NV, VG, RC>;
+  switch (op) {
+    case GDNOp::Conv: Steps::conv(bf, a, l.grid, st); break;
+    case GDNOp::NonFlush: Steps::nonflush(bf, a, l.grid, st); break;
+    case GDNOp::Flush: Steps::flush(bf, a, l.grid, st); break;
+    case GDNOp::Auto: Steps::auto_step(bf, a, l.grid, st); break;
+    case GDNOp::SpecAppend:
+    case GDNOp::ConvSpec: gdn_spec_kernels<NK, NV, VG, RC>(op, bf, a, l.grid, st); break;
+    case GDNOp::CommitFold: {
+      const int items = l.grid * gdn_slices<NV>();   // upper bound of listed work items
+      gdn_spec_kernels<NK, NV, VG, RC>(op, bf, a, items < 2048 ? items : 2048, st);
+      break;
+    }
+    case GDNOp::Restore: gdn_restore_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a); break;
+    case GDNOp::Requant: gdn_requant_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a, 0); break;
+    case GDNOp::RequantFolded: gdn_requant_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a, 1); break;
+  }
+}
+
 template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
-  const bool bf = l.in_bf16;
   // replay steps and appends: one workgroup per column slice of each state
   if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
       op == GDNOp::ConvSpec)
     l.grid *= gdn_slices<NV>();
-  switch (op) {
-    case GDNOp::Conv:
-      if (l.vg) gdn_step_kernels<NK, NV, true>::conv(bf, a, l.grid, st);
-      else gdn_step_kernels<NK, NV, false>::conv(bf, a, l.grid, st);
-      break;
-    case GDNOp::NonFlush:
-      if (l.vg) gdn_step_kernels<NK, NV, true>::nonflush(bf, a, l.grid, st);
-      else gdn_step_kernels<NK, NV, false>::nonflush(bf, a, l.grid, st);
-      break;
-    case GDNOp::Flush:
-      if (l.vg) gdn_step_kernels<NK, NV, true>::flush(bf, a, l.grid, st);
-      else gdn_step_kernels<NK, NV, false>::flush(bf, a, l.grid, st);
-      break;
-    case GDNOp::Auto:
-      if (l.vg) gdn_step_kernels<NK, NV, true>::auto_step(bf, a, l.grid, st);
-      else gdn_step_kernels<NK, NV, false>::auto_step(bf, a, l.grid, st);
-      break;
-    case GDNOp::SpecAppend:
-    case GDNOp::ConvSpec:
-      if (l.vg) gdn_spec_kernels<NK, NV, true>(op, bf, a, l.grid, st);
-      else gdn_spec_kernels<NK, NV, false>(op, bf, a, l.grid, st);
-      break;
-    case GDNOp::CommitFold: {
-      const int items = l.grid * gdn_slices<NV>();   // upper bound of listed work items
-      const int grid = items < 2048 ? items : 2048;
-      if (l.vg) gdn_spec_kernels<NK, NV, true>(op, bf, a, grid, st);
-      else gdn_spec_kernels<NK, NV, false>(op, bf, a, grid, st);
-      break;
-    }
-    case GDNOp::Restore:
-      gdn_restore_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a);
-      break;
+  if (l.vg) {
+    if (l.rc) gdn_launch_kind<NK, NV, true, true>(op, a, l, st);
+    else gdn_launch_kind<NK, NV, true, false>(op, a, l, st);
+  } else {
+    if (l.rc) gdn_launch_kind<NK, NV, false, true>(op, a, l, st);
+    else gdn_launch_kind<NK, NV, false, false>(op, a, l, st);
   }
 }
 

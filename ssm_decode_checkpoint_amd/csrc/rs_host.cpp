@@ -164,6 +164,7 @@ GDNArgs gdn_args(const rs_layer* L, const rs_buffers* buf) {
   a.vpk = c.n_v_heads / c.n_qk_heads;
   a.kmax = c.max_draft;
   a.ck = StateBuf{buf->ckpt, nullptr, nullptr};
+  if (c.read_copy == RS_NVFP4) a.rc = rc_buf(L, buf->read_copy);
   if (c.mode == RS_REPLAY) {
     char* r = static_cast<char*>(buf->ring);
     a.rq = r + L->ring_q_off;
@@ -205,6 +206,10 @@ rs_status gdn_common(const rs_layer* L, const rs_buffers* buf, const rs_inputs* 
   for (const void* p : ps)
     if (!aligned16(p)) return RS_E_ALIGN;
   if (c.mode == RS_REPLAY && (!aligned16(buf->ring) || !aligned16(buf->meta))) return RS_E_ALIGN;
+  if (c.read_copy == RS_NVFP4) {
+    if (!buf->read_copy) return RS_E_ARG;
+    if (!aligned16(buf->read_copy)) return RS_E_ALIGN;
+  }
   *a = gdn_args(L, buf);
   a->q = in->q;
   a->k = in->k;
@@ -222,8 +227,18 @@ GDNLaunch gdn_launch_cfg(const rs_layer* L) {
   l.dv = c.head_v_dim;
   l.in_bf16 = c.in_dtype == RS_BF16;
   l.vg = c.kind == RS_KDA;
+  l.rc = c.read_copy == RS_NVFP4;
   l.grid = c.batch * c.n_v_heads;
   return l;
+}
+
+// With a read copy, a launch that may fold (flush, self-scheduling step,
+// commit) is followed by the requant of the states it folded.
+rs_status gdn_refresh_copy(const rs_layer* L, const GDNArgs& a, void* st) {
+  if (L->cfg.read_copy != RS_NVFP4) return RS_OK;
+  if (rs_status s = launch_status()) return s;
+  gdn_launch(GDNOp::RequantFolded, a, gdn_launch_cfg(L), st);
+  return RS_OK;
 }
 
 }  // namespace
@@ -275,7 +290,8 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
     if (c.n_v_heads % c.n_qk_heads != 0) return RS_E_ARG;
     if (static_cast<uint64_t>(c.batch) * c.n_v_heads > (1u << 30)) return RS_E_ARG;
     if (!gdn_shape_supported(c.head_k_dim, c.head_v_dim)) return RS_E_UNSUPPORTED;
-    if (c.ckpt_dtype != RS_F32 || c.read_copy != RS_NONE) return RS_E_DTYPE;
+    if (c.ckpt_dtype != RS_F32) return RS_E_DTYPE;
+    if (!replay && c.read_copy != RS_NONE) return RS_E_DTYPE;
     L.heads = c.n_v_heads;
     L.in_heads = c.n_qk_heads;
     L.rows = c.head_k_dim;
@@ -357,6 +373,8 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(kind == StepKind::Flush ? GDNOp::Flush : kind == StepKind::Auto ? GDNOp::Auto : GDNOp::NonFlush, a,
                gdn_launch_cfg(L), st);
+    if (kind != StepKind::NonFlush)
+      if (rs_status s = gdn_refresh_copy(L, a, st)) return s;
     return launched();
   }
   M2Args a;
@@ -600,6 +618,8 @@ static rs_status spec_commit(const rs_layer* L, const rs_buffers* buf, const int
     if (L->cfg.mode == RS_REPLAY && (!buf->ring || !buf->meta)) return RS_E_ARG;
     if (!aligned16(buf->ckpt)) return RS_E_ALIGN;
     if (L->cfg.mode == RS_REPLAY && (!aligned16(buf->ring) || !aligned16(buf->meta))) return RS_E_ALIGN;
+    if (L->cfg.read_copy == RS_NVFP4 && !buf->read_copy) return RS_E_ARG;
+    if (L->cfg.read_copy == RS_NVFP4 && !aligned16(buf->read_copy)) return RS_E_ALIGN;
   } else if (!prm || !prm->A || !prm->D) {
     return RS_E_ARG;
   }
@@ -624,6 +644,7 @@ static rs_status spec_commit(const rs_layer* L, const rs_buffers* buf, const int
       commit_meta(ca, st);
       if (rs_status s = launch_status()) return s;
       gdn_launch(GDNOp::CommitFold, a, l, st);
+      if (rs_status s = gdn_refresh_copy(L, a, st)) return s;
     }
     return launched();
   }
@@ -664,9 +685,19 @@ rs_status rs_spec_commit_static(const rs_layer* L, const rs_buffers* buf, const 
 
 rs_status rs_requant_read_copy(const rs_layer* L, const rs_buffers* buf, void* stream) {
   if (rs_status s = check_layer(L)) return s;
-  if (L->cfg.read_copy != RS_NVFP4 || L->cfg.kind != RS_MAMBA2) return RS_E_MODE;
+  if (L->cfg.read_copy != RS_NVFP4) return RS_E_MODE;
   if (!buf || !buf->ckpt || !buf->read_copy) return RS_E_ARG;
   if (!aligned16(buf->ckpt) || !aligned16(buf->read_copy)) return RS_E_ALIGN;
+  if (L->cfg.kind != RS_MAMBA2) {
+    GDNArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.batch = L->cfg.batch;
+    a.nv = L->cfg.n_v_heads;
+    a.ck = StateBuf{buf->ckpt, nullptr, nullptr};
+    a.rc = rc_buf(L, buf->read_copy);
+    gdn_launch(GDNOp::Requant, a, gdn_launch_cfg(L), stream);
+    return launched();
+  }
   M2Args a;
   std::memset(&a, 0, sizeof(a));
   a.ck = ck_buf(L, buf->ckpt);

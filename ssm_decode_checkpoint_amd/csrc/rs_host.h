@@ -147,14 +147,20 @@ struct GDNArgs {
   const void *q, *k, *v;     // one token, or K drafts stacked [K][batch][...]
   const float *g, *beta;
   float* o;                  // [batch][nv][dv], or [K][batch][nv][dv]
+  StateBuf rc;               // NVFP4 read copy of the checkpoint (when configured)
 };
 
-enum class GDNOp { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore };
+// Requant: the read copy of every state from the checkpoint. RequantFolded:
+// the states of sequences whose buffer is empty and holds no drafts, i.e.
+// those a flush or commit has just folded (an unchanged state requantizes to
+// the same bytes, so the others it also takes cost only time).
+enum class GDNOp { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore, Requant, RequantFolded };
 
 struct GDNLaunch {
   int dk, dv;
   bool in_bf16;
   bool vg;        // Kimi Delta Attention: per-key-channel gate
+  bool rc;        // NVFP4 read copy: reads go to it, folds re-solve from the checkpoint
   int grid;
 };
 

@@ -252,6 +252,38 @@ int main(void) {
     SNAP(b8); expect_call(rs_step_nonflush(&G, &gb, &nb, NULL, y, NULL), RS_E_ARG, NULL, b8, "missing beta");
   }
 
+  /* ---- Gated DeltaNet and KDA with the NVFP4 read copy: a launch that can
+   * fold is followed by the copy's requant ---- */
+  {
+    const int GD2[STUB_KINDS] = {0, 2, 0, 0, 0, 0, 0, 0};
+    const int GDC2[STUB_KINDS] = {0, 2, 1, 0, 0, 0, 0, 0};
+    for (int kind = RS_GDN; kind <= RS_KDA; ++kind) {
+      rs_config cg = delta_cfg(kind, RS_REPLAY);
+      cg.read_copy = RS_NVFP4;
+      rs_layer G;
+      expect(rs_init(&cg, &G) == RS_OK, "delta-rule layer with a read copy");
+      expect(G.read_copy_bytes >= 4ull * 4 * (128 * 128 / 2 + 128 * 128 / 16 + 4), "delta-rule read copy bytes");
+      rs_buffers gb = {dev(70), dev(71), dev(72), dev(73), NULL};
+      rs_inputs gi;
+      memset(&gi, 0, sizeof gi);
+      gi.q = dev(74); gi.k = dev(75); gi.v = dev(76); gi.g = dev(77); gi.beta = dev(78);
+      SNAP(b); expect_call(rs_step_nonflush(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD, b, "non-flush reads the copy");
+      SNAP(b2); expect_call(rs_step_flush(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD2, b2, "flush, then requant");
+      SNAP(b3); expect_call(rs_step(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD2, b3, "self-scheduling step, then requant");
+      SNAP(b4); expect_call(rs_spec_append(&G, &gb, &gi, 4, NULL, y, NULL), RS_OK, GD, b4, "append reads the copy");
+      SNAP(b5); expect_call(rs_spec_commit(&G, &gb, acc, NULL, NULL), RS_OK, GDC2, b5, "commit, fold, requant");
+      SNAP(b6); expect_call(rs_requant_read_copy(&G, &gb, NULL), RS_OK, GD, b6, "delta-rule requant");
+      rs_buffers nb = gb;
+      nb.read_copy = NULL;
+      SNAP(b7); expect_call(rs_step_nonflush(&G, &nb, &gi, NULL, y, NULL), RS_E_ARG, NULL, b7, "missing read copy");
+      SNAP(b8); expect_call(rs_spec_commit(&G, &nb, acc, NULL, NULL), RS_E_ARG, NULL, b8, "commit without read copy");
+      rs_config cc = delta_cfg(kind, RS_CONVENTIONAL);
+      cc.read_copy = RS_NVFP4;
+      rs_layer X;
+      expect(rs_init(&cc, &X) == RS_E_DTYPE, "read copy refused in conventional mode");
+    }
+  }
+
   /* ---- rs_init refusals ---- */
   {
     rs_config bad = m2_cfg(RS_REPLAY);

@@ -48,7 +48,15 @@ void m2_launch(M2Op op, const M2Args& a, const M2Launch& l, void*) {
 }
 
 void gdn_launch(GDNOp op, const GDNArgs& a, const GDNLaunch& l, void*) {
-  require(l.grid > 0 && a.batch > 0 && a.nv > 0 && a.vpk * a.nqk == a.nv, "gdn launch shape");
+  require(l.grid > 0 && a.batch > 0 && a.nv > 0, "gdn launch shape");
+  if (op == GDNOp::Requant || op == GDNOp::RequantFolded) {   // the quantizer reads the states only
+    require(l.rc && a.ck.data && a.rc.data && a.rc.nv_scale && a.rc.tscale, "gdn requant buffers");
+    if (op == GDNOp::RequantFolded) require(a.meta != nullptr, "gdn requant counters");
+    g_calls[1] += 1;
+    return;
+  }
+  require(a.vpk * a.nqk == a.nv, "gdn head map");
+  if (l.rc) require(a.rc.data && a.rc.nv_scale && a.rc.tscale, "gdn read copy");
   if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
       op == GDNOp::CommitFold)
     require(a.meta && a.arrive && a.rq && a.rk && a.rv && a.rg && a.rbeta && a.ru, "gdn replay buffers");
