@@ -55,8 +55,8 @@ POOL_MAX = 16            # worker processes of the CPU oracle leg (the host's CP
 METRIC = "SSM-layer decode tokens/s at batch 256 + achieved HBM GB/s (% of peak) vs conventional"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["ssm_decode_checkpoint_amd/csrc/rs_mamba2_kernels.h", "ssm_decode_checkpoint_amd/csrc/rs_tile.h",
-                  "ssm_decode_checkpoint_amd/csrc/rs_device.h", "ssm_decode_checkpoint_amd/csrc/rs_internal.h",
-                  "ssm_decode_checkpoint_amd/build.py"]
+                  "ssm_decode_checkpoint_amd/csrc/rs_mtile.h", "ssm_decode_checkpoint_amd/csrc/rs_device.h",
+                  "ssm_decode_checkpoint_amd/csrc/rs_internal.h", "ssm_decode_checkpoint_amd/build.py"]
 
 
 def kernel_source_hash() -> str:
@@ -106,7 +106,16 @@ def gdn_bytes(w: W.GDNWorkload):
     nonflush = {j: S + (j - 1) * E_old + 2 * E_in + Urow + O for j in range(1, RING)}
     flush = 2 * S + (RING - 1) * E_old + E_in + O
     conv = 2 * S + E_in + O
-    return {"state": S, "E_in": E_in, "E_old": E_old, "O": O, "nonflush": nonflush, "flush": flush, "conv": conv}
+    # with the NVFP4 read copy: non-flush steps read the copy (4.5 bits per element and a
+    # tensor scale); the flush re-solves the held entries' rows from the fp32 checkpoint
+    # (re-reading their k, v, g and beta instead of u), folds, writes, and the requant
+    # that follows reads the new checkpoint and writes the copy
+    S_rc = w.n_v * w.dv * w.dk * (0.5 + 1 / 16) + w.n_v * 4
+    E_old_rc = w.n_qk * w.dk * s_in + w.n_v * w.dv * s_in + w.n_v * gw * 4 + w.n_v * 4
+    nonflush_rc = {j: S_rc + (j - 1) * E_old + 2 * E_in + Urow + O for j in range(1, RING)}
+    flush_rc = 2 * S + (RING - 1) * E_old_rc + E_in + O + S + S_rc
+    return {"state": S, "E_in": E_in, "E_old": E_old, "O": O, "nonflush": nonflush, "flush": flush, "conv": conv,
+            "state_rc": S_rc, "nonflush_rc": nonflush_rc, "flush_rc": flush_rc}
 
 
 # ---------------------------------------------------------------------------
@@ -584,18 +593,22 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
     gp = W.gdn_params(w)
     kda_layer = w.gate == "channel"
 
-    def mk(mode):
+    def mk(mode, rc=False):
         cfg = rs.make_config(rs.RS_KDA if kda_layer else rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk,
-                             n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv, in_dtype=rs.RS_BF16)
+                             n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv, in_dtype=rs.RS_BF16,
+                             read_copy=rs.RS_NVFP4 if rc else rs.RS_NONE)
         _, layer = rs.rs_init(cfg)
         return layer, rs.alloc_buffers(layer, dev)
 
     rl, rb = mk(rs.RS_REPLAY)
     cl, cb = mk(rs.RS_CONVENTIONAL)
+    ql, qb = mk(rs.RS_REPLAY, rc=True)
     ck = rs.ckpt_f32_view(rl, rb)
     for b in range(B):
         ck[b].copy_(torch.from_numpy(np.ascontiguousarray(W.gdn_init_state(w, b).transpose(0, 2, 1))).to(dev))
     rs.ckpt_f32_view(cl, cb).copy_(ck)
+    rs.ckpt_f32_view(ql, qb).copy_(ck)
+    rs.rs_requant_read_copy(ql, qb)
     pool = []
     for t in range(RING):
         tk = W.gdn_step(w, t, range(B), gp)
@@ -615,9 +628,15 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
         for t in range(RING):
             _marked(ev, t, tm.stream, lambda: rs.rs_step_conventional(cl, cb, pool[t], None, None, o))
 
+    def rc_window(ev):
+        for t in range(RING):
+            fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
+            _marked(ev, t, tm.stream, lambda: fn(ql, qb, pool[t], None, None, o))
+
     K, warm = args.steps, args.warmup
     total_r, per_r = tm.run(replay_window, K, warm, RING)
     total_c, per_c = tm.run(conv_window, K, warm, RING)
+    total_q, per_q = tm.run(rc_window, K, warm, RING)
     byt = gdn_bytes(w)
     ntok = B * RING * K
     nf_ms = per_r[:, : RING - 1]
@@ -628,6 +647,18 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
     win_bytes = nf_bytes + byt["flush"] * B
     value = ntok / (total_r * 1e-3)
     conv_value = ntok / (total_c * 1e-3)
+    q_nf = per_q[:, : RING - 1]
+    q_nf_bytes = sum(byt["nonflush_rc"][j] for j in range(1, RING)) * B
+    q_win_bytes = q_nf_bytes + byt["flush_rc"] * B
+    q_fl = float(per_q[:, RING - 1].mean())
+    q_value = ntok / (total_q * 1e-3)
+    read_copy = {"tokens_per_s": q_value, "window_ms": total_q / K, "window_alg_bytes": q_win_bytes,
+                 "window_gbs": q_win_bytes / (total_q / K * 1e-3) / 1e9, "nonflush_avg_ms": float(q_nf.mean()),
+                 "nonflush_gbs": q_nf_bytes / (q_nf.sum(axis=1).mean() * 1e-3) / 1e9,
+                 "flush_and_requant_ms": q_fl, "flush_and_requant_gbs": byt["flush_rc"] * B / (q_fl * 1e-3) / 1e9,
+                 "speedup_vs_fp32_replay": q_value / value, "speedup_vs_conventional": q_value / conv_value,
+                 "bytes_ratio_conventional_over_read_copy": byt["conv"] * B * RING / q_win_bytes,
+                 "note": "fp32 checkpoint, NVFP4 read copy; the flush call is the re-solving fold and the requant"}
     return {
         "metric": ("KDA" if kda_layer else "GDN") + "-layer decode tokens/s at batch 256 + achieved HBM GB/s vs conventional",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm, "ms_per_step": total_r / K,
@@ -645,6 +676,7 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
                          "gbs": byt["conv"] * B / (cv_ms * 1e-3) / 1e9},
         "speedup_vs_conventional": value / conv_value,
         "bytes_ratio_conventional_over_replay": byt["conv"] * B * RING / win_bytes,
+        "read_copy": read_copy,
     }
 
 
@@ -878,6 +910,54 @@ def lowprec_error(args, torch, rs):
             "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
 
 
+def delta_readcopy_error(args, torch, rs, w):
+    """Relative L2 error of o vs the fp64 recurrence over length for a delta-rule
+    layer (Qwen-style shapes, a few sequences, every head), with an fp32
+    checkpoint, with and without the NVFP4 read copy (sitech.ge ReplaySSM page,
+    "Bounding quantization error": 4-bit reads over a full-precision recurrence)."""
+    from oracle import decode, gdn, kda
+    nb, steps = args.delta_error_seqs, args.delta_error_steps
+    w = w.with_(batch=nb)
+    dev = "cuda"
+    gp = W.gdn_params(w)
+    S0 = W.gdn_init_states(w, range(nb))
+    kind = rs.RS_KDA if w.gate == "channel" else rs.RS_GDN
+    layers = {}
+    for name, rc in (("f32", rs.RS_NONE), ("f32+nvfp4_reads", rs.RS_NVFP4)):
+        cfg = rs.make_config(kind, nb, n_qk_heads=w.n_qk, n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv,
+                             in_dtype=rs.RS_BF16, read_copy=rc)
+        _, layer = rs.rs_init(cfg)
+        bufs = rs.alloc_buffers(layer, dev)
+        rs.ckpt_f32_view(layer, bufs).copy_(torch.from_numpy(np.ascontiguousarray(
+            S0.transpose(0, 1, 3, 2)).astype(np.float32)).to(dev))
+        if rc:
+            rs.rs_requant_read_copy(layer, bufs)
+        layers[name] = (layer, bufs)
+    exact = decode.GDNConventional(S0, rule=kda if w.gate == "channel" else gdn)
+    o = torch.empty(nb, w.n_v, w.dv, dtype=torch.float32, device=dev)
+    every = max(1, steps // 16)
+    curve = {k: [] for k in layers}
+    acc = {k: [0.0, 0.0] for k in layers}
+    for t in range(steps):
+        tk = W.gdn_step(w, t, range(nb), gp)
+        d = {k: _bf16_dev(torch, tk[k], dev) for k in ("q", "k", "v")}
+        d["g"] = torch.from_numpy(tk["g"]).to(dev)
+        d["beta"] = torch.from_numpy(tk["beta"]).to(dev)
+        oe = exact.step(tk)
+        for name, (layer, bufs) in layers.items():
+            fn = rs.rs_step_flush if t % RING == RING - 1 else rs.rs_step_nonflush
+            fn(layer, bufs, d, None, None, o)
+            og = o.cpu().numpy().astype(np.float64)
+            acc[name][0] += float(np.sum((og - oe) ** 2))
+            acc[name][1] += float(np.sum(oe ** 2))
+        if (t + 1) % every == 0:
+            for name in layers:
+                curve[name].append([t + 1, (acc[name][0] / acc[name][1]) ** 0.5])
+                acc[name] = [0.0, 0.0]
+            print(f"{w.name} read-copy error: step {t + 1} of {steps}", file=sys.stderr, flush=True)
+    return {"workload": w.name, "sequences": nb, "steps": steps, "bucket_steps": every, "rel_l2_by_bucket": curve}
+
+
 def probe_read_gbs(torch, tm, nbytes=1 << 30, threads=256, per=8, steps=10, warmup=2, write_bytes=0):
     """Bandwidth of a plain stream of the decode kernels' 32 KiB tiles over
     nbytes of device memory (librs_probe.so): read only (rs_probe_read), or
@@ -911,6 +991,29 @@ def probe_read_gbs(torch, tm, nbytes=1 << 30, threads=256, per=8, steps=10, warm
     return (nbytes + tiles * write_bytes) / (float(per_ms.mean()) * 1e-3) / 1e9
 
 
+PROBE_VARIANTS = ("reg_256x8_nt", "reg_256x8_plain", "reg_256x16_nt", "lds_256x8", "lds_256x16",
+                  "persistent_256x8_pairs")
+
+
+def probe_variant_gbs(torch, tm, nbytes, variant, steps=10, warmup=2):
+    """Read bandwidth of one rs_probe_read_variant scheme over nbytes."""
+    import ctypes
+    probe = ctypes.CDLL(os.path.join(ROOT, "ssm_decode_checkpoint_amd", "librs_probe.so"))
+    probe.rs_probe_read_variant.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int32,
+                                            ctypes.c_void_p]
+    probe.rs_probe_read_variant.restype = ctypes.c_int32
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    out = torch.empty(nbytes // (32 << 10), dtype=torch.float32, device="cuda")
+
+    def call():
+        st = probe.rs_probe_read_variant(src.data_ptr(), out.data_ptr(), nbytes, variant, tm.stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"librs_probe returned {st}")
+
+    _, per_ms = tm.run(lambda ev: _marked(ev, 0, tm.stream, call), steps, warmup, 1)
+    return nbytes / (float(per_ms.mean()) * 1e-3) / 1e9
+
+
 def m2_writes_per_tile(w, s_in=2):
     """Bytes a Mamba-2 non-flush step writes per (sequence, head) tile: y in
     fp32, the appended x row and dt, and the head's share of the group's B and
@@ -941,6 +1044,11 @@ def bench_copy(args, torch, rs):
     for threads, per in ((256, 8), (256, 4), (128, 16)):
         tiles[f"{threads}x{per}"] = {"tile_kib": threads * per * 16 // 1024,
                                      "gbs": probe_read_gbs(torch, tm, n, threads, per, args.steps, args.warmup)}
+    # other ways to stream the same bytes (rs_probe_read_variant): larger tiles,
+    # global-to-LDS loads, persistent workgroups, cached loads
+    variants = {}
+    for v, name in enumerate(PROBE_VARIANTS):
+        variants[name] = probe_variant_gbs(torch, tm, n, v, args.steps, args.warmup)
     # the 32 KiB tile stream with a write per tile after its sum, as a decode step
     # writes its output and appended record: what those writes cost in a read stream
     writes = {}
@@ -953,7 +1061,8 @@ def bench_copy(args, torch, rs):
                                "gbs": n / (rms * 1e-3) / 1e9},
             "read_probe": {"what": "1 GiB read as tiles of threads x 16-byte non-temporal loads per workgroup "
                                    "(rs_probe_read); 256x8 is the decode kernels' 32 KiB state tile",
-                           "tiles": tiles},
+                           "tiles": tiles,
+                           "variants_gbs": variants},
             "read_write_probe": {"what": "the 256x8 tile read with write_bytes written per tile after its sum "
                                          "(rs_probe_read_write); GB/s of bytes read plus written",
                                  "gbs_by_write_bytes": writes}}
@@ -973,6 +1082,9 @@ def main():
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
     ap.add_argument("--lowprec-error-seqs", type=int, default=2)
     ap.add_argument("--lowprec-batch", type=int, default=0, help="batch of the low-precision workload (0: 64)")
+    ap.add_argument("--delta-error-steps", type=int, default=0,
+                    help="gdn / kda: error over length with and without the NVFP4 read copy")
+    ap.add_argument("--delta-error-seqs", type=int, default=2)
     ap.add_argument("--lowprec-slow-decay", action="store_true",
                     help="error run with slowly decaying heads (outside the C5 configuration)")
     args = ap.parse_args()
@@ -995,6 +1107,9 @@ def main():
                                                          W.KDA_B256.with_(name="kda_spec_b256", max_draft=4)),
               "copy": bench_copy}[wl]
         out = fn(args, torch, rs)
+        if wl in ("gdn", "kda") and args.delta_error_steps:
+            out["read_copy_error_over_length"] = delta_readcopy_error(args, torch, rs,
+                                                                      W.GDN_QWEN if wl == "gdn" else W.KDA_B256)
         if wl == "mamba2":
             out["cpu_baseline"] = cpu
         print(json.dumps(out), flush=True)

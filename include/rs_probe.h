@@ -34,6 +34,29 @@ int32_t rs_probe_read(const void* src, float* out, uint64_t bytes, int32_t threa
 int32_t rs_probe_read_write(const void* src, void* dst, uint64_t bytes, int32_t threads, int32_t per_thread,
                             int32_t write_bytes, void* stream);
 
+/* Variants of the read stream, for how far a tile stream can go on this chip
+ * beyond the decode kernels' own scheme. Each reads `bytes` (a positive
+ * multiple of its tile) at `src` (16-byte aligned) and writes one float per
+ * tile to out[tile] (device float[bytes / tile bytes], caller-owned):
+ *   RS_PROBE_REG_256X8        32 KiB tiles into registers, non-temporal loads
+ *                             (the same stream as rs_probe_read at 256 x 8);
+ *   RS_PROBE_PLAIN_256X8      the same with ordinary (cached) loads;
+ *   RS_PROBE_REG_256X16       64 KiB tiles into registers;
+ *   RS_PROBE_LDS_256X8        32 KiB tiles by 16-byte global-to-LDS loads;
+ *   RS_PROBE_LDS_256X16       64 KiB tiles by 16-byte global-to-LDS loads;
+ *   RS_PROBE_PERSISTENT_256X8 persistent workgroups, as many as fit on the
+ *                             device at once, each looping over pairs of
+ *                             32 KiB tiles with both tiles of a pair in flight
+ *                             (bytes must be a multiple of 64 KiB).
+ * Returns as rs_probe_read (-4: unknown variant). Asynchronous. */
+#define RS_PROBE_REG_256X8 0
+#define RS_PROBE_PLAIN_256X8 1
+#define RS_PROBE_REG_256X16 2
+#define RS_PROBE_LDS_256X8 3
+#define RS_PROBE_LDS_256X16 4
+#define RS_PROBE_PERSISTENT_256X8 5
+int32_t rs_probe_read_variant(const void* src, float* out, uint64_t bytes, int32_t variant, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

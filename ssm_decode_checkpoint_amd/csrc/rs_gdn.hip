@@ -592,8 +592,6 @@ struct alignas(16) GSpecSmem {
   alignas(16) float K[KROWS][NK];
   alignas(16) float W[2 * KQ][NK];         // matvec weights k_d, q_d per draft (zero past K)
   float U[kRing][NVS];         // u rows, own columns (held from the ring, drafts solved here)
-  float V[KQ][NVS];            // v of the drafts, own columns
-  float out[2 * KQ][NVS];      // S0 k_d, S0 q_d
   float kk[KQ][kRing];         // beta_d r_{e,i} (k_e . k_i) for i < e = len + d
   float kq[KQ][kRing];         // r_{e,i} (k_i . q_d) for i <= e
   float rt[KQ][kRing];         // r_{e,i} for i <= e
@@ -602,9 +600,21 @@ struct alignas(16) GSpecSmem {
   float bet[KQ];
   // VG (per-channel decays, e = len + d): WS = k_e * P_d and q_d * P_d with
   // P_d = prod_{len<=l<=e} alpha_l; DW[d(d-1)/2 + j] = prod_{len+j<l<=e} alpha_l
-  // (the decay between draft j and draft d > j)
-  alignas(16) float WS[VG ? 2 * KQ : 1][NK];
-  alignas(16) float DW[VG && KQ > 1 ? KQ * (KQ - 1) / 2 : 1][NK];
+  // (the decay between draft j and draft d > j). They live only while the dots
+  // are taken; the drafts' v rows and the matvec outputs are written after
+  // that (with VG the v rows wait in registers), so the two share space.
+  struct Dots {
+    alignas(16) float WS[VG ? 2 * KQ : 1][NK];
+    alignas(16) float DW[VG && KQ > 1 ? KQ * (KQ - 1) / 2 : 1][NK];
+  };
+  struct Mv {
+    float V[KQ][NVS];          // v of the drafts, own columns
+    float out[2 * KQ][NVS];    // S0 k_d, S0 q_d
+  };
+  union {
+    Dots dots;
+    Mv mv;
+  };
 };
 
 // The dots of a speculative round on the matrix cores, for bf16 records (their
@@ -783,7 +793,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
     cd.to_lds(&s.W[0][0], 2 * NK, K, NK);
     cq.to_lds(&s.W[1][0], 2 * NK, K, NK);
     for (int idx = 2 * K * NK + threadIdx.x; idx < 2 * KQ * NK; idx += kThreads) (&s.W[0][0])[idx] = 0.0f;
-    cv.to_lds(&s.V[0][0], NVS, K, NVS);
+    if constexpr (!VG) cv.to_lds(&s.mv.V[0][0], NVS, K, NVS);
     if constexpr (!VG)
       if (static_cast<int>(threadIdx.x) < n) s.al[threadIdx.x] = expf(gv);
     if (static_cast<int>(threadIdx.x) < K) s.bet[threadIdx.x] = bv;
@@ -814,12 +824,12 @@ void gdn_spec_append_kernel(GDNArgs a) {
         float pd = 1.0f;
         for (int d = 0; d < K; ++d) {
           pd *= lg[len + d];                      // len + d < 16; wave-uniform index
-          s.WS[2 * d][c] = s.W[2 * d][c] * pd;
-          s.WS[2 * d + 1][c] = s.W[2 * d + 1][c] * pd;
+          s.dots.WS[2 * d][c] = s.W[2 * d][c] * pd;
+          s.dots.WS[2 * d + 1][c] = s.W[2 * d + 1][c] * pd;
           float q = 1.0f;
           for (int j = d - 1; j >= 0; --j) {
             q *= lg[len + j + 1];
-            s.DW[d * (d - 1) / 2 + j][c] = q;
+            s.dots.DW[d * (d - 1) / 2 + j][c] = q;
           }
         }
       }
@@ -840,13 +850,13 @@ void gdn_spec_append_kernel(GDNArgs a) {
         if (r < 2 * len) {                        // held entry i: k row already scaled by Rh_i
           isq = r >= len;
           i = isq ? r - len : r;
-          part = lds_dot16<NK>(&s.K[i][0], &s.WS[2 * d + (isq ? 1 : 0)][0], ln);
+          part = lds_dot16<NK>(&s.K[i][0], &s.dots.WS[2 * d + (isq ? 1 : 0)][0], ln);
         } else {                                  // earlier draft j (kk: j < d; kq: j <= d)
           const int t = r - 2 * len;
           isq = t >= d;
           const int j = isq ? t - d : t;
           i = len + j;
-          const float* w = j < d ? &s.DW[d * (d - 1) / 2 + j][0] : nullptr;
+          const float* w = j < d ? &s.dots.DW[d * (d - 1) / 2 + j][0] : nullptr;
           part = lds_dot16<NK>(&s.K[i][0], isq ? &s.W[2 * d + 1][0] : &s.K[ee][0], ln, w);
         }
         part = group_sum16(part);
@@ -859,8 +869,8 @@ void gdn_spec_append_kernel(GDNArgs a) {
       // matvec weights gamma_e * k_e and gamma_e * q_d (owners: their channel)
       if (static_cast<int>(threadIdx.x) < NK) {
         for (int d = 0; d < K; ++d) {
-          s.W[2 * d][threadIdx.x] = s.WS[2 * d][threadIdx.x] * gam_c;
-          s.W[2 * d + 1][threadIdx.x] = s.WS[2 * d + 1][threadIdx.x] * gam_c;
+          s.W[2 * d][threadIdx.x] = s.dots.WS[2 * d][threadIdx.x] * gam_c;
+          s.W[2 * d + 1][threadIdx.x] = s.dots.WS[2 * d + 1][threadIdx.x] * gam_c;
         }
       }
     } else {
@@ -903,6 +913,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
     float* HU = red;                 // [KQ][NVS], after the matvecs
     float* HO = red + KQ * NVS;      // [KQ][NVS]
     __syncthreads();                 // dots done: the k rows become scratch
+    if constexpr (VG) cv.to_lds(&s.mv.V[0][0], NVS, K, NVS);   // over WS (the matvec's barriers publish it)
     RegTile<4, NK, NVS> S;
     raw.decode(S);
     // S0 [k_d, q_d]: all 2 KQ weight rows in one pass on the matrix cores where the
@@ -912,10 +923,10 @@ void gdn_spec_append_kernel(GDNArgs a) {
     // half the scratch of one 2KQ-row pass). Barriers inside publish the dots.
     constexpr bool kMfmaMv = !VG && NVS == 64 && 4 * 2 * KQ * NVS <= GSpecSmem<NK, NVS, KQ, VG>::KROWS * NK;
     if constexpr (kMfmaMv) {
-      tile_matvec_mfma<2 * KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);
+      tile_matvec_mfma<2 * KQ>(S, &s.W[0][0], NK, red, &s.mv.out[0][0]);
     } else {
-      tile_matvec<KQ>(S, &s.W[0][0], NK, red, &s.out[0][0]);
-      if (2 * K > KQ) tile_matvec<KQ>(S, &s.W[KQ][0], NK, red, &s.out[KQ][0]);
+      tile_matvec<KQ>(S, &s.W[0][0], NK, red, &s.mv.out[0][0]);
+      if (2 * K > KQ) tile_matvec<KQ>(S, &s.W[KQ][0], NK, red, &s.mv.out[KQ][0]);
     }
     // every (draft, column) pair at once: the parts of the draft's row and output
     // that do not involve other drafts (checkpoint and held entries)
@@ -928,8 +939,8 @@ void gdn_spec_append_kernel(GDNArgs a) {
         hu += s.kk[d][i] * ui;
         ho += s.kq[d][i] * ui;
       }
-      HU[d * NVS + v] = s.bet[d] * (s.V[d][v] - s.gam[d] * s.out[2 * d][v]) - hu;
-      HO[d * NVS + v] = s.gam[d] * s.out[2 * d + 1][v] + ho;
+      HU[d * NVS + v] = s.bet[d] * (s.mv.V[d][v] - s.gam[d] * s.mv.out[2 * d][v]) - hu;
+      HO[d * NVS + v] = s.gam[d] * s.mv.out[2 * d + 1][v] + ho;
     }
     __syncthreads();
     // the drafts' rows in order (each depends on the drafts before it), one
@@ -1092,31 +1103,47 @@ __device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m
     }
     for (int idx = m * NK + threadIdx.x; idx < kRing * NK; idx += kThreads) (&s.K[0][0])[idx] = 0.0f;
   }
-  // L_{t,i} for i < t < m, one pair per 16-lane group
   const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
-  const int npairs = m * (m - 1) / 2;
-  for (int pr = grp; pr < npairs; pr += kThreads / 16) {
-    int t = 1, i = pr;
-    while (i >= t) {   // uniform over the group
-      i -= t;
-      ++t;
-    }
-    float part = 0.0f;
-    if constexpr (VG) {
-      for (int c = ln; c < NK; c += 16) {
-        float r = 1.0f;
-        for (int l = i + 1; l <= t; ++l) r *= s.A[l][c];
-        part += s.K[t][c] * (r * s.K[i][c]);
+  if constexpr (VG) {
+    // L_{t,i} for i < t < m, one row t per 16-lane group: walking i down from
+    // t - 1, each lane keeps the decays r_{t,i} = prod_{i<l<=t} alpha_l of its
+    // channels ln + 16 j as running products (one multiply per pair and channel)
+    static_assert(NK % 16 == 0, "16 lanes over the key channels");
+    constexpr int CPL = NK / 16;
+    for (int t = grp; t < m; t += kThreads / 16) {
+      float kt[CPL], r[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        kt[j] = s.K[t][ln + 16 * j];
+        r[j] = 1.0f;
       }
-    } else {
-      part = lds_dot16<NK>(&s.K[t][0], &s.K[i][0], ln);
+      for (int i = t - 1; i >= 0; --i) {
+        float part = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          r[j] *= s.A[i + 1][ln + 16 * j];
+          part += kt[j] * (r[j] * s.K[i][ln + 16 * j]);
+        }
+        part = group_sum16(part);
+        if (ln == 0) s.kk[t][i] = s.bt[t] * part;
+      }
     }
-    part = group_sum16(part);
-    if (ln == 0) {
-      float r = 1.0f;
-      if constexpr (!VG)
+  } else {
+    // L_{t,i} for i < t < m, one pair per 16-lane group
+    const int npairs = m * (m - 1) / 2;
+    for (int pr = grp; pr < npairs; pr += kThreads / 16) {
+      int t = 1, i = pr;
+      while (i >= t) {   // uniform over the group
+        i -= t;
+        ++t;
+      }
+      float part = lds_dot16<NK>(&s.K[t][0], &s.K[i][0], ln);
+      part = group_sum16(part);
+      if (ln == 0) {
+        float r = 1.0f;
         for (int l = i + 1; l <= t; ++l) r *= s.al[l];
-      s.kk[t][i] = s.bt[t] * r * part;
+        s.kk[t][i] = s.bt[t] * r * part;
+      }
     }
   }
   __syncthreads();

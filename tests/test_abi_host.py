@@ -35,7 +35,7 @@ def test_probe_library_exports_and_checks_arguments():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     hdr = open(os.path.join(root, "include", "rs_probe.h")).read()
     names = re.findall(r"^\s*int32_t\s+(rs_\w+)\s*\(", hdr, re.M)
-    assert names == ["rs_probe_read", "rs_probe_read_write"]
+    assert names == ["rs_probe_read", "rs_probe_read_write", "rs_probe_read_variant"]
     lib = C.CDLL(os.path.join(root, "ssm_decode_checkpoint_amd", "librs_probe.so"))
     f = lib.rs_probe_read
     f.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_int32, C.c_void_p]
@@ -55,6 +55,14 @@ def test_probe_library_exports_and_checks_arguments():
         assert g(p, p, 1 << 20, 256, 8, wb, None) == -5, wb
     assert g(p, p, 1 << 20, 128, 16, 128 * 16 + 16, None) == -5
     assert g(p, p, 1 << 20, 64, 8, 256, None) == -4
+    v = lib.rs_probe_read_variant
+    v.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_void_p]
+    v.restype = C.c_int32
+    assert v(None, p, 1 << 20, 0, None) == -1 and v(C.c_void_p(0x10004), p, 1 << 20, 0, None) == -1
+    assert v(p, p, 1 << 20, -1, None) == -4 and v(p, p, 1 << 20, 6, None) == -4
+    assert v(p, p, 32 << 10, 2, None) == -2 and v(p, p, 32 << 10, 4, None) == -2   # 64 KiB tiles
+    assert v(p, p, 32 << 10, 5, None) == -2 and v(p, p, 96 << 10, 5, None) == -2   # whole tile pairs
+    assert v(p, p, 0, 0, None) == -2
 
 
 def test_struct_sizes_match_header():

@@ -70,3 +70,26 @@ def test_read_write_stores_wave_sums(wbytes):
         exp = wave[:, lane // 64]
         for i in range(4):
             np.testing.assert_allclose(got[:, lane, i], exp, rtol=1e-4, atol=1e-3)
+
+
+# variant -> (threads, 16-byte loads per thread) of its tile
+VARIANTS = {0: (256, 8), 1: (256, 8), 2: (256, 16), 3: (256, 8), 4: (256, 16), 5: (256, 8)}
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_read_variants_sum_every_tile(variant):
+    """Each variant of rs_probe_read_variant reads every byte once per tile and
+    writes the tile's sum. The persistent variant runs enough tile pairs (6000
+    tiles) that every workgroup loops several times on this chip."""
+    lib = _lib()
+    lib.rs_probe_read_variant.argtypes = [C.c_void_p, C.c_void_p, C.c_uint64, C.c_int32, C.c_void_p]
+    lib.rs_probe_read_variant.restype = C.c_int32
+    threads, per = VARIANTS[variant]
+    tiles = 6000 if variant == 5 else 12
+    host, src = _src(tiles, threads, per)
+    out = torch.full((tiles,), float("nan"), dtype=torch.float32, device=DEV)
+    print(f"probe variant {variant}: {tiles} tiles of {threads * per * 16} bytes", flush=True)
+    assert lib.rs_probe_read_variant(src.data_ptr(), out.data_ptr(), src.numel() * 4, variant, _stream()) == 0
+    torch.cuda.synchronize()
+    ref = host.astype(np.float64).reshape(tiles, -1).sum(axis=1)
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-4, atol=1e-3)

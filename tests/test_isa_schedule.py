@@ -10,6 +10,11 @@ tile, and the workgroup barrier after the staging then holds every wave until
 the tile has arrived. Here: between the first non-temporal load and the first
 s_barrier of each step kernel there is no `s_waitcnt vmcnt(0)`.
 
+The exception, by measurement: the Mamba-2 flushes that fold on the matrix
+cores (FP8 and NVFP4 checkpoints, FP16 with the read copy, on 64-multiple
+shapes) issue the checkpoint tile before the counters and records, so their
+first barrier does wait for it; that is checked too.
+
 Also pinned: the occupancy the dominant kernels were tuned for (8 waves per
 SIMD for the fp32-read non-flush and flush kernels, 6 for the wave-per-head
 kernel on FP8 and NVFP4 reads), from the compiler's resource-usage remarks.
@@ -88,9 +93,18 @@ def _first_barrier_waits_all(lines):
     return any(re.search(r"s_waitcnt vmcnt\(0\)", lines[i]) for i in range(loads[0], bars[0]))
 
 
+def _tile_first(name):
+    """Mamba-2 flush (or self-scheduling) kernels whose fold runs on the matrix cores."""
+    m = re.search(r"m2_(?:flush|auto)_kernelI(?:NS_4bf16E|f)Li(\d)ELb([01])ELi(\d+)ELi(\d+)E", name)
+    if not m:
+        return False
+    ckf, rc, nr, nc = (int(x) for x in m.groups())
+    return nr % 64 == 0 and nc % 64 == 0 and (ckf in (2, 3) or (ckf == 1 and rc == 1))
+
+
 def test_records_stay_ahead_of_the_state_tile(isa):
     kernels, _ = isa
-    checked, bad = 0, []
+    checked, bad, first = 0, [], 0
     for name, lines in kernels.items():
         if not any(k in name for k in STEP_KERNELS):
             continue
@@ -98,9 +112,16 @@ def test_records_stay_ahead_of_the_state_tile(isa):
         if r is None:
             continue
         checked += 1
-        if r:
+        if _tile_first(name) and "m2_flush_kernel" in name:
+            first += 1
+            if not r:
+                bad.append(("tile not first", name))
+        elif _tile_first(name):
+            continue   # the self-scheduling kernel holds both orders behind its branch
+        elif r:
             bad.append(name)
     assert checked >= 40, checked
+    assert first == 10, first   # ({fp8, NVFP4} x {copy, none} + fp16 with the copy) x {bf16, fp32 inputs}
     assert not bad, bad
 
 
