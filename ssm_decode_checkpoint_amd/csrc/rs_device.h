@@ -89,6 +89,7 @@ __device__ __forceinline__ void nt_store(uint2 v, uint2* p) {
   __builtin_nontemporal_store(w, reinterpret_cast<vu2*>(p));
 }
 __device__ __forceinline__ void nt_store(uint32_t v, uint32_t* p) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void nt_store(float v, float* p) { __builtin_nontemporal_store(v, p); }
 
 // ----------------------------------------------------------------------------
 // stored-state access
@@ -184,6 +185,38 @@ __device__ __forceinline__ void decode_chunk(const Raw<FMT, E>& r, float ms, flo
   }
 }
 
+// The chunk's element values before the per-chunk and per-matrix scales (FP8:
+// the E4M3 values; NVFP4: the E2M1 values; FP16: the values), and the
+// per-chunk scale (NVFP4: the E4M3 block scale; otherwise 1). A reduction
+// that weights every element of a chunk by the same factor folds the chunk
+// scale into that factor and the matrix scale into its result.
+template <int FMT>
+__device__ __forceinline__ void decode_codes8(const Raw<FMT, 8>& r, float* v) {
+  static_assert(FMT == FMT_F16 || FMT == FMT_FP8 || FMT == FMT_NVFP4, "low-precision chunks");
+  if constexpr (FMT == FMT_F16) {
+    decode_chunk<FMT_F16, 8>(r, 1.0f, v);
+  } else if constexpr (FMT == FMT_FP8) {
+    const uint32_t w[2] = {r.v.x, r.v.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[h], 1.0f, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[h], 1.0f, true);
+      v[4 * h + 0] = lo.x; v[4 * h + 1] = lo.y; v[4 * h + 2] = hi.x; v[4 * h + 3] = hi.y;
+    }
+  } else {
+    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 0);
+    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 1);
+    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 2);
+    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r.v, 1.0f, 3);
+    v[0] = p0.x; v[1] = p0.y; v[2] = p1.x; v[3] = p1.y; v[4] = p2.x; v[5] = p2.y; v[6] = p3.x; v[7] = p3.y;
+  }
+}
+template <int FMT>
+__device__ __forceinline__ float chunk_scale(const Raw<FMT, 8>& r) {
+  if constexpr (FMT == FMT_NVFP4) return e4m3_value(r.s);
+  return 1.0f;
+}
+
 // ----------------------------------------------------------------------------
 // wavefront helpers
 // ----------------------------------------------------------------------------
@@ -253,6 +286,59 @@ __device__ __forceinline__ float lds_dot16(const float* a, const float* b, int l
     for (int n = ln; n < N; n += 16) part += (w ? a[n] * w[n] : a[n]) * b[n];
   }
   return part;
+}
+
+// Transposing sum over the 8 lanes that share (lane mod 8): each lane brings
+// 8 values, and after three exchange-and-add stages (lane bit 5 through the
+// half swap, bit 4 through the row-pair swap, bit 3 through a row rotation by
+// 8) each lane holds the 8-lane sum of one of them, whose index (0..7) goes to
+// `which`; every index is held by exactly one lane of the 8. 7 exchanges and 7
+// adds instead of 3 per value. The index is tracked through the same
+// exchanges, so it does not depend on which half of a swap moves.
+__device__ __forceinline__ float transpose_sum8(const float (&v)[8], int& which) {
+  const bool hi3 = (threadIdx.x & 8) != 0;
+  float a[4];
+  int ia = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+    a[i] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  {
+    const auto q = __builtin_amdgcn_permlane32_swap(0u, 4u, false, false);
+    ia = static_cast<int>(q[0]);   // 0 or 4: the column offset this lane now holds
+  }
+  float b[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[i]), __float_as_uint(a[i + 2]), false, false);
+    b[i] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+  }
+  {
+    const auto q = __builtin_amdgcn_permlane16_swap(0u, 2u, false, false);
+    ia += static_cast<int>(q[0]);
+  }
+  const float keep = hi3 ? b[1] : b[0], send = hi3 ? b[0] : b[1];
+  which = ia + (hi3 ? 1 : 0);
+  return keep + dpp_mov<kDppRor8>(send);
+}
+
+// Suffix products inside each aligned group of 16 lanes (a DPP row): lane l
+// gets the product of v over the lanes l .. 15 of its row, by four row shifts
+// toward lane 0 (row_shl; a lane whose source would lie past the row's end
+// reads 1). Every lane of the row must hold a value.
+__device__ __forceinline__ float row_suffix_prod16(float v) {
+  const int one = __float_as_int(1.0f);
+  v *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(v), 0x101, 0xF, 0xF, false));
+  v *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(v), 0x102, 0xF, 0xF, false));
+  v *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(v), 0x104, 0xF, 0xF, false));
+  v *= __int_as_float(__builtin_amdgcn_update_dpp(one, __float_as_int(v), 0x108, 0xF, 0xF, false));
+  return v;
+}
+
+// v of lane l + 1 of the same 16-lane row, 1 for the row's last lane.
+__device__ __forceinline__ float row_next16(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(v), 0x101, 0xF, 0xF, false));
 }
 
 // Sum over each aligned group of 16 lanes (a DPP row), in every lane of it.

@@ -143,7 +143,7 @@ struct alignas(16) M2NfSmem {
   float X[kRing][NC];
   float C[NR];
   float dt[kRing];
-  float a[kRing];
+  float a[kRing];            // prod_{i<l<j} exp(dt_l A): the decay from entry i to the current one
   float w[kRing];            // w_{j,i} dt_i (B_i . C_j)
   float L;
   float red[4 * NC];
@@ -199,9 +199,19 @@ __device__ __forceinline__ void m2_nonflush_body(const M2Args& a, M2NfSmem<NR, N
   cb.to_lds(&s.B[0][0], NR, j, NR);
   cx.to_lds(&s.X[0][0], NC, j, NC);
   cc.to_lds(s.C, NR, 1, NR);
-  if (static_cast<int>(threadIdx.x) < j) {
-    s.dt[threadIdx.x] = dtv;
-    s.a[threadIdx.x] = expf(dtv * Ah);
+  {
+    // decays: thread e < 16 holds a_e = exp(dt_e A) (1 past the window); the
+    // suffix products over its 16-lane row give the weights' decay
+    // prod_{e<l<j} a_l and the checkpoint's L = prod_{l<j} a_l
+    const int e = static_cast<int>(threadIdx.x);
+    const float ae = e < j ? expf(dtv * Ah) : 1.0f;
+    const float suf = row_suffix_prod16(ae);
+    const float after = row_next16(suf);
+    if (e < j) {
+      s.dt[e] = dtv;
+      s.a[e] = after;
+    }
+    if (e == 0) s.L = suf;
   }
   __syncthreads();
   {
@@ -209,16 +219,7 @@ __device__ __forceinline__ void m2_nonflush_body(const M2Args& a, M2NfSmem<NR, N
     for (int e = grp; e < j; e += kThreads / 16) {
       float part = lds_dot16<NR>(&s.B[e][0], s.C, ln);
       part = group_sum16(part);
-      if (ln == 0) {
-        float w = 1.0f;
-        for (int l = e + 1; l < j; ++l) w *= s.a[l];
-        s.w[e] = w * s.dt[e] * part;
-      }
-    }
-    if (threadIdx.x == 0) {
-      float L = 1.0f;
-      for (int l = 0; l < j; ++l) L *= s.a[l];
-      s.L = L;
+      if (ln == 0) s.w[e] = s.a[e] * s.dt[e] * part;
     }
   }
   __syncthreads();
@@ -269,11 +270,13 @@ struct alignas(16) M2WaveSmem {
   float B[kRing][NR];
   float C[NR];
   float bc[kRing];            // B_e . C_cur
-  float dt[kHPB][kRing];
-  float a[kHPB][kRing];       // exp(dt A) per head and entry
   float w[kHPB][kRing];       // w_{j,e} dt_e (B_e . C_cur) per head
   float L[kHPB];
-  uint8_t scl[kHPB][NR * NC / 16];   // NVFP4 reads: each head's block scales
+  // NVFP4 reads: each head's block scales, in the order the reduction reads
+  // them: the scale of row 8 k + r, column block c at ((r (NC/16) + c) NR/8 + k),
+  // so that a lane's scales (one row residue r and one block c, every k) are
+  // one contiguous run
+  alignas(16) uint8_t scl[kHPB][NR * NC / 16];
 };
 
 // FP8 and NVFP4 reads with bf16 records fit in 80 registers, which gives 6
@@ -379,13 +382,15 @@ void m2_nonflush_wave_kernel(M2Args a) {
   cb.to_lds(&s.B[0][0], NR, j, NR);
   cc.to_lds(s.C, NR, 1, NR);
   if constexpr (RDF == FMT_NVFP4) {
-    if constexpr (SPL == 8) *reinterpret_cast<uint2*>(&s.scl[wave][lane * 8]) = scv;
-    else *reinterpret_cast<uint32_t*>(&s.scl[wave][lane * 4]) = scv.x;
-  }
-  if (threadIdx.x < kHPB * 16) {
-    const int hw = threadIdx.x >> 4, e = threadIdx.x & 15;
-    s.dt[hw][e] = dtv;
-    s.a[hw][e] = expf(dtv * Av);
+    // lane's scale bytes i: row (SPL lane + i) / (NC/16), block (SPL lane + i) mod (NC/16)
+    constexpr int NB = NC / 16;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) {
+      const int idx = lane * SPL + i, row = idx / NB, blk = idx - row * NB;
+      const uint32_t word = i < 4 ? scv.x : scv.y;
+      s.scl[wave][((row & (RPP - 1)) * NB + blk) * PASSES + row / RPP] =
+          static_cast<uint8_t>(word >> (8 * (i & 3)));
+    }
   }
   __syncthreads();
   {
@@ -396,35 +401,54 @@ void m2_nonflush_wave_kernel(M2Args a) {
       if (ln == 0) s.bc[grp] = part;
     }
   }
+  // decays in registers: thread 16 hw + e holds a_e = exp(dt_e A) of head hw
+  // (1 past the window); the row's suffix products give the weights'
+  // decay prod_{e<l<j} a_l and the checkpoint's L = prod_{l<j} a_l
+  const int e_of = threadIdx.x & 15;
+  const float ae = threadIdx.x < kHPB * 16 && e_of < j ? expf(dtv * Av) : 1.0f;
+  const float suf = row_suffix_prod16(ae);
+  const float after = row_next16(suf);
   __syncthreads();
   if (threadIdx.x < kHPB * 16) {
-    const int hw = threadIdx.x >> 4, e = threadIdx.x & 15;
-    if (e < j) {
-      float wv = 1.0f;
-      for (int l = e + 1; l < j; ++l) wv *= s.a[hw][l];
-      s.w[hw][e] = wv * s.dt[hw][e] * s.bc[e];
-    }
-    if (e == 0) {
-      float L = 1.0f;
-      for (int l = 0; l < j; ++l) L *= s.a[hw][l];
-      s.L[hw] = L;
-    }
+    const int hw = threadIdx.x >> 4;
+    if (e_of < j) s.w[hw][e_of] = after * dtv * s.bc[e_of];
+    if (e_of == 0) s.L[hw] = suf;
   }
   __syncthreads();
-  // 4. this head's output inside its wavefront
+  // 4. this head's output inside its wavefront; a chunk's elements share one
+  //    row weight C_n, so its block scale joins that weight and the matrix
+  //    scale joins L (one multiply per chunk instead of one per element)
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  // NVFP4: this lane's PASSES block scales as one LDS read, decoded two per
+  // conversion (exactly, as E4M3 values) as the passes reach them
+  static_assert(RDF != FMT_NVFP4 || PASSES % 4 == 0, "whole words of scale bytes");
+  uint32_t sw[RDF == FMT_NVFP4 ? PASSES / 4 : 1];
+  if constexpr (RDF == FMT_NVFP4) {
+    const uint8_t* sp = &s.scl[wave][((lane >> 3) * (NC / 16) + (ce >> 1)) * PASSES];
+    if constexpr (PASSES == 16) {
+      const uint4 q = *reinterpret_cast<const uint4*>(sp);
+      sw[0] = q.x; sw[1] = q.y; sw[2] = q.z; sw[3] = q.w;
+    } else {
+#pragma unroll
+      for (int m = 0; m < PASSES / 4; ++m) sw[m] = reinterpret_cast<const uint32_t*>(sp)[m];
+    }
+  }
+  f32x2 bpair = {1.0f, 1.0f};
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
     float t[8];
-    if constexpr (RDF == FMT_NVFP4) raw[k].s = s.scl[wave][(k * RPP + (lane >> 3)) * (NC / 16) + (ce >> 1)];
-    decode_chunk<RDF, 8>(raw[k], ms, t);
-    const float cr = s.C[k * RPP + (lane >> 3)];
+    decode_codes8<RDF>(raw[k], t);
+    if constexpr (RDF == FMT_NVFP4) {
+      if (k % 4 == 0) bpair = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[k / 4], 1.0f, false);   // bytes 0, 1
+      if (k % 4 == 2) bpair = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[k / 4], 1.0f, true);    // bytes 2, 3
+    }
+    const float cr = (k % 2 == 0 ? bpair.x : bpair.y) * s.C[k * RPP + (lane >> 3)];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += t[i] * cr;
   }
-  const float L = s.L[wave];
+  const float L = s.L[wave] * ms;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] *= L;
 #pragma unroll
@@ -432,20 +456,18 @@ void m2_nonflush_wave_kernel(M2Args a) {
     const int e = q == 0 ? e0 : e1;
     float xv[8];
 #pragma unroll
-    for (int c = 0; c < XCH; ++c) unpack16(xr[q][c], static_cast<const TIN*>(nullptr), xv + c * V);
+    for (int c = 0; c < XCH; ++c) {
+      // entries past the window contribute 0 (their rows, copies of the last entry's, are cleared)
+      const uint4 xw = e < j ? xr[q][c] : make_uint4(0u, 0u, 0u, 0u);
+      unpack16(xw, static_cast<const TIN*>(nullptr), xv + c * V);
+    }
     const float we = e < j ? s.w[wave][e] + (e == j - 1 ? Dh : 0.0f) : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += e < j ? we * xv[i] : 0.0f;
+    for (int i = 0; i < 8; ++i) acc[i] += we * xv[i];
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    acc[i] = wave_sum_stride<8>(acc[i]);
-  }
-  if (lane < 8) {
-    float4* yp = reinterpret_cast<float4*>(a.y + mat * NC + lane * 8);
-    nt_store(make_float4(acc[0], acc[1], acc[2], acc[3]), yp);
-    nt_store(make_float4(acc[4], acc[5], acc[6], acc[7]), yp + 1);
-  }
+  int col;
+  const float yv = transpose_sum8(acc, col);
+  nt_store(yv, a.y + mat * NC + ce * 8 + col);
   // 5. append the current record (bit copies)
   const int slot = static_cast<int>((nck + len) & (kRing - 1));
   if (lane < NC / V) reinterpret_cast<uint4*>(rX + slot * NC)[lane] = reinterpret_cast<const uint4*>(inX)[lane];

@@ -166,7 +166,10 @@ def _run(w, layer, bufs, A, D, steps, t0=0):
 # bf16 inputs; 128 x 64 heads two to a group (the workgroup-per-head kernel)
 READ_SHAPES = [dict(), dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64),
                dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64, in_dtype="bf16"),
-               dict(batch=3, nheads=6, ngroups=3, dstate=128, headdim=64)]
+               dict(batch=3, nheads=6, ngroups=3, dstate=128, headdim=64),
+               # bf16 records with 8 or more heads per group: two heads per wavefront on FP8 / NVFP4 reads
+               dict(batch=3, nheads=16, ngroups=1, dstate=128, headdim=64, in_dtype="bf16"),
+               dict(batch=2, nheads=16, ngroups=2, dstate=128, headdim=64, in_dtype="bf16")]
 
 
 @pytest.mark.parametrize("shape", READ_SHAPES)

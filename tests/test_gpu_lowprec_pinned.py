@@ -29,7 +29,10 @@ CODE = {"f32": rs.RS_F32, "f16": rs.RS_F16, "fp8": rs.RS_FP8E4M3, "nvfp4": rs.RS
 # bf16 inputs; 128 x 64 heads two to a group (workgroup-per-head kernel)
 SHAPES = [dict(), dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64),
           dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64, in_dtype="bf16"),
-          dict(batch=3, nheads=6, ngroups=3, dstate=128, headdim=64)]
+          dict(batch=3, nheads=6, ngroups=3, dstate=128, headdim=64),
+          # bf16 records with 8 or more heads per group: two heads per wavefront on FP8 / NVFP4 reads
+          dict(batch=3, nheads=16, ngroups=1, dstate=128, headdim=64, in_dtype="bf16"),
+          dict(batch=2, nheads=16, ngroups=2, dstate=128, headdim=64, in_dtype="bf16")]
 FORMATS = [("f16", None), ("fp8", None), ("nvfp4", None), ("f16", "nvfp4"), ("fp8", "nvfp4"), ("f32", "nvfp4")]
 
 

@@ -91,7 +91,8 @@ class Twin:
             assert torch.equal(_bits(vp)[m], _bits(vc)[m]), f"call {self.calls}: held slots of ring {n} differ"
 
 
-M2_CASES = [dict(), dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64, in_dtype="bf16")]
+M2_CASES = [dict(), dict(batch=3, nheads=8, ngroups=2, dstate=128, headdim=64, in_dtype="bf16"),
+            dict(batch=2, nheads=16, ngroups=1, dstate=128, headdim=64, in_dtype="bf16")]
 M2_FORMATS = [(rs.RS_F32, rs.RS_NONE), (rs.RS_F32, rs.RS_NVFP4), (rs.RS_FP8E4M3, rs.RS_NONE)]
 
 
