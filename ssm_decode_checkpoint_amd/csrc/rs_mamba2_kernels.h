@@ -367,14 +367,21 @@ void m2_nonflush_wave_kernel(M2Args a) {
     if constexpr (SPL == 8) scv = nt_load(reinterpret_cast<const uint2*>(sp));
     else scv.x = nt_load(reinterpret_cast<const uint32_t*>(sp));
   }
+  // the head's tile from a scalar base plus one 32-bit lane offset, so that
+  // consecutive passes differ only in the load's immediate offset
+  constexpr int RB = RDF == FMT_F16 ? 2 * NC : RDF == FMT_FP8 ? NC : NC / 2;   // bytes per tile row
+  const uint8_t* tb = static_cast<const uint8_t*>(a.rd.data) + mat * static_cast<size_t>(NR * RB);
+  const uint32_t lo = static_cast<uint32_t>((lane >> 3) * RB + ce * (8 * RB / NC));
 #pragma unroll
   for (int k = 0; k < PASSES; ++k) {
+    const uint8_t* p = tb + lo + k * (RPP * RB);
     if constexpr (RDF == FMT_NVFP4) {
-      const size_t elem = (mat * NR + k * RPP + (lane >> 3)) * NC + static_cast<size_t>(ce) * 8;
-      raw[k].v = nt_load(reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(a.rd.data) + elem / 2));
+      raw[k].v = nt_load(reinterpret_cast<const uint32_t*>(p));
       raw[k].s = 0u;
+    } else if constexpr (RDF == FMT_FP8) {
+      raw[k].v = nt_load(reinterpret_cast<const uint2*>(p));
     } else {
-      raw[k] = load_chunk<RDF, 8, NC>(a.rd, mat, NR, k * RPP + (lane >> 3), ce);
+      raw[k].v = nt_load(reinterpret_cast<const uint4*>(p));
     }
   }
   arr.arrive(actr, hb, nck, len, nd);
