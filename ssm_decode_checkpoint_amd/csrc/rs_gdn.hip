@@ -144,21 +144,77 @@ struct GSlice {
 template <int NK, int NV, int NVS>
 struct GSliceNv {
   using TM = TileMap<4, NK, NVS>;
+  static constexpr bool kWhole = NK % TM::RPP == 0 && TM::RPP <= NK;   // every pass's rows exist
   uint32_t c[TM::PASSES];   // four codes (two bytes)
   uint32_t s[TM::PASSES];   // block scale code
   float ts;
   __device__ __forceinline__ void issue_read(const GDNArgs& a, size_t st, int c0) {
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* codes = static_cast<const uint8_t*>(a.rc.data);
+    // the slice's codes and scales from per-workgroup bases plus one 32-bit lane
+    // offset each, so that the passes differ only in the loads' immediate offsets
+    const size_t e0 = st * NK * NV + c0;   // the slice's first element
+    const uint8_t* cb = static_cast<const uint8_t*>(a.rc.data) + e0 / 2;
+    const uint8_t* sb = a.rc.nv_scale + e0 / 16;
+    const int r0 = static_cast<int>(threadIdx.x) / TM::TPR;
+    const uint32_t lo = static_cast<uint32_t>(r0 * NV + RegTile<4, NK, NVS>::col0());
 #pragma unroll
     for (int k = 0; k < TM::PASSES; ++k) {
-      int row = RegTile<4, NK, NVS>::row(k);
-      if constexpr (NK % TM::RPP != 0 || TM::RPP > NK) row = row < NK ? row : NK - 1;
-      const size_t elem = GSlice<NK, NV, NVS>::off(st, c0, row);
-      c[k] = *reinterpret_cast<const uint16_t*>(codes + elem / 2);
-      s[k] = a.rc.nv_scale[elem / 16];
+      uint32_t off = lo + static_cast<uint32_t>(k * TM::RPP * NV);
+      if constexpr (!kWhole) {
+        const int row = r0 + k * TM::RPP;
+        off = static_cast<uint32_t>((row < NK ? row : NK - 1) * NV + RegTile<4, NK, NVS>::col0());
+      }
+      c[k] = *reinterpret_cast<const uint16_t*>(cb + off / 2);
+      s[k] = sb[off / 16];
     }
     ts = a.rc.tscale[st];
+  }
+  // out[q][col] = sum_rows S0[row][col] w[q ws + row] for q = 0, 1 straight from
+  // the codes: a thread's four columns share a block scale, so the scale joins
+  // the two row weights (two multiplies instead of four) and the tensor scale
+  // joins the sum; the 4 lanes that share columns add their 8 values by a
+  // transposing exchange (each lane ends with 2). `red` is 4 * 2 * NVS floats
+  // of LDS, `out` 2 * NVS. Barriers inside; all threads call.
+  __device__ __forceinline__ void matvec2(const float* w, int ws, float* red, float* out) const {
+    static_assert(TM::TPR == 16, "16 lanes per row of four columns");
+    const int r0 = static_cast<int>(threadIdx.x) / TM::TPR;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = r0 + k * TM::RPP;
+      if (kWhole || row < NK) {
+        const float sd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s[k], 1.0f, false)[0];   // byte 0: the scale
+        const float w0 = w[row] * sd, w1 = w[ws + row] * sd;
+        const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 0);
+        const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[k], 1.0f, 1);
+        acc[0] += lo.x * w0; acc[1] += lo.y * w0; acc[2] += hi.x * w0; acc[3] += hi.y * w0;
+        acc[4] += lo.x * w1; acc[5] += lo.y * w1; acc[6] += hi.x * w1; acc[7] += hi.y * w1;
+      }
+    }
+    // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same columns: halves (bit 5)
+    // split the two weight rows, row pairs (bit 4) the column pairs
+    float a4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i + 4]), false, false);
+      a4[i] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    }
+    const int qr = static_cast<int>(__builtin_amdgcn_permlane32_swap(0u, 1u, false, false)[0]);   // weight row held
+    float a2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a4[i]), __float_as_uint(a4[i + 2]), false, false);
+      a2[i] = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    }
+    const int cp = static_cast<int>(__builtin_amdgcn_permlane16_swap(0u, 2u, false, false)[0]);   // column pair held
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    *reinterpret_cast<float2*>(&red[(wave * 2 + qr) * NVS + (lane & 15) * 4 + cp]) = make_float2(a2[0], a2[1]);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 2 * NVS; idx += kThreads)
+      out[idx] = ts * ((red[idx] + red[2 * NVS + idx]) + (red[4 * NVS + idx] + red[6 * NVS + idx]));
+    __syncthreads();
   }
   __device__ __forceinline__ void decode(RegTile<4, NK, NVS>& d) const {
 #pragma unroll
@@ -440,9 +496,13 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
     const int v = threadIdx.x;
     float hu = 0.0f, ho = 0.0f;
     if (v < NVS) gdn_held_sums(s, j, v, hu, ho);
-    RegTile<4, NK, NVS> S;
-    raw.decode(S);
-    tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
+    if constexpr (RC && NVS == 64) {
+      raw.matvec2(&s.W[0][0], NK, s.redp(), &s.out[0][0]);
+    } else {
+      RegTile<4, NK, NVS> S;
+      raw.decode(S);
+      tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
+    }
     const int slot = slot_of(nck, len);
     float* ru = static_cast<float*>(a.ru) + (p.st * kRing + slot) * NV + p.c0;
     if (v < NVS) {
