@@ -981,7 +981,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
     // with it the accumulators cost a wave of occupancy); otherwise on the VALU, rows
     // 0..KQ-1, then KQ..2KQ-1 if drafts reach them (fewer accumulator registers and
     // half the scratch of one 2KQ-row pass). Barriers inside publish the dots.
-    constexpr bool kMfmaMv = !VG && NVS == 64 && 4 * 2 * KQ * NVS <= GSpecSmem<NK, NVS, KQ, VG>::KROWS * NK;
+    constexpr bool kMfmaMv = NVS == 64 && 4 * 2 * KQ * NVS <= GSpecSmem<NK, NVS, KQ, VG>::KROWS * NK;
     if constexpr (kMfmaMv) {
       tile_matvec_mfma<2 * KQ>(S, &s.W[0][0], NK, red, &s.mv.out[0][0]);
     } else {
