@@ -934,14 +934,19 @@ void gdn_spec_append_kernel(GDNArgs a) {
         }
       }
     } else {
-      // decays r_{e,i} (direct products), one (draft, entry) pair per thread, and gamma
-      for (int idx = threadIdx.x; idx < K * kRing; idx += kThreads) {
-        const int d = idx / kRing, i = idx - d * kRing, ee = len + d;
-        if (i <= ee) {
-          float r = 1.0f;
-          for (int l = i + 1; l <= ee; ++l) r *= s.al[l];
+      // decays r_{e,i} = prod_{i<l<=e} alpha_l and gamma_e = prod_{l<=e} alpha_l for
+      // draft d (e = len + d): thread 16 d + i holds alpha_i (1 past e), and the
+      // suffix products over its 16-lane row give both (every lane takes part)
+      static_assert(KQ * kRing <= kThreads, "one thread per (draft, entry)");
+      {
+        const int d = static_cast<int>(threadIdx.x) / kRing, i = static_cast<int>(threadIdx.x) % kRing;
+        const int ee = len + d;
+        const float ai = d < K && i <= ee ? s.al[i] : 1.0f;
+        const float suf = row_suffix_prod16(ai);
+        const float r = row_next16(suf);
+        if (d < K && i <= ee) {
           s.rt[d][i] = r;
-          if (i == 0) s.gam[d] = r * s.al[0];
+          if (i == 0) s.gam[d] = suf;
         }
       }
       __syncthreads();
