@@ -742,7 +742,7 @@ __device__ __forceinline__ void spec_gram_bf16(SM& s, int K, int len) {
 // the instruction; the four wavefronts' partials meet in `red` (4 Q 64 floats of
 // LDS). fp32 products and sums: only the order of the additions differs from
 // tile_matvec. Barriers inside; all threads must call.
-template <int Q, int NK, int NVS>
+template <int Q, int NK, int NVS, bool HALF_RED = false, bool W_IN_RED = false>
 __device__ __forceinline__ void tile_matvec_mfma(const RegTile<4, NK, NVS>& S, const float* w, int ws, float* red,
                                                  float* out) {
   static_assert(NVS == 64 && Q <= 16, "16 lanes per row of four columns; at most 16 weight rows");
@@ -761,18 +761,49 @@ __device__ __forceinline__ void tile_matvec_mfma(const RegTile<4, NK, NVS>& S, c
                                                                               acc[c], 0, 0, 0);
   }
   // lane l: column 4 (l % 16) + c, rows 4 (l / 16) + i of the wavefront's partial
+  if constexpr (HALF_RED) {
+    // in two steps through 2 Q NVS floats of scratch: waves 2, 3 leave their
+    // partials, waves 0, 1 add theirs, then the two halves meet (W_IN_RED: the
+    // weight rows share the scratch, so every wave has read them first)
+    if constexpr (W_IN_RED) __syncthreads();
+    if (wave >= 2) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int mr = 4 * (l >> 4) + i;
-    if (mr < Q) {
-      float* dst = red + (wave * Q + mr) * NVS + 4 * (l & 15);
-      *reinterpret_cast<float4*>(dst) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      for (int i = 0; i < 4; ++i) {
+        const int mr = 4 * (l >> 4) + i;
+        if (mr < Q)
+          *reinterpret_cast<float4*>(red + ((wave - 2) * Q + mr) * NVS + 4 * (l & 15)) =
+              make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      }
     }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int mr = 4 * (l >> 4) + i;
+        if (mr < Q) {
+          float4* dst = reinterpret_cast<float4*>(red + (wave * Q + mr) * NVS + 4 * (l & 15));
+          const float4 o = *dst;
+          *dst = make_float4(acc[0][i] + o.x, acc[1][i] + o.y, acc[2][i] + o.z, acc[3][i] + o.w);
+        }
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < Q * NVS; idx += kThreads) out[idx] = red[idx] + red[Q * NVS + idx];
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mr = 4 * (l >> 4) + i;
+      if (mr < Q) {
+        float* dst = red + (wave * Q + mr) * NVS + 4 * (l & 15);
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0][i], acc[1][i], acc[2][i], acc[3][i]);
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < Q * NVS; idx += kThreads)
+      out[idx] = (red[idx] + red[Q * NVS + idx]) + (red[2 * Q * NVS + idx] + red[3 * Q * NVS + idx]);
+    __syncthreads();
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < Q * NVS; idx += kThreads)
-    out[idx] = (red[idx] + red[Q * NVS + idx]) + (red[2 * Q * NVS + idx] + red[3 * Q * NVS + idx]);
-  __syncthreads();
 }
 
 }  // namespace
@@ -1077,11 +1108,21 @@ namespace {
 template <int NK, int NVS, bool VG>
 struct alignas(16) GRcSmem {
   alignas(16) float K[kRing][NK];            // k rows of entries 0..m-1 (VG: then times r_{m-1,i})
-  alignas(16) float Wt[VG ? kRing : 1][NK];  // VG: matvec rows gamma_t * k_t
   alignas(16) float q[NK];                   // flush: q of the current token
   float U[kRing][NVS];                       // v rows, then the solved rows u (own columns)
-  float out[kRing][NVS];                     // S0 times the matvec rows
-  float red[4 * kRing * NVS];                // matvec scratch
+  // matvec scratch (the matrix-core matvec adds in two steps), and over its
+  // start the result: each output element is written by the thread that last
+  // reads the scratch at that index
+  union {
+    alignas(16) float red[(NVS == 64 ? 2 : 4) * kRing * NVS];
+    alignas(16) float out[kRing][NVS];       // S0 times the matvec rows
+    alignas(16) float Wt[VG && NVS == 64 ? kRing : 1][NK];   // VG: matvec rows gamma_t * k_t, until the matvec reads them
+  };
+  alignas(16) float Wt2[VG && NVS != 64 ? kRing : 1][NK];  // VG, other slice widths: the rows apart
+  __device__ __forceinline__ float* wt() {
+    if constexpr (NVS == 64) return &Wt[0][0];
+    else return &Wt2[0][0];
+  }
   float kk[kRing][kRing];                    // L_{t,i}, i < t
   float al[kRing], bt[kRing], gam[kRing], rr[kRing];
   alignas(16) float A[VG ? kRing : 1][NK];   // VG: alpha of entry e on channel c
@@ -1150,11 +1191,11 @@ __device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m
       float acc = 1.0f;
       for (int t = 0; t < m; ++t) {
         acc *= s.A[t][c];
-        s.Wt[t][c] = acc * s.K[t][c];
+        s.wt()[t * NK + c] = acc * s.K[t][c];
       }
       s.gv[c] = acc;
     }
-    for (int idx = m * NK + threadIdx.x; idx < kRing * NK; idx += kThreads) (&s.Wt[0][0])[idx] = 0.0f;
+    for (int idx = m * NK + threadIdx.x; idx < kRing * NK; idx += kThreads) s.wt()[idx] = 0.0f;
   } else {
     if (static_cast<int>(threadIdx.x) < m) {
       const int t = threadIdx.x;
@@ -1197,10 +1238,17 @@ __device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m
     // L_{t,i} for i < t < m, one pair per 16-lane group
     const int npairs = m * (m - 1) / 2;
     for (int pr = grp; pr < npairs; pr += kThreads / 16) {
-      int t = 1, i = pr;
-      while (i >= t) {   // uniform over the group
+      // pair pr = t (t - 1) / 2 + i, i < t, in closed form (the float root is
+      // exact enough below 120 pairs; the two steps fix a rounding either way)
+      int t = static_cast<int>((1.0f + sqrtf(8.0f * static_cast<float>(pr) + 1.0f)) * 0.5f);
+      int i = pr - t * (t - 1) / 2;
+      if (i >= t) {
         i -= t;
         ++t;
+      }
+      if (i < 0) {
+        --t;
+        i += t;
       }
       float part = lds_dot16<NK>(&s.K[t][0], &s.K[i][0], ln);
       part = group_sum16(part);
@@ -1218,8 +1266,8 @@ __device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m
 // fold into S. Barriers inside; all threads call.
 template <int NK, int NVS, bool VG>
 __device__ __forceinline__ void rc_solve_and_fold(RegTile<4, NK, NVS>& S, GRcSmem<NK, NVS, VG>& s, int m) {
-  const float* W = VG ? &s.Wt[0][0] : &s.K[0][0];
-  if constexpr (NVS == 64) tile_matvec_mfma<kRing>(S, W, NK, s.red, &s.out[0][0]);
+  const float* W = VG ? s.wt() : &s.K[0][0];
+  if constexpr (NVS == 64) tile_matvec_mfma<kRing, NK, NVS, true, VG>(S, W, NK, s.red, &s.out[0][0]);
   else tile_matvec<kRing>(S, W, NK, s.red, &s.out[0][0]);
   for (int v = threadIdx.x; v < NVS; v += kThreads) {
     float ur[kRing];
