@@ -301,6 +301,13 @@ struct GStage {
   }
 };
 
+// A KDA channel decay alpha = exp(g), as 2^(g log2 e) on the hardware
+// exponential: a relative error of about |g| 2^-24 per factor, |log r| 2^-24 on
+// a product r of them, at a fraction of the library exp's instructions. A
+// window takes 16 decays per key channel; every KDA kernel (the conventional
+// baselines included) forms them this way.
+__device__ __forceinline__ float kda_alpha(float g) { return __expf(g); }
+
 // VG only, after staging is visible: per key channel c, the decay products
 // r_{cur,e}[c] = prod_{e<l<=cur} alpha_l[c] replace the staged log decays (the
 // same descending order as the definition's direct products), gamma_cur[c] goes
@@ -314,7 +321,7 @@ __device__ __forceinline__ void kda_decays(SM& s, int m) {
 #pragma unroll
     for (int e = kRing - 1; e >= 0; --e) {
       if (e <= cur) {
-        const float al = expf(s.A[e][c]);
+        const float al = kda_alpha(s.A[e][c]);
         s.A[e][c] = acc;
         acc *= al;
       }
@@ -435,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
   if (ti < NK) {
     s.W[0][ti] = kv;
     s.W[1][ti] = qv;
-    s.W[2][ti] = VG ? expf(gvv) : 0.0f;   // VG: the channel decays
+    s.W[2][ti] = VG ? kda_alpha(gvv) : 0.0f;   // VG: the channel decays
     s.W[3][ti] = 0.0f;
   }
   if (ti < NVS) s.vc[ti] = vv;
@@ -902,10 +909,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
       if (static_cast<int>(threadIdx.x) < NK) {
         const int c = threadIdx.x;
 #pragma unroll
-        // alpha per entry, as 2^(g log2 e) on the hardware exponential: a relative
-        // error of about |g| 2^-24 per factor, |log r| 2^-24 on a window's decay
-        // product r, against 2^-24 for the library's exp (16 per channel here)
-        for (int e = 0; e < kRing; ++e) lg[e] = __expf(lg[e]);
+        for (int e = 0; e < kRing; ++e) lg[e] = kda_alpha(lg[e]);   // alpha per entry
         float acc = 1.0f;
 #pragma unroll
         for (int i = kRing - 1; i >= 0; --i) {
@@ -1188,7 +1192,7 @@ template <int NK, int NVS, bool VG>
 __device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m) {
   if constexpr (VG) {
     // alpha per entry and channel, then gamma_t * k_t (direct products in entry order)
-    for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) (&s.A[0][0])[idx] = expf((&s.A[0][0])[idx]);
+    for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) (&s.A[0][0])[idx] = kda_alpha((&s.A[0][0])[idx]);
     __syncthreads();
     for (int c = threadIdx.x; c < NK; c += kThreads) {
       float acc = 1.0f;
@@ -1469,7 +1473,7 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
         for (int i = kRing - 1; i >= 0; --i) {
           if (i < m) {
             s.K[i][threadIdx.x] *= acc;
-            acc *= expf(lg[i]);
+            acc *= kda_alpha(lg[i]);
           }
         }
         s.gv[threadIdx.x] = acc;
@@ -1573,7 +1577,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_spec_kernel(GDNArgs a) {
   }
   __syncthreads();
   if constexpr (VG) {
-    for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) (&s.AL[0][0])[idx] = expf((&s.AL[0][0])[idx]);
+    for (int idx = threadIdx.x; idx < K * NK; idx += kThreads) (&s.AL[0][0])[idx] = kda_alpha((&s.AL[0][0])[idx]);
     __syncthreads();
   }
   {
