@@ -244,3 +244,38 @@ def test_low_precision_checkpoints(fmt, rc, gate, shape):
     print(f"{fmt} checkpoint{' + nvfp4 reads' if rc else ''}: vs same-format oracle {worst:.2e}, "
           f"vs exact fp64 {lp:.2e}")
     assert worst <= gate
+
+
+LOWPREC_VARIANTS = [("f32", "nvfp4", 1e-4), ("f16", "nvfp4", 2e-2), ("fp8", "nvfp4", 2e-2), ("f16", None, 1e-4),
+                    ("fp8", None, 2e-2), ("nvfp4", None, 2e-2)]
+
+
+@pytest.mark.parametrize("fmt,rc,gate", LOWPREC_VARIANTS)
+def test_lowprec_config_batch64_shortened(fmt, rc, gate):
+    """The low-precision workload's own configuration (Nemotron-style shapes at
+    batch 64, bf16 records, zero initial state), shortened to 48 steps (3
+    flushes): the whole batch runs on the GPU, and two sequences are followed
+    by the oracle running the same storage formats. The first window (before
+    any fold quantizes) is held to 1e-5."""
+    w = W.M2_LOWPREC
+    seqs = [0, w.batch - 1]
+    p = W.m2_params(w)
+    A, D = params_dev(p)
+    code = {"f32": rs.RS_F32, "f16": rs.RS_F16, "fp8": rs.RS_FP8E4M3, "nvfp4": rs.RS_NVFP4}[fmt]
+    layer, bufs = m2_layer(w, ckpt_dtype=code, read_copy=rs.RS_NVFP4 if rc else rs.RS_NONE, fuse=1)
+    if rc:
+        rs.rs_requant_read_copy(layer, bufs)
+    H0 = W.m2_init_states(w, seqs)
+    ref = decode.M2Replay(H0, p["A"], p["D"], ckpt_fmt=fmt, read_copy=rc)
+    first, worst = 0.0, 0.0
+    for t in range(48):
+        tok = W.m2_step(w, t, range(w.batch))
+        y = y_buf(w.batch, w.nheads, w.headdim)
+        fn = rs.rs_step_flush if t % 16 == 15 else rs.rs_step_nonflush
+        fn(layer, bufs, m2_tok_dev(tok, w.in_dtype), A, D, y)
+        e = rel_l2(y.cpu().numpy()[seqs], ref.step(W.m2_step(w, t, seqs)))
+        if t < 15:
+            first = max(first, e)
+        worst = max(worst, e)
+    print(f"batch-64 {fmt}{' + nvfp4 reads' if rc else ''}: first window {first:.2e}, worst {worst:.2e}")
+    assert first <= 1e-5 and worst <= gate
