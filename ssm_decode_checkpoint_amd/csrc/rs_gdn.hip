@@ -834,7 +834,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
   __shared__ GSpecSmem<NK, NVS, KQ, VG> s;
   const GPtrs p = gdn_tile<NV, NS>(a);
   const int K = a.K;
-  static_assert(!VG || NK <= kThreads, "one thread per key channel");
+  static_assert(!VG || 2 * NK <= kThreads, "two threads per key channel");
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * NS + p.half;
   uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * NS) * kArriveStride;
@@ -869,7 +869,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
     float gv = 0.0f;
     float lg[kRing];   // VG: the log decays of window entries 0..n-1 of this thread's key channel
     if constexpr (VG) {
-      const int c = static_cast<int>(threadIdx.x) < NK ? static_cast<int>(threadIdx.x) : NK - 1;
+      const int c = static_cast<int>(threadIdx.x) % NK;
       const float* rgc = static_cast<const float*>(a.rg) + p.st * kRing * NK + c;
       const float* igc = a.g + p.st * NK + c;
 #pragma unroll
@@ -899,61 +899,65 @@ void gdn_spec_append_kernel(GDNArgs a) {
     if constexpr (VG) {
       // The decay from entry i to draft entry e = len + d factors at the first
       // draft: r_{e,i} = Rh_i * P_d for a held entry (Rh_i = prod_{i<l<len}
-      // alpha_l), and DW for a pair of drafts. Channel owners (one thread per
-      // key channel, window decays in registers) scale the held k rows by Rh in
-      // place and write WS and DW; then every dot of every draft in one pass:
+      // alpha_l), and DW for a pair of drafts. Two threads per key channel hold
+      // its window decays in registers: thread c scales the held k rows by Rh
+      // in place (and keeps Gam = prod_{l<len} alpha_l), thread NK + c writes
+      // WS and DW. Then every dot of every draft in one pass:
       //   kk[d][i] = beta_d <k_e, r_{e,i} * k_i>,  kq[d][i] = <q_d, r_{e,i} * k_i>.
-      // gamma_e = Gam * P_d with Gam = prod_{l<len} alpha_l.
+      // gamma_e = Gam * P_d.
       const int grp = threadIdx.x >> 4, ln = threadIdx.x & 15;
       float gam_c = 1.0f;
       if (static_cast<int>(threadIdx.x) < NK) {
         const int c = threadIdx.x;
-#pragma unroll
-        for (int e = 0; e < kRing; ++e) lg[e] = kda_alpha(lg[e]);   // alpha per entry
         float acc = 1.0f;
 #pragma unroll
         for (int i = kRing - 1; i >= 0; --i) {
           if (i < len) {
             s.K[i][c] *= acc;
-            acc *= lg[i];
+            acc *= kda_alpha(lg[i]);
           }
         }
         gam_c = acc;
+      } else if (static_cast<int>(threadIdx.x) < 2 * NK) {
+        const int c = threadIdx.x - NK;
         float pd = 1.0f;
         for (int d = 0; d < K; ++d) {
-          pd *= lg[len + d];                      // len + d < 16; wave-uniform index
+          pd *= kda_alpha(lg[len + d]);           // len + d < 16; wave-uniform index
           s.dots.WS[2 * d][c] = s.W[2 * d][c] * pd;
           s.dots.WS[2 * d + 1][c] = s.W[2 * d + 1][c] * pd;
           float q = 1.0f;
           for (int j = d - 1; j >= 0; --j) {
-            q *= lg[len + j + 1];
+            q *= kda_alpha(lg[len + j + 1]);
             s.dots.DW[d * (d - 1) / 2 + j][c] = q;
           }
         }
       }
       if (static_cast<int>(threadIdx.x) < K) s.gam[threadIdx.x] = 1.0f;
       __syncthreads();
-      // pairs of draft d: len held kk, len held kq, d draft kk, d + 1 draft kq
-      const int npairs = K * (2 * len + 1) + K * (K - 1);
+      // The 2 K len held pairs first (row 2 d + isq of WS against held entry
+      // i), then for each draft d its d draft kk and d + 1 draft kq pairs (K^2
+      // in all), so that the four groups of a wavefront take the same branch
+      // except where the two ranges meet.
+      const int nheld = 2 * K * len;
+      const int npairs = nheld + K * K;
       for (int pr = grp; pr < npairs; pr += kThreads / 16) {
-        int d = 0, r = pr;
-        while (r >= 2 * (len + d) + 1) {          // uniform over the group
-          r -= 2 * (len + d) + 1;
-          ++d;
-        }
-        const int ee = len + d;
         float part;
         bool isq;
-        int i;
-        if (r < 2 * len) {                        // held entry i: k row already scaled by Rh_i
-          isq = r >= len;
-          i = isq ? r - len : r;
-          part = lds_dot16<NK>(&s.K[i][0], &s.dots.WS[2 * d + (isq ? 1 : 0)][0], ln);
+        int d, i;
+        if (pr < nheld) {                         // held entry i: k row already scaled by Rh_i
+          const int row = pr / len;
+          i = pr - row * len;
+          d = row >> 1;
+          isq = (row & 1) != 0;
+          part = lds_dot16<NK>(&s.K[i][0], &s.dots.WS[row][0], ln);
         } else {                                  // earlier draft j (kk: j < d; kq: j <= d)
-          const int t = r - 2 * len;
-          isq = t >= d;
-          const int j = isq ? t - d : t;
+          const int t = pr - nheld;               // in [d^2, (d + 1)^2)
+          d = static_cast<int>(sqrtf(static_cast<float>(t) + 0.5f));
+          const int r = t - d * d;
+          isq = r >= d;
+          const int j = isq ? r - d : r;
           i = len + j;
+          const int ee = len + d;
           const float* w = j < d ? &s.dots.DW[d * (d - 1) / 2 + j][0] : nullptr;
           part = lds_dot16<NK>(&s.K[i][0], isq ? &s.W[2 * d + 1][0] : &s.K[ee][0], ln, w);
         }
