@@ -934,34 +934,33 @@ void gdn_spec_append_kernel(GDNArgs a) {
       }
       if (static_cast<int>(threadIdx.x) < K) s.gam[threadIdx.x] = 1.0f;
       __syncthreads();
-      // The 2 K len held pairs first (row 2 d + isq of WS against held entry
-      // i), then for each draft d its d draft kk and d + 1 draft kq pairs (K^2
-      // in all), so that the four groups of a wavefront take the same branch
-      // except where the two ranges meet.
-      const int nheld = 2 * K * len;
-      const int npairs = nheld + K * K;
-      for (int pr = grp; pr < npairs; pr += kThreads / 16) {
-        float part;
-        bool isq;
-        int d, i;
-        if (pr < nheld) {                         // held entry i: k row already scaled by Rh_i
-          const int row = pr / len;
-          i = pr - row * len;
-          d = row >> 1;
-          isq = (row & 1) != 0;
-          part = lds_dot16<NK>(&s.K[i][0], &s.dots.WS[row][0], ln);
-        } else {                                  // earlier draft j (kk: j < d; kq: j <= d)
-          const int t = pr - nheld;               // in [d^2, (d + 1)^2)
-          d = static_cast<int>(sqrtf(static_cast<float>(t) + 0.5f));
-          const int r = t - d * d;
-          isq = r >= d;
-          const int j = isq ? r - d : r;
-          i = len + j;
-          const int ee = len + d;
-          const float* w = j < d ? &s.dots.DW[d * (d - 1) / 2 + j][0] : nullptr;
-          part = lds_dot16<NK>(&s.K[i][0], isq ? &s.W[2 * d + 1][0] : &s.K[ee][0], ln, w);
+      // Held entry i: one 16-lane group takes its dots with all 2 K rows of WS
+      // (row 2 d + isq; the k row, already scaled by Rh_i, is read once). Then
+      // for each draft d its d draft kk and d + 1 draft kq pairs, K^2 in all.
+      for (int i = grp; i < len; i += kThreads / 16) {
+        float part[2 * KQ];
+#pragma unroll
+        for (int row = 0; row < 2 * KQ; ++row)
+          part[row] = row < 2 * K ? lds_dot16<NK>(&s.K[i][0], &s.dots.WS[row][0], ln) : 0.0f;
+#pragma unroll
+        for (int row = 0; row < 2 * KQ; ++row) {
+          if (row < 2 * K) {
+            const float v = group_sum16(part[row]);
+            if (ln == 0) {
+              if (row & 1) s.kq[row >> 1][i] = v;
+              else s.kk[row >> 1][i] = s.bet[row >> 1] * v;
+            }
+          }
         }
-        part = group_sum16(part);
+      }
+      for (int t = grp; t < K * K; t += kThreads / 16) {
+        const int d = static_cast<int>(sqrtf(static_cast<float>(t) + 0.5f));   // t in [d^2, (d + 1)^2)
+        const int r = t - d * d;
+        const bool isq = r >= d;                  // earlier draft j (kk: j < d; kq: j <= d)
+        const int j = isq ? r - d : r;
+        const int i = len + j, ee = len + d;
+        const float* w = j < d ? &s.dots.DW[d * (d - 1) / 2 + j][0] : nullptr;
+        const float part = group_sum16(lds_dot16<NK>(&s.K[i][0], isq ? &s.W[2 * d + 1][0] : &s.K[ee][0], ln, w));
         if (ln == 0) {
           if (isq) s.kq[d][i] = part;
           else s.kk[d][i] = s.bet[d] * part;
