@@ -815,6 +815,73 @@ __device__ __forceinline__ void tile_matvec_mfma(const RegTile<4, NK, NVS>& S, c
 
 }  // namespace
 
+// The K drafts' records of one speculative round in one set of register
+// chunks: thread chunk q < K NK / VK is a chunk of the drafts' q, the next K NK
+// / VK are their k, then K NVS / VK of their v (this slice's columns), so that
+// threads hold at most ceil((2 KQ NK + KQ NVS) / VK / 256) chunks instead of one
+// set per record kind. Chunks past the round's records load the first q chunk
+// (a valid address) and are never stored.
+template <typename TIN, int NK, int NVS, int KQ>
+struct DraftChunks {
+  static constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  static constexpr int CH = ((2 * KQ * NK + KQ * NVS) / VK + kThreads - 1) / kThreads;
+  uint4 c[CH];
+  __device__ __forceinline__ void load(const TIN* iq, const TIN* ik, size_t kstride, const TIN* iv, size_t vstride,
+                                       int K) {
+    const int qn = K * (NK / VK), vn = K * (NVS / VK);
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      const TIN* src;
+      if (q < 2 * qn) {
+        const int part = q < qn ? 0 : 1;
+        q -= part * qn;
+        const int e = q / (NK / VK), k = q - e * (NK / VK);
+        src = (part ? ik : iq) + e * kstride + k * VK;
+      } else if (q < 2 * qn + vn) {
+        q -= 2 * qn;
+        const int e = q / (NVS / VK), k = q - e * (NVS / VK);
+        src = iv + e * vstride + k * VK;
+      } else {
+        src = iq;
+      }
+      c[r] = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+  // q of draft d to row 2 d + 1 of W, its k to row 2 d (rows of NK floats)
+  __device__ __forceinline__ void qk_to_lds(float* W, int K) const {
+    const int qn = K * (NK / VK);
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      if (q < 2 * qn) {
+        const int part = q < qn ? 0 : 1;
+        q -= part * qn;
+        const int e = q / (NK / VK), k = q - e * (NK / VK);
+        float t[VK];
+        unpack16(c[r], static_cast<const TIN*>(nullptr), t);
+#pragma unroll
+        for (int i = 0; i < VK; ++i) W[(2 * e + 1 - part) * NK + k * VK + i] = t[i];
+      }
+    }
+  }
+  // v of draft d to row d of V (rows of NVS floats)
+  __device__ __forceinline__ void v_to_lds(float* V, int K) const {
+    const int qn = K * (NK / VK), vn = K * (NVS / VK);
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      int q = static_cast<int>(threadIdx.x) + r * kThreads - 2 * qn;
+      if (q >= 0 && q < vn) {
+        const int e = q / (NVS / VK), k = q - e * (NVS / VK);
+        float t[VK];
+        unpack16(c[r], static_cast<const TIN*>(nullptr), t);
+#pragma unroll
+        for (int i = 0; i < VK; ++i) V[e * NVS + k * VK + i] = t[i];
+      }
+    }
+  }
+};
+
 // Without the per-channel gate and up to 4 drafts: 7 waves per SIMD with the
 // matrix-core accumulators, the register budget the VALU dots and matvecs had;
 // otherwise the compiler puts the accumulators in separate registers and
@@ -829,8 +896,6 @@ void gdn_spec_append_kernel(GDNArgs a) {
   static_assert(NK % VK == 0 && NVS % VK == 0, "records are whole 16-byte chunks");
   constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
   constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
-  constexpr int CD = (KQ * NK / VK + kThreads - 1) / kThreads;
-  constexpr int CV = (KQ * NVS / VK + kThreads - 1) / kThreads;
   __shared__ GSpecSmem<NK, NVS, KQ, VG> s;
   const GPtrs p = gdn_tile<NV, NS>(a);
   const int K = a.K;
@@ -859,13 +924,10 @@ void gdn_spec_append_kernel(GDNArgs a) {
     // records into registers, then the state slice, then records to LDS
     RegChunks<TIN, CK> ck;
     RegChunks<float, CU> cu;
-    RegChunks<TIN, CD> cq, cd;
-    RegChunks<TIN, CV> cv;
+    DraftChunks<TIN, NK, NVS, KQ> cdr;
     ck.load(EntrySrc<TIN>{rk, ik, kstride, nck, len, NK}, n, NK);
     cu.load(EntrySrc<float>{ru, ru, 0, nck, len, NV}, len, NVS);
-    cq.load(EntrySrc<TIN>{iq, iq, kstride, 0, 0, NK}, K, NK);
-    cd.load(EntrySrc<TIN>{ik, ik, kstride, 0, 0, NK}, K, NK);
-    cv.load(EntrySrc<TIN>{iv, iv, vstride, 0, 0, NVS}, K, NVS);
+    cdr.load(iq, ik, kstride, iv, vstride, K);
     float gv = 0.0f;
     float lg[kRing];   // VG: the log decays of window entries 0..n-1 of this thread's key channel
     if constexpr (VG) {
@@ -888,10 +950,9 @@ void gdn_spec_append_kernel(GDNArgs a) {
     arr.arrive(actr, wg, nck, len, nd);
     ck.to_lds(&s.K[0][0], NK, n, NK);
     cu.to_lds(&s.U[0][0], NVS, len, NVS);
-    cd.to_lds(&s.W[0][0], 2 * NK, K, NK);
-    cq.to_lds(&s.W[1][0], 2 * NK, K, NK);
+    cdr.qk_to_lds(&s.W[0][0], K);
     for (int idx = 2 * K * NK + threadIdx.x; idx < 2 * KQ * NK; idx += kThreads) (&s.W[0][0])[idx] = 0.0f;
-    if constexpr (!VG) cv.to_lds(&s.mv.V[0][0], NVS, K, NVS);
+    if constexpr (!VG) cdr.v_to_lds(&s.mv.V[0][0], K);
     if constexpr (!VG)
       if (static_cast<int>(threadIdx.x) < n) s.al[threadIdx.x] = expf(gv);
     if (static_cast<int>(threadIdx.x) < K) s.bet[threadIdx.x] = bv;
@@ -1019,7 +1080,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
     float* HU = red;                 // [KQ][NVS], after the matvecs
     float* HO = red + KQ * NVS;      // [KQ][NVS]
     __syncthreads();                 // dots done: the k rows become scratch
-    if constexpr (VG) cv.to_lds(&s.mv.V[0][0], NVS, K, NVS);   // over WS (the matvec's barriers publish it)
+    if constexpr (VG) cdr.v_to_lds(&s.mv.V[0][0], K);   // over WS (the matvec's barriers publish it)
     RegTile<4, NK, NVS> S;
     raw.decode(S);
     // S0 [k_d, q_d]: all 2 KQ weight rows in one pass on the matrix cores where the
