@@ -865,6 +865,29 @@ struct DraftChunks {
       }
     }
   }
+  // The records into the ring as they came (bit copies), draft d at slot
+  // slot(d): q and k (rows of NK) when qk is set, v (this slice's NVS
+  // columns of rows of NV) always.
+  template <int NV, typename SLOT>
+  __device__ __forceinline__ void to_ring(TIN* rq, TIN* rk, TIN* rv, bool qk, int K, SLOT slot) const {
+    const int qn = K * (NK / VK), vn = K * (NVS / VK);
+#pragma unroll
+    for (int r = 0; r < CH; ++r) {
+      int q = static_cast<int>(threadIdx.x) + r * kThreads;
+      TIN* dst = nullptr;
+      if (q < 2 * qn) {
+        const int part = q < qn ? 0 : 1;
+        q -= part * qn;
+        const int e = q / (NK / VK), k = q - e * (NK / VK);
+        if (qk) dst = (part ? rk : rq) + static_cast<size_t>(slot(e)) * NK + k * VK;
+      } else if (q < 2 * qn + vn) {
+        q -= 2 * qn;
+        const int e = q / (NVS / VK), k = q - e * (NVS / VK);
+        dst = rv + static_cast<size_t>(slot(e)) * NV + k * VK;
+      }
+      if (dst) *reinterpret_cast<uint4*>(dst) = c[r];
+    }
+  }
   // v of draft d to row d of V (rows of NVS floats)
   __device__ __forceinline__ void v_to_lds(float* V, int K) const {
     const int qn = K * (NK / VK), vn = K * (NVS / VK);
@@ -953,6 +976,19 @@ void gdn_spec_append_kernel(GDNArgs a) {
     cdr.qk_to_lds(&s.W[0][0], K);
     for (int idx = 2 * K * NK + threadIdx.x; idx < 2 * KQ * NK; idx += kThreads) (&s.W[0][0])[idx] = 0.0f;
     if constexpr (!VG) cdr.v_to_lds(&s.mv.V[0][0], K);
+    // the drafts' records into the ring now, from the registers (this launch reads
+    // none of those slots; q and k rows are shared by the value heads of a
+    // key head, one slice of one of which writes them)
+    const auto dslot = [&](int d) { return slot_of(nck, len + d); };
+    cdr.template to_ring<NV>(static_cast<TIN*>(a.rq) + bk * kRing * NK, static_cast<TIN*>(a.rk) + bk * kRing * NK,
+                             static_cast<TIN*>(a.rv) + p.st * kRing * NV + p.c0, p.half == 0 && p.h % a.vpk == 0,
+                             K, dslot);
+    if constexpr (VG) {
+      if (p.half == 0 && static_cast<int>(threadIdx.x) < NK) {
+        float* rgw = static_cast<float*>(a.rg) + p.st * kRing * NK + threadIdx.x;
+        for (int d = 0; d < K; ++d) rgw[static_cast<size_t>(dslot(d)) * NK] = lg[len + d];   // the raw log decays
+      }
+    }
     if constexpr (!VG)
       if (static_cast<int>(threadIdx.x) < n) s.al[threadIdx.x] = expf(gv);
     if (static_cast<int>(threadIdx.x) < K) s.bet[threadIdx.x] = bv;
@@ -1138,26 +1174,11 @@ void gdn_spec_append_kernel(GDNArgs a) {
                     : 0.0f;
       a.o[d * vstride + p.st * NV + p.c0 + v] = o;
     }
-    // drafts into the ring (bit copies); each slice its own v columns
-    TIN* rv = static_cast<TIN*>(a.rv) + p.st * kRing * NV + p.c0;
-    const auto dslot = [&](int d) { return slot_of(nck, len + d); };
-    copy_rows16(rv, NV, iv, vstride, K, NVS, dslot);
-    if (p.half == 0) {
-      if (static_cast<int>(threadIdx.x) < K) {
-        const int d = threadIdx.x, sl = slot_of(nck, len + d);
-        if constexpr (!VG) static_cast<float*>(a.rg)[p.st * kRing + sl] = a.g[d * gstride + p.st];
-        static_cast<float*>(a.rbeta)[p.st * kRing + sl] = a.beta[d * gstride + p.st];
-      }
-      if constexpr (VG) {
-        float* rgw = static_cast<float*>(a.rg) + p.st * kRing * NK;
-        copy_rows16(rgw, NK, a.g + p.st * NK, gstride * NK, K, NK, dslot);
-      }
-      if (p.h % a.vpk == 0) {
-        TIN* rkw = static_cast<TIN*>(a.rk) + bk * kRing * NK;
-        TIN* rqw = static_cast<TIN*>(a.rq) + bk * kRing * NK;
-        copy_rows16(rkw, NK, ik, kstride, K, NK, dslot);
-        copy_rows16(rqw, NK, iq, kstride, K, NK, dslot);
-      }
+    // the drafts' gates and betas into the ring (the records went earlier)
+    if (p.half == 0 && static_cast<int>(threadIdx.x) < K) {
+      const int d = threadIdx.x, sl = slot_of(nck, len + d);
+      if constexpr (!VG) static_cast<float*>(a.rg)[p.st * kRing + sl] = a.g[d * gstride + p.st];
+      static_cast<float*>(a.rbeta)[p.st * kRing + sl] = a.beta[d * gstride + p.st];
     }
   }
   arr.finish(mp, actr, wg, a.nv * NS, MetaOp::Append, K, nck, len, nd);
