@@ -984,9 +984,14 @@ void gdn_spec_append_kernel(GDNArgs a) {
                              static_cast<TIN*>(a.rv) + p.st * kRing * NV + p.c0, p.half == 0 && p.h % a.vpk == 0,
                              K, dslot);
     if constexpr (VG) {
+      // the raw log decays, each from its own register (an index that is not
+      // a constant would make the wait before these stores one for every
+      // load in flight, the state tile's included)
       if (p.half == 0 && static_cast<int>(threadIdx.x) < NK) {
         float* rgw = static_cast<float*>(a.rg) + p.st * kRing * NK + threadIdx.x;
-        for (int d = 0; d < K; ++d) rgw[static_cast<size_t>(dslot(d)) * NK] = lg[len + d];   // the raw log decays
+#pragma unroll
+        for (int e = 0; e < kRing; ++e)
+          if (e >= len && e < n) rgw[static_cast<size_t>(slot_of(nck, e)) * NK] = lg[e];
       }
     }
     if constexpr (!VG)
