@@ -494,19 +494,19 @@ void m2_nonflush_wave_kernel(M2Args a) {
 // ----------------------------------------------------------------------------
 // Coefficients of the fold into LDS: L = l_m and xt_e = w_{m,e} dt_e x_e.
 // Barriers inside; all threads must call.
+// The decay products come from suffix products over one 16-lane row (lane e
+// holds a_e, 1 from m on): w_{m,e} is the product from e + 1 on, l_m the
+// row's whole product.
 template <typename SM>
 __device__ __forceinline__ void fold_coeffs(SM& s, int m) {
   constexpr int NC = sizeof(s.X[0]) / sizeof(float);
-  if (static_cast<int>(threadIdx.x) < m) {
+  static_assert(kRing == 16, "one DPP row holds the window");
+  if (threadIdx.x < 16) {
     const int e = threadIdx.x;
-    float w = 1.0f;
-    for (int l = e + 1; l < m; ++l) w *= s.a[l];
-    s.w[0][e] = w * s.dt[e];
-  }
-  if (threadIdx.x == 0) {
-    float L = 1.0f;
-    for (int l = 0; l < m; ++l) L *= s.a[l];
-    s.L[0] = L;
+    const float suf = row_suffix_prod16(e < m ? s.a[e] : 1.0f);   // prod_{e <= l < m} a_l
+    const float w = row_next16(suf);                                // prod_{e < l < m} a_l
+    if (e < m) s.w[0][e] = w * s.dt[e];
+    if (e == 0) s.L[0] = suf;
   }
   __syncthreads();
   static_assert(NC % 4 == 0, "float4 rows");
