@@ -168,9 +168,12 @@ __device__ __forceinline__ float clamp_mag(float q, float m) { return fminf(fmax
 // correction step (Markstein 1990; Muller et al., Handbook of Floating-Point
 // Arithmetic): q = RN(x y) is within one ulp of x / d, the remainder x - d q is
 // exact by FMA, and RN(q + (x - d q) y) = RN(x / d) when neither 1/d nor the
-// quotient overflows or underflows. A zero quotient takes the sign of x, as the
-// division gives it. Below the scale kRecipMin the callers divide: there 1/d
-// could overflow. Subnormal quotients (|x / d| < 2^-126) cannot change a code.
+// quotient overflows or underflows. The remainder is formed negated, t = q d -
+// x, and subtracted, RN(q - t y): the same value, and a zero quotient keeps
+// the sign of x as the division gives it (for x = -0, q = -0 and t = +0, so
+// -0 - (+0) y = -0; with the remainder added instead, +0 + -0 would give
+// +0). Below the scale kRecipMin the callers divide: there 1/d could
+// overflow. Subnormal quotients (|x / d| < 2^-126) cannot change a code.
 constexpr float kRecipMin = 0x1p-125f;
 
 // q[i] = RN(x[i] / d) for i < N, with y = RN(1/d) when d >= kRecipMin. The
@@ -182,8 +185,8 @@ __device__ __forceinline__ void quot_n(const float* x, float d, float y, float* 
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const float q0 = x[i] * y;
-      const float r = fmaf(-q0, d, x[i]);
-      q[i] = copysignf(fmaf(r, y, q0), x[i]);
+      const float t = fmaf(q0, d, -x[i]);
+      q[i] = fmaf(-t, y, q0);
     }
   } else {
 #pragma unroll
@@ -192,7 +195,10 @@ __device__ __forceinline__ void quot_n(const float* x, float d, float y, float* 
 }
 
 // E4M3FN codes of x[0..N) / sc, element i in byte i of w (N a multiple of 4;
-// y = RN(1/sc)).
+// y = RN(1/sc)), for a matrix scale sc = RN(amax / 448) of the same values:
+// then |x / sc| <= 448 (1 + 2^-23) and its correctly rounded quotient stays far
+// below 464, where the conversion would give the NaN code, and rounds to 448
+// at most, as saturation would; so the quotients need no clamp.
 template <int N>
 __device__ __forceinline__ void fp8_codes(const float* x, float sc, float y, uint32_t* w) {
   float q[N];
@@ -200,10 +206,8 @@ __device__ __forceinline__ void fp8_codes(const float* x, float sc, float y, uin
 #pragma unroll
   for (int i = 0; i < N / 4; ++i) {
     s16x2 r = {0, 0};
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(q[4 * i], 448.0f), clamp_mag(q[4 * i + 1], 448.0f),
-                                                 1.0f, false);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp_mag(q[4 * i + 2], 448.0f), clamp_mag(q[4 * i + 3], 448.0f),
-                                                 1.0f, true);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, q[4 * i], q[4 * i + 1], 1.0f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, q[4 * i + 2], q[4 * i + 3], 1.0f, true);
     w[i] = static_cast<uint32_t>(static_cast<uint16_t>(r.x)) | (static_cast<uint32_t>(static_cast<uint16_t>(r.y)) << 16);
   }
 }
