@@ -576,7 +576,7 @@ __device__ __forceinline__ void store_folded(const M2Args& a, size_t tile, RegTi
 // v_mfma_f32_16x16x4f32; each lane owns 16 consecutive columns of a row).
 template <int CKF, bool RC, int NR, int NC>
 struct ValuFold {
-  static constexpr int E = (CKF == FMT_F32 && !RC) ? 4 : 8;
+  static constexpr int E = CKF == FMT_F32 ? 4 : 8;
   using Raw = RawTile<CKF, E, NR, NC>;
   using Tile = RegTile<E, NR, NC>;
   template <typename SM>

@@ -248,14 +248,29 @@ __device__ __forceinline__ float nvfp4_tscale_of(float amax) {
   return ts == 0.0f ? 1.0f : ts;
 }
 
-// NVFP4 block scale code for a block whose |max| is bm (the pair of threads
-// holding the block's sixteen columns exchange their halves' maxima).
+// NVFP4 block scale code of a block of sixteen columns held E per thread by
+// 16 / E neighbouring lanes (E = 8: a lane pair; E = 4: a quad), which
+// exchange their parts' maxima.
+template <int E = 8>
 __device__ __forceinline__ uint32_t nvfp4_block_code(const float* x, float ts) {
+  static_assert(E == 4 || E == 8, "eight or four columns per thread");
   float bm = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) bm = fmaxf(bm, fabsf(x[i]));
+  for (int i = 0; i < E; ++i) bm = fmaxf(bm, fabsf(x[i]));
   bm = fmaxf(bm, dpp_mov<kDppXor1>(bm));
+  if constexpr (E == 4) bm = fmaxf(bm, dpp_mov<kDppXor2>(bm));
   return e4m3_code_of(bm / (6.0f * ts));
+}
+
+// E2M1 codes of four values x[0..4) / sd in the low 16 bits (element i in
+// nibble i; 0 when sd = 0), with the arithmetic of nvfp4_codes.
+__device__ __forceinline__ uint32_t nvfp4_codes4(const float* x, float sd) {
+  float q[4];
+  quot_n<4>(x, sd, 1.0f / sd, q);
+  uint32_t v = 0u;
+  v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, clamp_mag(q[0], 6.0f), clamp_mag(q[1], 6.0f), 1.0f, 0);
+  v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, clamp_mag(q[2], 6.0f), clamp_mag(q[3], 6.0f), 1.0f, 1);
+  return sd == 0.0f ? 0u : (v & 0xFFFFu);
 }
 
 // Replace M by the value it reads back as after being stored in FMT (scales
@@ -358,25 +373,32 @@ template <int E, int NR, int NC>
 __device__ __forceinline__ void tile_store_nvfp4(const StateBuf& sb, size_t mat, const RegTile<E, NR, NC>& M,
                                                  float amax) {
   using TM = TileMap<E, NR, NC>;
+  static_assert(E == 8 || E == 4, "NVFP4 blocks span two threads of eight columns or four of four");
   const int c = static_cast<int>(threadIdx.x % TM::TPR);
-  {
-    static_assert(E == 8, "NVFP4 blocks span two threads of eight columns");
-    const float ts = nvfp4_tscale_of(amax);
-    uint8_t* base = static_cast<uint8_t*>(sb.data) + mat * NR * NC / 2;
-    uint8_t* sbase = sb.nv_scale + mat * NR * NC / 16;
+  const float ts = nvfp4_tscale_of(amax);
+  uint8_t* base = static_cast<uint8_t*>(sb.data) + mat * NR * NC / 2;
+  uint8_t* sbase = sb.nv_scale + mat * NR * NC / 16;
 #pragma unroll
-    for (int k = 0; k < TM::PASSES; ++k) {
-      const int row = RegTile<E, NR, NC>::row(k);
-      const uint32_t s = nvfp4_block_code(M.v[k], ts);
+  for (int k = 0; k < TM::PASSES; ++k) {
+    const int row = RegTile<E, NR, NC>::row(k);
+    const uint32_t s = nvfp4_block_code<E>(M.v[k], ts);
+    const float sd = e4m3_value(s) * ts;
+    if constexpr (E == 8) {
       uint32_t w;
-      nvfp4_codes<8>(M.v[k], e4m3_value(s) * ts, &w);
+      nvfp4_codes<8>(M.v[k], sd, &w);
       if (row < NR) {
         nt_store(w, reinterpret_cast<uint32_t*>(base + (row * NC + c * 8) / 2));
         if ((c & 1) == 0) sbase[(row * NC + c * 8) / 16] = static_cast<uint8_t>(s);
       }
+    } else {
+      const uint32_t w = nvfp4_codes4(M.v[k], sd);
+      if (row < NR) {
+        *reinterpret_cast<uint16_t*>(base + (row * NC + c * 4) / 2) = static_cast<uint16_t>(w);
+        if ((c & 3) == 0) sbase[(row * NC + c * 4) / 16] = static_cast<uint8_t>(s);
+      }
     }
-    if (threadIdx.x == 0) sb.tscale[mat] = ts;
   }
+  if (threadIdx.x == 0) sb.tscale[mat] = ts;
 }
 
 // H <- L*H + sum_{e<m} row[e][r] * col[e][c]: a rank-m update of the held
