@@ -1499,9 +1499,9 @@ __global__ __launch_bounds__(kThreads) void gdn_requant_kernel(GDNArgs a, int fo
     const rs_meta* mp = a.meta + mat / a.nv;
     if (mp->len != 0 || mp->nd != 0) return;   // uniform over the workgroup
   }
-  RawTile<FMT_F32, 8, NK, NV> raw;
+  RawTile<FMT_F32, 4, NK, NV> raw;   // four columns per thread: loads that cover whole rows
   raw.issue(a.ck, mat);
-  RegTile<8, NK, NV> H;
+  RegTile<4, NK, NV> H;
   raw.decode(H);
   tile_store<FMT_NVFP4>(a.rc, mat, H, s4);
 }

@@ -971,13 +971,16 @@ __global__ __launch_bounds__(kThreads) void m2_restore_kernel(M2Args a) {
 // ----------------------------------------------------------------------------
 // standalone read-copy quantizer: NVFP4 copy of the stored checkpoint
 // ----------------------------------------------------------------------------
+// (an fp32 checkpoint streams four columns per thread, the layout whose
+// loads cover whole rows; the other formats' chunks are eight elements)
 template <int CKF, int NR, int NC>
 __global__ __launch_bounds__(kThreads) void requant_kernel(StateBuf ck, StateBuf rc) {
+  constexpr int E = CKF == FMT_F32 ? 4 : 8;
   __shared__ float s4[4];
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  RawTile<CKF, 8, NR, NC> raw;
+  RawTile<CKF, E, NR, NC> raw;
   raw.issue(ck, tile);
-  RegTile<8, NR, NC> H;
+  RegTile<E, NR, NC> H;
   raw.decode(H);
   tile_store<FMT_NVFP4>(rc, tile, H, s4);
 }
