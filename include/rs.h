@@ -155,7 +155,9 @@ typedef struct rs_config {
   int32_t max_draft;     /* 0 = no speculative decoding; else 1..ring/2 */
   int32_t in_dtype;      /* RS_F32 | RS_BF16 (GDN g and beta are always float) */
   int32_t ckpt_dtype;    /* RS_F32 | RS_F16 | RS_FP8E4M3 | RS_NVFP4 (uniform comparator);
-                            Gated DeltaNet and KDA: RS_F32 only */
+                            Gated DeltaNet and KDA: RS_F32, or RS_F16 / RS_FP8E4M3 in
+                            replay mode without a read copy on 16 x 16 and 128 x 128
+                            states (RS_E_UNSUPPORTED on 64 x 64) */
   int32_t read_copy;     /* RS_NONE | RS_NVFP4 (replay mode). Gated DeltaNet and KDA:
                             with an RS_F32 checkpoint; every fold rewrites the copy of the
                             sequences it folded in a second launch on the same stream

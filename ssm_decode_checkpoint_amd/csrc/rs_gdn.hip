@@ -233,8 +233,90 @@ struct GSliceNv {
 
 // What the non-flush step and the speculative append read: the checkpoint, or
 // its read copy.
-template <bool RC, int NK, int NV, int NVS>
-using ReadSlice = typename std::conditional<RC, GSliceNv<NK, NV, NVS>, GSlice<NK, NV, NVS>>::type;
+// The slice of a checkpoint stored in format CKF (fp32, FP16, or E4M3 codes with
+// one fp32 scale per matrix), in GSlice's register layout: four columns per
+// thread and pass, i.e. 16, 8 or 4 bytes per load and store.
+template <int CKF, int NK, int NV, int NVS>
+struct GSliceF {
+  static_assert(CKF == FMT_F32 || CKF == FMT_F16 || CKF == FMT_FP8, "fp32, FP16 or FP8 checkpoints");
+  using TM = TileMap<4, NK, NVS>;
+  using Word = typename std::conditional<CKF == FMT_F32, float4,
+                                         typename std::conditional<CKF == FMT_F16, uint2, uint32_t>::type>::type;
+  using Elem = typename std::conditional<CKF == FMT_F32, float,
+                                         typename std::conditional<CKF == FMT_F16, uint16_t, uint8_t>::type>::type;
+  Word r[TM::PASSES];
+  float ms;   // FP8: the matrix scale
+  __device__ __forceinline__ static size_t off(size_t st, int c0, int row) {
+    return (st * NK + row) * NV + c0 + RegTile<4, NK, NVS>::col0();
+  }
+  // (loads written before the slice stay ahead of it, as for RawTile::issue)
+  __device__ __forceinline__ void issue(const StateBuf& sb, size_t st, int c0) {
+    __builtin_amdgcn_sched_barrier(0);
+    const Elem* base = static_cast<const Elem*>(sb.data);
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      int row = RegTile<4, NK, NVS>::row(k);
+      if constexpr (NK % TM::RPP != 0 || TM::RPP > NK) row = row < NK ? row : NK - 1;
+      r[k] = nt_load(reinterpret_cast<const Word*>(base + off(st, c0, row)));
+    }
+    ms = CKF == FMT_FP8 ? sb.tscale[st] : 1.0f;
+  }
+  __device__ __forceinline__ void issue_read(const GDNArgs& a, size_t st, int c0) { issue(a.ck, st, c0); }
+  __device__ __forceinline__ void decode(RegTile<4, NK, NVS>& d) const {
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const bool in = (NK % TM::RPP == 0 && TM::RPP <= NK) || RegTile<4, NK, NVS>::row(k) < NK;
+      float t[4];
+      if constexpr (CKF == FMT_F32) {
+        t[0] = r[k].x; t[1] = r[k].y; t[2] = r[k].z; t[3] = r[k].w;
+      } else if constexpr (CKF == FMT_F16) {
+        const uint32_t w[2] = {r[k].x, r[k].y};
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          t[2 * i] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] & 0xFFFFu)));
+          t[2 * i + 1] = __half2float(__ushort_as_half(static_cast<unsigned short>(w[i] >> 16)));
+        }
+      } else {
+        // two E4M3FN codes per conversion, exactly; the scale applied after
+        const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[k], 1.0f, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[k], 1.0f, true);
+        t[0] = lo.x * ms; t[1] = lo.y * ms; t[2] = hi.x * ms; t[3] = hi.y * ms;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d.v[k][i] = in ? t[i] : 0.0f;
+    }
+  }
+  // Store S (FP8: codes under the matrix scale sc, y = RN(1/sc), which the
+  // caller derived from the whole matrix's |max|; the scale itself is the
+  // caller's to write).
+  __device__ __forceinline__ static void store(const StateBuf& sb, size_t st, int c0, const RegTile<4, NK, NVS>& S,
+                                               float sc = 1.0f, float y = 1.0f) {
+    Elem* base = static_cast<Elem*>(sb.data);
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const int row = RegTile<4, NK, NVS>::row(k);
+      if (row >= NK) continue;
+      Word* dst = reinterpret_cast<Word*>(base + off(st, c0, row));
+      if constexpr (CKF == FMT_F32) {
+        nt_store(make_float4(S.v[k][0], S.v[k][1], S.v[k][2], S.v[k][3]), dst);
+      } else if constexpr (CKF == FMT_F16) {
+        uint32_t w[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          w[i] = static_cast<uint32_t>(__half_as_ushort(__float2half_rn(S.v[k][2 * i]))) |
+                 (static_cast<uint32_t>(__half_as_ushort(__float2half_rn(S.v[k][2 * i + 1]))) << 16);
+        nt_store(make_uint2(w[0], w[1]), dst);
+      } else {
+        uint32_t w;
+        fp8_codes<4>(S.v[k], sc, y, &w);
+        nt_store(w, dst);
+      }
+    }
+  }
+};
+
+template <bool RC, int CKF, int NK, int NV, int NVS>
+using ReadSlice = typename std::conditional<RC, GSliceNv<NK, NV, NVS>, GSliceF<CKF, NK, NV, NVS>>::type;
 
 // Stage the window's entries 0..m-1 (entry m-1 is the current token, the
 // others come from the ring): k rows, the own columns of the held entries' u
@@ -471,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 // non-flush step: o from checkpoint + buffer, append (with its u row), no state write
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV, bool VG, bool RC>
+template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF = FMT_F32>
 __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
   constexpr int NVS = NV / gdn_slices<NV>();
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
@@ -488,7 +570,7 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
     const int j = len + 1;
     GStage<TIN, NK, NV, NVS, VG> stg;
     stg.load(a, p, nck, j);            // records first, then the state tile
-    ReadSlice<RC, NK, NV, NVS> raw;   // the checkpoint slice, or the read copy's
+    ReadSlice<RC, CKF, NK, NV, NVS> raw;   // the checkpoint slice, or the read copy's
     raw.issue_read(a, p.st, p.c0);
     arr.arrive(actr, wg, nck, len, nd);
     stg.store(s, j);
@@ -544,98 +626,148 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::NonFlush, 0, nck, len, nd);
 }
 
-template <typename TIN, int NK, int NV, bool VG, bool RC>
+template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
-  gdn_nonflush_body<TIN, NK, NV, VG, RC>(a, s);
+  gdn_nonflush_body<TIN, NK, NV, VG, RC, CKF>(a, s);
 }
 
 // ----------------------------------------------------------------------------
 // flush step: fold the len held entries and the current token, write once, o
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV, bool VG>
-__device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
+// One column slice's share of a flush: the window staged for its columns, the
+// slice read, the dots, the matvec, the current row, o, and the rank-m update
+// into S. arr: count the workgroup in after the slice's loads are issued
+// (null: another call of the workgroup does).
+template <typename TIN, int CKF, int NK, int NV, bool VG>
+__device__ __forceinline__ void gdn_flush_slice(const GDNArgs& a, const GPtrs& p,
+                                                GSmem<NK, NV / gdn_slices<NV>(), VG>& s, int m, long long nck,
+                                                Arrival* arr, uint32_t* actr, int wg, int len, int nd,
+                                                RegTile<4, NK, NV / gdn_slices<NV>()>& S) {
   constexpr int NVS = NV / gdn_slices<NV>();
-  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+  GStage<TIN, NK, NV, NVS, VG> stg;
+  stg.load(a, p, nck, m);            // records first, then the state tile
+  GSliceF<CKF, NK, NV, NVS> raw;
+  raw.issue(a.ck, p.st, p.c0);
+  if (arr) arr->arrive(actr, wg, nck, len, nd);
+  stg.store(s, m);
+  __syncthreads();
+  if constexpr (VG) {
+    kda_decays(s, m);
+    __syncthreads();
+  }
+  gdn_dots(s, m);
+  if constexpr (VG) {
+    // the fold's decayed k rows r_{m,i} * k_i, made now so that the decay table
+    // can serve as matvec scratch
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) {
+      const int i = idx / NK, c = idx - i * NK;
+      s.K[i][c] *= s.A[i][c];
+    }
+    __syncthreads();
+  }
+  if constexpr (!VG) __syncthreads();   // dots visible (VG: the barrier above)
+  static_assert(NVS <= kThreads, "one thread per column");
+  const int v = threadIdx.x;
+  float hu = 0.0f, ho = 0.0f;
+  if (v < NVS) gdn_held_sums(s, m, v, hu, ho);
+  raw.decode(S);
+  tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
+  if (v < NVS) {
+    a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, m, v, hu, ho);
+    if constexpr (!VG) {
+      // fold columns r_{cur,i} u_i (same thread, same column v)
+#pragma unroll
+      for (int i = 0; i < kRing; ++i)
+        if (i < m) s.U[i][v] *= s.rr[i];
+    }
+  }
+  __syncthreads();
+  if constexpr (VG) {
+    // S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T (k rows decayed above)
+    tile_scale_rows(S, s.gv);
+    tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  } else {
+    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  }
+}
+
+// Store a folded state into an FP8 checkpoint with one scale from the whole
+// matrix's |max|: held by this workgroup as one tile (NS = 1), or as the two
+// column slices S0 (columns 0..) and S1 (NVS..). Barriers inside.
+template <int NK, int NV, bool VG>
+__device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem<NK, NV / gdn_slices<NV>(), VG>& s,
+                                              const RegTile<4, NK, NV / gdn_slices<NV>()>& S0) {
+  constexpr int NVS = NV / gdn_slices<NV>();
+  const float sc = fp8_scale_of(tile_absmax(S0, s.s4)), y = 1.0f / sc;
+  GSliceF<FMT_FP8, NK, NV, NVS>::store(a.ck, st, 0, S0, sc, y);
+  if (threadIdx.x == 0) a.ck.tscale[st] = sc;
+}
+template <int NK, int NV, bool VG>
+__device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem<NK, NV / gdn_slices<NV>(), VG>& s,
+                                              const RegTile<4, NK, NV / gdn_slices<NV>()>& S0,
+                                              const RegTile<4, NK, NV / gdn_slices<NV>()>& S1) {
+  constexpr int NVS = NV / gdn_slices<NV>();
+  const float amax = fmaxf(tile_absmax(S0, s.s4), tile_absmax(S1, s.s4));
+  const float sc = fp8_scale_of(amax), y = 1.0f / sc;
+  GSliceF<FMT_FP8, NK, NV, NVS>::store(a.ck, st, 0, S0, sc, y);
+  GSliceF<FMT_FP8, NK, NV, NVS>::store(a.ck, st, NVS, S1, sc, y);
+  if (threadIdx.x == 0) a.ck.tscale[st] = sc;
+}
+
+// flush step: fold the len held entries and the current token, write once, o.
+// FP8 checkpoints: one scale spans the matrix, so the workgroup of the first
+// column slice folds both slices (reading both before it writes either) and
+// the second only counts in.
+template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
+__device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
+  constexpr int NS = gdn_slices<NV>();
+  constexpr int NVS = NV / NS;
+  const GPtrs p = gdn_tile<NV, NS>(a);
   rs_meta* mp = a.meta + p.b;
-  const int wg = p.h * gdn_slices<NV>() + p.half;
-  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * gdn_slices<NV>()) * kArriveStride;
+  const int wg = p.h * NS + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * NS) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
   Arrival arr;
-  if (errbit != 0) {
+  if (errbit != 0 || (CKF == FMT_FP8 && NS == 2 && p.half == 1)) {
     arr.arrive(actr, wg, nck, len, nd);
+  } else if constexpr (CKF == FMT_FP8 && NS == 2) {
+    RegTile<4, NK, NVS> S0, S1;
+    GPtrs p1 = p;
+    p1.half = 1;
+    p1.c0 = NVS;
+    gdn_flush_slice<TIN, CKF, NK, NV, VG>(a, p, s, m, nck, &arr, actr, wg, len, nd, S0);
+    __syncthreads();   // the second slice's staging reuses the LDS
+    gdn_flush_slice<TIN, CKF, NK, NV, VG>(a, p1, s, m, nck, nullptr, actr, wg, len, nd, S1);
+    gdn_store_fp8<NK, NV, VG>(a, p.st, s, S0, S1);
   } else {
-    float* ck = static_cast<float*>(a.ck.data);
-    GStage<TIN, NK, NV, NVS, VG> stg;
-    stg.load(a, p, nck, m);            // records first, then the state tile
-    GSlice<NK, NV, NVS> raw;
-    raw.issue(ck, p.st, p.c0);
-    arr.arrive(actr, wg, nck, len, nd);
-    stg.store(s, m);
-    __syncthreads();
-    if constexpr (VG) {
-      kda_decays(s, m);
-      __syncthreads();
-    }
-    gdn_dots(s, m);
-    if constexpr (VG) {
-      // the fold's decayed k rows r_{m,i} * k_i, made now so that the decay table
-      // can serve as matvec scratch
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) {
-        const int i = idx / NK, c = idx - i * NK;
-        s.K[i][c] *= s.A[i][c];
-      }
-      __syncthreads();
-    }
-    if constexpr (!VG) __syncthreads();   // dots visible (VG: the barrier above)
-    static_assert(NVS <= kThreads, "one thread per column");
-    const int v = threadIdx.x;
-    float hu = 0.0f, ho = 0.0f;
-    if (v < NVS) gdn_held_sums(s, m, v, hu, ho);
     RegTile<4, NK, NVS> S;
-    raw.decode(S);
-    tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
-    if (v < NVS) {
-      a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, m, v, hu, ho);
-      if constexpr (!VG) {
-        // fold columns r_{cur,i} u_i (same thread, same column v)
-#pragma unroll
-        for (int i = 0; i < kRing; ++i)
-          if (i < m) s.U[i][v] *= s.rr[i];
-      }
-    }
-    __syncthreads();
-    if constexpr (VG) {
-      // S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T (k rows decayed above)
-      tile_scale_rows(S, s.gv);
-      tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
-    } else {
-      tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
-    }
-    GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
+    gdn_flush_slice<TIN, CKF, NK, NV, VG>(a, p, s, m, nck, &arr, actr, wg, len, nd, S);
+    if constexpr (CKF == FMT_FP8) gdn_store_fp8<NK, NV, VG>(a, p.st, s, S);
+    else GSliceF<CKF, NK, NV, NVS>::store(a.ck, p.st, p.c0, S);
   }
-  arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
+  arr.finish(mp, actr, wg, a.nv * NS, MetaOp::Flush, 0, nck, len, nd);
 }
 
-template <typename TIN, int NK, int NV, bool VG>
+template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
-  gdn_flush_body<TIN, NK, NV, VG>(a, s);
+  gdn_flush_body<TIN, NK, NV, VG, CKF>(a, s);
 }
 
 // self-scheduling step (continuous batching): a sequence whose buffer is full
 // takes the flush, every other one a non-flush step, in one launch (the branch
 // is uniform per workgroup)
-template <typename TIN, int NK, int NV, bool VG>
+template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_auto_kernel(GDNArgs a) {
   __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
-  if (a.meta[p.b].len == kRing - 1) gdn_flush_body<TIN, NK, NV, VG>(a, s);
-  else gdn_nonflush_body<TIN, NK, NV, VG, false>(a, s);
+  if (a.meta[p.b].len == kRing - 1) gdn_flush_body<TIN, NK, NV, VG, CKF>(a, s);
+  else gdn_nonflush_body<TIN, NK, NV, VG, false, CKF>(a, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -909,7 +1041,7 @@ struct DraftChunks {
 // matrix-core accumulators, the register budget the VALU dots and matvecs had;
 // otherwise the compiler puts the accumulators in separate registers and
 // occupancy drops.
-template <typename TIN, int NK, int NV, int KQ, bool VG, bool RC>
+template <typename TIN, int NK, int NV, int KQ, bool VG, bool RC, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu((!VG && KQ <= 4) ? 7 : 1, 8)))
 void gdn_spec_append_kernel(GDNArgs a) {
@@ -968,7 +1100,7 @@ void gdn_spec_append_kernel(GDNArgs a) {
     }
     const int dd = static_cast<int>(threadIdx.x) < K ? static_cast<int>(threadIdx.x) : K - 1;
     const float bv = a.beta[static_cast<size_t>(dd) * gstride + p.st];
-    ReadSlice<RC, NK, NV, NVS> raw;   // the checkpoint slice, or the read copy's
+    ReadSlice<RC, CKF, NK, NV, NVS> raw;   // the checkpoint slice, or the read copy's
     raw.issue_read(a, p.st, p.c0);
     arr.arrive(actr, wg, nck, len, nd);
     ck.to_lds(&s.K[0][0], NK, n, NK);
@@ -1507,96 +1639,124 @@ __global__ __launch_bounds__(kThreads) void gdn_requant_kernel(GDNArgs a, int fo
 }
 
 // ----------------------------------------------------------------------------
+// speculative commit: the fold of the committed entries
+// ----------------------------------------------------------------------------
+// One column slice (columns c0..) of a commit fold of state st over its m
+// committed entries, into S (the checkpoint's slice read first).
+template <typename TIN, int CKF, int NK, int NV, bool VG>
+__device__ __forceinline__ void gdn_commit_slice(const GDNArgs& a, const FoldItem& it, int h, int c0,
+                                                 GSmem<NK, NV / gdn_slices<NV>(), VG>& s,
+                                                 RegTile<4, NK, NV / gdn_slices<NV>()>& S) {
+  constexpr int NVS = NV / gdn_slices<NV>();
+  constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
+  constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
+  constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
+  const int m = it.m;
+  const size_t st = static_cast<size_t>(it.b) * a.nv + h;
+  const size_t bk = static_cast<size_t>(it.b) * a.nqk + h / a.vpk;
+  const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
+  const float* ru = static_cast<const float*>(a.ru) + st * kRing * NV + c0;
+  RegChunks<TIN, CK> ck;
+  RegChunks<float, CU> cu;
+  ck.load(EntrySrc<TIN>{rk, rk, 0, it.nck, m, NK}, m, NK);
+  cu.load(EntrySrc<float>{ru, ru, 0, it.nck, m, NV}, m, NVS);
+  float gv = 0.0f;
+  float lg[VG ? kRing : 1];   // VG: log decays of the m entries, this thread's key channel
+  if constexpr (VG) {
+    const int c = static_cast<int>(threadIdx.x) < NK ? static_cast<int>(threadIdx.x) : NK - 1;
+    const float* rgc = static_cast<const float*>(a.rg) + st * kRing * NK + c;
+#pragma unroll
+    for (int e = 0; e < kRing; ++e) lg[e] = rgc[slot_of(it.nck, e < m ? e : m - 1) * NK];
+  } else {
+    const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
+    gv = static_cast<const float*>(a.rg)[st * kRing + slot_of(it.nck, e)];
+  }
+  GSliceF<CKF, NK, NV, NVS> raw;
+  raw.issue(a.ck, st, c0);
+  ck.to_lds(&s.K[0][0], NK, m, NK);
+  cu.to_lds(&s.U[0][0], NVS, m, NVS);
+  if constexpr (!VG)
+    if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(gv);
+  __syncthreads();
+  if constexpr (VG) {
+    // channel owners: k rows times r_{m,i} (descending direct products), gamma_m
+    if (static_cast<int>(threadIdx.x) < NK) {
+      float acc = 1.0f;
+#pragma unroll
+      for (int i = kRing - 1; i >= 0; --i) {
+        if (i < m) {
+          s.K[i][threadIdx.x] *= acc;
+          acc *= kda_alpha(lg[i]);
+        }
+      }
+      s.gv[threadIdx.x] = acc;
+    }
+  } else {
+    if (static_cast<int>(threadIdx.x) < m) {
+      float w = 1.0f;
+#pragma unroll
+      for (int l = 1; l < kRing; ++l) w *= (l > static_cast<int>(threadIdx.x) && l < m) ? s.al[l] : 1.0f;
+      s.rr[threadIdx.x] = w;
+    }
+    if (threadIdx.x == 0) {
+      float gm = 1.0f;
+#pragma unroll
+      for (int l = 0; l < kRing; ++l) gm *= l < m ? s.al[l] : 1.0f;
+      s.gam = gm;
+    }
+    __syncthreads();
+    for (int v = threadIdx.x; v < NVS; v += kThreads)
+#pragma unroll
+      for (int i = 0; i < kRing; ++i)
+        if (i < m) s.U[i][v] *= s.rr[i];
+  }
+  __syncthreads();
+  raw.decode(S);
+  if constexpr (VG) {
+    tile_scale_rows(S, s.gv);
+    tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  } else {
+    tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  }
+}
+
 // speculative commit (ReplaySSM), fold part: for each sequence listed by
 // commit_meta, S <- gamma_m S0 + sum_i r_{m,i} u_i k_i^T over its m committed
 // entries (u rows from the ring), one column slice per work item, over a
 // fixed grid (every workgroup leaves when the list is done). VG (KDA):
 // S <- S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T with per-channel decays.
-// ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV, bool VG>
+// FP8 checkpoints: the first slice's item folds both slices (one scale spans
+// the matrix), the second has nothing to do.
+template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
   constexpr int NS = gdn_slices<NV>();
   constexpr int NVS = NV / NS;
-  constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
-  constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
-  constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
   static_assert(!VG || NK <= kThreads, "one thread per key channel");
   __shared__ GSmem<NK, NVS, VG> s;
   const int per = a.nv * NS;
   const int total = *a.work_count * per;
-  float* ckp = static_cast<float*>(a.ck.data);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     const FoldItem it = a.work[item / per];
     const int r = item - (item / per) * per;
-    const int h = r / NS, half = r - h * NS, c0 = half * NVS, m = it.m;
+    const int h = r / NS, half = r - h * NS;
     const size_t st = static_cast<size_t>(it.b) * a.nv + h;
-    const size_t bk = static_cast<size_t>(it.b) * a.nqk + h / a.vpk;
-    const TIN* rk = static_cast<const TIN*>(a.rk) + bk * kRing * NK;
-    const float* ru = static_cast<const float*>(a.ru) + st * kRing * NV + c0;
-    RegChunks<TIN, CK> ck;
-    RegChunks<float, CU> cu;
-    ck.load(EntrySrc<TIN>{rk, rk, 0, it.nck, m, NK}, m, NK);
-    cu.load(EntrySrc<float>{ru, ru, 0, it.nck, m, NV}, m, NVS);
-    float gv = 0.0f;
-    float lg[VG ? kRing : 1];   // VG: log decays of the m entries, this thread's key channel
-    if constexpr (VG) {
-      const int c = static_cast<int>(threadIdx.x) < NK ? static_cast<int>(threadIdx.x) : NK - 1;
-      const float* rgc = static_cast<const float*>(a.rg) + st * kRing * NK + c;
-#pragma unroll
-      for (int e = 0; e < kRing; ++e) lg[e] = rgc[slot_of(it.nck, e < m ? e : m - 1) * NK];
-    } else {
-      const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
-      gv = static_cast<const float*>(a.rg)[st * kRing + slot_of(it.nck, e)];
-    }
-    GSlice<NK, NV, NVS> raw;
-    raw.issue(ckp, st, c0);
-    ck.to_lds(&s.K[0][0], NK, m, NK);
-    cu.to_lds(&s.U[0][0], NVS, m, NVS);
-    if constexpr (!VG)
-      if (static_cast<int>(threadIdx.x) < m) s.al[threadIdx.x] = expf(gv);
-    __syncthreads();
-    if constexpr (VG) {
-      // channel owners: k rows times r_{m,i} (descending direct products), gamma_m
-      if (static_cast<int>(threadIdx.x) < NK) {
-        float acc = 1.0f;
-#pragma unroll
-        for (int i = kRing - 1; i >= 0; --i) {
-          if (i < m) {
-            s.K[i][threadIdx.x] *= acc;
-            acc *= kda_alpha(lg[i]);
-          }
-        }
-        s.gv[threadIdx.x] = acc;
+    if constexpr (CKF == FMT_FP8) {
+      if (half != 0) continue;   // uniform over the workgroup
+      RegTile<4, NK, NVS> S0;
+      gdn_commit_slice<TIN, CKF, NK, NV, VG>(a, it, h, 0, s, S0);
+      if constexpr (NS == 2) {
+        RegTile<4, NK, NVS> S1;
+        __syncthreads();   // the second slice's staging reuses the LDS
+        gdn_commit_slice<TIN, CKF, NK, NV, VG>(a, it, h, NVS, s, S1);
+        gdn_store_fp8<NK, NV, VG>(a, st, s, S0, S1);
+      } else {
+        gdn_store_fp8<NK, NV, VG>(a, st, s, S0);
       }
     } else {
-      if (static_cast<int>(threadIdx.x) < m) {
-        float w = 1.0f;
-#pragma unroll
-        for (int l = 1; l < kRing; ++l) w *= (l > static_cast<int>(threadIdx.x) && l < m) ? s.al[l] : 1.0f;
-        s.rr[threadIdx.x] = w;
-      }
-      if (threadIdx.x == 0) {
-        float gm = 1.0f;
-#pragma unroll
-        for (int l = 0; l < kRing; ++l) gm *= l < m ? s.al[l] : 1.0f;
-        s.gam = gm;
-      }
-      __syncthreads();
-      for (int v = threadIdx.x; v < NVS; v += kThreads)
-#pragma unroll
-        for (int i = 0; i < kRing; ++i)
-          if (i < m) s.U[i][v] *= s.rr[i];
+      RegTile<4, NK, NVS> S;
+      gdn_commit_slice<TIN, CKF, NK, NV, VG>(a, it, h, half * NVS, s, S);
+      GSliceF<CKF, NK, NV, NVS>::store(a.ck, st, half * NVS, S);
     }
-    __syncthreads();
-    RegTile<4, NK, NVS> S;
-    raw.decode(S);
-    if constexpr (VG) {
-      tile_scale_rows(S, s.gv);
-      tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
-    } else {
-      tile_rank_update(S, s.gam, &s.K[0][0], NK, &s.U[0][0], NVS, m);
-    }
-    GSlice<NK, NV, NVS>::store(ckp, st, c0, S);
     __syncthreads();
   }
 }
@@ -1715,23 +1875,23 @@ __global__ __launch_bounds__(kThreads) void gdn_restore_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int NK, int NV, bool VG, bool RC>
+template <int NK, int NV, bool VG, bool RC, int CKF>
 struct gdn_step_kernels {
   static void conv(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
     if (bf) gdn_conv_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     else gdn_conv_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
   }
   static void nonflush(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
-    if (bf) gdn_nonflush_kernel<bf16, NK, NV, VG, RC><<<grid, kThreads, 0, st>>>(a);
-    else gdn_nonflush_kernel<float, NK, NV, VG, RC><<<grid, kThreads, 0, st>>>(a);
+    if (bf) gdn_nonflush_kernel<bf16, NK, NV, VG, RC, CKF><<<grid, kThreads, 0, st>>>(a);
+    else gdn_nonflush_kernel<float, NK, NV, VG, RC, CKF><<<grid, kThreads, 0, st>>>(a);
   }
   static void flush(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
     if constexpr (RC) {
       if (bf) gdn_flush_rc_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
       else gdn_flush_rc_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     } else {
-      if (bf) gdn_flush_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
-      else gdn_flush_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+      if (bf) gdn_flush_kernel<bf16, NK, NV, VG, CKF><<<grid, kThreads, 0, st>>>(a);
+      else gdn_flush_kernel<float, NK, NV, VG, CKF><<<grid, kThreads, 0, st>>>(a);
     }
   }
   static void auto_step(bool bf, const GDNArgs& a, int grid, hipStream_t st) {
@@ -1739,17 +1899,17 @@ struct gdn_step_kernels {
       if (bf) gdn_auto_rc_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
       else gdn_auto_rc_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     } else {
-      if (bf) gdn_auto_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
-      else gdn_auto_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+      if (bf) gdn_auto_kernel<bf16, NK, NV, VG, CKF><<<grid, kThreads, 0, st>>>(a);
+      else gdn_auto_kernel<float, NK, NV, VG, CKF><<<grid, kThreads, 0, st>>>(a);
     }
   }
 };
 
-template <typename TIN, int NK, int NV, bool VG, bool RC>
+template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF>
 void gdn_spec_append(const GDNArgs& a, int grid, hipStream_t st) {
-  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2, VG, RC><<<grid, kThreads, 0, st>>>(a);
-  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4, VG, RC><<<grid, kThreads, 0, st>>>(a);
-  else gdn_spec_append_kernel<TIN, NK, NV, 8, VG, RC><<<grid, kThreads, 0, st>>>(a);
+  if (a.K <= 2) gdn_spec_append_kernel<TIN, NK, NV, 2, VG, RC, CKF><<<grid, kThreads, 0, st>>>(a);
+  else if (a.K <= 4) gdn_spec_append_kernel<TIN, NK, NV, 4, VG, RC, CKF><<<grid, kThreads, 0, st>>>(a);
+  else gdn_spec_append_kernel<TIN, NK, NV, 8, VG, RC, CKF><<<grid, kThreads, 0, st>>>(a);
 }
 
 template <typename TIN, int NK, int NV, bool VG>
@@ -1759,11 +1919,11 @@ void gdn_conv_spec(const GDNArgs& a, int grid, hipStream_t st) {
   else gdn_conv_spec_kernel<TIN, NK, NV, 8, VG><<<grid, kThreads, 0, st>>>(a);
 }
 
-template <int NK, int NV, bool VG, bool RC>
+template <int NK, int NV, bool VG, bool RC, int CKF>
 void gdn_spec_kernels(GDNOp op, bool bf, const GDNArgs& a, int grid, hipStream_t st) {
   if (op == GDNOp::SpecAppend) {
-    if (bf) gdn_spec_append<bf16, NK, NV, VG, RC>(a, grid, st);
-    else gdn_spec_append<float, NK, NV, VG, RC>(a, grid, st);
+    if (bf) gdn_spec_append<bf16, NK, NV, VG, RC, CKF>(a, grid, st);
+    else gdn_spec_append<float, NK, NV, VG, RC, CKF>(a, grid, st);
   } else if (op == GDNOp::ConvSpec) {
     if (bf) gdn_conv_spec<bf16, NK, NV, VG>(a, grid, st);
     else gdn_conv_spec<float, NK, NV, VG>(a, grid, st);
@@ -1771,25 +1931,25 @@ void gdn_spec_kernels(GDNOp op, bool bf, const GDNArgs& a, int grid, hipStream_t
     if (bf) gdn_commit_fold_rc_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
     else gdn_commit_fold_rc_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
   } else {
-    if (bf) gdn_commit_fold_kernel<bf16, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
-    else gdn_commit_fold_kernel<float, NK, NV, VG><<<grid, kThreads, 0, st>>>(a);
+    if (bf) gdn_commit_fold_kernel<bf16, NK, NV, VG, CKF><<<grid, kThreads, 0, st>>>(a);
+    else gdn_commit_fold_kernel<float, NK, NV, VG, CKF><<<grid, kThreads, 0, st>>>(a);
   }
 }
 
-template <int NK, int NV, bool VG, bool RC>
+template <int NK, int NV, bool VG, bool RC, int CKF>
 void gdn_launch_kind(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   const bool bf = l.in_bf16;
-  using Steps = gdn_step_kernels<NK, NV, VG, RC>;
+  using Steps = gdn_step_kernels<NK, NV, VG, RC, CKF>;
   switch (op) {
     case GDNOp::Conv: Steps::conv(bf, a, l.grid, st); break;
     case GDNOp::NonFlush: Steps::nonflush(bf, a, l.grid, st); break;
     case GDNOp::Flush: Steps::flush(bf, a, l.grid, st); break;
     case GDNOp::Auto: Steps::auto_step(bf, a, l.grid, st); break;
     case GDNOp::SpecAppend:
-    case GDNOp::ConvSpec: gdn_spec_kernels<NK, NV, VG, RC>(op, bf, a, l.grid, st); break;
+    case GDNOp::ConvSpec: gdn_spec_kernels<NK, NV, VG, RC, CKF>(op, bf, a, l.grid, st); break;
     case GDNOp::CommitFold: {
       const int items = l.grid * gdn_slices<NV>();   // upper bound of listed work items
-      gdn_spec_kernels<NK, NV, VG, RC>(op, bf, a, items < 2048 ? items : 2048, st);
+      gdn_spec_kernels<NK, NV, VG, RC, CKF>(op, bf, a, items < 2048 ? items : 2048, st);
       break;
     }
     case GDNOp::Restore: gdn_restore_kernel<NK, NV><<<l.grid, kThreads, 0, st>>>(a); break;
@@ -1804,13 +1964,25 @@ void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
       op == GDNOp::ConvSpec)
     l.grid *= gdn_slices<NV>();
-  if (l.vg) {
-    if (l.rc) gdn_launch_kind<NK, NV, true, true>(op, a, l, st);
-    else gdn_launch_kind<NK, NV, true, false>(op, a, l, st);
-  } else {
-    if (l.rc) gdn_launch_kind<NK, NV, false, true>(op, a, l, st);
-    else gdn_launch_kind<NK, NV, false, false>(op, a, l, st);
+  if (l.rc) {   // the read copy sits beside an fp32 checkpoint
+    if (l.vg) gdn_launch_kind<NK, NV, true, true, FMT_F32>(op, a, l, st);
+    else gdn_launch_kind<NK, NV, false, true, FMT_F32>(op, a, l, st);
+    return;
   }
+  if constexpr (NK != 64) {   // FP16 / FP8 checkpoints: the 16 x 16 and 128 x 128 states
+    if (l.ckf == FMT_F16) {
+      if (l.vg) gdn_launch_kind<NK, NV, true, false, FMT_F16>(op, a, l, st);
+      else gdn_launch_kind<NK, NV, false, false, FMT_F16>(op, a, l, st);
+      return;
+    }
+    if (l.ckf == FMT_FP8) {
+      if (l.vg) gdn_launch_kind<NK, NV, true, false, FMT_FP8>(op, a, l, st);
+      else gdn_launch_kind<NK, NV, false, false, FMT_FP8>(op, a, l, st);
+      return;
+    }
+  }
+  if (l.vg) gdn_launch_kind<NK, NV, true, false, FMT_F32>(op, a, l, st);
+  else gdn_launch_kind<NK, NV, false, false, FMT_F32>(op, a, l, st);
 }
 
 }  // namespace

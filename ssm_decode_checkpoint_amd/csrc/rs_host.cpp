@@ -163,7 +163,7 @@ GDNArgs gdn_args(const rs_layer* L, const rs_buffers* buf) {
   a.nqk = c.n_qk_heads;
   a.vpk = c.n_v_heads / c.n_qk_heads;
   a.kmax = c.max_draft;
-  a.ck = StateBuf{buf->ckpt, nullptr, nullptr};
+  a.ck = ck_buf(L, buf->ckpt);
   if (c.read_copy == RS_NVFP4) a.rc = rc_buf(L, buf->read_copy);
   if (c.mode == RS_REPLAY) {
     char* r = static_cast<char*>(buf->ring);
@@ -228,6 +228,7 @@ GDNLaunch gdn_launch_cfg(const rs_layer* L) {
   l.in_bf16 = c.in_dtype == RS_BF16;
   l.vg = c.kind == RS_KDA;
   l.rc = c.read_copy == RS_NVFP4;
+  l.ckf = fmt_of(c.ckpt_dtype);
   l.grid = c.batch * c.n_v_heads;
   return l;
 }
@@ -290,7 +291,11 @@ rs_status rs_init(const rs_config* cfg, rs_layer* out) {
     if (c.n_v_heads % c.n_qk_heads != 0) return RS_E_ARG;
     if (static_cast<uint64_t>(c.batch) * c.n_v_heads > (1u << 30)) return RS_E_ARG;
     if (!gdn_shape_supported(c.head_k_dim, c.head_v_dim)) return RS_E_UNSUPPORTED;
-    if (c.ckpt_dtype != RS_F32) return RS_E_DTYPE;
+    // FP16 / FP8 checkpoints: replay mode, without a read copy, on the 16 x 16 and
+    // 128 x 128 states
+    if (c.ckpt_dtype != RS_F32 && c.ckpt_dtype != RS_F16 && c.ckpt_dtype != RS_FP8E4M3) return RS_E_DTYPE;
+    if (c.ckpt_dtype != RS_F32 && (!replay || c.read_copy != RS_NONE)) return RS_E_DTYPE;
+    if (c.ckpt_dtype != RS_F32 && c.head_k_dim == 64) return RS_E_UNSUPPORTED;
     if (!replay && c.read_copy != RS_NONE) return RS_E_DTYPE;
     L.heads = c.n_v_heads;
     L.in_heads = c.n_qk_heads;

@@ -161,6 +161,7 @@ struct GDNLaunch {
   bool in_bf16;
   bool vg;        // Kimi Delta Attention: per-key-channel gate
   bool rc;        // NVFP4 read copy: reads go to it, folds re-solve from the checkpoint
+  int ckf;        // checkpoint format FMT_F32 / FMT_F16 / FMT_FP8 (without a read copy)
   int grid;
 };
 

@@ -70,13 +70,15 @@ def m2_layer(w: W.Mamba2Workload, mode=rs.RS_REPLAY, ckpt_dtype=rs.RS_F32, read_
     return layer, rs.alloc_buffers(layer, DEV)
 
 
-def gdn_layer(w: W.GDNWorkload, mode=rs.RS_REPLAY, batch=None, max_draft=None, read_copy=rs.RS_NONE):
+def gdn_layer(w: W.GDNWorkload, mode=rs.RS_REPLAY, batch=None, max_draft=None, read_copy=rs.RS_NONE,
+              ckpt_dtype=rs.RS_F32):
     """A Gated DeltaNet layer, or a Kimi Delta Attention layer for a per-channel gate."""
     kind = rs.RS_KDA if w.gate == "channel" else rs.RS_GDN
     cfg = rs.make_config(kind, w.batch if batch is None else batch, mode=mode, n_qk_heads=w.n_qk,
                          n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv,
                          max_draft=w.max_draft if max_draft is None else max_draft,
-                         in_dtype=rs.RS_BF16 if w.in_dtype == "bf16" else rs.RS_F32, read_copy=read_copy)
+                         in_dtype=rs.RS_BF16 if w.in_dtype == "bf16" else rs.RS_F32, read_copy=read_copy,
+                         ckpt_dtype=ckpt_dtype)
     _, layer = rs.rs_init(cfg)
     return layer, rs.alloc_buffers(layer, DEV)
 

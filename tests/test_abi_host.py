@@ -105,6 +105,33 @@ def test_gdn_layout_sizes():
         assert L.ckpt_bytes == 256 * 32 * 128 * 128 * 4
 
 
+@pytest.mark.parametrize("kind", ["gdn", "kda"])
+def test_delta_rule_low_precision_checkpoints(kind):
+    """FP16 / FP8 checkpoints of the delta-rule layers: replay mode without a read
+    copy, on the 16 x 16 and 128 x 128 states; the stored matrix in 2 or 1 bytes
+    per element, FP8 with one fp32 scale per matrix after the codes."""
+    k = rs.RS_KDA if kind == "kda" else rs.RS_GDN
+    kw = dict(n_qk_heads=2, n_v_heads=4, head_k_dim=128, head_v_dim=128)
+    mats = 8 * 4
+    _, L32 = rs.rs_init(rs.make_config(k, 8, **kw))
+    _, L16 = rs.rs_init(rs.make_config(k, 8, ckpt_dtype=rs.RS_F16, **kw))
+    _, L8 = rs.rs_init(rs.make_config(k, 8, ckpt_dtype=rs.RS_FP8E4M3, **kw))
+    assert L32.ckpt_bytes == mats * 128 * 128 * 4
+    assert L16.ckpt_bytes >= mats * 128 * 128 * 2
+    assert L8.ck_scale_off >= mats * 128 * 128 and L8.ckpt_bytes >= L8.ck_scale_off + mats * 4
+    assert L16.ring_bytes == L32.ring_bytes and L8.meta_bytes == L32.meta_bytes
+    tiny = dict(n_qk_heads=1, n_v_heads=2, head_k_dim=16, head_v_dim=16)
+    for dt in (rs.RS_F16, rs.RS_FP8E4M3):
+        assert rs.rs_init(rs.make_config(k, 2, ckpt_dtype=dt, **tiny), raise_on_error=False)[0] == rs.RS_OK
+        assert rs.rs_init(rs.make_config(k, 2, ckpt_dtype=dt, mode=rs.RS_CONVENTIONAL, **tiny),
+                          raise_on_error=False)[0] == rs.RS_E_DTYPE
+        assert rs.rs_init(rs.make_config(k, 2, ckpt_dtype=dt, read_copy=rs.RS_NVFP4, **tiny),
+                          raise_on_error=False)[0] == rs.RS_E_DTYPE
+        assert rs.rs_init(rs.make_config(k, 2, ckpt_dtype=dt, n_qk_heads=1, n_v_heads=2, head_k_dim=64,
+                                         head_v_dim=64), raise_on_error=False)[0] == rs.RS_E_UNSUPPORTED
+    assert rs.rs_init(rs.make_config(k, 2, ckpt_dtype=rs.RS_NVFP4, **tiny), raise_on_error=False)[0] == rs.RS_E_DTYPE
+
+
 def test_reset_slots_host_checks():
     """rs_reset_slots: argument and mode checks happen on the host; count == 0 launches nothing."""
     lib = rs.lib()
