@@ -128,8 +128,16 @@ def gdn_bytes(w: W.GDNWorkload):
     E_old_rc = w.n_qk * w.dk * s_in + w.n_v * w.dv * s_in + w.n_v * gw * 4 + w.n_v * 4
     nonflush_rc = {j: S_rc + (j - 1) * E_old + 2 * E_in + Urow + O for j in range(1, RING)}
     flush_rc = 2 * S + (RING - 1) * E_old_rc + E_in + O + S + S_rc
+    # FP16 / FP8 checkpoints: the state in 2 or 1 bytes per element (FP8 with a
+    # 4-byte scale per matrix), read by every step and written by the flush
+    lp = {}
+    for fmt, es, extra in (("f16", 2, 0), ("fp8", 1, 4)):
+        S_lp = w.n_v * w.dv * w.dk * es + w.n_v * extra
+        lp[fmt] = {"state": S_lp,
+                   "nonflush": {j: S_lp + (j - 1) * E_old + 2 * E_in + Urow + O for j in range(1, RING)},
+                   "flush": 2 * S_lp + (RING - 1) * E_old + E_in + O}
     return {"state": S, "E_in": E_in, "E_old": E_old, "O": O, "nonflush": nonflush, "flush": flush, "conv": conv,
-            "state_rc": S_rc, "nonflush_rc": nonflush_rc, "flush_rc": flush_rc}
+            "state_rc": S_rc, "nonflush_rc": nonflush_rc, "flush_rc": flush_rc, "lowprec": lp}
 
 
 # ---------------------------------------------------------------------------
@@ -607,10 +615,10 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
     gp = W.gdn_params(w)
     kda_layer = w.gate == "channel"
 
-    def mk(mode, rc=False):
+    def mk(mode, rc=False, ckpt=rs.RS_F32):
         cfg = rs.make_config(rs.RS_KDA if kda_layer else rs.RS_GDN, B, mode=mode, n_qk_heads=w.n_qk,
                              n_v_heads=w.n_v, head_k_dim=w.dk, head_v_dim=w.dv, in_dtype=rs.RS_BF16,
-                             read_copy=rs.RS_NVFP4 if rc else rs.RS_NONE)
+                             read_copy=rs.RS_NVFP4 if rc else rs.RS_NONE, ckpt_dtype=ckpt)
         _, layer = rs.rs_init(cfg)
         return layer, rs.alloc_buffers(layer, dev)
 
@@ -647,10 +655,24 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
             fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
             _marked(ev, t, tm.stream, lambda: fn(ql, qb, pool[t], None, None, o))
 
+    # FP16 / FP8 checkpoints, from a zero state (the warm-up windows fold real
+    # entries into it before the timed ones)
+    lp_layers = {"f16": mk(rs.RS_REPLAY, ckpt=rs.RS_F16), "fp8": mk(rs.RS_REPLAY, ckpt=rs.RS_FP8E4M3)}
+
+    def lp_window(fmt):
+        ll, lb = lp_layers[fmt]
+
+        def run(ev):
+            for t in range(RING):
+                fn = rs.rs_step_flush if t == RING - 1 else rs.rs_step_nonflush
+                _marked(ev, t, tm.stream, lambda: fn(ll, lb, pool[t], None, None, o))
+        return run
+
     K, warm = args.steps, args.warmup
     total_r, per_r = tm.run(replay_window, K, warm, RING)
     total_c, per_c = tm.run(conv_window, K, warm, RING)
     total_q, per_q = tm.run(rc_window, K, warm, RING)
+    lp_runs = {fmt: tm.run(lp_window(fmt), K, warm, RING) for fmt in lp_layers}
     byt = gdn_bytes(w)
     ntok = B * RING * K
     nf_ms = per_r[:, : RING - 1]
@@ -673,6 +695,19 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
                  "speedup_vs_fp32_replay": q_value / value, "speedup_vs_conventional": q_value / conv_value,
                  "bytes_ratio_conventional_over_read_copy": byt["conv"] * B * RING / q_win_bytes,
                  "note": "fp32 checkpoint, NVFP4 read copy; the flush call is the re-solving fold and the requant"}
+    lowprec = {}
+    for fmt, (total_l, per_l) in lp_runs.items():
+        lb_ = byt["lowprec"][fmt]
+        l_nf = per_l[:, : RING - 1]
+        l_nf_bytes = sum(lb_["nonflush"][j] for j in range(1, RING)) * B
+        l_win = l_nf_bytes + lb_["flush"] * B
+        l_fl = float(per_l[:, RING - 1].mean())
+        l_value = ntok / (total_l * 1e-3)
+        lowprec[fmt] = {"tokens_per_s": l_value, "window_ms": total_l / K, "window_alg_bytes": l_win,
+                        "window_gbs": l_win / (total_l / K * 1e-3) / 1e9, "nonflush_avg_ms": float(l_nf.mean()),
+                        "nonflush_gbs": l_nf_bytes / (l_nf.sum(axis=1).mean() * 1e-3) / 1e9, "flush_ms": l_fl,
+                        "flush_gbs": lb_["flush"] * B / (l_fl * 1e-3) / 1e9,
+                        "speedup_vs_fp32_replay": l_value / value, "speedup_vs_conventional": l_value / conv_value}
     return {
         "metric": ("KDA" if kda_layer else "GDN") + "-layer decode tokens/s at batch 256 + achieved HBM GB/s vs conventional",
         "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": warm, "ms_per_step": total_r / K,
@@ -691,6 +726,7 @@ def bench_gdn(args, torch, rs, w=W.GDN_QWEN):
         "speedup_vs_conventional": value / conv_value,
         "bytes_ratio_conventional_over_replay": byt["conv"] * B * RING / win_bytes,
         "read_copy": read_copy,
+        "lowprec_checkpoints": lowprec,
     }
 
 
