@@ -3,7 +3,8 @@
 Before every call, each ring slot of a sequence outside its held and pending
 entries (slots (n_ckpt + i) mod 16 for i < len + nd) is filled with NaN in every
 ring array: Mamba-2 x, B, C, dt; Gated DeltaNet and KDA q, k, v, g, beta and
-the solved rows u (with and without the NVFP4 read copy). A twin layer runs
+the solved rows u (fp32 checkpoints with and without the NVFP4 read copy, FP16
+and FP8 checkpoints). A twin layer runs
 the same calls without poison. Outputs,
 checkpoints, counters and the held slots must match bit for bit: a kernel that
 touched an unheld slot, even to multiply it by zero, would carry a NaN into
@@ -18,6 +19,7 @@ import ssm_decode_checkpoint_amd as rs
 import workloads as W
 from gpu_harness import (gdn_drafts_dev, gdn_layer, gdn_tok_dev, load_state_f32, m2_drafts_dev, m2_layer, m2_tok_dev,
                          params_dev, read_meta, require_gpu, y_buf)
+import lowprec_codes as LC
 
 pytestmark = pytest.mark.gpu
 
@@ -138,25 +140,34 @@ def test_mamba2_spec_under_poison(shape):
 
 
 DELTA_CASES = [dict(), dict(batch=2, n_qk=2, n_v=4, dk=128, dv=128, in_dtype="bf16")]
+# (checkpoint format, read copy): fp32 with and without the NVFP4 read copy, FP16 and FP8 checkpoints
+DELTA_FORMATS = [(rs.RS_F32, rs.RS_NONE), (rs.RS_F32, rs.RS_NVFP4), (rs.RS_F16, rs.RS_NONE),
+                 (rs.RS_FP8E4M3, rs.RS_NONE)]
+_LC_FMT = {rs.RS_F16: "f16", rs.RS_FP8E4M3: "fp8"}
 
 
-def _delta_load(S0, rc):
+def _delta_load(S0, ckpt, rc):
     def load(layer, bufs):
-        load_state_f32(layer, bufs, S0)
+        if ckpt == rs.RS_F32:
+            load_state_f32(layer, bufs, S0)
+        else:
+            fmt = _LC_FMT[ckpt]
+            enc = LC.encode(fmt, np.ascontiguousarray(np.swapaxes(np.asarray(S0, np.float32), -1, -2)))
+            bufs.ckpt.copy_(torch.from_numpy(LC.to_device_bytes(layer, fmt, enc)).cuda())
         if rc:
             rs.rs_requant_read_copy(layer, bufs)
     return load
 
 
-@pytest.mark.parametrize("rc", [rs.RS_NONE, rs.RS_NVFP4])
+@pytest.mark.parametrize("ckpt,rc", DELTA_FORMATS)
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("shape", DELTA_CASES)
-def test_delta_decode_under_poison(shape, gate, rc):
+def test_delta_decode_under_poison(shape, gate, ckpt, rc):
     base = W.TINY_GDN if gate == "scalar" else W.TINY_KDA
     w = base.with_(init_std=0.3, seed=182, **shape)
     gp = W.gdn_params(w)
     S0 = W.gdn_init_states(w, range(w.batch))
-    tw = Twin(lambda: gdn_layer(w, read_copy=rc), _delta_load(S0, rc))
+    tw = Twin(lambda: gdn_layer(w, read_copy=rc, ckpt_dtype=ckpt), _delta_load(S0, ckpt, rc))
     oshape = (w.batch, w.n_v, w.dv)
     for t in range(40):
         dtok = gdn_tok_dev(W.gdn_step(w, t, range(w.batch), gp), w.in_dtype)
@@ -167,15 +178,15 @@ def test_delta_decode_under_poison(shape, gate, rc):
         tw.call(lambda l, b, o: rs.rs_step(l, b, dtok, None, None, o[0]), oshape)
 
 
-@pytest.mark.parametrize("rc", [rs.RS_NONE, rs.RS_NVFP4])
+@pytest.mark.parametrize("ckpt,rc", DELTA_FORMATS)
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
 @pytest.mark.parametrize("shape", DELTA_CASES)
-def test_delta_spec_under_poison(shape, gate, rc):
+def test_delta_spec_under_poison(shape, gate, ckpt, rc):
     base = W.TINY_GDN if gate == "scalar" else W.TINY_KDA
     w = base.with_(init_std=0.3, seed=183, max_draft=4, **shape)
     gp = W.gdn_params(w)
     S0 = W.gdn_init_states(w, range(w.batch))
-    tw = Twin(lambda: gdn_layer(w, read_copy=rc), _delta_load(S0, rc))
+    tw = Twin(lambda: gdn_layer(w, read_copy=rc, ckpt_dtype=ckpt), _delta_load(S0, ckpt, rc))
     K = 4
     for r in range(16):
         drafts = gdn_drafts_dev([W.gdn_step(w, 5000 + r * K + d, range(w.batch), gp) for d in range(K)], w.in_dtype)
