@@ -28,6 +28,7 @@
 
 #include "rs_device.h"
 #include "rs_tile.h"
+#include "rs_mtile.h"
 #include "rs_internal.h"
 
 namespace rs {
@@ -40,6 +41,21 @@ namespace {
 // length-dk dots of the other slices.
 template <int NV>
 constexpr int gdn_slices() { return NV >= 128 ? 2 : 1; }
+
+// Columns that one flush or commit-fold workgroup folds: its own slice, or for
+// an FP8 checkpoint the whole state (one scale spans the matrix, and its amax
+// needs every folded column in one workgroup).
+template <int NV, int CKF>
+constexpr int gdn_fold_cols() { return CKF == FMT_FP8 ? NV : NV / gdn_slices<NV>(); }
+
+// The state tile a fold holds. Column slices (fp32 and FP16 checkpoints) keep
+// the streaming register layout, four columns per thread and pass. A whole FP8
+// state whose sides are multiples of 64 is held in the matrix-core
+// accumulator layout instead: its rank-m update runs on v_mfma_f32_16x16x4f32
+// in fp32, and its loads and stores move 16 codes (one row's 16 consecutive
+// columns) per lane.
+template <int CKF, int NK, int NV, int NVS>
+constexpr bool gdn_mfma_fold() { return CKF == FMT_FP8 && NVS == NV && NK % 64 == 0 && NV % 64 == 0; }
 
 // VG: Kimi Delta Attention, the decay is a vector over the dk key channels
 // (a per-channel gate) instead of one scalar per head.
@@ -317,6 +333,40 @@ struct GSliceF {
 
 template <bool RC, int CKF, int NK, int NV, int NVS>
 using ReadSlice = typename std::conditional<RC, GSliceNv<NK, NV, NVS>, GSliceF<CKF, NK, NV, NVS>>::type;
+
+template <bool MF, int CKF, int NK, int NV, int NVS>
+struct GFoldTypes {
+  using Tile = RegTile<4, NK, NVS>;
+  using Raw = GSliceF<CKF, NK, NV, NVS>;
+};
+template <int CKF, int NK, int NV, int NVS>
+struct GFoldTypes<true, CKF, NK, NV, NVS> {
+  using Tile = MTile<NK, NV>;
+  using Raw = MRaw<FMT_FP8, NK, NV>;
+};
+template <int CKF, int NK, int NV, int NVS>
+using GFoldTile = typename GFoldTypes<gdn_mfma_fold<CKF, NK, NV, NVS>(), CKF, NK, NV, NVS>::Tile;
+template <int CKF, int NK, int NV, int NVS>
+using GFoldRaw = typename GFoldTypes<gdn_mfma_fold<CKF, NK, NV, NVS>(), CKF, NK, NV, NVS>::Raw;
+
+// The fold's loads and output matvec on either layout: issue the checkpoint's
+// columns c0.., and the matvec against the two weight rows.
+template <int CKF, int NK, int NV, int NVS>
+__device__ __forceinline__ void fold_issue(GSliceF<CKF, NK, NV, NVS>& r, const StateBuf& sb, size_t st, int c0) {
+  r.issue(sb, st, c0);
+}
+template <int NK, int NV>
+__device__ __forceinline__ void fold_issue(MRaw<FMT_FP8, NK, NV>& r, const StateBuf& sb, size_t st, int) {
+  r.issue(sb, st);
+}
+template <int NK, int NVS>
+__device__ __forceinline__ void fold_matvec2(const RegTile<4, NK, NVS>& S, const float* w, int ws, float* red, float* out) {
+  tile_matvec<2>(S, w, ws, red, out);
+}
+template <int NK, int NV>
+__device__ __forceinline__ void fold_matvec2(const MTile<NK, NV>& S, const float* w, int ws, float* red, float* out) {
+  mtile_matvec2(S, w, ws, red, out);
+}
 
 // Stage the window's entries 0..m-1 (entry m-1 is the current token, the
 // others come from the ring): k rows, the own columns of the held entries' u
@@ -635,21 +685,19 @@ __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 // flush step: fold the len held entries and the current token, write once, o
 // ----------------------------------------------------------------------------
-// One column slice's share of a flush: the window staged for its columns, the
-// slice read, the dots, the matvec, the current row, o, and the rank-m update
-// into S. arr: count the workgroup in after the slice's loads are issued
-// (null: another call of the workgroup does).
-template <typename TIN, int CKF, int NK, int NV, bool VG>
-__device__ __forceinline__ void gdn_flush_slice(const GDNArgs& a, const GPtrs& p,
-                                                GSmem<NK, NV / gdn_slices<NV>(), VG>& s, int m, long long nck,
-                                                Arrival* arr, uint32_t* actr, int wg, int len, int nd,
-                                                RegTile<4, NK, NV / gdn_slices<NV>()>& S) {
-  constexpr int NVS = NV / gdn_slices<NV>();
+// A flush of the NVS columns c0.. of one state (a column slice, or the whole
+// state): the window staged for those columns, the checkpoint's columns read,
+// the dots, the matvec, the current row, o, and the rank-m update into S. The
+// workgroup counts in through arr once its loads are issued.
+template <typename TIN, int CKF, int NK, int NV, int NVS, bool VG>
+__device__ __forceinline__ void gdn_flush_cols(const GDNArgs& a, const GPtrs& p, GSmem<NK, NVS, VG>& s, int m,
+                                               long long nck, Arrival& arr, uint32_t* actr, int wg, int len, int nd,
+                                               GFoldTile<CKF, NK, NV, NVS>& S) {
   GStage<TIN, NK, NV, NVS, VG> stg;
   stg.load(a, p, nck, m);            // records first, then the state tile
-  GSliceF<CKF, NK, NV, NVS> raw;
-  raw.issue(a.ck, p.st, p.c0);
-  if (arr) arr->arrive(actr, wg, nck, len, nd);
+  GFoldRaw<CKF, NK, NV, NVS> raw;
+  fold_issue(raw, a.ck, p.st, p.c0);
+  arr.arrive(actr, wg, nck, len, nd);
   stg.store(s, m);
   __syncthreads();
   if constexpr (VG) {
@@ -673,7 +721,7 @@ __device__ __forceinline__ void gdn_flush_slice(const GDNArgs& a, const GPtrs& p
   float hu = 0.0f, ho = 0.0f;
   if (v < NVS) gdn_held_sums(s, m, v, hu, ho);
   raw.decode(S);
-  tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
+  fold_matvec2(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
   if (v < NVS) {
     a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, m, v, hu, ho);
     if constexpr (!VG) {
@@ -684,8 +732,12 @@ __device__ __forceinline__ void gdn_flush_slice(const GDNArgs& a, const GPtrs& p
     }
   }
   __syncthreads();
-  if constexpr (VG) {
-    // S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T (k rows decayed above)
+  // VG: S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T (k rows decayed above)
+  if constexpr (gdn_mfma_fold<CKF, NK, NV, NVS>()) {
+    if constexpr (VG) mtile_scale_rows(S, s.gv);
+    else mtile_scale(S, s.gam);
+    mtile_rank_update(S, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  } else if constexpr (VG) {
     tile_scale_rows(S, s.gv);
     tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
   } else {
@@ -693,37 +745,29 @@ __device__ __forceinline__ void gdn_flush_slice(const GDNArgs& a, const GPtrs& p
   }
 }
 
-// Store a folded state into an FP8 checkpoint with one scale from the whole
-// matrix's |max|: held by this workgroup as one tile (NS = 1), or as the two
-// column slices S0 (columns 0..) and S1 (NVS..). Barriers inside.
+// Store a whole folded state (held by this workgroup as one tile) into an FP8
+// checkpoint with one scale from its |max|. Barriers inside.
 template <int NK, int NV, bool VG>
-__device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem<NK, NV / gdn_slices<NV>(), VG>& s,
-                                              const RegTile<4, NK, NV / gdn_slices<NV>()>& S0) {
-  constexpr int NVS = NV / gdn_slices<NV>();
-  const float sc = fp8_scale_of(tile_absmax(S0, s.s4)), y = 1.0f / sc;
-  GSliceF<FMT_FP8, NK, NV, NVS>::store(a.ck, st, 0, S0, sc, y);
+__device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem<NK, NV, VG>& s,
+                                              const RegTile<4, NK, NV>& S) {
+  const float sc = fp8_scale_of(tile_absmax(S, s.s4)), y = 1.0f / sc;
+  GSliceF<FMT_FP8, NK, NV, NV>::store(a.ck, st, 0, S, sc, y);
   if (threadIdx.x == 0) a.ck.tscale[st] = sc;
 }
 template <int NK, int NV, bool VG>
-__device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem<NK, NV / gdn_slices<NV>(), VG>& s,
-                                              const RegTile<4, NK, NV / gdn_slices<NV>()>& S0,
-                                              const RegTile<4, NK, NV / gdn_slices<NV>()>& S1) {
-  constexpr int NVS = NV / gdn_slices<NV>();
-  const float amax = fmaxf(tile_absmax(S0, s.s4), tile_absmax(S1, s.s4));
-  const float sc = fp8_scale_of(amax), y = 1.0f / sc;
-  GSliceF<FMT_FP8, NK, NV, NVS>::store(a.ck, st, 0, S0, sc, y);
-  GSliceF<FMT_FP8, NK, NV, NVS>::store(a.ck, st, NVS, S1, sc, y);
-  if (threadIdx.x == 0) a.ck.tscale[st] = sc;
+__device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem<NK, NV, VG>& s,
+                                              const MTile<NK, NV>& S) {
+  mtile_store<FMT_FP8>(a.ck, st, S, s.s4);
 }
 
 // flush step: fold the len held entries and the current token, write once, o.
 // FP8 checkpoints: one scale spans the matrix, so the workgroup of the first
-// column slice folds both slices (reading both before it writes either) and
-// the second only counts in.
+// column slice folds the whole state in one pass (staged once, one matvec and
+// one rank update over every column) and the second only counts in.
 template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
-__device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
+__device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, gdn_fold_cols<NV, CKF>(), VG>& s) {
   constexpr int NS = gdn_slices<NV>();
-  constexpr int NVS = NV / NS;
+  constexpr int NF = gdn_fold_cols<NV, CKF>();
   const GPtrs p = gdn_tile<NV, NS>(a);
   rs_meta* mp = a.meta + p.b;
   const int wg = p.h * NS + p.half;
@@ -733,41 +777,39 @@ __device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, NV / 
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
   const int m = len + 1;
   Arrival arr;
-  if (errbit != 0 || (CKF == FMT_FP8 && NS == 2 && p.half == 1)) {
+  if (errbit != 0 || (NF == NV && p.half != 0)) {
     arr.arrive(actr, wg, nck, len, nd);
-  } else if constexpr (CKF == FMT_FP8 && NS == 2) {
-    RegTile<4, NK, NVS> S0, S1;
-    GPtrs p1 = p;
-    p1.half = 1;
-    p1.c0 = NVS;
-    gdn_flush_slice<TIN, CKF, NK, NV, VG>(a, p, s, m, nck, &arr, actr, wg, len, nd, S0);
-    __syncthreads();   // the second slice's staging reuses the LDS
-    gdn_flush_slice<TIN, CKF, NK, NV, VG>(a, p1, s, m, nck, nullptr, actr, wg, len, nd, S1);
-    gdn_store_fp8<NK, NV, VG>(a, p.st, s, S0, S1);
   } else {
-    RegTile<4, NK, NVS> S;
-    gdn_flush_slice<TIN, CKF, NK, NV, VG>(a, p, s, m, nck, &arr, actr, wg, len, nd, S);
-    if constexpr (CKF == FMT_FP8) gdn_store_fp8<NK, NV, VG>(a, p.st, s, S);
-    else GSliceF<CKF, NK, NV, NVS>::store(a.ck, p.st, p.c0, S);
+    // (a whole-state fold runs in the slice-0 workgroup, whose columns start at 0)
+    GFoldTile<CKF, NK, NV, NF> S;
+    gdn_flush_cols<TIN, CKF, NK, NV, NF, VG>(a, p, s, m, nck, arr, actr, wg, len, nd, S);
+    if constexpr (CKF == FMT_FP8) gdn_store_fp8(a, p.st, s, S);
+    else GSliceF<CKF, NK, NV, NF>::store(a.ck, p.st, p.c0, S);
   }
   arr.finish(mp, actr, wg, a.nv * NS, MetaOp::Flush, 0, nck, len, nd);
 }
 
 template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
-  __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
+  __shared__ GSmem<NK, gdn_fold_cols<NV, CKF>(), VG> s;
   gdn_flush_body<TIN, NK, NV, VG, CKF>(a, s);
 }
+
+template <int NK, int NV, bool VG, int CKF>
+union GAutoSmem {
+  GSmem<NK, NV / gdn_slices<NV>(), VG> nf;
+  GSmem<NK, gdn_fold_cols<NV, CKF>(), VG> fl;
+};
 
 // self-scheduling step (continuous batching): a sequence whose buffer is full
 // takes the flush, every other one a non-flush step, in one launch (the branch
 // is uniform per workgroup)
 template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_auto_kernel(GDNArgs a) {
-  __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
+  __shared__ GAutoSmem<NK, NV, VG, CKF> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
-  if (a.meta[p.b].len == kRing - 1) gdn_flush_body<TIN, NK, NV, VG, CKF>(a, s);
-  else gdn_nonflush_body<TIN, NK, NV, VG, false, CKF>(a, s);
+  if (a.meta[p.b].len == kRing - 1) gdn_flush_body<TIN, NK, NV, VG, CKF>(a, s.fl);
+  else gdn_nonflush_body<TIN, NK, NV, VG, false, CKF>(a, s.nf);
 }
 
 // ----------------------------------------------------------------------------
@@ -1641,13 +1683,12 @@ __global__ __launch_bounds__(kThreads) void gdn_requant_kernel(GDNArgs a, int fo
 // ----------------------------------------------------------------------------
 // speculative commit: the fold of the committed entries
 // ----------------------------------------------------------------------------
-// One column slice (columns c0..) of a commit fold of state st over its m
-// committed entries, into S (the checkpoint's slice read first).
-template <typename TIN, int CKF, int NK, int NV, bool VG>
-__device__ __forceinline__ void gdn_commit_slice(const GDNArgs& a, const FoldItem& it, int h, int c0,
-                                                 GSmem<NK, NV / gdn_slices<NV>(), VG>& s,
-                                                 RegTile<4, NK, NV / gdn_slices<NV>()>& S) {
-  constexpr int NVS = NV / gdn_slices<NV>();
+// The NVS columns c0.. (a column slice, or the whole state) of a commit fold
+// of state st over its m committed entries, into S (the checkpoint's columns
+// read first).
+template <typename TIN, int CKF, int NK, int NV, int NVS, bool VG>
+__device__ __forceinline__ void gdn_commit_cols(const GDNArgs& a, const FoldItem& it, int h, int c0,
+                                                GSmem<NK, NVS, VG>& s, GFoldTile<CKF, NK, NV, NVS>& S) {
   constexpr int VK = 16 / static_cast<int>(sizeof(TIN));
   constexpr int CK = (kRing * NK / VK + kThreads - 1) / kThreads;
   constexpr int CU = (kRing * NVS / 4 + kThreads - 1) / kThreads;
@@ -1671,8 +1712,8 @@ __device__ __forceinline__ void gdn_commit_slice(const GDNArgs& a, const FoldIte
     const int e = static_cast<int>(threadIdx.x) < m ? static_cast<int>(threadIdx.x) : m - 1;
     gv = static_cast<const float*>(a.rg)[st * kRing + slot_of(it.nck, e)];
   }
-  GSliceF<CKF, NK, NV, NVS> raw;
-  raw.issue(a.ck, st, c0);
+  GFoldRaw<CKF, NK, NV, NVS> raw;
+  fold_issue(raw, a.ck, st, c0);
   ck.to_lds(&s.K[0][0], NK, m, NK);
   cu.to_lds(&s.U[0][0], NVS, m, NVS);
   if constexpr (!VG)
@@ -1712,7 +1753,11 @@ __device__ __forceinline__ void gdn_commit_slice(const GDNArgs& a, const FoldIte
   }
   __syncthreads();
   raw.decode(S);
-  if constexpr (VG) {
+  if constexpr (gdn_mfma_fold<CKF, NK, NV, NVS>()) {
+    if constexpr (VG) mtile_scale_rows(S, s.gv);
+    else mtile_scale(S, s.gam);
+    mtile_rank_update(S, &s.K[0][0], NK, &s.U[0][0], NVS, m);
+  } else if constexpr (VG) {
     tile_scale_rows(S, s.gv);
     tile_rank_update(S, 1.0f, &s.K[0][0], NK, &s.U[0][0], NVS, m);
   } else {
@@ -1725,12 +1770,12 @@ __device__ __forceinline__ void gdn_commit_slice(const GDNArgs& a, const FoldIte
 // entries (u rows from the ring), one column slice per work item, over a
 // fixed grid (every workgroup leaves when the list is done). VG (KDA):
 // S <- S0 Diag(gamma_m) + sum_i u_i (r_{m,i} * k_i)^T with per-channel decays.
-// FP8 checkpoints: the first slice's item folds both slices (one scale spans
-// the matrix), the second has nothing to do.
+// FP8 checkpoints: one item per state, folding every column (one scale spans
+// the matrix).
 template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
-  constexpr int NS = gdn_slices<NV>();
-  constexpr int NVS = NV / NS;
+  constexpr int NVS = gdn_fold_cols<NV, CKF>();
+  constexpr int NS = NV / NVS;
   static_assert(!VG || NK <= kThreads, "one thread per key channel");
   __shared__ GSmem<NK, NVS, VG> s;
   const int per = a.nv * NS;
@@ -1740,23 +1785,10 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_fold_kernel(GDNArgs a) {
     const int r = item - (item / per) * per;
     const int h = r / NS, half = r - h * NS;
     const size_t st = static_cast<size_t>(it.b) * a.nv + h;
-    if constexpr (CKF == FMT_FP8) {
-      if (half != 0) continue;   // uniform over the workgroup
-      RegTile<4, NK, NVS> S0;
-      gdn_commit_slice<TIN, CKF, NK, NV, VG>(a, it, h, 0, s, S0);
-      if constexpr (NS == 2) {
-        RegTile<4, NK, NVS> S1;
-        __syncthreads();   // the second slice's staging reuses the LDS
-        gdn_commit_slice<TIN, CKF, NK, NV, VG>(a, it, h, NVS, s, S1);
-        gdn_store_fp8<NK, NV, VG>(a, st, s, S0, S1);
-      } else {
-        gdn_store_fp8<NK, NV, VG>(a, st, s, S0);
-      }
-    } else {
-      RegTile<4, NK, NVS> S;
-      gdn_commit_slice<TIN, CKF, NK, NV, VG>(a, it, h, half * NVS, s, S);
-      GSliceF<CKF, NK, NV, NVS>::store(a.ck, st, half * NVS, S);
-    }
+    GFoldTile<CKF, NK, NV, NVS> S;
+    gdn_commit_cols<TIN, CKF, NK, NV, NVS, VG>(a, it, h, half * NVS, s, S);
+    if constexpr (CKF == FMT_FP8) gdn_store_fp8(a, st, s, S);
+    else GSliceF<CKF, NK, NV, NVS>::store(a.ck, st, half * NVS, S);
     __syncthreads();
   }
 }

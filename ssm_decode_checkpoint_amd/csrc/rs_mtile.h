@@ -284,6 +284,66 @@ __device__ __forceinline__ void mtile_matvec(const MTile<NR, NC>& M, const float
   __syncthreads();
 }
 
+// out[j][p] = sum_n M[n][p] w[j ws + n] for the two weight rows j = 0, 1 (w:
+// LDS; out: 2 NC floats of LDS; red: 8 NC floats of LDS scratch). Barriers
+// inside; all threads must call.
+template <int NR, int NC>
+__device__ __forceinline__ void mtile_matvec2(const MTile<NR, NC>& M, const float* w, int ws, float* red, float* out) {
+  using T = MTile<NR, NC>;
+  float wr[2][T::RB];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < T::RB; ++r) wr[j][r] = w[j * ws + T::row(r)];
+  const int wave = static_cast<int>(threadIdx.x >> 6), ln = static_cast<int>(threadIdx.x & 15);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < T::CG; ++q) {
+      float part[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int r = 0; r < T::RB; ++r) acc += M.at(r, q, k) * wr[j][r];
+        part[k] = acc;
+      }
+      red[(wave * 2 + j) * NC + T::col(q) + ln] = row_transpose_sum16(part);
+    }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 2 * NC; idx += kThreads) {
+    const int j = idx / NC, c = idx - j * NC;
+    out[idx] = (red[j * NC + c] + red[(2 + j) * NC + c]) + (red[(4 + j) * NC + c] + red[(6 + j) * NC + c]);
+  }
+  __syncthreads();
+}
+
+// M <- M Diag-on-rows(f): row n times f[n] (f: NR floats of LDS).
+template <int NR, int NC>
+__device__ __forceinline__ void mtile_scale_rows(MTile<NR, NC>& M, const float* f) {
+  using T = MTile<NR, NC>;
+#pragma unroll
+  for (int r = 0; r < T::RB; ++r) {
+    const float x = f[T::row(r)];
+#pragma unroll
+    for (int q = 0; q < T::CG; ++q)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) M.v[r][q][b] *= x;
+  }
+}
+
+// M <- L M.
+template <int NR, int NC>
+__device__ __forceinline__ void mtile_scale(MTile<NR, NC>& M, float L) {
+  using T = MTile<NR, NC>;
+#pragma unroll
+  for (int r = 0; r < T::RB; ++r)
+#pragma unroll
+    for (int q = 0; q < T::CG; ++q)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) M.v[r][q][b] *= L;
+}
+
 // Workgroup max of |M|, in every thread. Barriers inside.
 template <int NR, int NC>
 __device__ __forceinline__ float mtile_absmax(const MTile<NR, NC>& M, float* scratch4) {
