@@ -47,6 +47,11 @@ constexpr int gdn_slices() { return NV >= 128 ? 2 : 1; }
 // needs every folded column in one workgroup).
 template <int NV, int CKF>
 constexpr int gdn_fold_cols() { return CKF == FMT_FP8 ? NV : NV / gdn_slices<NV>(); }
+// Workgroups per state of the flush kernel: one per folded column range. (The
+// self-scheduling kernel keeps the non-flush step's slices; there the other
+// slices' workgroups of an FP8 flush only count in.)
+template <int NV, int CKF>
+constexpr int gdn_flush_slices() { return NV / gdn_fold_cols<NV, CKF>(); }
 
 // The state tile a fold holds. Column slices (fp32 and FP16 checkpoints) keep
 // the streaming register layout, four columns per thread and pass. A whole FP8
@@ -761,12 +766,13 @@ __device__ __forceinline__ void gdn_store_fp8(const GDNArgs& a, size_t st, GSmem
 }
 
 // flush step: fold the len held entries and the current token, write once, o.
-// FP8 checkpoints: one scale spans the matrix, so the workgroup of the first
-// column slice folds the whole state in one pass (staged once, one matvec and
-// one rank update over every column) and the second only counts in.
-template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
+// FP8 checkpoints: one scale spans the matrix, so one workgroup folds the whole
+// state in one pass (staged once, one matvec and one rank update over every
+// column). NS: workgroups per state in the launch; where it exceeds the
+// folding ones (an FP8 flush inside the self-scheduling step), the others only
+// count in.
+template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32, int NS = gdn_slices<NV>()>
 __device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, gdn_fold_cols<NV, CKF>(), VG>& s) {
-  constexpr int NS = gdn_slices<NV>();
   constexpr int NF = gdn_fold_cols<NV, CKF>();
   const GPtrs p = gdn_tile<NV, NS>(a);
   rs_meta* mp = a.meta + p.b;
@@ -792,7 +798,7 @@ __device__ __forceinline__ void gdn_flush_body(const GDNArgs& a, GSmem<NK, gdn_f
 template <typename TIN, int NK, int NV, bool VG, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_flush_kernel(GDNArgs a) {
   __shared__ GSmem<NK, gdn_fold_cols<NV, CKF>(), VG> s;
-  gdn_flush_body<TIN, NK, NV, VG, CKF>(a, s);
+  gdn_flush_body<TIN, NK, NV, VG, CKF, gdn_flush_slices<NV, CKF>()>(a, s);
 }
 
 template <int NK, int NV, bool VG, int CKF>
@@ -1993,8 +1999,11 @@ void gdn_launch_kind(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
 template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   // replay steps and appends: one workgroup per column slice of each state
-  if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
-      op == GDNOp::ConvSpec)
+  // (the flush of an FP8 checkpoint: one per state)
+  if (op == GDNOp::Flush && !l.rc && l.ckf == FMT_FP8)
+    l.grid *= gdn_flush_slices<NV, FMT_FP8>();
+  else if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
+           op == GDNOp::ConvSpec)
     l.grid *= gdn_slices<NV>();
   if (l.rc) {   // the read copy sits beside an fp32 checkpoint
     if (l.vg) gdn_launch_kind<NK, NV, true, true, FMT_F32>(op, a, l, st);
