@@ -1382,22 +1382,25 @@ void gdn_spec_append_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 namespace {
 
-template <int NK, int NVS, bool VG>
+// NVS: the columns of one matvec; NU: the columns held (NU = 2 NVS when one
+// workgroup folds a whole state as two 64-column halves).
+template <int NK, int NVS, bool VG, int NU = NVS>
 struct alignas(16) GRcSmem {
+  static constexpr bool kWtInRed = NVS == 64 && NU == NVS;   // the matvec reads its rows once
   alignas(16) float K[kRing][NK];            // k rows of entries 0..m-1 (VG: then times r_{m-1,i})
   alignas(16) float q[NK];                   // flush: q of the current token
-  float U[kRing][NVS];                       // v rows, then the solved rows u (own columns)
+  float U[kRing][NU];                        // v rows, then the solved rows u (own columns)
   // matvec scratch (the matrix-core matvec adds in two steps), and over its
   // start the result: each output element is written by the thread that last
   // reads the scratch at that index
   union {
     alignas(16) float red[(NVS == 64 ? 2 : 4) * kRing * NVS];
     alignas(16) float out[kRing][NVS];       // S0 times the matvec rows
-    alignas(16) float Wt[VG && NVS == 64 ? kRing : 1][NK];   // VG: matvec rows gamma_t * k_t, until the matvec reads them
+    alignas(16) float Wt[VG && kWtInRed ? kRing : 1][NK];   // VG: matvec rows gamma_t * k_t, until the matvec reads them
   };
-  alignas(16) float Wt2[VG && NVS != 64 ? kRing : 1][NK];  // VG, other slice widths: the rows apart
+  alignas(16) float Wt2[VG && !kWtInRed ? kRing : 1][NK];  // VG, otherwise: the rows apart
   __device__ __forceinline__ float* wt() {
-    if constexpr (NVS == 64) return &Wt[0][0];
+    if constexpr (kWtInRed) return &Wt[0][0];
     else return &Wt2[0][0];
   }
   float kk[kRing][kRing];                    // L_{t,i}, i < t
@@ -1458,8 +1461,8 @@ struct GRcStage {
 
 // After the staging is visible: gates, the matvec rows and L. Rows past m are
 // zeroed (the matvec takes all 16). Barrier at the end.
-template <int NK, int NVS, bool VG>
-__device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG>& s, int m) {
+template <int NK, int NVS, bool VG, int NU>
+__device__ __forceinline__ void rc_gates_and_gram(GRcSmem<NK, NVS, VG, NU>& s, int m) {
   if constexpr (VG) {
     // alpha per entry and channel, then gamma_t * k_t (direct products in entry order)
     for (int idx = threadIdx.x; idx < m * NK; idx += kThreads) (&s.A[0][0])[idx] = kda_alpha((&s.A[0][0])[idx]);
@@ -1578,12 +1581,63 @@ __device__ __forceinline__ void rc_solve_and_fold(RegTile<4, NK, NVS>& S, GRcSme
   }
 }
 
+// A whole state held as two 64-column halves: S0 times the matvec rows for the
+// half of columns c0.. and the forward substitution of those columns (as in
+// rc_solve_and_fold). The weight rows stay in LDS for the other half.
+// Barriers inside; all threads call.
+template <int NK, int NU, bool VG>
+__device__ __forceinline__ void rc_solve_half(const RegTile<4, NK, 64>& S, GRcSmem<NK, 64, VG, NU>& s, int m,
+                                              int c0) {
+  const float* W = VG ? s.wt() : &s.K[0][0];
+  tile_matvec_mfma<kRing, NK, 64, true, false>(S, W, NK, s.red, &s.out[0][0]);
+  for (int v = threadIdx.x; v < 64; v += kThreads) {
+    float ur[kRing];
+#pragma unroll
+    for (int t = 0; t < kRing; ++t) {
+      if (t < m) {
+        float u = VG ? s.bt[t] * (s.U[t][c0 + v] - s.out[t][v])
+                     : s.bt[t] * (s.U[t][c0 + v] - s.gam[t] * s.out[t][v]);
+#pragma unroll
+        for (int i = 0; i < t; ++i) u -= s.kk[t][i] * ur[i];
+        ur[t] = u;
+        s.U[t][c0 + v] = VG ? u : u * s.rr[t];
+      }
+    }
+  }
+  __syncthreads();   // out read before the scratch is reused
+}
+
+// NVFP4 codes and block scales of the 64 columns c0.. of state st held as
+// RegTile<4, NK, 64>, under the tensor scale ts of the whole matrix: the bytes
+// the whole-matrix quantizer writes for those columns (its blocks are the same
+// four threads' 16 columns of one row).
+template <int NK, int NV>
+__device__ __forceinline__ void rc_store_nvfp4_half(const StateBuf& sb, size_t st, int c0, const RegTile<4, NK, 64>& M,
+                                                    float ts) {
+  using TM = TileMap<4, NK, 64>;
+  const int c = static_cast<int>(threadIdx.x % TM::TPR);
+  uint8_t* base = static_cast<uint8_t*>(sb.data) + st * NK * NV / 2;
+  uint8_t* sbase = sb.nv_scale + st * NK * NV / 16;
+#pragma unroll
+  for (int k = 0; k < TM::PASSES; ++k) {
+    const int row = RegTile<4, NK, 64>::row(k);
+    const uint32_t sc = nvfp4_block_code<4>(M.v[k], ts);
+    const uint32_t w = nvfp4_codes4(M.v[k], e4m3_value(sc) * ts);
+    if (row < NK) {
+      const int e = row * NV + c0 + 4 * c;
+      *reinterpret_cast<uint16_t*>(base + e / 2) = static_cast<uint16_t>(w);
+      if ((c & 3) == 0) sbase[e / 16] = static_cast<uint8_t>(sc);
+    }
+  }
+}
+
 }  // namespace
 
 // flush step with a read copy: the rows of the len held entries and the
-// current token re-solved from the checkpoint, the fold, one write, o = S q
-// (the read copy is refreshed by the requant that follows)
-template <typename TIN, int NK, int NV, bool VG>
+// current token re-solved from the checkpoint, the fold, one write, o = S q.
+// COPY (a whole state per workgroup): the NVFP4 read copy of the new state is
+// written from the same registers; otherwise a requant that follows refreshes it.
+template <typename TIN, int NK, int NV, bool VG, bool COPY = false>
 __device__ __forceinline__ void gdn_flush_rc_body(const GDNArgs& a, GRcSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
   constexpr int NVS = NV / gdn_slices<NV>();
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
@@ -1613,14 +1667,100 @@ __device__ __forceinline__ void gdn_flush_rc_body(const GDNArgs& a, GRcSmem<NK, 
     GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
     tile_matvec<1>(S, s.q, NK, s.red, &s.out[0][0]);   // o = S_m q (barriers inside)
     for (int v = threadIdx.x; v < NVS; v += kThreads) a.o[p.st * NV + p.c0 + v] = s.out[0][v];
+    if constexpr (COPY) {
+      static_assert(NVS == NV, "the copy needs the whole state");
+      tile_store_nvfp4(a.rc, p.st, S, tile_absmax(S, s.s4));
+    }
   }
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
 }
 
+// The same flush for a state of two 64-column halves, in one workgroup per
+// state: the entries staged once, each half's rows re-solved against its own
+// columns, both halves folded and written, and the NVFP4 read copy of the new
+// state from the same registers under one tensor scale.
+template <typename TIN, int NK, int NV, bool VG>
+__device__ __forceinline__ void gdn_flush_rc_whole_body(const GDNArgs& a, GRcSmem<NK, 64, VG, NV>& s) {
+  static_assert(NV == 128, "two 64-column halves");
+  const GPtrs p = gdn_tile<NV, 1>(a);
+  rs_meta* mp = a.meta + p.b;
+  const int wg = p.h;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv) * kArriveStride;
+  const int len = mp->len, nd = mp->nd;
+  const long long nck = mp->n_ckpt;
+  const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
+  const int m = len + 1;
+  Arrival arr;
+  if (errbit != 0) {
+    arr.arrive(actr, wg, nck, len, nd);
+  } else {
+    float* ck = static_cast<float*>(a.ck.data);
+    GRcStage<TIN, NK, NV, NV, VG> stg;
+    stg.load(a, p.st, p.b, p.kh, 0, nck, len, true);   // records first, then the state
+    GSlice<NK, NV, 64> raw[2];
+    raw[0].issue(ck, p.st, 0);
+    raw[1].issue(ck, p.st, 64);
+    arr.arrive(actr, wg, nck, len, nd);
+    stg.store(s, m, true);
+    __syncthreads();
+    rc_gates_and_gram(s, m);
+    RegTile<4, NK, 64> S[2];
+    raw[0].decode(S[0]);
+    raw[1].decode(S[1]);
+    rc_solve_half(S[0], s, m, 0);
+    rc_solve_half(S[1], s, m, 64);
+    if constexpr (VG) {
+      // fold rows r_{m-1,i} * k_i (descending direct products)
+      for (int c = threadIdx.x; c < NK; c += kThreads) {
+        float acc = 1.0f;
+        for (int i = m - 1; i >= 0; --i) {
+          s.K[i][c] *= acc;
+          acc *= s.A[i][c];
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (VG) {
+        tile_scale_rows(S[h], s.gv);
+        tile_rank_update(S[h], 1.0f, &s.K[0][0], NK, &s.U[0][64 * h], NV, m);
+      } else {
+        tile_rank_update(S[h], s.gam[m - 1], &s.K[0][0], NK, &s.U[0][64 * h], NV, m);
+      }
+      GSlice<NK, NV, 64>::store(ck, p.st, 64 * h, S[h]);
+    }
+    tiles_matvec<2>(S, s.q, s.red, &s.out[0][0]);   // o = S_m q: out[h][v] for column 64 h + v
+    for (int v = threadIdx.x; v < NV; v += kThreads) a.o[p.st * NV + v] = (&s.out[0][0])[v];
+    // the read copy: one tensor scale from both halves' |max|
+    float mx = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int k = 0; k < RegTile<4, NK, 64>::P; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(S[h].v[k][i]));
+    mx = wave_max(mx);
+    if ((threadIdx.x & 63) == 0) s.s4[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    const float ts = nvfp4_tscale_of(fmaxf(fmaxf(s.s4[0], s.s4[1]), fmaxf(s.s4[2], s.s4[3])));
+    rc_store_nvfp4_half<NK, NV>(a.rc, p.st, 0, S[0], ts);
+    rc_store_nvfp4_half<NK, NV>(a.rc, p.st, 64, S[1], ts);
+    if (threadIdx.x == 0) a.rc.tscale[p.st] = ts;
+  }
+  arr.finish(mp, actr, wg, a.nv, MetaOp::Flush, 0, nck, len, nd);
+}
+
+// One workgroup per state, the read copy written in the same launch.
 template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_flush_rc_kernel(GDNArgs a) {
-  __shared__ GRcSmem<NK, NV / gdn_slices<NV>(), VG> s;
-  gdn_flush_rc_body<TIN, NK, NV, VG>(a, s);
+  if constexpr (gdn_slices<NV>() == 1) {
+    __shared__ GRcSmem<NK, NV, VG> s;
+    gdn_flush_rc_body<TIN, NK, NV, VG, true>(a, s);
+  } else {
+    __shared__ GRcSmem<NK, 64, VG, NV> s;
+    gdn_flush_rc_whole_body<TIN, NK, NV, VG>(a, s);
+  }
 }
 
 template <int NK, int NV, bool VG>
@@ -1999,9 +2139,9 @@ void gdn_launch_kind(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
 template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   // replay steps and appends: one workgroup per column slice of each state
-  // (the flush of an FP8 checkpoint: one per state)
-  if (op == GDNOp::Flush && !l.rc && l.ckf == FMT_FP8)
-    l.grid *= gdn_flush_slices<NV, FMT_FP8>();
+  // (the flush of an FP8 checkpoint or with a read copy: one per state)
+  if (op == GDNOp::Flush && (l.rc || l.ckf == FMT_FP8))
+    l.grid *= 1;
   else if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
            op == GDNOp::ConvSpec)
     l.grid *= gdn_slices<NV>();

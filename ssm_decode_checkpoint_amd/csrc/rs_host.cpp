@@ -233,8 +233,9 @@ GDNLaunch gdn_launch_cfg(const rs_layer* L) {
   return l;
 }
 
-// With a read copy, a launch that may fold (flush, self-scheduling step,
-// commit) is followed by the requant of the states it folded.
+// With a read copy, a launch that may fold without writing the copy
+// (self-scheduling step, commit) is followed by the requant of the states it
+// folded.
 rs_status gdn_refresh_copy(const rs_layer* L, const GDNArgs& a, void* st) {
   if (L->cfg.read_copy != RS_NVFP4) return RS_OK;
   if (rs_status s = launch_status()) return s;
@@ -378,7 +379,8 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(kind == StepKind::Flush ? GDNOp::Flush : kind == StepKind::Auto ? GDNOp::Auto : GDNOp::NonFlush, a,
                gdn_launch_cfg(L), st);
-    if (kind != StepKind::NonFlush)
+    // (the flush writes the read copy itself; the self-scheduling step is followed by the requant)
+    if (kind == StepKind::Auto)
       if (rs_status s = gdn_refresh_copy(L, a, st)) return s;
     return launched();
   }

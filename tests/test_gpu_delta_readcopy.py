@@ -112,7 +112,7 @@ class Synced:
 
 
 @pytest.mark.parametrize("gate", ["scalar", "channel"])
-@pytest.mark.parametrize("shape", SHAPES[:2])
+@pytest.mark.parametrize("shape", SHAPES)
 def test_decode_reads_the_copy(shape, gate):
     base, rule = (W.TINY_GDN, gdn) if gate == "scalar" else (W.TINY_KDA, kda)
     w = base.with_(init_std=0.4, seed=310, **shape)
