@@ -252,8 +252,9 @@ int main(void) {
     SNAP(b8); expect_call(rs_step_nonflush(&G, &gb, &nb, NULL, y, NULL), RS_E_ARG, NULL, b8, "missing beta");
   }
 
-  /* ---- Gated DeltaNet and KDA with the NVFP4 read copy: a launch that can
-   * fold is followed by the copy's requant ---- */
+  /* ---- Gated DeltaNet and KDA with the NVFP4 read copy: the flush writes the
+   * copy itself; the self-scheduling step and the commit, which can fold, are
+   * followed by the copy's requant ---- */
   {
     const int GD2[STUB_KINDS] = {0, 2, 0, 0, 0, 0, 0, 0};
     const int GDC2[STUB_KINDS] = {0, 2, 1, 0, 0, 0, 0, 0};
@@ -268,7 +269,7 @@ int main(void) {
       memset(&gi, 0, sizeof gi);
       gi.q = dev(74); gi.k = dev(75); gi.v = dev(76); gi.g = dev(77); gi.beta = dev(78);
       SNAP(b); expect_call(rs_step_nonflush(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD, b, "non-flush reads the copy");
-      SNAP(b2); expect_call(rs_step_flush(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD2, b2, "flush, then requant");
+      SNAP(b2); expect_call(rs_step_flush(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD, b2, "flush writes the copy");
       SNAP(b3); expect_call(rs_step(&G, &gb, &gi, NULL, y, NULL), RS_OK, GD2, b3, "self-scheduling step, then requant");
       SNAP(b4); expect_call(rs_spec_append(&G, &gb, &gi, 4, NULL, y, NULL), RS_OK, GD, b4, "append reads the copy");
       SNAP(b5); expect_call(rs_spec_commit(&G, &gb, acc, NULL, NULL), RS_OK, GDC2, b5, "commit, fold, requant");
