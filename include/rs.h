@@ -159,10 +159,11 @@ typedef struct rs_config {
                             replay mode without a read copy on 16 x 16 and 128 x 128
                             states (RS_E_UNSUPPORTED on 64 x 64) */
   int32_t read_copy;     /* RS_NONE | RS_NVFP4 (replay mode). Gated DeltaNet and KDA:
-                            with an RS_F32 checkpoint; every fold rewrites the copy of the
-                            sequences it folded in a second launch on the same stream
-                            (one tensor scale spans the whole matrix, which the fold
-                            writes in slices), whatever fuse_requant says */
+                            with an RS_F32 checkpoint; the flush and the commit fold
+                            rewrite the copy of the states they fold in the same launch;
+                            rs_step rewrites it in a second launch on the same stream
+                            (its flushes fold in column slices); whatever fuse_requant
+                            says */
   int32_t fuse_requant;  /* Mamba-2: 1: flush and commit-fold rewrite the read copy in
                             their epilogue; 0: the caller calls rs_requant_read_copy */
 } rs_config;

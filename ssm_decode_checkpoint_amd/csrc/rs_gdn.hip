@@ -1635,10 +1635,11 @@ __device__ __forceinline__ void rc_store_nvfp4_half(const StateBuf& sb, size_t s
 
 // flush step with a read copy: the rows of the len held entries and the
 // current token re-solved from the checkpoint, the fold, one write, o = S q.
-// COPY (a whole state per workgroup): the NVFP4 read copy of the new state is
-// written from the same registers; otherwise a requant that follows refreshes it.
-template <typename TIN, int NK, int NV, bool VG, bool COPY = false>
+// COPY (states held whole, one workgroup per state): the NVFP4 read copy of the
+// new state from the same registers; otherwise a requant launch follows.
+template <typename TIN, int NK, int NV, bool VG, bool COPY>
 __device__ __forceinline__ void gdn_flush_rc_body(const GDNArgs& a, GRcSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
+  static_assert(!COPY || gdn_slices<NV>() == 1, "the copy needs the whole state");
   constexpr int NVS = NV / gdn_slices<NV>();
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
   rs_meta* mp = a.meta + p.b;
@@ -1667,88 +1668,105 @@ __device__ __forceinline__ void gdn_flush_rc_body(const GDNArgs& a, GRcSmem<NK, 
     GSlice<NK, NV, NVS>::store(ck, p.st, p.c0, S);
     tile_matvec<1>(S, s.q, NK, s.red, &s.out[0][0]);   // o = S_m q (barriers inside)
     for (int v = threadIdx.x; v < NVS; v += kThreads) a.o[p.st * NV + p.c0 + v] = s.out[0][v];
-    if constexpr (COPY) {
-      static_assert(NVS == NV, "the copy needs the whole state");
-      tile_store_nvfp4(a.rc, p.st, S, tile_absmax(S, s.s4));
-    }
+    if constexpr (COPY) tile_store_nvfp4(a.rc, p.st, S, tile_absmax(S, s.s4));
   }
   arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::Flush, 0, nck, len, nd);
 }
 
-// The same flush for a state of two 64-column halves, in one workgroup per
-// state: the entries staged once, each half's rows re-solved against its own
-// columns, both halves folded and written, and the NVFP4 read copy of the new
-// state from the same registers under one tensor scale.
-template <typename TIN, int NK, int NV, bool VG>
-__device__ __forceinline__ void gdn_flush_rc_whole_body(const GDNArgs& a, GRcSmem<NK, 64, VG, NV>& s) {
+// A whole state of two 64-column halves folded with a read copy by one
+// workgroup: the entries staged once (held entries, and with cur the current
+// token), each half's rows re-solved against its own columns, both halves
+// folded into S and written to the checkpoint. counted_in() runs between the
+// loads and the staging (a step counts its workgroup in there). Barriers inside.
+template <typename TIN, int NK, int NV, bool VG, typename F>
+__device__ __forceinline__ void rc_fold_whole(const GDNArgs& a, GRcSmem<NK, 64, VG, NV>& s, size_t st, int b, int kh,
+                                              long long nck, int held, bool cur, RegTile<4, NK, 64> (&S)[2],
+                                              F counted_in) {
   static_assert(NV == 128, "two 64-column halves");
-  const GPtrs p = gdn_tile<NV, 1>(a);
+  const int m = held + (cur ? 1 : 0);
+  float* ck = static_cast<float*>(a.ck.data);
+  GRcStage<TIN, NK, NV, NV, VG> stg;
+  stg.load(a, st, b, kh, 0, nck, held, cur);   // records first, then the state
+  GSlice<NK, NV, 64> raw[2];
+  raw[0].issue(ck, st, 0);
+  raw[1].issue(ck, st, 64);
+  counted_in();
+  stg.store(s, m, cur);
+  __syncthreads();
+  rc_gates_and_gram(s, m);
+  raw[0].decode(S[0]);
+  raw[1].decode(S[1]);
+  rc_solve_half(S[0], s, m, 0);
+  rc_solve_half(S[1], s, m, 64);
+  if constexpr (VG) {
+    // fold rows r_{m-1,i} * k_i (descending direct products)
+    for (int c = threadIdx.x; c < NK; c += kThreads) {
+      float acc = 1.0f;
+      for (int i = m - 1; i >= 0; --i) {
+        s.K[i][c] *= acc;
+        acc *= s.A[i][c];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if constexpr (VG) {
+      tile_scale_rows(S[h], s.gv);
+      tile_rank_update(S[h], 1.0f, &s.K[0][0], NK, &s.U[0][64 * h], NV, m);
+    } else {
+      tile_rank_update(S[h], s.gam[m - 1], &s.K[0][0], NK, &s.U[0][64 * h], NV, m);
+    }
+    GSlice<NK, NV, 64>::store(ck, st, 64 * h, S[h]);
+  }
+}
+
+// The NVFP4 read copy of a whole state held as two 64-column halves: one
+// tensor scale from both halves' |max|. Barriers inside.
+template <int NK, int NV, bool VG>
+__device__ __forceinline__ void rc_copy_whole(const GDNArgs& a, GRcSmem<NK, 64, VG, NV>& s, size_t st,
+                                              const RegTile<4, NK, 64> (&S)[2]) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int k = 0; k < RegTile<4, NK, 64>::P; ++k)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(S[h].v[k][i]));
+  mx = wave_max(mx);
+  __syncthreads();   // earlier readers of s4 are done
+  if ((threadIdx.x & 63) == 0) s.s4[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  const float ts = nvfp4_tscale_of(fmaxf(fmaxf(s.s4[0], s.s4[1]), fmaxf(s.s4[2], s.s4[3])));
+  rc_store_nvfp4_half<NK, NV>(a.rc, st, 0, S[0], ts);
+  rc_store_nvfp4_half<NK, NV>(a.rc, st, 64, S[1], ts);
+  if (threadIdx.x == 0) a.rc.tscale[st] = ts;
+}
+
+// The read-copy flush of a state of two 64-column halves, folded by one
+// workgroup with o = S_m q and the copy written from the same registers. NS:
+// workgroups per state in the launch (any beyond the first only count in).
+template <typename TIN, int NK, int NV, bool VG, int NS>
+__device__ __forceinline__ void gdn_flush_rc_whole_body(const GDNArgs& a, GRcSmem<NK, 64, VG, NV>& s) {
+  const GPtrs p = gdn_tile<NV, NS>(a);
   rs_meta* mp = a.meta + p.b;
-  const int wg = p.h;
-  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv) * kArriveStride;
+  const int wg = p.h * NS + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * NS) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 1 ? RS_ERR_FULL : 0);
-  const int m = len + 1;
   Arrival arr;
-  if (errbit != 0) {
+  if (errbit != 0 || p.half != 0) {
     arr.arrive(actr, wg, nck, len, nd);
   } else {
-    float* ck = static_cast<float*>(a.ck.data);
-    GRcStage<TIN, NK, NV, NV, VG> stg;
-    stg.load(a, p.st, p.b, p.kh, 0, nck, len, true);   // records first, then the state
-    GSlice<NK, NV, 64> raw[2];
-    raw[0].issue(ck, p.st, 0);
-    raw[1].issue(ck, p.st, 64);
-    arr.arrive(actr, wg, nck, len, nd);
-    stg.store(s, m, true);
-    __syncthreads();
-    rc_gates_and_gram(s, m);
     RegTile<4, NK, 64> S[2];
-    raw[0].decode(S[0]);
-    raw[1].decode(S[1]);
-    rc_solve_half(S[0], s, m, 0);
-    rc_solve_half(S[1], s, m, 64);
-    if constexpr (VG) {
-      // fold rows r_{m-1,i} * k_i (descending direct products)
-      for (int c = threadIdx.x; c < NK; c += kThreads) {
-        float acc = 1.0f;
-        for (int i = m - 1; i >= 0; --i) {
-          s.K[i][c] *= acc;
-          acc *= s.A[i][c];
-        }
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if constexpr (VG) {
-        tile_scale_rows(S[h], s.gv);
-        tile_rank_update(S[h], 1.0f, &s.K[0][0], NK, &s.U[0][64 * h], NV, m);
-      } else {
-        tile_rank_update(S[h], s.gam[m - 1], &s.K[0][0], NK, &s.U[0][64 * h], NV, m);
-      }
-      GSlice<NK, NV, 64>::store(ck, p.st, 64 * h, S[h]);
-    }
+    rc_fold_whole<TIN, NK, NV, VG>(a, s, p.st, p.b, p.kh, nck, len, true, S,
+                                   [&] { arr.arrive(actr, wg, nck, len, nd); });
     tiles_matvec<2>(S, s.q, s.red, &s.out[0][0]);   // o = S_m q: out[h][v] for column 64 h + v
     for (int v = threadIdx.x; v < NV; v += kThreads) a.o[p.st * NV + v] = (&s.out[0][0])[v];
-    // the read copy: one tensor scale from both halves' |max|
-    float mx = 0.0f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int k = 0; k < RegTile<4, NK, 64>::P; ++k)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(S[h].v[k][i]));
-    mx = wave_max(mx);
-    if ((threadIdx.x & 63) == 0) s.s4[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    const float ts = nvfp4_tscale_of(fmaxf(fmaxf(s.s4[0], s.s4[1]), fmaxf(s.s4[2], s.s4[3])));
-    rc_store_nvfp4_half<NK, NV>(a.rc, p.st, 0, S[0], ts);
-    rc_store_nvfp4_half<NK, NV>(a.rc, p.st, 64, S[1], ts);
-    if (threadIdx.x == 0) a.rc.tscale[p.st] = ts;
+    rc_copy_whole(a, s, p.st, S);
   }
-  arr.finish(mp, actr, wg, a.nv, MetaOp::Flush, 0, nck, len, nd);
+  arr.finish(mp, actr, wg, a.nv * NS, MetaOp::Flush, 0, nck, len, nd);
 }
 
 // One workgroup per state, the read copy written in the same launch.
@@ -1759,9 +1777,14 @@ __global__ __launch_bounds__(kThreads) void gdn_flush_rc_kernel(GDNArgs a) {
     gdn_flush_rc_body<TIN, NK, NV, VG, true>(a, s);
   } else {
     __shared__ GRcSmem<NK, 64, VG, NV> s;
-    gdn_flush_rc_whole_body<TIN, NK, NV, VG>(a, s);
+    gdn_flush_rc_whole_body<TIN, NK, NV, VG, 1>(a, s);
   }
 }
+
+// The LDS of a read-copy flush that folds the whole state: one tile, or two
+// 64-column halves.
+template <int NK, int NV, bool VG>
+using GRcWholeSmem = typename std::conditional<gdn_slices<NV>() == 1, GRcSmem<NK, NV, VG>, GRcSmem<NK, 64, VG, NV>>::type;
 
 template <int NK, int NV, bool VG>
 union GAutoRcSmem {
@@ -1769,40 +1792,49 @@ union GAutoRcSmem {
   GRcSmem<NK, NV / gdn_slices<NV>(), VG> fl;
 };
 
+// self-scheduling step with a read copy: the flushes fold in column slices, on
+// the non-flush steps' grid, and a requant launch follows. (A whole-state flush
+// here was measured slower: the non-flush steps pay its registers, and on the
+// slice grid the second slice's workgroups would only count in.)
 template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_auto_rc_kernel(GDNArgs a) {
   __shared__ GAutoRcSmem<NK, NV, VG> s;
   const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
-  if (a.meta[p.b].len == kRing - 1) gdn_flush_rc_body<TIN, NK, NV, VG>(a, s.fl);
+  if (a.meta[p.b].len == kRing - 1) gdn_flush_rc_body<TIN, NK, NV, VG, false>(a, s.fl);
   else gdn_nonflush_body<TIN, NK, NV, VG, true>(a, s.nf);
 }
 
 // speculative commit with a read copy, fold part: as gdn_commit_fold_kernel,
-// with the rows of the m committed entries re-solved from the checkpoint
+// with the rows of the m committed entries re-solved from the checkpoint. One
+// work item per state: the new checkpoint and its NVFP4 read copy are written
+// from the same registers.
 template <typename TIN, int NK, int NV, bool VG>
 __global__ __launch_bounds__(kThreads) void gdn_commit_fold_rc_kernel(GDNArgs a) {
-  constexpr int NS = gdn_slices<NV>();
-  constexpr int NVS = NV / NS;
-  __shared__ GRcSmem<NK, NVS, VG> s;
-  const int per = a.nv * NS;
-  const int total = *a.work_count * per;
+  __shared__ GRcWholeSmem<NK, NV, VG> s;
+  const int total = *a.work_count * a.nv;
   float* ckp = static_cast<float*>(a.ck.data);
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
-    const FoldItem it = a.work[item / per];
-    const int r = item - (item / per) * per;
-    const int h = r / NS, half = r - h * NS, c0 = half * NVS, m = it.m;
+    const FoldItem it = a.work[item / a.nv];
+    const int h = item - (item / a.nv) * a.nv, m = it.m;
     const size_t st = static_cast<size_t>(it.b) * a.nv + h;
-    GRcStage<TIN, NK, NV, NVS, VG> stg;
-    stg.load(a, st, it.b, h / a.vpk, c0, it.nck, m, false);
-    GSlice<NK, NV, NVS> raw;
-    raw.issue(ckp, st, c0);
-    stg.store(s, m, false);
-    __syncthreads();
-    rc_gates_and_gram(s, m);
-    RegTile<4, NK, NVS> S;
-    raw.decode(S);
-    rc_solve_and_fold(S, s, m);
-    GSlice<NK, NV, NVS>::store(ckp, st, c0, S);
+    if constexpr (gdn_slices<NV>() == 1) {
+      GRcStage<TIN, NK, NV, NV, VG> stg;
+      stg.load(a, st, it.b, h / a.vpk, 0, it.nck, m, false);
+      GSlice<NK, NV, NV> raw;
+      raw.issue(ckp, st, 0);
+      stg.store(s, m, false);
+      __syncthreads();
+      rc_gates_and_gram(s, m);
+      RegTile<4, NK, NV> S;
+      raw.decode(S);
+      rc_solve_and_fold(S, s, m);
+      GSlice<NK, NV, NV>::store(ckp, st, 0, S);
+      tile_store_nvfp4(a.rc, st, S, tile_absmax(S, s.s4));
+    } else {
+      RegTile<4, NK, 64> S[2];
+      rc_fold_whole<TIN, NK, NV, VG>(a, s, st, it.b, h / a.vpk, it.nck, m, false, S, [] {});
+      rc_copy_whole(a, s, st, S);
+    }
     __syncthreads();
   }
 }
@@ -1810,7 +1842,8 @@ __global__ __launch_bounds__(kThreads) void gdn_commit_fold_rc_kernel(GDNArgs a)
 // The NVFP4 read copy of whole states from the fp32 checkpoint, one workgroup
 // per state: every state, or (folded) those of sequences whose buffer is empty
 // and holds no drafts. Bytes identical to the Mamba-2 quantizer's for the same
-// matrix (same tile layout and encoder).
+// matrix (same tile layout and encoder), and to what the folds that write the
+// copy themselves store.
 template <int NK, int NV>
 __global__ __launch_bounds__(kThreads) void gdn_requant_kernel(GDNArgs a, int folded) {
   __shared__ float s4[4];

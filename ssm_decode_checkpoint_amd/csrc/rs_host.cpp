@@ -220,6 +220,17 @@ rs_status gdn_common(const rs_layer* L, const rs_buffers* buf, const rs_inputs* 
   return RS_OK;
 }
 
+GDNLaunch gdn_launch_cfg(const rs_layer* L);
+
+// With a read copy, the self-scheduling step (whose flushes fold in column
+// slices) is followed by the requant of the states it folded.
+rs_status gdn_refresh_copy(const rs_layer* L, const GDNArgs& a, void* st) {
+  if (L->cfg.read_copy != RS_NVFP4) return RS_OK;
+  if (rs_status s = launch_status()) return s;
+  gdn_launch(GDNOp::RequantFolded, a, gdn_launch_cfg(L), st);
+  return RS_OK;
+}
+
 GDNLaunch gdn_launch_cfg(const rs_layer* L) {
   const rs_config& c = L->cfg;
   GDNLaunch l;
@@ -231,16 +242,6 @@ GDNLaunch gdn_launch_cfg(const rs_layer* L) {
   l.ckf = fmt_of(c.ckpt_dtype);
   l.grid = c.batch * c.n_v_heads;
   return l;
-}
-
-// With a read copy, a launch that may fold without writing the copy
-// (self-scheduling step, commit) is followed by the requant of the states it
-// folded.
-rs_status gdn_refresh_copy(const rs_layer* L, const GDNArgs& a, void* st) {
-  if (L->cfg.read_copy != RS_NVFP4) return RS_OK;
-  if (rs_status s = launch_status()) return s;
-  gdn_launch(GDNOp::RequantFolded, a, gdn_launch_cfg(L), st);
-  return RS_OK;
 }
 
 }  // namespace
@@ -379,7 +380,6 @@ static rs_status replay_step(const rs_layer* L, const rs_buffers* buf, const rs_
     if (rs_status s = gdn_common(L, buf, in, y, &a)) return s;
     gdn_launch(kind == StepKind::Flush ? GDNOp::Flush : kind == StepKind::Auto ? GDNOp::Auto : GDNOp::NonFlush, a,
                gdn_launch_cfg(L), st);
-    // (the flush writes the read copy itself; the self-scheduling step is followed by the requant)
     if (kind == StepKind::Auto)
       if (rs_status s = gdn_refresh_copy(L, a, st)) return s;
     return launched();
@@ -651,7 +651,6 @@ static rs_status spec_commit(const rs_layer* L, const rs_buffers* buf, const int
       commit_meta(ca, st);
       if (rs_status s = launch_status()) return s;
       gdn_launch(GDNOp::CommitFold, a, l, st);
-      if (rs_status s = gdn_refresh_copy(L, a, st)) return s;
     }
     return launched();
   }

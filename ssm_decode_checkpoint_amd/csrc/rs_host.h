@@ -152,8 +152,9 @@ struct GDNArgs {
 
 // Requant: the read copy of every state from the checkpoint. RequantFolded:
 // the states of sequences whose buffer is empty and holds no drafts, i.e.
-// those a flush or commit has just folded (an unchanged state requantizes to
-// the same bytes, so the others it also takes cost only time).
+// those a self-scheduling step has just flushed (an unchanged state
+// requantizes to the same bytes, so the others it also takes cost only time).
+// The flush and the commit fold write the copy of what they fold themselves.
 enum class GDNOp { Conv, NonFlush, Flush, Auto, SpecAppend, CommitFold, ConvSpec, Restore, Requant, RequantFolded };
 
 struct GDNLaunch {
