@@ -307,6 +307,21 @@ struct GSliceF {
       for (int i = 0; i < 4; ++i) d.v[k][i] = in ? t[i] : 0.0f;
     }
   }
+  // FP8: the E4M3 values of the codes without the matrix scale (ms), for a
+  // caller that applies it to sums instead.
+  __device__ __forceinline__ void decode_values(RegTile<4, NK, NVS>& d) const {
+    static_assert(CKF == FMT_FP8, "FP8 codes");
+#pragma unroll
+    for (int k = 0; k < TM::PASSES; ++k) {
+      const bool in = (NK % TM::RPP == 0 && TM::RPP <= NK) || RegTile<4, NK, NVS>::row(k) < NK;
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[k], 1.0f, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r[k], 1.0f, true);
+      d.v[k][0] = in ? lo.x : 0.0f;
+      d.v[k][1] = in ? lo.y : 0.0f;
+      d.v[k][2] = in ? hi.x : 0.0f;
+      d.v[k][3] = in ? hi.y : 0.0f;
+    }
+  }
   // Store S (FP8: codes under the matrix scale sc, y = RN(1/sc), which the
   // caller derived from the whole matrix's |max|; the scale itself is the
   // caller's to write).
@@ -529,13 +544,15 @@ __device__ __forceinline__ void gdn_held_sums(const SM& s, int m, int v, float& 
 }
 
 // After the matvec: u_cur[v] = beta (v_cur - gamma S0 k_cur) - hu, stored in
-// U[cur]; returns o[v] = gamma S0 q + ho + kq[cur] u_cur.
+// U[cur]; returns o[v] = gamma S0 q + ho + kq[cur] u_cur. ms: a scale of the
+// matvec's sums (an FP8 matrix scale the matvec left out), else 1.
 template <typename SM>
-__device__ __forceinline__ float gdn_finish_row(SM& s, int m, int v, float hu, float ho) {
+__device__ __forceinline__ float gdn_finish_row(SM& s, int m, int v, float hu, float ho, float ms = 1.0f) {
   const int cur = m - 1;
-  const float u = s.bet * (s.vc[v] - s.gam * s.out[0][v]) - hu;
+  const float sk = ms * s.out[0][v], sq = ms * s.out[1][v];
+  const float u = s.bet * (s.vc[v] - s.gam * sk) - hu;
   s.U[cur][v] = u;
-  return s.gam * s.out[1][v] + ho + s.kq[cur] * u;
+  return s.gam * sq + ho + s.kq[cur] * u;
 }
 
 // S <- S Diag(f) for a [dk][dv] tile: row r (key channel r) times f[r].
@@ -640,17 +657,25 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
     const int v = threadIdx.x;
     float hu = 0.0f, ho = 0.0f;
     if (v < NVS) gdn_held_sums(s, j, v, hu, ho);
+    // FP8: the matvec runs on the codes' values and the one matrix scale goes
+    // on its two sums, not on every element
+    float ms = 1.0f;
     if constexpr (RC && NVS == 64) {
       raw.matvec2(&s.W[0][0], NK, s.redp(), &s.out[0][0]);
     } else {
       RegTile<4, NK, NVS> S;
-      raw.decode(S);
+      if constexpr (!RC && CKF == FMT_FP8) {
+        raw.decode_values(S);
+        ms = raw.ms;
+      } else {
+        raw.decode(S);
+      }
       tile_matvec<2>(S, &s.W[0][0], NK, s.redp(), &s.out[0][0]);
     }
     const int slot = slot_of(nck, len);
     float* ru = static_cast<float*>(a.ru) + (p.st * kRing + slot) * NV + p.c0;
     if (v < NVS) {
-      a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, j, v, hu, ho);
+      a.o[p.st * NV + p.c0 + v] = gdn_finish_row(s, j, v, hu, ho, ms);
       ru[v] = s.U[j - 1][v];
     }
     // append the current record (bit copies); each slice its own v columns
