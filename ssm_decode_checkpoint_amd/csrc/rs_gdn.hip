@@ -625,13 +625,13 @@ __global__ __launch_bounds__(kThreads) void gdn_conv_kernel(GDNArgs a) {
 // ----------------------------------------------------------------------------
 // non-flush step: o from checkpoint + buffer, append (with its u row), no state write
 // ----------------------------------------------------------------------------
-template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF = FMT_F32>
-__device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV / gdn_slices<NV>(), VG>& s) {
-  constexpr int NVS = NV / gdn_slices<NV>();
-  const GPtrs p = gdn_tile<NV, gdn_slices<NV>()>(a);
+template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF = FMT_F32, int NS = gdn_slices<NV>()>
+__device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV / NS, VG>& s) {
+  constexpr int NVS = NV / NS;
+  const GPtrs p = gdn_tile<NV, NS>(a);
   rs_meta* mp = a.meta + p.b;
-  const int wg = p.h * gdn_slices<NV>() + p.half;
-  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * gdn_slices<NV>()) * kArriveStride;
+  const int wg = p.h * NS + p.half;
+  uint32_t* actr = a.arrive + static_cast<size_t>(p.b) * arrive_groups(a.nv * NS) * kArriveStride;
   const int len = mp->len, nd = mp->nd;
   const long long nck = mp->n_ckpt;
   const int errbit = nd != 0 ? RS_ERR_PENDING : (len > kRing - 2 ? RS_ERR_FULL : 0);
@@ -703,13 +703,20 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
       }
     }
   }
-  arr.finish(mp, actr, wg, a.nv * gdn_slices<NV>(), MetaOp::NonFlush, 0, nck, len, nd);
+  arr.finish(mp, actr, wg, a.nv * NS, MetaOp::NonFlush, 0, nck, len, nd);
 }
+
+// Workgroups per state of the non-flush kernel: column slices for fp32 states
+// and their read copies; FP16 / FP8 states are small enough for one workgroup,
+// which then stages the records and forms the dots once.
+template <int NV, bool RC, int CKF>
+constexpr int gdn_nonflush_slices() { return !RC && CKF != FMT_F32 ? 1 : gdn_slices<NV>(); }
 
 template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
-  __shared__ GSmem<NK, NV / gdn_slices<NV>(), VG> s;
-  gdn_nonflush_body<TIN, NK, NV, VG, RC, CKF>(a, s);
+  constexpr int NS = gdn_nonflush_slices<NV, RC, CKF>();
+  __shared__ GSmem<NK, NV / NS, VG> s;
+  gdn_nonflush_body<TIN, NK, NV, VG, RC, CKF, NS>(a, s);
 }
 
 // ----------------------------------------------------------------------------
@@ -2198,7 +2205,7 @@ template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   // replay steps and appends: one workgroup per column slice of each state
   // (the flush of an FP8 checkpoint or with a read copy: one per state)
-  if (op == GDNOp::Flush && (l.rc || l.ckf == FMT_FP8))
+  if ((op == GDNOp::Flush && (l.rc || l.ckf == FMT_FP8)) || (op == GDNOp::NonFlush && !l.rc && l.ckf != FMT_F32))
     l.grid *= 1;
   else if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
            op == GDNOp::ConvSpec)
