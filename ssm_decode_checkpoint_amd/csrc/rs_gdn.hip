@@ -710,7 +710,7 @@ __device__ __forceinline__ void gdn_nonflush_body(const GDNArgs& a, GSmem<NK, NV
 // and their read copies; FP16 / FP8 states are small enough for one workgroup,
 // which then stages the records and forms the dots once.
 template <int NV, bool RC, int CKF>
-constexpr int gdn_nonflush_slices() { return !RC && CKF != FMT_F32 ? 1 : gdn_slices<NV>(); }
+constexpr int gdn_nonflush_slices() { return RC || CKF != FMT_F32 ? 1 : gdn_slices<NV>(); }
 
 template <typename TIN, int NK, int NV, bool VG, bool RC, int CKF = FMT_F32>
 __global__ __launch_bounds__(kThreads) void gdn_nonflush_kernel(GDNArgs a) {
@@ -2205,7 +2205,7 @@ template <int NK, int NV>
 void gdn_launch_shape(GDNOp op, const GDNArgs& a, GDNLaunch l, hipStream_t st) {
   // replay steps and appends: one workgroup per column slice of each state
   // (the flush of an FP8 checkpoint or with a read copy: one per state)
-  if ((op == GDNOp::Flush && (l.rc || l.ckf == FMT_FP8)) || (op == GDNOp::NonFlush && !l.rc && l.ckf != FMT_F32))
+  if ((op == GDNOp::Flush && (l.rc || l.ckf == FMT_FP8)) || (op == GDNOp::NonFlush && (l.rc || l.ckf != FMT_F32)))
     l.grid *= 1;
   else if (op == GDNOp::NonFlush || op == GDNOp::Flush || op == GDNOp::Auto || op == GDNOp::SpecAppend ||
            op == GDNOp::ConvSpec)
