@@ -1118,6 +1118,41 @@ def bench_copy(args, torch, rs):
                                  "gbs_by_write_bytes": writes}}
 
 
+# legs the default run times after the headline, and the figures of each that its line carries
+OTHER_LEGS = ("gdn", "kda", "spec", "gdn_spec", "kda_spec", "lowprec")
+SUMMARY_KEYS = ("value", "unit", "speedup_vs_conventional", "speedup_vs_snapshot", "roofline.frac",
+                "replay.nonflush_avg_ms", "replay.flush_ms", "replay.append_ms", "read_copy.tokens_per_s",
+                "read_copy.speedup_vs_fp32_replay", "lowprec_checkpoints.f16.tokens_per_s",
+                "lowprec_checkpoints.fp8.tokens_per_s")
+
+
+def leg_summary(out: dict) -> dict:
+    """The figures of one leg's output that the headline line repeats."""
+    summ = {"workload": out.get("config", {}).get("workload")}
+    for key in SUMMARY_KEYS:
+        v = out
+        for part in key.split("."):
+            v = v.get(part) if isinstance(v, dict) else None
+        if v is not None:
+            summ[key] = v
+    for name, var in out.get("variants", {}).items():
+        summ[f"variants.{name}.tokens_per_s"] = var.get("tokens_per_s")
+    return summ
+
+
+def other_workloads(args, torch, fns, rs) -> dict:
+    """Run the other layers' legs (Gated DeltaNet, KDA, speculative, low precision) after the
+    headline, with the same step counts, and return a summary of each."""
+    res = {}
+    for wl in OTHER_LEGS:
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        res[wl] = leg_summary(fns[wl](args, torch, rs))
+        res[wl]["wall_s"] = round(time.time() - t0, 1)
+        print(f"bench: {wl} leg done in {res[wl]['wall_s']} s", file=sys.stderr, flush=True)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1127,7 +1162,10 @@ def main():
     ap.add_argument("--workload", action="append",
                     choices=["mamba2", "gdn", "kda", "spec", "gdn_spec", "kda_spec", "lowprec", "copy", "sweep",
                              "serve", "block"],
-                    help="workloads to run (default: mamba2 only); repeat for several")
+                    help="workloads to run, one JSON line each; repeat for several (default: mamba2, whose line "
+                         "also summarises the gdn, kda, spec, gdn_spec, kda_spec and lowprec legs)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="default run: skip the other layers' legs that the headline line summarises")
     ap.add_argument("--spec-rounds", type=int, default=64)
     ap.add_argument("--lowprec-error-steps", type=int, default=0)
     ap.add_argument("--lowprec-error-seqs", type=int, default=2)
@@ -1149,19 +1187,21 @@ def main():
     import torch
     import ssm_decode_checkpoint_amd as rs
     torch.cuda.set_device(0)
+    fns = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
+           "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve, "block": bench_block,
+           "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
+           "kda_spec": lambda a, t, r: bench_gdn_spec(a, t, r,
+                                                      W.KDA_B256.with_(name="kda_spec_b256", max_draft=4)),
+           "copy": bench_copy}
     for wl in wls:
-        fn = {"mamba2": bench_mamba2, "gdn": bench_gdn, "spec": bench_spec, "lowprec": bench_lowprec,
-              "sweep": bench_sweep, "gdn_spec": bench_gdn_spec, "serve": bench_serve, "block": bench_block,
-              "kda": lambda a, t, r: bench_gdn(a, t, r, W.KDA_B256),
-              "kda_spec": lambda a, t, r: bench_gdn_spec(a, t, r,
-                                                         W.KDA_B256.with_(name="kda_spec_b256", max_draft=4)),
-              "copy": bench_copy}[wl]
-        out = fn(args, torch, rs)
+        out = fns[wl](args, torch, rs)
         if wl in ("gdn", "kda") and args.delta_error_steps:
             out["read_copy_error_over_length"] = delta_readcopy_error(args, torch, rs,
                                                                       W.GDN_QWEN if wl == "gdn" else W.KDA_B256)
         if wl == "mamba2":
             out["cpu_baseline"] = cpu
+            if args.workload is None and not args.headline_only:
+                out["other_workloads"] = other_workloads(args, torch, fns, rs)
         print(json.dumps(out), flush=True)
         torch.cuda.empty_cache()
 
